@@ -1,0 +1,354 @@
+"""CPU oracle for the DeepSeek-V4 compressed attention core (CSA / HCA layers).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module; the HIP library never
+does, and this module imports nothing from it.
+
+Plain float64 numpy, one query at a time, in the order the pages state the
+layer.  Stored intermediates (rotated queries, pooled entries, window rows and
+the layer output) are rounded to the storage dtype with round-to-nearest-even
+where the layer stores them; ``dtype="f64"`` turns every rounding off (used by
+the invariance pins).
+
+Sources (titles and sections of the pages this follows):
+
+* [HF-doc] Transformers documentation, DeepSeek-V4 model page, sections
+  "Hybrid attention (sec. 2.3)", "Attention mask layout" and "Cache layers".
+* [HF-PR] huggingface/transformers pull request 45616 (DeepSeek-V4 port),
+  commit notes on RoPE apply, the attention sink, stateless compressor /
+  indexer and the output-rope un-rotation comment.
+* [TL] TransformerLens ``deepseek_v4.py`` adapter, ``_compressor_bridge``
+  (compressor and indexer submodule lists).
+* [OV] optimum-intel issue 1748, "What V4-Flash adds vs V3".
+* [MLX] mlx-lm pull request 1797, architecture list.
+
+Readings where the pages are silent (each is also listed in the design doc):
+
+* gate logits are per channel; the pooling softmax runs over the window's
+  tokens separately for every channel;
+* CSA entry w pools tokens [(w-1)m, (w+1)m) (windows of 2m, stride m), HCA
+  entry w pools [wm, (w+1)m); tokens before position 0 do not exist and are
+  left out of the softmax;
+* a pooled entry is rotated at position w*m (parity unpinned by the pages:
+  no printed value fixes it);
+* the indexer score is sum_h w[t,h] * ReLU(rot(q_I[t,h]) . k_I[w]) (the
+  paper's formulas are referenced, not printed: parity unpinned by the pages);
+* top-k ranks by score descending then entry index ascending, -0 == +0, and
+  is emitted in ascending index order padded with -1;
+* softmax scale 1/sqrt(D) on the logits, the sink logit unscaled.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+__all__ = [
+    "round_to", "rope", "pool_entry", "compress", "visible_entries",
+    "window_positions", "index_scores", "topk_select", "attend",
+    "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step",
+]
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage dtype, nearest-even, in one step.
+
+    "bf16": 8 significant bits, exponent range of float32 (subnormal quantum
+    2^-133); "f32": IEEE single; "f64": unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x.copy()
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -125)           # below 2^-126 the quantum stays 2^-133
+    q = np.ldexp(np.round(np.ldexp(x, 8 - e)), e - 8)   # np.round: half to even
+    return np.where(np.abs(q) > _BF16_MAX, np.copysign(np.inf, x), q)
+
+
+def rope(x, pos, rope_dim: int, base: float, sign: int = 1) -> np.ndarray:
+    """Partial interleaved-pair rotary embedding [HF-PR RoPE apply; HF-doc sec. 2.3].
+
+    The last ``rope_dim`` channels of each row, taken as pairs (c, c+1), are a
+    complex number x_c + i x_{c+1} multiplied by exp(i * sign * pos * theta_j),
+    theta_j = base^(-2j/rope_dim) for pair j; other channels pass unchanged.
+    ``pos`` broadcasts against the leading axes of ``x``.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    if rope_dim == 0:
+        return x
+    D = x.shape[-1]
+    j = np.arange(rope_dim // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / rope_dim)
+    ang = sign * np.asarray(pos, dtype=np.float64)[..., None] * theta
+    z = x[..., D - rope_dim::2] + 1j * x[..., D - rope_dim + 1::2]
+    z = z * np.exp(1j * ang)
+    x[..., D - rope_dim::2] = z.real
+    x[..., D - rope_dim + 1::2] = z.imag
+    return x
+
+
+def pool_entry(kv, gate, pos: int, rope_dim: int, base: float,
+               norm_weight=None, eps: float = 1e-6) -> np.ndarray:
+    """One compressed entry from its window's tokens [HF-doc sec. 2.3; TL compressor].
+
+    Learned gated pooling: for every channel, softmax of the gate logits over
+    the window's tokens, then the weighted sum of the kv values.  The
+    compressor's submodules are kv_proj, gate_proj, kv_norm, rotary_emb: after
+    pooling come the optional RMSNorm and the rotation at ``pos``.  Returns
+    float64, unrounded.
+    """
+    kv = np.asarray(kv, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    g = g - g.max(axis=0, keepdims=True)
+    e = np.exp(g)
+    alpha = e / e.sum(axis=0, keepdims=True)
+    pooled = (alpha * kv).sum(axis=0)
+    if norm_weight is not None:
+        pooled = pooled / np.sqrt(np.mean(pooled * pooled) + eps) * np.asarray(norm_weight, np.float64)
+    return rope(pooled, pos, rope_dim, base, +1)
+
+
+def entry_tokens(w: int, ratio: int, overlap: int, p0: int = 0):
+    """Token positions [lo, hi) pooled into entry w (tokens before p0 do not exist)."""
+    return max((w - overlap) * ratio, p0), (w + 1) * ratio
+
+
+def compress(kv, gate, ratio: int, overlap: int, rope_dim: int, base: float, dtype: str,
+             norm_weight=None, eps: float = 1e-6, p0: int = 0) -> np.ndarray:
+    """All entries that close inside a sequence of tokens at positions p0..p0+S-1.
+
+    CSA (overlap=1): entry w covers tokens [(w-1)m, (w+1)m); HCA (overlap=0):
+    [wm, (w+1)m).  Entry w closes at token (w+1)m-1 [HF-doc, attention mask
+    layout: entry w is visible to query t iff w < (t+1)//m].  ``p0`` must be a
+    multiple of ``ratio``; row i of the result is entry p0/ratio + i, rounded
+    to ``dtype`` (the pool is stored).
+    """
+    kv = np.asarray(kv, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    S = kv.shape[0]
+    assert p0 % ratio == 0
+    w0, w1 = p0 // ratio, (p0 + S) // ratio
+    out = np.zeros((w1 - w0, kv.shape[1]))
+    for w in range(w0, w1):
+        lo, hi = entry_tokens(w, ratio, overlap, p0)
+        out[w - w0] = pool_entry(kv[lo - p0:hi - p0], gate[lo - p0:hi - p0], w * ratio,
+                                 rope_dim, base, norm_weight, eps)
+    return round_to(out, dtype)
+
+
+def visible_entries(t: int, ratio: int, p0: int = 0) -> range:
+    """Entries query t may use: w < (t+1)//m [HF-doc, attention mask layout, HCA]."""
+    if ratio == 0:
+        return range(0)
+    return range(p0 // ratio, (t + 1) // ratio)
+
+
+def window_positions(t: int, window: int, p0: int = 0) -> range:
+    """Key positions of the sliding branch for query t: t-W < s <= t [HF-doc, mask layout]."""
+    return range(max(p0, t - window + 1), t + 1)
+
+
+def index_scores(qi_t, wi_t, keys, t: int, rope_dim: int, base: float, dtype: str) -> np.ndarray:
+    """Lightning Indexer scores of query t against pooled indexer keys [HF-doc sec. 2.3 CSA; TL indexer].
+
+    The indexer owns q_b_proj, a scorer with per-head weights_proj and a
+    rotary embedding; its query is rotated at t (stored at the storage dtype)
+    and each head's dot product with a key passes a ReLU before the weighted
+    sum over heads.  ``keys`` are the visible keys, already rotated.
+    """
+    q = round_to(rope(qi_t, t, rope_dim, base, +1), dtype)          # [Hi, Di]
+    dots = q @ np.asarray(keys, dtype=np.float64).T                   # [Hi, n]
+    return (np.asarray(wi_t, np.float64)[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+
+
+def topk_select(scores, k: int, first: int = 0) -> np.ndarray:
+    """Per-query top-k block selection [HF-doc sec. 2.3 CSA and mask layout].
+
+    Candidates are entries first..first+n-1 with the given scores.  If n <= k
+    all are selected; otherwise the k best under (score descending, index
+    ascending).  Emitted ascending, then -1 for every empty slot (the
+    indexer's sentinel passed straight into the mask).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    if n <= k:
+        sel = np.arange(n)
+    else:
+        order = np.lexsort((np.arange(n), -s))
+        sel = np.sort(order[:k])
+    out = np.full(k, -1, dtype=np.int64)
+    out[:len(sel)] = sel + first
+    return out
+
+
+def attend(q_t, t: int, rows, sinks, scale: float, rope_dim: int, base: float,
+           dtype: str) -> np.ndarray:
+    """Attention of query t's heads over one row list (K = V) [HF-doc sec. 2.3; HF-PR].
+
+    Shared K=V MQA: each row is both key and value.  The query is rotated at
+    t; per head the sink logit joins the softmax as one more column with no
+    value (GPT-OSS eager form); the output's rope slice is rotated back at -t
+    (eq. 26 of the paper, per the model page) and stored.
+    """
+    rows = np.asarray(rows, dtype=np.float64)
+    q = round_to(rope(q_t, t, rope_dim, base, +1), dtype)              # [H, D]
+    logits = scale * (q @ rows.T)                                       # [H, n]
+    M = logits.max(axis=1)
+    if sinks is not None:
+        sinks = np.asarray(sinks, dtype=np.float64)
+        M = np.maximum(M, sinks)
+    e = np.exp(logits - M[:, None])
+    Z = e.sum(axis=1)
+    if sinks is not None:
+        Z = Z + np.exp(sinks - M)
+    o = (e @ rows) / Z[:, None]
+    o = rope(o, t, rope_dim, base, -1)
+    return round_to(o, dtype)
+
+
+# ----------------------------------------------------------------------------
+# layer drivers: the steps above in the layer's order, over chosen queries
+
+def _spec_scale(L, scale):
+    return 1.0 / math.sqrt(L.head_dim) if scale is None else scale
+
+
+def _window_rows(kv, L, p0, dtype):
+    S = kv.shape[0]
+    return round_to(rope(kv, np.arange(p0, p0 + S), L.rope_dim, L.rope_theta, +1), dtype)
+
+
+def csa_prefill(L, inp: Dict[str, np.ndarray], queries: Optional[Iterable[int]] = None,
+                p0: int = 0, dtype: Optional[str] = None, scale: Optional[float] = None,
+                norm_weight=None, inorm_weight=None, eps: float = 1e-6):
+    """One sequence of a CSA layer, prefilled from position p0 (inputs float64).
+
+    inp: q [S,H,D], kv [S,D], ckv/cgate [S,D], ikv/igate [S,Di], qi [S,Hi,Di],
+    wi [S,Hi], sinks [H] (or None).  Returns dict with pool, ipool, win (the
+    stored rotated window rows), idx [nq,k] (absolute entry ids) and out
+    [nq,H,D] for the chosen queries (indices into the sequence).
+    """
+    dt = L.dtype if dtype is None else dtype
+    S = inp["q"].shape[0]
+    qs = range(S) if queries is None else list(queries)
+    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, L.rope_theta,
+                    dt, norm_weight, eps, p0)
+    ipool = compress(inp["ikv"], inp["igate"], L.ratio, L.overlap, L.index_rope_dim,
+                     L.rope_theta, dt, inorm_weight, eps, p0)
+    win = _window_rows(inp["kv"], L, p0, dt)
+    w0 = p0 // L.ratio
+    sc_ = _spec_scale(L, scale)
+    idx = np.zeros((len(qs), L.topk), dtype=np.int64)
+    out = np.zeros((len(qs), L.num_heads, L.head_dim))
+    for n, i in enumerate(qs):
+        t = p0 + i
+        vis = visible_entries(t, L.ratio, p0)
+        sc = index_scores(inp["qi"][i], inp["wi"][i], ipool[vis.start - w0:vis.stop - w0], t,
+                          L.index_rope_dim, L.rope_theta, dt)
+        idx[n] = topk_select(sc, L.topk, first=vis.start)
+        wp = window_positions(t, L.window, p0)
+        rows = np.concatenate([win[wp.start - p0:wp.stop - p0],
+                               pool[idx[n][idx[n] >= 0] - w0]])
+        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, L.rope_theta, dt)
+    return {"pool": pool, "ipool": ipool, "win": win, "idx": idx, "out": out}
+
+
+def hca_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None,
+                norm_weight=None, eps: float = 1e-6):
+    """One sequence of an HCA layer: every visible entry plus the window [HF-doc sec. 2.3 HCA]."""
+    dt = L.dtype if dtype is None else dtype
+    S = inp["q"].shape[0]
+    qs = range(S) if queries is None else list(queries)
+    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, L.rope_theta,
+                    dt, norm_weight, eps, p0)
+    win = _window_rows(inp["kv"], L, p0, dt)
+    w0 = p0 // L.ratio
+    sc_ = _spec_scale(L, scale)
+    out = np.zeros((len(qs), L.num_heads, L.head_dim))
+    for n, i in enumerate(qs):
+        t = p0 + i
+        vis = visible_entries(t, L.ratio, p0)
+        wp = window_positions(t, L.window, p0)
+        rows = np.concatenate([win[wp.start - p0:wp.stop - p0], pool[vis.start - w0:vis.stop - w0]])
+        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, L.rope_theta, dt)
+    return {"pool": pool, "win": win, "out": out}
+
+
+def sliding_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None):
+    """Sliding-only layer: the window branch alone [HF-doc sec. 2.3, sliding_attention]."""
+    dt = L.dtype if dtype is None else dtype
+    S = inp["q"].shape[0]
+    qs = range(S) if queries is None else list(queries)
+    win = _window_rows(inp["kv"], L, p0, dt)
+    sc_ = _spec_scale(L, scale)
+    out = np.zeros((len(qs), L.num_heads, L.head_dim))
+    for n, i in enumerate(qs):
+        t = p0 + i
+        wp = window_positions(t, L.window, p0)
+        out[n] = attend(inp["q"][i], t, win[wp.start - p0:wp.stop - p0], inp["sinks"], sc_,
+                        L.rope_dim, L.rope_theta, dt)
+    return {"win": win, "out": out}
+
+
+def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarray],
+                dtype=None, scale=None, norm_weight=None, inorm_weight=None, eps=1e-6):
+    """One new token at position t of one sequence, against its caches.
+
+    new: q [H,D], kv [D], ckv/cgate [D], ikv/igate [Di], qi [Hi,Di], wi [Hi],
+    sinks.  cache: win [W,D] (rotated rows of positions t-W..t-1 at slot
+    position mod W), pool [P,D], ipool [P,Di] (entries 0..P-1), and the raw
+    compressor tokens of the positions before t (cstate_* / istate_*, slot
+    position mod (1+overlap)m).  P = t // m: the entries closed before t.  The caches are updated the way the layer's
+    cache would be [HF-doc, cache layers; HF-PR stateless compressor]: the
+    window gains row t, and an entry closes when (t+1) % m == 0.  Returns
+    idx (CSA), out [H,D], and the new entries (if any).
+    """
+    dt = L.dtype if dtype is None else dtype
+    W = L.window
+    res = {}
+    win = np.array(cache["win"], dtype=np.float64, copy=True)
+    cap = win.shape[0]
+    win[t % cap] = round_to(rope(new["kv"], t, L.rope_dim, L.rope_theta, +1), dt)
+    wrows = np.stack([win[s % cap] for s in window_positions(t, W)])
+    rows = [wrows]
+    if L.ratio > 0:
+        m, ov = L.ratio, L.overlap
+        Ls = (1 + ov) * m
+        streams = [("pool", "ckv", "cgate", "cstate_kv", "cstate_gate", L.rope_dim, norm_weight)]
+        if L.has_indexer:
+            streams.append(("ipool", "ikv", "igate", "istate_kv", "istate_gate",
+                            L.index_rope_dim, inorm_weight))
+        pools = {}
+        for pk, kk, gk, sk, sg, rd, nw in streams:
+            pool = np.asarray(cache[pk], dtype=np.float64)
+            if (t + 1) % m == 0:
+                w = (t + 1) // m - 1
+                lo, hi = entry_tokens(w, m, ov)
+                toks = list(range(lo, hi))
+                kvs = np.stack([new[kk] if s == t else cache[sk][s % Ls] for s in toks])
+                gts = np.stack([new[gk] if s == t else cache[sg][s % Ls] for s in toks])
+                ent = round_to(pool_entry(kvs, gts, w * m, rd, L.rope_theta, nw, eps), dt)
+                assert pool.shape[0] == w, "cache must hold the entries closed before t"
+                pool = np.concatenate([pool, ent[None]])
+                res["new_" + pk] = ent
+            pools[pk] = pool
+        vis = visible_entries(t, m)
+        if L.has_indexer:
+            sc = index_scores(new["qi"], new["wi"], pools["ipool"][vis.start:vis.stop], t,
+                              L.index_rope_dim, L.rope_theta, dt)
+            idx = topk_select(sc, L.topk, first=vis.start)
+            res["idx"] = idx
+            rows.append(pools["pool"][idx[idx >= 0]])
+        else:
+            rows.append(pools["pool"][vis.start:vis.stop])
+    rows = np.concatenate(rows)
+    res["out"] = attend(new["q"], t, rows, new["sinks"], _spec_scale(L, scale), L.rope_dim,
+                        L.rope_theta, dt)
+    return res

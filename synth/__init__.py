@@ -1,0 +1,293 @@
+"""Seeded synthetic inputs for the compressed-attention layer workloads.
+
+This module only draws random numbers and stores them in the layer's storage
+dtype.  It holds none of the layer's arithmetic: RoPE, pooling, scoring,
+selection and attention live in ``oracle/`` (CPU definition) and in the HIP
+library, and neither of those is imported here.
+
+Every tensor is drawn from ``numpy.random.default_rng([seed, tensor_id, b])``
+(PCG64) as float32 normals, scaled, and rounded to bfloat16 with
+round-to-nearest-even when the workload is bf16.  Seeding per (tensor,
+sequence) lets a test regenerate one sequence of a large decode cache without
+drawing the whole batch.  bf16 tensors are returned as ``uint16`` bit patterns;
+``bf16_bits_to_f32`` / ``to_f64`` decode them exactly.
+
+Workloads (names used by tests and the benchmark):
+
+* ``tiny_csa``      fp32, B=1, S=256, H=8, D=64, R=16, W=32, m=4 overlapping,
+                    indexer 4x32, top-k 16, base 10000.
+* ``csa_prefill``   bf16, B=1, S=8192, H=64, D=512, R=64, W=128, m=4
+                    overlapping, indexer 64x128, top-k 512, base 160000.
+* ``hca_prefill``   bf16, B=1, S=65536, H=64, D=512, R=64, W=128, m=128,
+                    no indexer, base 160000.
+* ``csa_decode``    bf16, 64 sequences x 1 token at position 131072; caches of
+                    32768 pooled entries, 32768 indexer keys, 128 window rows.
+* ``mixed_decode``  bf16, 4 sequences x 1 token at position 1048576; a CSA layer
+                    (262144 entries), an HCA layer (8192 entries) and a
+                    sliding-only layer (base 10000).
+
+Smaller variants (``scaled``) keep the per-layer shapes and shrink S or the
+context so the CPU oracle finishes in seconds.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+__all__ = [
+    "LayerSpec", "Workload", "WORKLOADS", "workload", "prefill_inputs",
+    "decode_inputs", "bf16_bits_to_f32", "f32_to_bf16_bits", "to_f64",
+    "grid_index_inputs",
+]
+
+# Tensor ids keep streams independent of draw order.
+_TID = {
+    "q": 1, "kv": 2, "ckv": 3, "cgate": 4, "ikv": 5, "igate": 6, "qi": 7,
+    "wi": 8, "sinks": 9, "pool": 10, "ipool": 11, "win": 12, "cstate_kv": 13,
+    "cstate_gate": 14, "istate_kv": 15, "istate_gate": 16, "norm": 17,
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    kind: str                 # "csa" | "hca" | "sliding"
+    dtype: str                # "bf16" | "f32"
+    num_heads: int = 64
+    head_dim: int = 512
+    rope_dim: int = 64
+    rope_theta: float = 160000.0
+    window: int = 128
+    ratio: int = 4            # 0 for sliding-only
+    overlap: int = 1
+    index_heads: int = 64
+    index_dim: int = 128
+    index_rope_dim: int = 64
+    topk: int = 512
+
+    @property
+    def has_indexer(self) -> bool:
+        return self.kind == "csa"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    layers: List[LayerSpec]
+    batch: int
+    n_new: int                # tokens per sequence in this call
+    pos0: int                 # absolute position of the first new token
+    # distribution knobs (standard deviations)
+    q_std: float = 1.0
+    kv_std: float = 1.0
+    qi_std: float = 1.0
+    ikv_std: float = 1.0
+    wi_std: float = 1.0
+    cache_std: float = 1.0
+    sink_std: float = 1.0
+
+    @property
+    def decode(self) -> bool:
+        return self.pos0 > 0
+
+
+def _tiny_layer() -> LayerSpec:
+    return LayerSpec(kind="csa", dtype="f32", num_heads=8, head_dim=64, rope_dim=16,
+                     rope_theta=10000.0, window=32, ratio=4, overlap=1,
+                     index_heads=4, index_dim=32, index_rope_dim=16, topk=16)
+
+
+def _csa_layer(dtype="bf16") -> LayerSpec:
+    return LayerSpec(kind="csa", dtype=dtype)
+
+
+def _hca_layer(dtype="bf16") -> LayerSpec:
+    return LayerSpec(kind="hca", dtype=dtype, ratio=128, overlap=0)
+
+
+def _sliding_layer(dtype="bf16") -> LayerSpec:
+    return LayerSpec(kind="sliding", dtype=dtype, ratio=0, overlap=0, rope_theta=10000.0)
+
+
+def _prefill(name, layer, S, batch=1):
+    D, Di = layer.head_dim, layer.index_dim
+    return Workload(name=name, layers=[layer], batch=batch, n_new=S, pos0=0,
+                    q_std=1 / math.sqrt(D), kv_std=1 / math.sqrt(D),
+                    qi_std=1 / math.sqrt(Di), ikv_std=1 / math.sqrt(Di),
+                    wi_std=1 / math.sqrt(layer.index_heads), cache_std=1.0)
+
+
+def _decode(name, layers, batch, pos):
+    D, Di = 512, 128
+    return Workload(name=name, layers=layers, batch=batch, n_new=1, pos0=pos,
+                    q_std=1 / math.sqrt(D), kv_std=1 / math.sqrt(D),
+                    qi_std=1 / math.sqrt(Di), ikv_std=1 / math.sqrt(Di),
+                    wi_std=1 / 8, cache_std=1.0)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_csa": dataclasses.replace(
+        _prefill("tiny_csa", _tiny_layer(), 256), q_std=1 / 8, kv_std=1 / 8,
+        qi_std=1 / math.sqrt(32), ikv_std=1 / math.sqrt(32), wi_std=0.5),
+    "csa_prefill": dataclasses.replace(_prefill("csa_prefill", _csa_layer(), 8192), wi_std=1 / 8),
+    "hca_prefill": _prefill("hca_prefill", _hca_layer(), 65536),
+    "csa_decode": _decode("csa_decode", [_csa_layer()], 64, 131072),
+    "mixed_decode": _decode("mixed_decode", [_csa_layer(), _hca_layer(), _sliding_layer()],
+                            4, 1048576),
+}
+
+
+def workload(name: str, *, S: Optional[int] = None, batch: Optional[int] = None,
+             pos0: Optional[int] = None, variant: str = "plain") -> Workload:
+    """A named workload, optionally rescaled.
+
+    ``variant``: ``"plain"`` (the stated distributions) or ``"peaked"`` (q and
+    window/compressor kv drawn at unit scale and sinks at 4x, so that logits
+    spread over several units and softmax weights are far from uniform).
+    """
+    w = WORKLOADS[name]
+    kw = {}
+    if S is not None:
+        kw["n_new"] = S
+    if batch is not None:
+        kw["batch"] = batch
+    if pos0 is not None:
+        kw["pos0"] = pos0
+    if variant == "peaked":
+        kw.update(q_std=1.0, kv_std=1.0 if w.layers[0].dtype == "bf16" else 0.5,
+                  sink_std=4.0)
+    elif variant != "plain":
+        raise ValueError(variant)
+    return dataclasses.replace(w, **kw) if kw else w
+
+
+# ----------------------------------------------------------------------------
+# storage conversions (no layer arithmetic)
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact decode of a stored tensor (uint16 = bf16 bits, else float) to float64."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def _draw(seed: int, name: str, b: int, shape, std: float, dtype: str) -> np.ndarray:
+    rng = np.random.default_rng([seed, _TID[name], b])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def _stack(seed, name, batch, shape, std, dtype):
+    return np.stack([_draw(seed, name, b, shape, std, dtype) for b in range(batch)])
+
+
+def prefill_inputs(w: Workload, seed: int = 0, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of one prefill call of ``w.n_new`` tokens per sequence.
+
+    Keys: q [B,S,H,D]; kv [B,S,D] (window stream, un-rotated); ckv, cgate
+    [B,S,D] (compressor stream and per-channel gate logits); ikv, igate
+    [B,S,D_I]; qi [B,S,H_I,D_I] (un-rotated); wi [B,S,H_I]; sinks [H] float32.
+    """
+    L = w.layers[layer]
+    B, S, H, D = w.batch, w.n_new, L.num_heads, L.head_dim
+    dt = L.dtype
+    s = seed * 16 + layer
+    out = {
+        "q": _stack(s, "q", B, (S, H, D), w.q_std, dt),
+        "kv": _stack(s, "kv", B, (S, D), w.kv_std, dt),
+        "sinks": _draw(s, "sinks", 0, (H,), w.sink_std, "f32"),
+    }
+    if L.ratio > 0:
+        out["ckv"] = _stack(s, "ckv", B, (S, D), w.kv_std, dt)
+        out["cgate"] = _stack(s, "cgate", B, (S, D), 1.0, dt)
+    if L.has_indexer:
+        Hi, Di = L.index_heads, L.index_dim
+        out["ikv"] = _stack(s, "ikv", B, (S, Di), w.ikv_std, dt)
+        out["igate"] = _stack(s, "igate", B, (S, Di), 1.0, dt)
+        out["qi"] = _stack(s, "qi", B, (S, Hi, Di), w.qi_std, dt)
+        out["wi"] = _stack(s, "wi", B, (S, Hi), w.wi_std, dt)
+    return out
+
+
+def decode_cache_seq(w: Workload, seed: int, layer: int, b: int) -> Dict[str, np.ndarray]:
+    """Cache contents of one sequence for a decode workload.
+
+    pool [P,D] and ipool [P,D_I] hold rotated pooled entries 0..P-1 with
+    P = pos0//m (the entries closed before the new token); win [W,D] holds rotated window rows for positions
+    pos0-W .. pos0-1 at ring slot (position mod W); cstate_* / istate_* hold
+    the raw compressor tokens of the (1+overlap)*m positions before pos0 at
+    slot (position mod (1+overlap)*m).
+    """
+    L = w.layers[layer]
+    s = seed * 16 + layer
+    D, dt, std = L.head_dim, L.dtype, w.cache_std
+    out = {"win": _draw(s, "win", b, (L.window, D), std, dt)}
+    if L.ratio > 0:
+        P = w.pos0 // L.ratio
+        Ls = (1 + L.overlap) * L.ratio
+        out["pool"] = _draw(s, "pool", b, (P, D), std, dt)
+        out["cstate_kv"] = _draw(s, "cstate_kv", b, (Ls, D), w.kv_std, dt)
+        out["cstate_gate"] = _draw(s, "cstate_gate", b, (Ls, D), 1.0, dt)
+        if L.has_indexer:
+            Di = L.index_dim
+            out["ipool"] = _draw(s, "ipool", b, (P, Di), std, dt)
+            out["istate_kv"] = _draw(s, "istate_kv", b, (Ls, Di), w.ikv_std, dt)
+            out["istate_gate"] = _draw(s, "istate_gate", b, (Ls, Di), 1.0, dt)
+    return out
+
+
+def decode_inputs(w: Workload, seed: int = 0, layer: int = 0,
+                  seqs: Optional[List[int]] = None) -> Dict[str, np.ndarray]:
+    """New-token inputs (prefill_inputs with S=1) plus per-sequence caches.
+
+    ``seqs`` restricts the cache draw to those sequences (the new-token
+    tensors always cover the whole batch); cache arrays are then stacked in
+    the order of ``seqs``.
+    """
+    assert w.n_new == 1
+    out = prefill_inputs(w, seed, layer)
+    seqs = list(range(w.batch)) if seqs is None else list(seqs)
+    caches = [decode_cache_seq(w, seed, layer, b) for b in seqs]
+    for k in caches[0]:
+        out[k] = np.stack([c[k] for c in caches])
+    return out
+
+
+def grid_index_inputs(n_q: int, pool: int, Hi: int, Di: int, Ri: int, seed: int = 0,
+                      distinct_rows: int = 0):
+    """Indexer inputs on exact grids: q, k in (1/8)Z and w in (1/4)Z, all in [-1, 1].
+
+    The rope channels of the keys are zero, so the rotated query's rope part
+    never contributes.  Every product, ReLU, weighted sum and partial sum of
+    the index score is then an exact float32 value whatever the summation
+    order, so any correct implementation selects bit-identical top-k sets.
+    ``distinct_rows`` > 0 builds the keys from that many distinct rows
+    (repeated at random), so equal scores occur between different entries and
+    the lowest-index tie-break decides.  Returns float32 arrays (all values
+    exact in bf16).
+    """
+    rng = np.random.default_rng([seed, 99])
+    q = rng.integers(-8, 9, size=(n_q, Hi, Di)).astype(np.float32) / 8
+    k = rng.integers(-8, 9, size=(pool, Di)).astype(np.float32) / 8
+    if distinct_rows > 0:
+        k = k[rng.integers(0, distinct_rows, size=pool)]
+    k[:, Di - Ri:] = 0
+    wt = rng.integers(-4, 5, size=(n_q, Hi)).astype(np.float32) / 4
+    return q, k, wt

@@ -1,0 +1,74 @@
+"""The pins must catch plausible mistakes: each case plants one in a temporary
+copy of the oracle (on the CPU, never in the repository) and expects the pin
+suite to fail on the mutated copy."""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (file, original text, planted mistake)
+MUTATIONS = {
+    "rope_sign": ("csa_oracle.py", "z = z * np.exp(1j * ang)", "z = z * np.exp(-1j * ang)"),
+    "rope_half_split": ("csa_oracle.py",
+                        "z = x[..., D - rope_dim::2] + 1j * x[..., D - rope_dim + 1::2]",
+                        "z = x[..., D - rope_dim:D - rope_dim // 2] + 1j * x[..., D - rope_dim // 2:]"),
+    "rope_freq": ("csa_oracle.py", "theta = base ** (-2.0 * j / rope_dim)",
+                  "theta = base ** (-1.0 * j / rope_dim)"),
+    "pool_axis": ("csa_oracle.py", "alpha = e / e.sum(axis=0, keepdims=True)",
+                  "alpha = e / e.sum(axis=1, keepdims=True)"),
+    "pool_window_edge": ("csa_oracle.py", "return max((w - overlap) * ratio, p0), (w + 1) * ratio",
+                         "return max((w - overlap) * ratio + 1, p0), (w + 1) * ratio"),
+    "pool_rope_pos": ("csa_oracle.py", "w * ratio,\n                                 rope_dim",
+                      "(w + 1) * ratio - 1,\n                                 rope_dim"),
+    "visibility": ("csa_oracle.py", "return range(p0 // ratio, (t + 1) // ratio)",
+                   "return range(p0 // ratio, t // ratio)"),
+    "window_edge": ("csa_oracle.py", "return range(max(p0, t - window + 1), t + 1)",
+                    "return range(max(p0, t - window), t + 1)"),
+    "relu_place": ("csa_oracle.py",
+                   "return (np.asarray(wi_t, np.float64)[:, None] * np.maximum(dots, 0.0)).sum(axis=0)",
+                   "return np.maximum(np.asarray(wi_t, np.float64)[:, None] * dots, 0.0).sum(axis=0)"),
+    "tie_break": ("csa_oracle.py", "order = np.lexsort((np.arange(n), -s))",
+                  "order = np.lexsort((-np.arange(n), -s))"),
+    "sink_dropped": ("csa_oracle.py", "Z = Z + np.exp(sinks - M)", "Z = Z + 0.0 * np.exp(sinks - M)"),
+    "no_unrotate": ("csa_oracle.py", "o = rope(o, t, rope_dim, base, -1)",
+                    "o = rope(o, t, rope_dim, base, +1)"),
+    "query_unrotated": ("csa_oracle.py", "q = round_to(rope(q_t, t, rope_dim, base, +1), dtype)",
+                        "q = round_to(np.asarray(q_t, np.float64), dtype)"),
+    "round_bits": ("csa_oracle.py", "q = np.ldexp(np.round(np.ldexp(x, 8 - e)), e - 8)",
+                   "q = np.ldexp(np.round(np.ldexp(x, 9 - e)), e - 9)"),
+    "round_double": ("csa_oracle.py", "_, e = np.frexp(x)",
+                     "x = x.astype(np.float32).astype(np.float64)\n    _, e = np.frexp(x)"),
+}
+
+
+def _run_mutant(name, tmp_root):
+    fname, old, new = MUTATIONS[name]
+    d = os.path.join(tmp_root, name)
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"))
+    shutil.copytree(os.path.join(ROOT, "synth"), os.path.join(d, "synth"))
+    os.makedirs(os.path.join(d, "tests"))
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(d, "tests", "golden"))
+    shutil.copy(os.path.join(ROOT, "tests", "test_oracle_pins.py"), os.path.join(d, "tests"))
+    shutil.copy(os.path.join(ROOT, "tests", "conftest.py"), os.path.join(d, "tests"))
+    path = os.path.join(d, "oracle", fname)
+    src = open(path).read()
+    assert src.count(old) == 1, f"mutation {name} does not match the oracle source"
+    open(path, "w").write(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(d, "tests", "test_oracle_pins.py")],
+                       cwd=d, capture_output=True, text=True, timeout=300)
+    return r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    names = sorted(MUTATIONS)
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        codes = dict(zip(names, ex.map(lambda n: _run_mutant(n, str(tmp_path)), names)))
+    # exit code 1 means tests ran and at least one failed (not a collection error)
+    survivors = [n for n, c in codes.items() if c != 1]
+    assert not survivors, f"mutations not caught by a failing pin: {survivors} {codes}"
