@@ -1,0 +1,224 @@
+/*
+ * csa.h -- C ABI of the compressed attention core of a DeepSeek-V4 layer
+ * (CSA: compressed sparse attention; HCA: heavily compressed attention;
+ * sliding-only layers), for AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the Transformers documentation page for DeepSeek-V4,
+ * section "Hybrid attention (sec. 2.3)": every attention block has one
+ * shared K=V head (multi-query attention, the same tensor is key and value),
+ * partial interleaved-pair RoPE on the last qk_rope_head_dim channels, the
+ * same rotation at -t applied to the output's rope slice, a learnable sink
+ * logit per head, and a sliding window branch whose rows are concatenated
+ * with the compressor's rows before one softmax.  CSA layers pool the K=V
+ * stream at ratio m (overlapping windows) and a Lightning Indexer picks the
+ * top-k pooled entries per query; HCA layers pool at ratio m' (no overlap)
+ * and attend to every closed entry.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is DEVICE memory owned by the caller.  The library
+ *    allocates nothing and keeps no mutable global state; calls on different
+ *    streams may run concurrently when their buffers do not overlap.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Argument errors are returned before any launch and leave all
+ *    buffers untouched.  A failed launch returns CSA_ERR_HIP; a device fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Tensors are dense, row-major, with the shapes written next to each
+ *    argument.  "dtype" means the layer's storage dtype (csa_layer.dtype):
+ *    IEEE float32 or bfloat16.  Sinks, norm weights and scores are float32;
+ *    positions are int64; top-k indices are int32.
+ *  - A call covers `batch` sequences with `n_new` new tokens each.  Token i of
+ *    sequence b sits at absolute position t = pos0[b] + i.  n_new == 1 is a
+ *    decode step; the library picks its kernels from the sizes, both sides
+ *    compute the same function.
+ *  - Pooled entry w of a layer with ratio m closes at token (w+1)m-1 and is
+ *    visible to query t iff w < (t+1)/m (integer division).  Window rows of
+ *    query t are the positions t-W+1 .. t that are >= 0.
+ *  - Every rounding to a bf16 or float32 store is round-to-nearest-even.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  CSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range               */
+  CSA_ERR_DTYPE = 3,       /* unknown storage dtype                            */
+  CSA_ERR_UNSUPPORTED = 4, /* valid request this library does not implement    */
+  CSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
+  CSA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed       */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+/* One attention layer.  Field names follow the model configuration fields the
+ * DeepSeek-V4 pages name (head_dim, qk_rope_head_dim via partial_rotary_factor,
+ * sliding_window, compress ratios, index_topk, index_head_dim). */
+typedef struct {
+  int32_t dtype;            /* csa_dtype of every stored tensor                */
+  int32_t num_heads;        /* H query heads; one shared K=V head              */
+  int32_t head_dim;         /* D, even                                         */
+  int32_t qk_rope_head_dim; /* R: last R channels rotate in pairs; even, <= D  */
+  double rope_theta;        /* RoPE base of this layer (compressed layers use
+                               the slower compressed base)                     */
+  int32_t sliding_window;   /* W >= 1                                          */
+  int32_t compress_ratio;   /* m: 4 for CSA, 128 for HCA, 0 = sliding-only     */
+  int32_t overlap;          /* 1: windows of 2m tokens at stride m (CSA);
+                               0: windows of m tokens (HCA)                    */
+  int32_t index_n_heads;    /* H_I (CSA only)                                  */
+  int32_t index_head_dim;   /* D_I (CSA only), even                            */
+  int32_t index_rope_dim;   /* R_I: rope channels of the indexer (<= D_I)      */
+  int32_t index_topk;       /* k entries selected per query, 1..4096           */
+  float softmax_scale;      /* logit scale; 0 selects 1/sqrt(head_dim).  The
+                               sink logit is not scaled.                       */
+} csa_layer;
+
+/* Geometry of one call. */
+typedef struct {
+  int32_t batch;            /* B >= 1 sequences                                */
+  int32_t n_new;            /* tokens per sequence in this call, >= 1          */
+  const int64_t* pos0;      /* device [B]: position of each first new token    */
+  int64_t pos0_max;         /* host: an upper bound of every pos0[b] (>= 0),
+                               used to validate capacities                     */
+} csa_batch;
+
+/* Write the window rows of the new tokens into a ring buffer.
+ * Layout and meaning: kv [B, n_new, D] (dtype) holds the un-rotated K=V rows
+ * of the new tokens; each is rotated at its position t (rope on the last R
+ * channels, base rope_theta) and stored at ring[b, t mod cap, :], ring being
+ * [B, cap, D] (dtype).  For a query of this call to find all its window rows,
+ * cap must be >= min(W + n_new - 1, pos0_max + n_new); a linear buffer of a
+ * prefill from position 0 is the case cap >= n_new + pos0_max.
+ * Source: model page, sec. 2.3 (sliding window branch, K=V stored once). */
+csa_status csa_window_append(const csa_layer* layer, const csa_batch* batch,
+                             const void* kv, void* ring, int64_t cap,
+                             hipStream_t stream);
+
+/* Rotate rows in place: x [B, n_new, rows_per_token, width] (dtype); row r of
+ * token i of sequence b is rotated at position sign * (pos0[b] + i) on its
+ * last rope_dim channels, interleaved pairs (c, c+1) as complex numbers,
+ * frequency base^(-2j/rope_dim) for pair j.  sign is +1 or -1.
+ * Source: transformers PR 45616 notes on RoPE apply (interleaved-pair
+ * rotation via complex multiplication) and the model page, sec. 2.3. */
+csa_status csa_rope(const csa_layer* layer, const csa_batch* batch, void* x,
+                    int32_t rows_per_token, int32_t width, int32_t rope_dim,
+                    int32_t sign, hipStream_t stream);
+
+/* KV compressor: learned gated pooling of one stream (the main K=V stream,
+ * width = head_dim and rope_dim = qk_rope_head_dim, or the indexer's key
+ * stream, width = index_head_dim and rope_dim = index_rope_dim).
+ *  kv, gate    [B, n_new, width] dtype: raw rows and per-channel gate logits
+ *              of the new tokens.
+ *  norm_weight [width] float32 or NULL: optional RMSNorm after pooling
+ *              (x / sqrt(mean(x^2) + norm_eps) * weight).
+ *  state_kv, state_gate [B, (1+overlap)*m, width] dtype: the caller-owned
+ *              compressor state, raw tokens of position p at slot
+ *              p mod ((1+overlap)*m); zero-fill before a sequence starts,
+ *              then pass unchanged between calls.  Updated by this call.
+ *  pool        [B, pool_cap, width] dtype: entry w at row w.  Every entry
+ *              closing in this call, w in [pos0/m, (pos0+n_new)/m), is
+ *              written: per channel, softmax over the entry's tokens of the
+ *              gate logits weights the kv values; then RMSNorm if given; then
+ *              rotation at position w*m.  Entry w pools tokens
+ *              [(w-overlap)*m, (w+1)*m) that are >= 0.  Rows of entries that
+ *              do not close are left untouched; a call in which no entry
+ *              closes writes only the state and returns CSA_OK.
+ *  Requires m >= 1, pool_cap >= (pos0_max + n_new)/m.
+ * Source: model page, sec. 2.3 (CSA overlapping windows, HCA non-overlapping)
+ * and "Cache layers" (buffer, pool, counter, overlap state);
+ * TransformerLens adapter, compressor submodules kv_proj, gate_proj,
+ * kv_norm, rotary_emb; transformers PR 45616 (stateless compressor, state
+ * in the cache, always returns a possibly empty tensor). */
+csa_status csa_compress(const csa_layer* layer, const csa_batch* batch,
+                        int32_t width, int32_t rope_dim, const void* kv,
+                        const void* gate, const float* norm_weight,
+                        float norm_eps, void* state_kv, void* state_gate,
+                        void* pool, int64_t pool_cap, hipStream_t stream);
+
+/* Lightning Indexer and per-query top-k (CSA layers).
+ *  q_idx    [B, n_new, H_I, D_I] dtype: indexer queries, un-rotated (rotated
+ *           here at t on their last R_I channels, stored at dtype).
+ *  weights  [B, n_new, H_I] dtype: per-head weights of the scorer.
+ *  k_pool   [B, pool_cap, D_I] dtype: pooled indexer keys (csa_compress
+ *           output of the indexer stream, rotated).
+ *  score(t, w) = sum_h weights[t,h] * ReLU(rot(q_idx[t,h]) . k_pool[w]) for
+ *           every visible w < (t+1)/m, accumulated in float32.
+ *  topk_idx [B, n_new, index_topk] int32 out: the index_topk visible entries
+ *           of highest score, ties to the lower entry id, -0 == +0; emitted in
+ *           ascending entry order and padded with -1 when fewer are visible.
+ *  scores_out [B, n_new, pool_cap] float32 or NULL: the scores of the visible
+ *           entries (other columns untouched), for inspection.
+ *  workspace of at least csa_workspace_bytes(layer, B, n_new, pool_cap,
+ *           CSA_OP_INDEX_TOPK) bytes.  Scores must be finite.
+ * Source: model page, sec. 2.3 (Lightning Indexer scores queries against the
+ * pool and gathers the top index_topk blocks per query) and "Attention mask
+ * layout" (the -1 sentinel); TransformerLens adapter (indexer q_b_proj,
+ * scorer.weights_proj, rotary_emb). */
+csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch,
+                          const void* q_idx, const void* weights,
+                          const void* k_pool, int64_t pool_cap,
+                          int32_t* topk_idx, float* scores_out,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* CSA attention: per query t and head h, one softmax over the window rows of
+ * t (from the ring written by csa_window_append) and the pooled rows listed in
+ * topk_idx[t] (entries < 0 are skipped), plus the sink logit sinks[h]; the
+ * value of every row is the row itself (K = V).
+ *  q      [B, n_new, H, D] dtype, un-rotated (rotated at t, stored at dtype).
+ *  win    [B, win_cap, D] dtype ring (row of position p at slot p mod cap).
+ *  pool   [B, pool_cap, D] dtype rotated pooled rows.
+ *  topk_idx [B, n_new, index_topk] int32.
+ *  sinks  [H] float32 or NULL (no sink).
+ *  out    [B, n_new, H, D] dtype: sum_j p_j row_j, its rope slice rotated at
+ *         -t (eq. 26 on the model page).
+ *  workspace of csa_workspace_bytes(..., CSA_OP_ATTEND) bytes (decode splits).
+ * Source: model page, sec. 2.3 (shared K=V MQA, sliding branch concatenated
+ * with the compressor output before the main attention, sink eq. 27, output
+ * rotation eq. 26) and "Attention mask layout"; transformers PR 45616 (sink
+ * ported from the GPT-OSS eager attention). */
+csa_status csa_attend(const csa_layer* layer, const csa_batch* batch,
+                      const void* q, const void* win, int64_t win_cap,
+                      const void* pool, int64_t pool_cap,
+                      const int32_t* topk_idx, const float* sinks, void* out,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* HCA / sliding-only attention: as csa_attend, but the pooled rows of query t
+ * are every visible entry w < (t+1)/m; compress_ratio == 0 attends to the
+ * window alone.  workspace: csa_workspace_bytes(..., CSA_OP_HCA_ATTEND).
+ * Source: model page, sec. 2.3 (HCA has no indexer, every pool entry takes
+ * part; sliding_attention layers have no long-range branch). */
+csa_status hca_attend(const csa_layer* layer, const csa_batch* batch,
+                      const void* q, const void* win, int64_t win_cap,
+                      const void* pool, int64_t pool_cap, const float* sinks,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
+
+/* Workspace bytes an entry point needs for these sizes (0 if none); the
+ * pointer passed must be 256-byte aligned.  Returns (size_t)-1 for an
+ * invalid layer or op. */
+size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
+                           int64_t pool_cap, int32_t op);
+
+/* Static description of a status code. */
+const char* csa_status_str(csa_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

@@ -1,0 +1,268 @@
+"""Python binding of libcsa, the MI355X compressed-attention core of DeepSeek-V4.
+
+Argument marshalling only: every function checks the torch tensors it is
+given (device, dtype, contiguity, shape), passes their device pointers and
+the current HIP stream to the C entry point of the same name
+(``include/csa.h``), and raises ``RuntimeError`` with the library's status
+string when the call is rejected.  No arithmetic happens here; if the shared
+library is missing the import of a function fails loudly (there is no other
+code path).
+
+Build the library with ``python -m long_context_sparse_gated_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "Layer", "load_library", "library_path", "csa_window_append", "csa_rope", "csa_compress",
+    "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
+    "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+CSA_OP_INDEX_TOPK, CSA_OP_ATTEND, CSA_OP_HCA_ATTEND = 1, 2, 3
+EXPORTED_SYMBOLS = ("csa_window_append", "csa_rope", "csa_compress", "csa_index_topk",
+                    "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
+                    "csa_version")
+
+
+class _CLayer(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("sliding_window", ctypes.c_int32),
+                ("compress_ratio", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("index_n_heads", ctypes.c_int32), ("index_head_dim", ctypes.c_int32),
+                ("index_rope_dim", ctypes.c_int32), ("index_topk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class _CBatch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_new", ctypes.c_int32),
+                ("pos0", ctypes.c_void_p), ("pos0_max", ctypes.c_int64)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    """Mirror of ``csa_layer``; dtype is ``"bf16"`` or ``"f32"``."""
+    dtype: str
+    num_heads: int
+    head_dim: int
+    qk_rope_head_dim: int
+    rope_theta: float
+    sliding_window: int
+    compress_ratio: int
+    overlap: int
+    index_n_heads: int = 0
+    index_head_dim: int = 0
+    index_rope_dim: int = 0
+    index_topk: int = 0
+    softmax_scale: float = 0.0
+
+    @classmethod
+    def from_spec(cls, spec) -> "Layer":
+        """From a ``synth.LayerSpec``-like object (field names of the workloads)."""
+        return cls(dtype=spec.dtype, num_heads=spec.num_heads, head_dim=spec.head_dim,
+                   qk_rope_head_dim=spec.rope_dim, rope_theta=spec.rope_theta,
+                   sliding_window=spec.window, compress_ratio=spec.ratio, overlap=spec.overlap,
+                   index_n_heads=spec.index_heads if spec.kind == "csa" else 0,
+                   index_head_dim=spec.index_dim if spec.kind == "csa" else 0,
+                   index_rope_dim=spec.index_rope_dim if spec.kind == "csa" else 0,
+                   index_topk=spec.topk if spec.kind == "csa" else 0)
+
+    def _c(self) -> _CLayer:
+        return _CLayer(1 if self.dtype == "bf16" else (0 if self.dtype == "f32" else 99),
+                       self.num_heads, self.head_dim, self.qk_rope_head_dim, self.rope_theta,
+                       self.sliding_window, self.compress_ratio, self.overlap,
+                       self.index_n_heads, self.index_head_dim, self.index_rope_dim,
+                       self.index_topk, self.softmax_scale)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libcsa.so")
+
+
+def load_library():
+    """Load libcsa.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m long_context_sparse_gated_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    LP, BP = ctypes.POINTER(_CLayer), ctypes.POINTER(_CBatch)
+    sig = {
+        "csa_window_append": [LP, BP, P, P, I64, P],
+        "csa_rope": [LP, BP, P, I32, I32, I32, I32, P],
+        "csa_compress": [LP, BP, I32, I32, P, P, P, ctypes.c_float, P, P, P, I64, P],
+        "csa_index_topk": [LP, BP, P, P, P, I64, P, P, P, SZ, P],
+        "csa_attend": [LP, BP, P, P, I64, P, I64, P, P, P, P, SZ, P],
+        "hca_attend": [LP, BP, P, P, I64, P, I64, P, P, P, SZ, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.csa_workspace_bytes.argtypes = [LP, I32, I32, I64, I32]
+    lib.csa_workspace_bytes.restype = SZ
+    lib.csa_status_str.argtypes = [ctypes.c_int]
+    lib.csa_status_str.restype = ctypes.c_char_p
+    lib.csa_version.argtypes = []
+    lib.csa_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def csa_status_str(status: int) -> str:
+    return load_library().csa_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise RuntimeError(f"{what}: {csa_status_str(status)}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _store_dtype(layer: Layer):
+    torch = _torch()
+    return torch.bfloat16 if layer.dtype == "bf16" else torch.float32
+
+
+def _batch(pos0, pos0_max, B, n):
+    torch = _torch()
+    _ptr(pos0, "pos0", torch.int64)
+    if pos0.numel() != B:
+        raise ValueError("pos0 must hold one position per sequence")
+    return _CBatch(B, n, pos0.data_ptr(), int(pos0_max))
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def csa_workspace_bytes(layer: Layer, batch: int, n_new: int, pool_cap: int, op: int) -> int:
+    lay = layer._c()
+    n = load_library().csa_workspace_bytes(ctypes.byref(lay), batch, n_new, pool_cap, op)
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError("csa_workspace_bytes: invalid layer or op")
+    return int(n)
+
+
+def _workspace(layer, B, n, pool_cap, op, ws, device):
+    need = csa_workspace_bytes(layer, B, n, pool_cap, op)
+    if ws is None:
+        if need == 0:
+            return None, 0
+        torch = _torch()
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def csa_window_append(layer: Layer, pos0, pos0_max: int, kv, ring):
+    """kv [B, n_new, D] -> ring [B, cap, D] at slot position % cap, rotated."""
+    dt = _store_dtype(layer)
+    B, n, D = kv.shape
+    bt = _batch(pos0, pos0_max, B, n)
+    lay = layer._c()
+    _check(load_library().csa_window_append(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(kv, "kv", dt), _ptr(ring, "ring", dt),
+        ring.shape[1], _stream()), "csa_window_append")
+
+
+def csa_rope(layer: Layer, pos0, pos0_max: int, x, rope_dim: int, sign: int = 1):
+    """x [B, n_new, rows, width] rotated in place at sign * position."""
+    dt = _store_dtype(layer)
+    B, n, rows, width = x.shape
+    bt = _batch(pos0, pos0_max, B, n)
+    lay = layer._c()
+    _check(load_library().csa_rope(ctypes.byref(lay), ctypes.byref(bt), _ptr(x, "x", dt), rows,
+                                   width, rope_dim, sign, _stream()), "csa_rope")
+
+
+def csa_compress(layer: Layer, pos0, pos0_max: int, kv, gate, state_kv, state_gate, pool,
+                 rope_dim: int, norm_weight=None, norm_eps: float = 1e-6):
+    """kv, gate [B, n_new, width]; state_* [B, (1+overlap)m, width]; pool [B, cap, width]."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n, width = kv.shape
+    bt = _batch(pos0, pos0_max, B, n)
+    lay = layer._c()
+    _check(load_library().csa_compress(
+        ctypes.byref(lay), ctypes.byref(bt), width, rope_dim, _ptr(kv, "kv", dt),
+        _ptr(gate, "gate", dt), _ptr(norm_weight, "norm_weight", torch.float32), norm_eps,
+        _ptr(state_kv, "state_kv", dt), _ptr(state_gate, "state_gate", dt),
+        _ptr(pool, "pool", dt), pool.shape[1], _stream()), "csa_compress")
+
+
+def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,
+                   scores_out=None, workspace=None):
+    """q_idx [B,n,H_I,D_I], weights [B,n,H_I], k_pool [B,cap,D_I] -> topk_idx [B,n,k] int32."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n = q_idx.shape[:2]
+    bt = _batch(pos0, pos0_max, B, n)
+    ws, wsb = _workspace(layer, B, n, k_pool.shape[1], CSA_OP_INDEX_TOPK, workspace, q_idx.device)
+    lay = layer._c()
+    _check(load_library().csa_index_topk(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(q_idx, "q_idx", dt), _ptr(weights, "weights", dt),
+        _ptr(k_pool, "k_pool", dt), k_pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(scores_out, "scores_out", torch.float32), _ptr(ws, "workspace"), wsb, _stream()),
+        "csa_index_topk")
+
+
+def csa_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, topk_idx, sinks, out,
+               workspace=None):
+    """q [B,n,H,D], win [B,cap,D], pool [B,pcap,D], topk_idx [B,n,k], sinks [H] -> out."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n = q.shape[:2]
+    bt = _batch(pos0, pos0_max, B, n)
+    ws, wsb = _workspace(layer, B, n, pool.shape[1], CSA_OP_ATTEND, workspace, q.device)
+    lay = layer._c()
+    _check(load_library().csa_attend(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(q, "q", dt), _ptr(win, "win", dt), win.shape[1],
+        _ptr(pool, "pool", dt), pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(sinks, "sinks", torch.float32), _ptr(out, "out", dt), _ptr(ws, "workspace"), wsb,
+        _stream()), "csa_attend")
+
+
+def hca_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, sinks, out, workspace=None):
+    """As csa_attend with every visible entry (compress_ratio 0: window only; pool may be None)."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n = q.shape[:2]
+    bt = _batch(pos0, pos0_max, B, n)
+    pcap = pool.shape[1] if pool is not None else 0
+    ws, wsb = _workspace(layer, B, n, pcap, CSA_OP_HCA_ATTEND, workspace, q.device)
+    lay = layer._c()
+    _check(load_library().hca_attend(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(q, "q", dt), _ptr(win, "win", dt), win.shape[1],
+        _ptr(pool, "pool", dt), pcap, _ptr(sinks, "sinks", torch.float32), _ptr(out, "out", dt),
+        _ptr(ws, "workspace"), wsb, _stream()), "hca_attend")

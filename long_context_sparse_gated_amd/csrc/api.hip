@@ -1,0 +1,237 @@
+// C ABI of libcsa: argument validation, workspace sizing and kernel dispatch.
+// Every check runs on the host before any launch; a rejected call touches no
+// buffer.  See include/csa.h for the contract of each entry point.
+#include <math.h>
+
+#include "csa.h"
+#include "csa_internal.h"
+
+namespace {
+
+using csa::Batch;
+using csa::Layer;
+
+constexpr int kMaxTopk = 4096;
+constexpr int kMaxWidth = 2048;   // compressor row width (LDS row buffer)
+constexpr int64_t kMaxRowId = 2147483000LL;
+
+csa_status to_layer(const csa_layer* in, Layer* L) {
+  if (!in) return CSA_ERR_NULL;
+  if (in->dtype != CSA_F32 && in->dtype != CSA_BF16) return CSA_ERR_DTYPE;
+  if (in->num_heads < 1 || in->head_dim < 2 || (in->head_dim & 1) || in->qk_rope_head_dim < 0 ||
+      (in->qk_rope_head_dim & 1) || in->qk_rope_head_dim > in->head_dim ||
+      in->sliding_window < 1 || in->compress_ratio < 0 || in->overlap < 0 || in->overlap > 1 ||
+      !(in->rope_theta > 0.0) || !isfinite(in->rope_theta) || in->softmax_scale < 0.f ||
+      !isfinite(in->softmax_scale))
+    return CSA_ERR_SHAPE;
+  L->dtype = in->dtype;
+  L->H = in->num_heads;
+  L->D = in->head_dim;
+  L->R = in->qk_rope_head_dim;
+  L->base = in->rope_theta;
+  L->W = in->sliding_window;
+  L->m = in->compress_ratio;
+  L->overlap = in->overlap;
+  L->Hi = in->index_n_heads;
+  L->Di = in->index_head_dim;
+  L->Ri = in->index_rope_dim;
+  L->k = in->index_topk;
+  L->scale = in->softmax_scale > 0.f ? in->softmax_scale : (float)(1.0 / sqrt((double)L->D));
+  return CSA_OK;
+}
+
+csa_status to_batch(const csa_batch* in, Batch* b) {
+  if (!in) return CSA_ERR_NULL;
+  if (!in->pos0) return CSA_ERR_NULL;
+  if (in->batch < 1 || in->n_new < 1 || in->pos0_max < 0 ||
+      in->pos0_max > (int64_t)1 << 48)
+    return CSA_ERR_SHAPE;
+  b->B = in->batch;
+  b->n = in->n_new;
+  b->pos0 = in->pos0;
+  b->pos0_max = in->pos0_max;
+  return CSA_OK;
+}
+
+csa_status indexer_ok(const Layer& L) {
+  if (L.m < 1 || L.Hi < 1 || L.Di < 2 || (L.Di & 1) || L.Ri < 0 || (L.Ri & 1) || L.Ri > L.Di ||
+      L.k < 1 || L.k > kMaxTopk)
+    return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+int64_t entries_needed(const Layer& L, const Batch& b) {
+  return L.m > 0 ? (b.pos0_max + b.n) / L.m : 0;
+}
+
+csa_status window_ok(const Layer& L, const Batch& b, int64_t cap) {
+  if (cap < 1) return CSA_ERR_SHAPE;
+  const int64_t need_a = (int64_t)L.W + b.n - 1, need_b = b.pos0_max + b.n;
+  if (cap < (need_a < need_b ? need_a : need_b)) return CSA_ERR_SHAPE;
+  if ((int64_t)b.B * cap > kMaxRowId) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
+
+size_t generic_attend_limit_ok(const Layer& L) {
+  // float32 LDS copies of q, the accumulator and a 32-row chunk
+  const size_t shm = ((size_t)2 * L.H * L.D + (size_t)32 * L.D + (size_t)L.H * 32 + 3 * L.H + 32) *
+                     sizeof(float);
+  return shm <= 64 * 1024;
+}
+
+bool generic_index_ok(const Layer& L) {
+  return ((size_t)L.Hi * L.Di + L.Hi) * sizeof(float) <= 64 * 1024;
+}
+
+csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const void* q,
+                         const void* win, int64_t win_cap, const void* pool, int64_t pool_cap,
+                         const int32_t* topk_idx, const float* sinks, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, bool csa_layer_kind) {
+  Layer L;
+  Batch b;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if (!q || !win || !out) return CSA_ERR_NULL;
+  if (csa_layer_kind) {
+    if (L.m < 1 || L.k < 1 || L.k > kMaxTopk) return CSA_ERR_SHAPE;
+    if (!topk_idx || !pool) return CSA_ERR_NULL;
+  }
+  if (L.m > 0) {
+    if (!pool) return CSA_ERR_NULL;
+    if (pool_cap < entries_needed(L, b)) return CSA_ERR_SHAPE;
+    if ((int64_t)b.B * pool_cap > kMaxRowId) return CSA_ERR_UNSUPPORTED;
+  }
+  if ((st = window_ok(L, b, win_cap)) != CSA_OK) return st;
+  if (!csa::attend_fast_shape(L) && !generic_attend_limit_ok(L)) return CSA_ERR_UNSUPPORTED;
+  const size_t need = csa::attend_workspace_bytes(L, b.B, b.n, L.m > 0 ? pool_cap : 0,
+                                                  csa_layer_kind);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
+    return CSA_ERR_WORKSPACE;
+  return hip_status(csa::launch_attend(L, b, q, win, win_cap, pool, L.m > 0 ? pool_cap : 0,
+                                       topk_idx, sinks, out, workspace, csa_layer_kind, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status csa_window_append(const csa_layer* layer, const csa_batch* batch, const void* kv,
+                             void* ring, int64_t cap, hipStream_t stream) {
+  Layer L;
+  Batch b;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if (!kv || !ring) return CSA_ERR_NULL;
+  if ((st = window_ok(L, b, cap)) != CSA_OK) return st;
+  return hip_status(csa::launch_window_append(L, b, kv, ring, cap, stream));
+}
+
+csa_status csa_rope(const csa_layer* layer, const csa_batch* batch, void* x,
+                    int32_t rows_per_token, int32_t width, int32_t rope_dim, int32_t sign,
+                    hipStream_t stream) {
+  Layer L;
+  Batch b;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if (!x) return CSA_ERR_NULL;
+  if (rows_per_token < 1 || width < 2 || (width & 1) || rope_dim < 0 || (rope_dim & 1) ||
+      rope_dim > width || (sign != 1 && sign != -1))
+    return CSA_ERR_SHAPE;
+  return hip_status(csa::launch_rope(L, b, x, rows_per_token, width, rope_dim, sign, stream));
+}
+
+csa_status csa_compress(const csa_layer* layer, const csa_batch* batch, int32_t width,
+                        int32_t rope_dim, const void* kv, const void* gate,
+                        const float* norm_weight, float norm_eps, void* state_kv,
+                        void* state_gate, void* pool, int64_t pool_cap, hipStream_t stream) {
+  Layer L;
+  Batch b;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if (!kv || !gate || !state_kv || !state_gate || !pool) return CSA_ERR_NULL;
+  if (L.m < 1) return CSA_ERR_SHAPE;
+  if (width < 2 || (width & 1) || width > kMaxWidth || rope_dim < 0 || (rope_dim & 1) ||
+      rope_dim > width || !(norm_eps >= 0.f))
+    return CSA_ERR_SHAPE;
+  if (pool_cap < entries_needed(L, b)) return CSA_ERR_SHAPE;
+  return hip_status(csa::launch_compress(L, b, width, rope_dim, kv, gate, norm_weight, norm_eps,
+                                         state_kv, state_gate, pool, pool_cap, stream));
+}
+
+csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch, const void* q_idx,
+                          const void* weights, const void* k_pool, int64_t pool_cap,
+                          int32_t* topk_idx, float* scores_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  Layer L;
+  Batch b;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if (!q_idx || !weights || !k_pool || !topk_idx) return CSA_ERR_NULL;
+  if ((st = indexer_ok(L)) != CSA_OK) return st;
+  if (pool_cap < entries_needed(L, b) || pool_cap < 1) return CSA_ERR_SHAPE;
+  if (!(L.dtype == CSA_BF16 && L.Hi == 64 && L.Di == 128) && !generic_index_ok(L))
+    return CSA_ERR_UNSUPPORTED;
+  const size_t need = csa::index_workspace_bytes(L, b.B, b.n, pool_cap);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return CSA_ERR_WORKSPACE;
+  return hip_status(csa::launch_index_topk(L, b, q_idx, weights, k_pool, pool_cap, topk_idx,
+                                           scores_out, workspace, stream));
+}
+
+csa_status csa_attend(const csa_layer* layer, const csa_batch* batch, const void* q,
+                      const void* win, int64_t win_cap, const void* pool, int64_t pool_cap,
+                      const int32_t* topk_idx, const float* sinks, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return attend_common(layer, batch, q, win, win_cap, pool, pool_cap, topk_idx, sinks, out,
+                       workspace, workspace_bytes, stream, true);
+}
+
+csa_status hca_attend(const csa_layer* layer, const csa_batch* batch, const void* q,
+                      const void* win, int64_t win_cap, const void* pool, int64_t pool_cap,
+                      const float* sinks, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return attend_common(layer, batch, q, win, win_cap, pool, pool_cap, nullptr, sinks, out,
+                       workspace, workspace_bytes, stream, false);
+}
+
+size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
+                           int64_t pool_cap, int32_t op) {
+  Layer L;
+  if (to_layer(layer, &L) != CSA_OK || batch < 1 || n_new < 1 || pool_cap < 0) return (size_t)-1;
+  switch (op) {
+    case CSA_OP_INDEX_TOPK:
+      if (indexer_ok(L) != CSA_OK) return (size_t)-1;
+      return csa::index_workspace_bytes(L, batch, n_new, pool_cap);
+    case CSA_OP_ATTEND:
+      if (L.m < 1 || L.k < 1 || L.k > kMaxTopk) return (size_t)-1;
+      return csa::attend_workspace_bytes(L, batch, n_new, pool_cap, true);
+    case CSA_OP_HCA_ATTEND:
+      return csa::attend_workspace_bytes(L, batch, n_new, L.m > 0 ? pool_cap : 0, false);
+    default:
+      return (size_t)-1;
+  }
+}
+
+const char* csa_status_str(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_NULL: return "CSA_ERR_NULL: a required pointer is NULL";
+    case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE: sizes inconsistent or out of range";
+    case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE: unknown storage dtype";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: configuration not implemented";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing, short or misaligned";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP: HIP launch failed";
+  }
+  return "unknown csa_status";
+}
+
+int32_t csa_version(void) { return 100; }
+
+}  // extern "C"

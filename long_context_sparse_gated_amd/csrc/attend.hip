@@ -1,0 +1,501 @@
+// Attention over the sliding window plus compressed rows, K = V, with sink.
+//
+// For query t and head h the row list is the window positions
+// max(0, t-W+1) .. t (ring slot = position mod cap) followed by the pooled
+// rows: the top-k entries of t (CSA) or every visible entry w < (t+1)/m
+// (HCA; none for sliding-only layers).  logits = scale * rot_t(q) . row; one
+// softmax over all rows plus the unscaled sink logit of h; the output is the
+// probability-weighted sum of the same rows, its rope slice rotated at -t
+// [DeepSeek-V4 model page, sec. 2.3: shared K=V MQA, sliding branch
+// concatenated with the compressor rows before the main attention, sink
+// (eq. 27), output rotation (eq. 26); transformers PR 45616: sink from the
+// GPT-OSS eager attention].
+//
+// attend_mfma (H = 64, D = 512, bf16) -- one block per (token, split):
+//  * four waves, 16 heads each; the rotated query of a wave's heads lives in
+//    VGPRs as the B operand of S^T = K Q^T (16 x 16 x 32 bf16 MFMA);
+//  * rows are gathered 32 at a time into LDS twice: row-major (A operand of
+//    K Q^T, 16-byte reads along d) and transposed (A operand of O^T = V^T P^T,
+//    16-byte reads along rows).  The transposed copy is written from an 8 x 8
+//    register transpose during staging, so one HBM/L2 read feeds both uses of
+//    the K = V row;
+//  * S^T puts one head per lane column, so the online softmax state (max,
+//    partial sum) and the O^T accumulators of a lane all belong to one head:
+//    rescaling O is one multiply per accumulator, no cross-lane traffic;
+//  * P is rounded to bf16 for the PV product; accumulation is float32;
+//  * the sink enters once, at the end: (m, l) -> (max(m, s), l e^(m-M) +
+//    e^(s-M)); with several splits the merge kernel does this instead.
+// attend_generic: any H, D; float32 VALU; used for float32 layers and small
+// shapes.
+#include "csa_device.h"
+#include "csa_internal.h"
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kAH = 64, kAD = 512, kCH = 32;
+constexpr int kKRow = kAD + 8;   // row-major copy stride (bf16)
+constexpr int kVRow = kCH + 8;   // transposed copy stride (bf16)
+constexpr int kMaxRows = 1024;   // rows handled by one block
+constexpr int kMaxRope = 128;    // rope channels supported by the fast path
+constexpr int kPart = kAD + 4;    // split partial row: O[512], m, l, 2 pad (16-byte rows)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
+__device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
+                                      int64_t pool_cap, const int32_t* idx_row, int csa,
+                                      int64_t nvis) {
+  if (jr < nwin) return (int)((int64_t)b * win_cap + (lo + jr) % win_cap);
+  const int e = jr - nwin;
+  const int64_t w = csa ? (int64_t)idx_row[e] : (int64_t)e;
+  if (w < 0 || w >= nvis) return -1;
+  return (int)(-2 - ((int64_t)b * pool_cap + w));
+}
+
+__global__ void __launch_bounds__(256, 2) attend_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
+    const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
+    const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
+    const int64_t* __restrict__ pos0, int n_new, int W, int m, int R, double base, float scale,
+    int nsplit, int csa) {
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[kCH * kKRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[kAD * kVRow];
+  __shared__ int32_t rid[kMaxRows];
+  __shared__ double2 cs[kMaxRope / 2];
+
+  const int i = n_new - 1 - (int)blockIdx.x;  // longest rows first
+  const int b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int64_t t = pos0[b] + i;
+  const int64_t tok = (int64_t)b * n_new + i;
+  const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int nwin = (int)(t - lo + 1);
+  int64_t nvis = m > 0 ? (t + 1) / m : 0;
+  if (nvis > pool_cap) nvis = pool_cap;
+  const int npool = csa ? (int)(nvis < k ? nvis : k) : (int)nvis;
+  const int nrows = nwin + npool;
+  const int nch = (nrows + kCH - 1) / kCH;
+  const int cps = (nch + nsplit - 1) / nsplit;
+  const int c0 = split * cps, c1 = min(nch, c0 + cps);
+  const int r0 = c0 * kCH, r1 = min(nrows, c1 * kCH);
+  const int32_t* idx_row = csa ? idx + tok * k : nullptr;
+
+  for (int j = tid; j < r1 - r0; j += 256)
+    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis);
+  for (int j = tid; j < R / 2; j += 256) {
+    double sn, c;
+    sincos((double)t * rope_freq(base, j, R), &sn, &c);
+    cs[j] = make_double2(c, sn);
+  }
+  __syncthreads();
+
+  // rotated query fragments: heads 16*wv + r16, channels 32*kk + 8*g + 0..7
+  const int head = 16 * wv + r16;
+  const bf16_t* qrow = q + (tok * kAH + head) * kAD;
+  const int first = kAD - R;
+  uint4 Qf[16];
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int d0 = 32 * kk + 8 * g;
+    uint4 v = *(const uint4*)(qrow + d0);
+    if (d0 + 8 > first) {
+      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int d = d0 + 2 * p;
+        if (d >= first) {
+          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu)), bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+          const double2 c = cs[(d - first) >> 1];
+          rot64(a, bb, c.x, c.y);
+          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+        }
+      }
+      v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    Qf[kk] = v;
+  }
+
+  f32x4 O[32];
+#pragma unroll
+  for (int mt = 0; mt < 32; ++mt) O[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = scale * kLog2e;
+
+  const int rg = tid & 3, d0s = 8 * (tid >> 2);
+  for (int c = c0; c < c1; ++c) {
+    // ---- stage 32 rows: row-major copy and transposed copy
+    uint4 rv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int rr = e < 4 ? 4 * rg + e : 16 + 4 * rg + (e - 4);
+      const int jr = c * kCH + rr;
+      const int id = jr < r1 ? rid[jr - r0] : -1;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (id >= 0)
+        v = *(const uint4*)(win + (int64_t)id * kAD + d0s);
+      else if (id <= -2)
+        v = *(const uint4*)(pool + (int64_t)(-2 - id) * kAD + d0s);
+      rv[e] = v;
+      *(uint4*)(Kt + rr * kKRow + d0s) = v;
+    }
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      uint32_t o4[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint4 x0 = rv[2 * p], x1 = rv[2 * p + 1];
+        const uint32_t w0 = (dd >> 1) == 0 ? x0.x : (dd >> 1) == 1 ? x0.y : (dd >> 1) == 2 ? x0.z : x0.w;
+        const uint32_t w1 = (dd >> 1) == 0 ? x1.x : (dd >> 1) == 1 ? x1.y : (dd >> 1) == 2 ? x1.z : x1.w;
+        const uint32_t e0 = (dd & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+        const uint32_t e1 = (dd & 1) ? (w1 >> 16) : (w1 & 0xffffu);
+        o4[p] = e0 | (e1 << 16);
+      }
+      *(uint4*)(Vt + (d0s + dd) * kVRow + 8 * rg) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 32 rows x 16 heads
+    f32x4 S[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint4 a = *(const uint4*)(Kt + (16 * mt + r16) * kKRow + 32 * kk + 8 * g);
+        S[mt] = mfma16(a, Qf[kk], S[mt]);
+      }
+    }
+    // ---- online softmax (log2 domain); lane column = one head
+    float s[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int jr = c * kCH + 16 * mt + 4 * g + ii;
+        const bool ok = jr < r1 && rid[jr - r0] != -1;
+        const float v = ok ? S[mt][ii] * sl2 : -INFINITY;
+        s[4 * mt + ii] = v;
+        cmax = fmaxf(cmax, v);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float pa = m_new == -INFINITY ? 0.f : exp2f(s[j] - m_new);
+      const float pb = m_new == -INFINITY ? 0.f : exp2f(s[j + 1] - m_new);
+      psum += pa + pb;
+      pk[j >> 1] = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const uint4 Pf = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) {
+      O[mt] *= alpha;
+      const uint4 a = *(const uint4*)(Vt + (16 * mt + r16) * kVRow + 8 * g);
+      O[mt] = mfma16(a, Pf, O[mt]);
+    }
+    __syncthreads();
+  }
+
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  if (nsplit == 1) {
+    const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
+    const float M = fmaxf(m_run, sink);
+    const float f = exp2f(m_run - M);
+    const float lt = l_run * f + (sinks ? exp2f(sink - M) : 0.f);
+    const float inv = f / lt;
+    bf16_t* orow = out + (tok * kAH + head) * kAD;
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) {
+      const int d = 16 * mt + 4 * g;
+      float o0 = O[mt][0] * inv, o1 = O[mt][1] * inv, o2 = O[mt][2] * inv, o3 = O[mt][3] * inv;
+      if (d >= first) {  // pair (d, d+1) rotated at -t
+        const double2 ca = cs[(d - first) >> 1];
+        const float c0f = (float)ca.x, s0f = (float)ca.y;
+        const float a0 = o0 * c0f + o1 * s0f, a1 = o1 * c0f - o0 * s0f;
+        o0 = a0; o1 = a1;
+      }
+      if (d + 2 >= first) {  // pair (d+2, d+3)
+        const double2 cb = cs[(d + 2 - first) >> 1];
+        const float c1f = (float)cb.x, s1f = (float)cb.y;
+        const float b0 = o2 * c1f + o3 * s1f, b1 = o3 * c1f - o2 * s1f;
+        o2 = b0; o3 = b1;
+      }
+      uint2 st;
+      st.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+      st.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+      *(uint2*)(orow + d) = st;
+    }
+  } else {
+    float* prow = part + ((tok * nsplit + split) * kAH + head) * kPart;
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt)
+      *(f32x4*)(prow + 16 * mt + 4 * g) = O[mt];
+    if (g == 0) {
+      prow[kAD] = m_run;
+      prow[kAD + 1] = l_run;
+    }
+  }
+}
+
+// Merge of split partials (m in log2 units, l, unnormalised O) with the sink,
+// then the -t rotation of the rope slice and the store.
+__global__ void __launch_bounds__(256) attend_merge(const float* __restrict__ part,
+                                                    const float* __restrict__ sinks,
+                                                    bf16_t* __restrict__ out,
+                                                    const int64_t* __restrict__ pos0, int n_new,
+                                                    int R, double base, int nsplit) {
+  __shared__ double2 cs[kAD / 2];
+  const int64_t tok = blockIdx.x;
+  const int b = (int)(tok / n_new), i = (int)(tok % n_new);
+  const int64_t t = pos0[b] + i;
+  for (int j = threadIdx.x; j < R / 2; j += 256) {
+    double sn, c;
+    sincos((double)t * rope_freq(base, j, R), &sn, &c);
+    cs[j] = make_double2(c, sn);
+  }
+  __syncthreads();
+  const int h = threadIdx.x >> 2, dq = (threadIdx.x & 3) * (kAD / 4);
+  const float sink = sinks ? sinks[h] * kLog2e : -INFINITY;
+  float M = sink;
+  for (int s = 0; s < nsplit; ++s)
+    M = fmaxf(M, part[((tok * nsplit + s) * kAH + h) * kPart + kAD]);
+  float lt = sinks ? exp2f(sink - M) : 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* pr = part + ((tok * nsplit + s) * kAH + h) * kPart;
+    if (pr[kAD] != -INFINITY) lt += pr[kAD + 1] * exp2f(pr[kAD] - M);
+  }
+  const int first = kAD - R;
+  bf16_t* orow = out + (tok * kAH + h) * kAD;
+  for (int d = dq; d < dq + kAD / 4; d += 4) {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float* pr = part + ((tok * nsplit + s) * kAH + h) * kPart;
+      if (pr[kAD] == -INFINITY) continue;
+      const float f = exp2f(pr[kAD] - M);
+      const f32x4 v = *(const f32x4*)(pr + d);
+      o[0] += f * v[0]; o[1] += f * v[1]; o[2] += f * v[2]; o[3] += f * v[3];
+    }
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= inv;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      if (d + e >= first) {
+        const double2 c = cs[(d + e - first) >> 1];
+        const float cf = (float)c.x, sf = (float)c.y;
+        const float a = o[e] * cf + o[e + 1] * sf, bb = o[e + 1] * cf - o[e] * sf;
+        o[e] = a;
+        o[e + 1] = bb;
+      }
+    }
+    uint2 st;
+    st.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    st.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *(uint2*)(orow + d) = st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// generic path
+
+constexpr int kGCh = 32;
+
+template <typename T>
+__global__ void __launch_bounds__(256) attend_generic(
+    const T* __restrict__ q, const T* __restrict__ win, int64_t win_cap, const T* __restrict__ pool,
+    int64_t pool_cap, const int32_t* __restrict__ idx, int k, const float* __restrict__ sinks,
+    T* __restrict__ out, const int64_t* __restrict__ pos0, int n_new, int H, int D, int R, int W,
+    int m, double base, float scale, int csa) {
+  extern __shared__ float sm[];
+  float* qs = sm;                      // [H*D]
+  float* acc = qs + H * D;             // [H*D]
+  float* rows = acc + H * D;           // [kGCh*D]
+  float* lg = rows + kGCh * D;         // [H*kGCh]
+  float* mrun = lg + H * kGCh;         // [H]
+  float* lrun = mrun + H;              // [H]
+  float* alph = lrun + H;              // [H]
+  int* ok = (int*)(alph + H);          // [kGCh]
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int64_t t = pos0[b] + i;
+  const int64_t tok = (int64_t)b * n_new + i;
+  const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int nwin = (int)(t - lo + 1);
+  int64_t nvis = m > 0 ? (t + 1) / m : 0;
+  if (nvis > pool_cap) nvis = pool_cap;
+  const int npool = csa ? (int)(nvis < k ? nvis : k) : (int)nvis;
+  const int nrows = nwin + npool;
+  const int first = D - R;
+  const T* qrow = q + tok * H * D;
+  for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+    const int d = e % D;
+    acc[e] = 0.f;
+    if (d < first) {
+      qs[e] = store_t<T>::ld(qrow + e);
+    } else if (((d - first) & 1) == 0) {
+      double sn, c;
+      sincos((double)t * rope_freq(base, (d - first) >> 1, R), &sn, &c);
+      double a = store_t<T>::ld(qrow + e), bb = store_t<T>::ld(qrow + e + 1);
+      rot64(a, bb, c, sn);
+      T ra, rb;
+      store_t<T>::st64(&ra, a);
+      store_t<T>::st64(&rb, bb);
+      qs[e] = store_t<T>::cvt(ra);
+      qs[e + 1] = store_t<T>::cvt(rb);
+    }
+  }
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    mrun[h] = -INFINITY;
+    lrun[h] = 0.f;
+  }
+  const int32_t* idx_row = csa ? idx + tok * k : nullptr;
+  for (int c0 = 0; c0 < nrows; c0 += kGCh) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kGCh * D; e += blockDim.x) {
+      const int r = e / D, d = e % D;
+      const int id = c0 + r < nrows ? row_id(c0 + r, nwin, lo, win_cap, b, pool_cap, idx_row,
+                                              csa, nvis)
+                                    : -1;
+      float v = 0.f;
+      if (id >= 0) v = store_t<T>::ld(win + (int64_t)id * D + d);
+      else if (id <= -2) v = store_t<T>::ld(pool + (int64_t)(-2 - id) * D + d);
+      rows[e] = v;
+      if (d == 0) ok[r] = id != -1;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < H * kGCh; e += blockDim.x) {
+      const int h = e / kGCh, r = e % kGCh;
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(qs[h * D + d], rows[r * D + d], s);
+      lg[e] = ok[r] ? s * scale : -INFINITY;
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+      float mx = -INFINITY;
+      for (int r = 0; r < kGCh; ++r) mx = fmaxf(mx, lg[h * kGCh + r]);
+      const float mn = fmaxf(mrun[h], mx);
+      const float a = mn == -INFINITY ? 1.f : expf(mrun[h] - mn);
+      float ps = 0.f;
+      for (int r = 0; r < kGCh; ++r) {
+        const float p = mn == -INFINITY ? 0.f : expf(lg[h * kGCh + r] - mn);
+        lg[h * kGCh + r] = p;
+        ps += p;
+      }
+      lrun[h] = lrun[h] * a + ps;
+      mrun[h] = mn;
+      alph[h] = a;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+      const int h = e / D, d = e % D;
+      float s = acc[e] * alph[h];
+      for (int r = 0; r < kGCh; ++r) s = fmaf(lg[h * kGCh + r], rows[r * D + d], s);
+      acc[e] = s;
+    }
+  }
+  __syncthreads();
+  T* orow = out + tok * H * D;
+  for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+    const int h = e / D, d = e % D;
+    const float sink = sinks ? sinks[h] : -INFINITY;
+    const float M = fmaxf(mrun[h], sink);
+    const float f = expf(mrun[h] - M);
+    const float lt = lrun[h] * f + (sinks ? expf(sink - M) : 0.f);
+    const double inv = (double)f / (double)lt;
+    if (d < first) {
+      store_t<T>::st64(orow + e, (double)acc[e] * inv);
+    } else if (((d - first) & 1) == 0) {
+      double sn, c;
+      sincos(-(double)t * rope_freq(base, (d - first) >> 1, R), &sn, &c);
+      double a = (double)acc[e] * inv, bb = (double)acc[e + 1] * inv;
+      rot64(a, bb, c, sn);
+      store_t<T>::st64(orow + e, a);
+      store_t<T>::st64(orow + e + 1, bb);
+    }
+  }
+}
+
+size_t attend_generic_shm(const Layer& L) {
+  return ((size_t)2 * L.H * L.D + (size_t)kGCh * L.D + (size_t)L.H * kGCh + 3 * L.H + kGCh) *
+         sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+
+bool attend_fast_shape(const Layer& L) {
+  return L.dtype == 1 && L.H == kAH && L.D == kAD && L.R <= kMaxRope && L.W >= 1;
+}
+
+int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
+  if (!attend_fast_shape(L)) return 1;
+  int64_t npool = 0;
+  if (L.m > 0) npool = csa ? (pool_cap < L.k ? pool_cap : (int64_t)L.k) : pool_cap;
+  const int64_t rows = (int64_t)L.W + npool;
+  const int64_t nch = (rows + kCH - 1) / kCH;
+  const int64_t tokens = (int64_t)B * n;
+  // No block above kMaxRows rows.  Beyond that, split only while a split
+  // keeps >= 256 rows (its float32 partial, 64 x 514 words, costs about as
+  // much traffic as 128 rows) and the grid is short of ~256 blocks.
+  const int64_t need = (nch * kCH + kMaxRows - 1) / kMaxRows;
+  int64_t s = (256 + tokens - 1) / tokens;
+  const int64_t cap = nch / 8 > 1 ? nch / 8 : 1;
+  if (s > cap) s = cap;
+  if (s < need) s = need;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
+  const int s = attend_splits(L, B, n, pool_cap, csa);
+  if (s <= 1) return 0;
+  return (size_t)B * n * s * kAH * kPart * sizeof(float);
+}
+
+hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const void* win,
+                         int64_t win_cap, const void* pool, int64_t pool_cap, const int32_t* idx,
+                         const float* sinks, void* out, void* ws, bool csa, hipStream_t s) {
+  const int m = L.m;
+  if (attend_fast_shape(L)) {
+    const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
+    dim3 grid(bt.n, bt.B, ns);
+    attend_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)win, win_cap,
+                                     (const bf16_t*)pool, pool_cap, idx, L.k, sinks, (bf16_t*)out,
+                                     (float*)ws, bt.pos0, bt.n, L.W, m, L.R, L.base, L.scale, ns,
+                                     csa ? 1 : 0);
+    if (ns > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      attend_merge<<<bt.B * bt.n, 256, 0, s>>>((const float*)ws, sinks, (bf16_t*)out, bt.pos0,
+                                               bt.n, L.R, L.base, ns);
+    }
+    return hipGetLastError();
+  }
+  const size_t shm = attend_generic_shm(L);
+  dim3 grid(bt.n, bt.B);
+  if (L.dtype == 1)
+    attend_generic<bf16_t><<<grid, 256, shm, s>>>(
+        (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k,
+        sinks, (bf16_t*)out, bt.pos0, bt.n, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
+  else
+    attend_generic<float><<<grid, 256, shm, s>>>(
+        (const float*)q, (const float*)win, win_cap, (const float*)pool, pool_cap, idx, L.k,
+        sinks, (float*)out, bt.pos0, bt.n, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,136 @@
+// KV compressor: learned gated pooling with streaming state.
+//
+// Entry w of a stream pools the tokens [(w - overlap) m, (w + 1) m) that are
+// >= 0: per channel, a softmax of the gate logits over those tokens weights
+// their kv values; then an optional RMSNorm over the entry; then RoPE at
+// position w m [DeepSeek-V4 model page, sec. 2.3 (CSA overlapping windows at
+// m = 4, HCA non-overlapping at m' = 128) and "Cache layers" (buffer, pool,
+// counter and overlap state); TransformerLens adapter, compressor submodules
+// kv_proj, gate_proj, kv_norm, rotary_emb].
+//
+// A call carries n new tokens per sequence at positions p0 .. p0+n-1.  The
+// tokens an entry needs from before p0 live in the caller's state ring of
+// (1 + overlap) m raw rows (slot = position mod ring length).  The math is
+// float64 (exp, sums, norm, rotation) and each pooled value is rounded once
+// to the storage dtype.  The work is a few hundred bytes per entry channel
+// and is bound by reading kv and gate once from HBM.
+#include "csa_device.h"
+#include "csa_internal.h"
+
+namespace csa {
+
+constexpr int kMaxWidth = 2048;
+
+template <typename T>
+__global__ void __launch_bounds__(256) compress_kernel(
+    const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
+    float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
+    const int64_t* __restrict__ pos0, int n_new, int width, int R, double base, int m,
+    int overlap, int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double red[256 / 64];
+  const int b = blockIdx.y;
+  const int64_t p0 = pos0[b];
+  const int64_t w = p0 / m + blockIdx.x;
+  if (w >= (p0 + n_new) / m || w >= pool_cap) return;
+  const int Ls = (1 + overlap) * m;
+  const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
+  const T* kv_b = kv + (int64_t)b * n_new * width;
+  const T* g_b = gate + (int64_t)b * n_new * width;
+  const T* skv_b = st_kv + (int64_t)b * Ls * width;
+  const T* sg_b = st_gate + (int64_t)b * Ls * width;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) {
+    double gmax = -INFINITY;
+    for (int64_t s = lo; s < hi; ++s) {
+      const T* g = s >= p0 ? g_b + (s - p0) * width : sg_b + (int64_t)(s % Ls) * width;
+      gmax = fmax(gmax, (double)store_t<T>::ld(g + c));
+    }
+    double num = 0.0, den = 0.0;
+    for (int64_t s = lo; s < hi; ++s) {
+      const T* g = s >= p0 ? g_b + (s - p0) * width : sg_b + (int64_t)(s % Ls) * width;
+      const T* v = s >= p0 ? kv_b + (s - p0) * width : skv_b + (int64_t)(s % Ls) * width;
+      const double e = exp((double)store_t<T>::ld(g + c) - gmax);
+      den += e;
+      num += e * (double)store_t<T>::ld(v + c);
+    }
+    const double x = num / den;
+    pooled[c] = x;
+    ss += x * x;
+  }
+  if (norm_w != nullptr) {
+    ss = wave_sum64(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
+    const double inv = 1.0 / sqrt(tot / (double)width + (double)eps);
+    for (int c = threadIdx.x; c < width; c += blockDim.x)
+      pooled[c] = pooled[c] * inv * (double)norm_w[c];
+  }
+  __syncthreads();
+  T* dst = pool + ((int64_t)b * pool_cap + w) * width;
+  for (int c = threadIdx.x; c < width - R; c += blockDim.x) store_t<T>::st64(dst + c, pooled[c]);
+  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) {
+    const int c = width - R + 2 * j;
+    double sn, cs;
+    sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
+    double a = pooled[c], bb = pooled[c + 1];
+    rot64(a, bb, cs, sn);
+    store_t<T>::st64(dst + c, a);
+    store_t<T>::st64(dst + c + 1, bb);
+  }
+}
+
+// Keep the raw rows of the last (1 + overlap) m positions for later calls.
+// Runs after compress_kernel on the same stream (it overwrites slots that
+// kernel reads).
+template <typename T>
+__global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__ kv,
+                                                           const T* __restrict__ gate,
+                                                           T* __restrict__ st_kv,
+                                                           T* __restrict__ st_gate,
+                                                           const int64_t* __restrict__ pos0,
+                                                           int n_new, int width, int Ls) {
+  const int b = blockIdx.y;
+  const int64_t p0 = pos0[b];
+  const int64_t s = p0 + n_new - Ls + blockIdx.x;
+  if (s < p0) return;
+  const T* src_kv = kv + ((int64_t)b * n_new + (s - p0)) * width;
+  const T* src_g = gate + ((int64_t)b * n_new + (s - p0)) * width;
+  T* dk = st_kv + ((int64_t)b * Ls + (s % Ls)) * width;
+  T* dg = st_gate + ((int64_t)b * Ls + (s % Ls)) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) {
+    dk[c] = src_kv[c];
+    dg[c] = src_g[c];
+  }
+}
+
+hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_dim,
+                           const void* kv, const void* gate, const float* norm_w, float eps,
+                           void* st_kv, void* st_gate, void* pool, int64_t pool_cap,
+                           hipStream_t s) {
+  const int m = L.m, Ls = (1 + L.overlap) * m;
+  const int max_entries = bt.n / m + 1;
+  dim3 g1(max_entries, bt.B), g2(Ls, bt.B);
+  if (L.dtype == 1) {
+    compress_kernel<bf16_t><<<g1, 256, 0, s>>>(
+        (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
+        (const bf16_t*)st_gate, (bf16_t*)pool, bt.pos0, bt.n, width, rope_dim, L.base, m,
+        L.overlap, pool_cap);
+    state_update_kernel<bf16_t><<<g2, 256, 0, s>>>((const bf16_t*)kv, (const bf16_t*)gate,
+                                                   (bf16_t*)st_kv, (bf16_t*)st_gate, bt.pos0,
+                                                   bt.n, width, Ls);
+  } else {
+    compress_kernel<float><<<g1, 256, 0, s>>>((const float*)kv, (const float*)gate, norm_w, eps,
+                                              (const float*)st_kv, (const float*)st_gate,
+                                              (float*)pool, bt.pos0, bt.n, width, rope_dim,
+                                              L.base, m, L.overlap, pool_cap);
+    state_update_kernel<float><<<g2, 256, 0, s>>>((const float*)kv, (const float*)gate,
+                                                  (float*)st_kv, (float*)st_gate, bt.pos0, bt.n,
+                                                  width, Ls);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct Layer {
+  int dtype;       // 0 float32, 1 bf16
+  int H, D, R;     // heads, head_dim, rope channels
+  double base;     // rope base
+  int W;           // sliding window
+  int m, overlap;  // compress ratio (0 = none), overlap flag
+  int Hi, Di, Ri;  // indexer heads, dim, rope channels
+  int k;           // top-k
+  float scale;     // logit scale (resolved, never 0)
+};
+
+struct Batch {
+  int B, n;             // sequences, new tokens per sequence
+  const int64_t* pos0;  // device [B]
+  int64_t pos0_max;     // host bound
+};
+
+// rope.hip
+hipError_t launch_window_append(const Layer& L, const Batch& b, const void* kv, void* ring,
+                                int64_t cap, hipStream_t s);
+hipError_t launch_rope(const Layer& L, const Batch& b, void* x, int rows, int width, int rope_dim,
+                       int sign, hipStream_t s);
+// compress.hip
+hipError_t launch_compress(const Layer& L, const Batch& b, int width, int rope_dim, const void* kv,
+                           const void* gate, const float* norm_w, float eps, void* st_kv,
+                           void* st_gate, void* pool, int64_t pool_cap, hipStream_t s);
+// index.hip
+size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap);
+hipError_t launch_index_topk(const Layer& L, const Batch& b, const void* q, const void* w,
+                             const void* keys, int64_t pool_cap, int32_t* idx, float* scores_out,
+                             void* ws, hipStream_t s);
+// attend.hip
+bool attend_fast_shape(const Layer& L);
+int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
+size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
+hipError_t launch_attend(const Layer& L, const Batch& b, const void* q, const void* win,
+                         int64_t win_cap, const void* pool, int64_t pool_cap, const int32_t* idx,
+                         const float* sinks, void* out, void* ws, bool csa, hipStream_t s);
+
+}  // namespace csa

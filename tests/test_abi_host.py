@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/csa.h declares, sizes workspaces, and rejects bad arguments before any
+launch.  Every call here fails validation or computes a size, so nothing
+reaches a device (the pointers passed are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_gated_amd as m
+from long_context_sparse_gated_amd import _CBatch, _CLayer
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: each call below is rejected first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.library_path()):
+        pytest.skip("libcsa.so not built")
+    return m.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:csa_status|size_t|const char\*|int32_t)\s+(\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(m.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        assert m.csa_status_str(code).startswith("CSA_")
+    assert lib.csa_version() >= 100
+
+
+def csa_layer(**kw):
+    base = dict(dtype=1, num_heads=64, head_dim=512, qk_rope_head_dim=64, rope_theta=160000.0,
+                sliding_window=128, compress_ratio=4, overlap=1, index_n_heads=64,
+                index_head_dim=128, index_rope_dim=64, index_topk=512, softmax_scale=0.0)
+    base.update(kw)
+    return _CLayer(**base)
+
+
+def batch(**kw):
+    base = dict(batch=1, n_new=8192, pos0=FAKE.value, pos0_max=0)
+    base.update(kw)
+    return _CBatch(**base)
+
+
+def test_workspace_sizes(lib):
+    L = csa_layer()
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 8192, 2048, m.CSA_OP_INDEX_TOPK) >= 8192 * 2048 * 4
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 8192, 2048, m.CSA_OP_ATTEND) == 0
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 64, 1, 32768, m.CSA_OP_ATTEND) > 0
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 1, 1, 99) == ctypes.c_size_t(-1).value
+    bad = csa_layer(dtype=7)
+    assert lib.csa_workspace_bytes(ctypes.byref(bad), 1, 1, 1, 1) == ctypes.c_size_t(-1).value
+
+
+def call_attend(lib, L, B, win_cap=8192, pool_cap=2048, idx=FAKE, ws=None, wsb=0, q=FAKE):
+    return lib.csa_attend(ctypes.byref(L), ctypes.byref(B), q, FAKE, win_cap, FAKE, pool_cap,
+                          idx, None, FAKE, ws, wsb, None)
+
+
+def test_rejections_return_before_launch(lib):
+    L, B = csa_layer(), batch()
+    NULL, SHAPE, DTYPE, WS, UNSUP = 1, 2, 3, 5, 4
+    assert lib.csa_attend(None, ctypes.byref(B), FAKE, FAKE, 8192, FAKE, 2048, FAKE, None, FAKE,
+                          None, 0, None) == NULL
+    assert call_attend(lib, L, batch(pos0=None)) == NULL
+    assert call_attend(lib, L, B, q=None) == NULL
+    assert call_attend(lib, L, B, idx=None) == NULL
+    assert call_attend(lib, csa_layer(dtype=5), B) == DTYPE
+    assert call_attend(lib, csa_layer(qk_rope_head_dim=63), B) == SHAPE
+    assert call_attend(lib, csa_layer(qk_rope_head_dim=514), B) == SHAPE
+    assert call_attend(lib, csa_layer(index_topk=5000), B) == SHAPE
+    assert call_attend(lib, csa_layer(overlap=2), B) == SHAPE
+    assert call_attend(lib, L, B, pool_cap=2047) == SHAPE          # entries (0+8192)/4 = 2048
+    assert call_attend(lib, L, B, win_cap=8191) == SHAPE           # needs min(128+8191, 8192)
+    assert call_attend(lib, L, batch(n_new=0)) == SHAPE
+    # decode shapes need split partials: missing workspace
+    Bd = batch(batch=64, n_new=1, pos0_max=131072)
+    assert call_attend(lib, L, Bd, win_cap=128, pool_cap=32768) == WS
+    # generic path limits: a large float32 layer is not implemented
+    assert call_attend(lib, csa_layer(dtype=0), B) == UNSUP
+    # compressor
+    assert lib.csa_compress(ctypes.byref(L), ctypes.byref(B), 512, 64, FAKE, FAKE, None,
+                            ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2047, None) == SHAPE
+    assert lib.csa_compress(ctypes.byref(L), ctypes.byref(B), 513, 64, FAKE, FAKE, None,
+                            ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2048, None) == SHAPE
+    assert lib.csa_compress(ctypes.byref(L), ctypes.byref(B), 512, 64, None, FAKE, None,
+                            ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2048, None) == NULL
+    assert lib.csa_compress(ctypes.byref(csa_layer(compress_ratio=0)), ctypes.byref(B), 512, 64,
+                            FAKE, FAKE, None, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2048,
+                            None) == SHAPE
+    # indexer
+    assert lib.csa_index_topk(ctypes.byref(L), ctypes.byref(B), FAKE, FAKE, FAKE, 2048, FAKE, None,
+                              None, 0, None) == WS
+    assert lib.csa_index_topk(ctypes.byref(L), ctypes.byref(B), FAKE, FAKE, FAKE, 2048, FAKE, None,
+                              ctypes.c_void_p(0x1010), 1 << 40, None) == WS   # misaligned
+    assert lib.csa_index_topk(ctypes.byref(csa_layer(index_rope_dim=200)), ctypes.byref(B), FAKE,
+                              FAKE, FAKE, 2048, FAKE, None, FAKE, 1 << 40, None) == SHAPE
+    # rope / window
+    assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 64, 2, None) == SHAPE
+    assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 65, 1, None) == SHAPE
+    assert lib.csa_window_append(ctypes.byref(L), ctypes.byref(B), FAKE, FAKE, 100, None) == SHAPE
+    assert lib.hca_attend(ctypes.byref(csa_layer(compress_ratio=128, overlap=0)), ctypes.byref(B),
+                          FAKE, FAKE, 8192, FAKE, 63, None, FAKE, None, 0, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    L = m.Layer("bf16", 64, 512, 64, 160000.0, 128, 4, 1, 64, 128, 64, 512)
+    x = torch.zeros(1, 4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.csa_window_append(L, torch.zeros(1, dtype=torch.int64), 0, x, x)

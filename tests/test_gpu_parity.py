@@ -1,0 +1,314 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case prints its name before touching the GPU.  Sizes here let the
+oracle finish in seconds while spanning several tiles with ragged tails;
+the full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import csa_oracle as O
+from synth import to_f64
+from tests.helpers import (assert_close, audit_topk, dev, host, say, score_bounds, seq_f64,
+                           ulp_diff_ok)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sparse_gated_amd as m
+    m.load_library()
+    return m
+
+
+def _prefill_gpu(m, spec, inp, B, S):
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    L = m.Layer.from_spec(spec)
+    pool_cap = max(1, S // spec.ratio) if spec.ratio else 0
+    cache = LayerCache(L, B, S, pool_cap)
+    pos0 = torch.zeros(B, dtype=torch.int64, device="cuda")
+    args = {k: dev(v) for k, v in inp.items() if k != "sinks"}
+    sinks = dev(inp["sinks"])
+    out, idx = layer_step(cache, pos0, 0, args["q"], args["kv"], args.get("ckv"), args.get("cgate"),
+                          args.get("ikv"), args.get("igate"), args.get("qi"), args.get("wi"), sinks)
+    torch.cuda.synchronize()
+    return L, cache, pos0, args, sinks, out, idx
+
+
+def _check_csa_prefill(m, spec, w, seed, queries_per_seq=None):
+    import torch
+    inp = synth.prefill_inputs(w, seed)
+    B, S = w.batch, w.n_new
+    L, cache, pos0, args, sinks, out, idx = _prefill_gpu(m, spec, inp, B, S)
+    gidx = idx.cpu().numpy()
+    ndiff = 0
+    for b in range(B):
+        x = seq_f64(inp, b)
+        qs = list(range(S)) if queries_per_seq is None else queries_per_seq
+        ref = O.csa_prefill(spec, x, queries=qs)
+        ulp_diff_ok(host(cache.pool[b]), ref["pool"], spec.dtype, "pool")
+        ulp_diff_ok(host(cache.ipool[b]), ref["ipool"], spec.dtype, "ipool")
+        ulp_diff_ok(host(cache.ring[b]), ref["win"], spec.dtype, "window rows")
+        for n, t in enumerate(qs):
+            nv = (t + 1) // spec.ratio
+            keys = ref["ipool"][:nv]
+            sc = O.index_scores(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim,
+                                spec.rope_theta, spec.dtype)
+            ab = score_bounds(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim,
+                              spec.rope_theta, spec.dtype)
+            ndiff += audit_topk(gidx[b, t], ref["idx"][n], sc, ab, spec.index_dim,
+                                spec.index_heads)
+        go = host(out[b])[qs]
+        same = [n for n, t in enumerate(qs) if np.array_equal(gidx[b, t], ref["idx"][n])]
+        assert_close(go[same], ref["out"][same], spec.dtype, "attention output (same ids)")
+        # attention with the oracle's ids on both sides
+        if len(same) < len(qs):
+            idx2 = idx.clone()
+            idx2[b, qs] = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+            out2 = torch.empty_like(out)
+            m.csa_attend(L, pos0, 0, args["q"], cache.ring, cache.pool, idx2, sinks, out2,
+                         cache.workspace(S, m.CSA_OP_ATTEND))
+            torch.cuda.synchronize()
+            assert_close(host(out2[b])[qs], ref["out"], spec.dtype, "attention output (oracle ids)")
+    say(f"  near-tie id differences: {ndiff}")
+    return ndiff
+
+
+def test_tiny_csa_layer_f32(csa):
+    say("case: tiny_csa f32 S=256 (generic kernels)")
+    w = synth.workload("tiny_csa")
+    for seed in (0, 1):
+        _check_csa_prefill(csa, w.layers[0], w, seed)
+
+
+def test_tiny_csa_layer_f32_peaked(csa):
+    say("case: tiny_csa f32 peaked")
+    w = synth.workload("tiny_csa", variant="peaked")
+    _check_csa_prefill(csa, w.layers[0], w, 2)
+
+
+def test_csa_prefill_bf16_small_topk(csa):
+    say("case: csa_prefill bf16 S=1000 k=64 B=2 (mfma kernels)")
+    import dataclasses
+    w = synth.workload("csa_prefill", S=1000, batch=2)
+    spec = dataclasses.replace(w.layers[0], topk=64)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 0, queries_per_seq=[0, 1, 2, 3, 4, 7, 100, 255, 256, 257,
+                                                        500, 777, 998, 999])
+
+
+def test_csa_prefill_bf16_k512(csa):
+    say("case: csa_prefill bf16 S=2600 k=512 (mfma kernels)")
+    w = synth.workload("csa_prefill", S=2600)
+    _check_csa_prefill(csa, w.layers[0], w, 3,
+                       queries_per_seq=[0, 3, 127, 128, 2046, 2047, 2048, 2100, 2555, 2598, 2599])
+
+
+def test_csa_prefill_bf16_peaked(csa):
+    say("case: csa_prefill bf16 peaked S=2200")
+    w = synth.workload("csa_prefill", S=2200, variant="peaked")
+    _check_csa_prefill(csa, w.layers[0], w, 4, queries_per_seq=[5, 600, 2047, 2100, 2199])
+
+
+def _check_dense_prefill(m, kind, S, seed, queries, variant="plain"):
+    import torch
+    name = "hca_prefill"
+    w = synth.workload(name, S=S, variant=variant)
+    spec = w.layers[0]
+    if kind == "sliding":
+        import dataclasses
+        spec = synth.LayerSpec(kind="sliding", dtype="bf16", ratio=0, overlap=0, rope_theta=10000.0)
+        w = dataclasses.replace(w, layers=[spec])
+    inp = synth.prefill_inputs(w, seed)
+    L, cache, pos0, args, sinks, out, _ = _prefill_gpu(m, spec, inp, w.batch, S)
+    x = seq_f64(inp, 0)
+    if kind == "sliding":
+        ref = O.sliding_prefill(spec, x, queries=queries)
+    else:
+        ref = O.hca_prefill(spec, x, queries=queries)
+        ulp_diff_ok(host(cache.pool[0]), ref["pool"], "bf16", "pool")
+    ulp_diff_ok(host(cache.ring[0]), ref["win"], "bf16", "window rows")
+    err = assert_close(host(out[0])[queries], ref["out"], "bf16", f"{kind} output")
+    say(f"  max abs err {err:.3e}")
+
+
+def test_hca_prefill_bf16(csa):
+    say("case: hca_prefill bf16 S=4200")
+    _check_dense_prefill(csa, "hca", 4200, 0, [0, 1, 126, 127, 128, 255, 1000, 4095, 4096, 4199])
+
+
+def test_hca_prefill_bf16_peaked(csa):
+    say("case: hca_prefill bf16 peaked S=3000")
+    _check_dense_prefill(csa, "hca", 3000, 1, [0, 127, 1500, 2999], variant="peaked")
+
+
+def test_sliding_prefill_bf16(csa):
+    say("case: sliding prefill bf16 S=700")
+    _check_dense_prefill(csa, "sliding", 700, 2, [0, 1, 64, 127, 128, 129, 699])
+
+
+def _decode_case(m, name, pos0, batch, seed, layers=None):
+    """One decode step at pos0 for every sequence and layer, against the oracle."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    w = synth.workload(name, pos0=pos0, batch=batch)
+    for li, spec in enumerate(w.layers):
+        if layers is not None and li not in layers:
+            continue
+        say(f"  layer {li} {spec.kind}")
+        inp = synth.decode_inputs(w, seed, li)
+        L = m.Layer.from_spec(spec)
+        pool_cap = (pos0 + 1) // spec.ratio if spec.ratio else 0
+        cache = LayerCache(L, batch, spec.window, max(pool_cap, 1))
+        cache.ring.copy_(dev(inp["win"]))
+        if spec.ratio:
+            P = pos0 // spec.ratio
+            cache.pool[:, :P].copy_(dev(inp["pool"]))
+            cache.cstate_kv.copy_(dev(inp["cstate_kv"]))
+            cache.cstate_gate.copy_(dev(inp["cstate_gate"]))
+            if spec.has_indexer:
+                cache.ipool[:, :P].copy_(dev(inp["ipool"]))
+                cache.istate_kv.copy_(dev(inp["istate_kv"]))
+                cache.istate_gate.copy_(dev(inp["istate_gate"]))
+        p0 = torch.full((batch,), pos0, dtype=torch.int64, device="cuda")
+        a = {k: dev(inp[k]) for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+             if k in inp}
+        out, idx = layer_step(cache, p0, pos0, a["q"], a["kv"], a.get("ckv"), a.get("cgate"),
+                              a.get("ikv"), a.get("igate"), a.get("qi"), a.get("wi"),
+                              dev(inp["sinks"]))
+        torch.cuda.synchronize()
+        for b in range(batch):
+            new = {k: (to_f64(inp[k]) if k == "sinks" else to_f64(inp[k][b, 0]))
+                   for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi", "sinks")
+                   if k in inp}
+            cch = {k: to_f64(inp[k][b]) for k in ("win", "pool", "ipool", "cstate_kv",
+                                                  "cstate_gate", "istate_kv", "istate_gate")
+                   if k in inp}
+            ref = O.decode_step(spec, pos0, new, cch)
+            if "new_pool" in ref:
+                w_new = (pos0 + 1) // spec.ratio - 1
+                ulp_diff_ok(host(cache.pool[b, w_new]), ref["new_pool"], "bf16", "new entry")
+            if spec.has_indexer:
+                nv = (pos0 + 1) // spec.ratio
+                keys = to_f64(inp["ipool"][b])
+                if "new_ipool" in ref:
+                    keys = np.concatenate([keys, ref["new_ipool"][None]])
+                keys = keys[:nv]
+                sc = O.index_scores(new["qi"], new["wi"], keys, pos0, spec.index_rope_dim,
+                                    spec.rope_theta, "bf16")
+                ab = score_bounds(new["qi"], new["wi"], keys, pos0, spec.index_rope_dim,
+                                  spec.rope_theta, "bf16")
+                gi = idx[b, 0].cpu().numpy()
+                nd = audit_topk(gi, ref["idx"], sc, ab, spec.index_dim, spec.index_heads)
+                if nd:
+                    say(f"  seq {b}: {nd} near-tie id differences; re-attend with oracle ids")
+                    idx2 = idx.clone()
+                    idx2[b, 0] = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+                    m.csa_attend(L, p0, pos0, a["q"], cache.ring, cache.pool, idx2,
+                                 dev(inp["sinks"]), out, cache.workspace(1, m.CSA_OP_ATTEND))
+                    torch.cuda.synchronize()
+            assert_close(host(out[b, 0]), ref["out"], "bf16", f"decode out seq {b}")
+
+
+def test_csa_decode_small(csa):
+    say("case: csa decode B=3 pos0=5000")
+    _decode_case(csa, "csa_decode", 5000, 3, 0)
+
+
+def test_csa_decode_entry_closes(csa):
+    say("case: csa decode B=2 pos0=4099 (entry closes at t)")
+    _decode_case(csa, "csa_decode", 4099, 2, 1)
+
+
+def test_mixed_decode_small(csa):
+    say("case: mixed decode B=2 pos0=40959 (HCA entry closes) three layers")
+    _decode_case(csa, "mixed_decode", 40959, 2, 2)
+
+
+def test_mixed_decode_long_topk_path(csa):
+    say("case: mixed decode B=2 pos0=70001, CSA layer only (1024-thread top-k)")
+    _decode_case(csa, "mixed_decode", 70001, 2, 3, layers=[0])
+
+
+@pytest.mark.parametrize("n_q,pool,distinct,pos0", [
+    (37, 700, 0, 2700), (64, 900, 5, 3000), (9, 300, 0, 0), (1, 5000, 0, 19999),
+    (1, 30000, 7, 119999), (3, 2048, 3, 8191)])
+def test_topk_bit_exact_on_grid_inputs(csa, n_q, pool, distinct, pos0):
+    """Exact-arithmetic scores: both sides must select identical ids (ties: lowest id)."""
+    import torch
+    say(f"case: grid top-k n_q={n_q} pool={pool} distinct={distinct} pos0={pos0}")
+    m = csa
+    spec = synth.LayerSpec(kind="csa", dtype="bf16")
+    L = m.Layer.from_spec(spec)
+    k = spec.topk
+    q, keys, wt = synth.grid_index_inputs(n_q, pool, 64, 128, 64, seed=n_q + pool,
+                                          distinct_rows=distinct)
+    B = 1
+    pos0_t = torch.full((B,), pos0, dtype=torch.int64, device="cuda")
+    assert (pos0 + n_q) // 4 <= pool
+    qd = torch.from_numpy(q[None]).to(torch.bfloat16).cuda()
+    kd = torch.from_numpy(keys[None]).to(torch.bfloat16).cuda()
+    wd = torch.from_numpy(wt[None]).to(torch.bfloat16).cuda()
+    idx = torch.empty(B, n_q, k, dtype=torch.int32, device="cuda")
+    sc_out = torch.full((B, n_q, pool), float("nan"), dtype=torch.float32, device="cuda")
+    m.csa_index_topk(L, pos0_t, pos0, qd, wd, kd, idx, scores_out=sc_out)
+    torch.cuda.synchronize()
+    gi, gs = idx.cpu().numpy()[0], sc_out.cpu().numpy()[0]
+    for i in range(n_q):
+        t = pos0 + i
+        nv = (t + 1) // 4
+        sc = O.index_scores(q[i].astype(np.float64), wt[i].astype(np.float64),
+                            keys[:nv].astype(np.float64), t, 64, spec.rope_theta, "bf16")
+        assert np.array_equal(gs[i, :nv].astype(np.float64), sc), "scores must be exact"
+        ref = O.topk_select(sc, k)
+        assert np.array_equal(gi[i], ref), f"query {i}: ids differ"
+
+
+def test_chunked_prefill_equals_one_shot(csa):
+    """Streaming state: prefill in chunks (including a single-token call) matches one call."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    say("case: chunked prefill vs one-shot, csa bf16 S=1030")
+    m = csa
+    w = synth.workload("csa_prefill", S=1030)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 5)
+    L = m.Layer.from_spec(spec)
+    S = w.n_new
+    a = {k: dev(v) for k, v in inp.items() if k != "sinks"}
+    sinks = dev(inp["sinks"])
+    one = LayerCache(L, 1, S, S // 4)
+    p = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out1, idx1 = layer_step(one, p, 0, a["q"], a["kv"], a["ckv"], a["cgate"], a["ikv"], a["igate"],
+                            a["qi"], a["wi"], sinks)
+    ch = LayerCache(L, 1, S, S // 4)
+    outs, idxs = [], []
+    for lo, hi in ((0, 301), (301, 302), (302, 303), (303, 771), (771, 1030)):
+        p = torch.full((1,), lo, dtype=torch.int64, device="cuda")
+        sl = {k: v[:, lo:hi].contiguous() for k, v in a.items()}
+        o, ix = layer_step(ch, p, lo, sl["q"], sl["kv"], sl["ckv"], sl["cgate"], sl["ikv"],
+                           sl["igate"], sl["qi"], sl["wi"], sinks)
+        outs.append(o)
+        idxs.append(ix)
+    torch.cuda.synchronize()
+    assert torch.equal(one.pool, ch.pool) and torch.equal(one.ipool, ch.ipool)
+    assert torch.equal(one.ring, ch.ring)
+    assert torch.equal(idx1, torch.cat(idxs, 1))
+    assert torch.equal(out1.view(torch.int16), torch.cat(outs, 1).view(torch.int16))
+
+
+def test_repeat_runs_are_bitwise_identical(csa):
+    import torch
+    say("case: determinism, csa bf16 S=900 twice")
+    w = synth.workload("csa_prefill", S=900)
+    inp = synth.prefill_inputs(w, 6)
+    r1 = _prefill_gpu(csa, w.layers[0], inp, 1, 900)
+    r2 = _prefill_gpu(csa, w.layers[0], inp, 1, 900)
+    assert torch.equal(r1[6], r2[6])
+    assert torch.equal(r1[5].view(torch.int16), r2[5].view(torch.int16))
