@@ -94,6 +94,10 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: the library then binds to the HIP runtime torch already
+    # loaded (same soname), so device memory, streams and launches share one
+    # runtime in the process.
+    _torch()
     path = library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
