@@ -11,20 +11,28 @@
 // (eq. 27), output rotation (eq. 26); transformers PR 45616: sink from the
 // GPT-OSS eager attention].
 //
-// attend_mfma (H = 64, D = 512, bf16) -- one block per (token, split):
-//  * four waves, 16 heads each; the rotated query of a wave's heads lives in
-//    VGPRs as the B operand of S^T = K Q^T (16 x 16 x 32 bf16 MFMA);
-//  * rows are gathered 32 at a time into LDS twice: row-major (A operand of
-//    K Q^T, 16-byte reads along d) and transposed (A operand of O^T = V^T P^T,
-//    16-byte reads along rows).  The transposed copy is written from an 8 x 8
-//    register transpose during staging, so one HBM/L2 read feeds both uses of
-//    the K = V row;
-//  * S^T puts one head per lane column, so the online softmax state (max,
-//    partial sum) and the O^T accumulators of a lane all belong to one head:
-//    rescaling O is one multiply per accumulator, no cross-lane traffic;
+// attend_mfma (H = 64, D = 512, bf16) -- one block of two waves per
+// (token, split); each wave owns 32 heads:
+//  * the rotated query of a wave's 32 heads lives in VGPRs as the B operand
+//    of S^T = K Q^T (16 x 16 x 32 bf16 MFMA), so every K byte read from LDS
+//    feeds 32 heads;
+//  * the K = V rows are gathered 32 at a time straight from HBM/L2 into LDS
+//    by the LDS-DMA loads (one 1 KB row per wave instruction), double
+//    buffered so the next chunk's gather overlaps this chunk's MFMAs.  Each
+//    row is stored once, row-major; the V^T operand of O^T = V^T P^T comes
+//    from the same bytes through the LDS transpose read (ds_read_b64_tr_b16),
+//    so one load feeds both uses of the K = V row;
+//  * 16-byte chunks of row r sit at chunk (c ^ (2 (r mod 8) + (r/8 mod 2))):
+//    the QK^T reads (16 rows, one chunk) and the transpose reads (8 rows,
+//    two chunks) both hit distinct banks;
+//  * S^T puts one head per lane column, so the online softmax state and the
+//    O^T accumulators of a lane all belong to one head; the running max is
+//    only raised when a chunk exceeds it by more than 2^8 (P stays <= 256,
+//    exact to bf16 precision), which skips most rescales of O;
 //  * P is rounded to bf16 for the PV product; accumulation is float32;
 //  * the sink enters once, at the end: (m, l) -> (max(m, s), l e^(m-M) +
-//    e^(s-M)); with several splits the merge kernel does this instead.
+//    e^(s-M)); with several splits the merge kernel does this instead;
+//  * the bf16 output is staged through LDS and written as whole 1 KB rows.
 // attend_generic: any H, D; float32 VALU; used for float32 layers and small
 // shapes.
 #include "csa_device.h"
@@ -41,12 +49,24 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 }
 
 constexpr int kAH = 64, kAD = 512, kCH = 32;
-constexpr int kKRow = kAD + 8;   // row-major copy stride (bf16)
-constexpr int kVRow = kCH + 8;   // transposed copy stride (bf16)
 constexpr int kMaxRows = 1024;   // rows handled by one block
 constexpr int kMaxRope = 128;    // rope channels supported by the fast path
-constexpr int kPart = kAD + 4;    // split partial row: O[512], m, l, 2 pad (16-byte rows)
+constexpr int kPart = kAD + 4;   // split partial row: O[512], m, l, 2 pad (16-byte rows)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;    // log2 headroom before the running max is raised
+// Tuning (compile time): 16-head tiles per wave (1: four waves per token,
+// 2: two waves per token) and the blocks per CU the register budget targets.
+#ifndef CSA_ATTN_HEAD_TILES
+#define CSA_ATTN_HEAD_TILES 1
+#endif
+#ifndef CSA_ATTN_MIN_BLOCKS
+#define CSA_ATTN_MIN_BLOCKS 2
+#endif
+constexpr int kHeadTiles = CSA_ATTN_HEAD_TILES;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
 __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
@@ -59,17 +79,27 @@ __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_
   return (int)(-2 - ((int64_t)b * pool_cap + w));
 }
 
-__global__ void __launch_bounds__(256, 2) attend_mfma(
+// chunk swizzle of LDS row r (16-byte chunks, 64 per row)
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+
+template <int NT>
+__global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
     const int64_t* __restrict__ pos0, int n_new, int W, int m, int R, double base, float scale,
     int nsplit, int csa) {
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[kCH * kKRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kAD * kVRow];
+  // two separate arrays (not one indexed by parity) so the compiler can tell
+  // the DMA target from the tile being read and need not wait for the DMA
+  __shared__ __attribute__((aligned(1024))) bf16_t kbuf0[kCH * kAD];
+  __shared__ __attribute__((aligned(1024))) bf16_t kbuf1[kCH * kAD];
   __shared__ int32_t rid[kMaxRows];
+  __shared__ uint32_t vmask[kMaxRows / 32 + 1];
   __shared__ double2 cs[kMaxRope / 2];
 
+  constexpr int NW = 4 / NT;          // waves per block (16*NT heads each)
+  constexpr int NTH = 64 * NW;        // threads per block
+  constexpr int RPW = kCH / NW;       // rows each wave gathers per chunk
   const int i = n_new - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -86,169 +116,262 @@ __global__ void __launch_bounds__(256, 2) attend_mfma(
   const int c0 = split * cps, c1 = min(nch, c0 + cps);
   const int r0 = c0 * kCH, r1 = min(nrows, c1 * kCH);
   const int32_t* idx_row = csa ? idx + tok * k : nullptr;
+  const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
-  for (int j = tid; j < r1 - r0; j += 256)
+  for (int j = tid; j < r1 - r0; j += NTH)
     rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis);
-  for (int j = tid; j < R / 2; j += 256) {
+  for (int j = tid; j < R / 2; j += NTH) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
   __syncthreads();
-
-  // rotated query fragments: heads 16*wv + r16, channels 32*kk + 8*g + 0..7
-  const int head = 16 * wv + r16;
-  const bf16_t* qrow = q + (tok * kAH + head) * kAD;
-  const int first = kAD - R;
-  uint4 Qf[16];
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk) {
-    const int d0 = 32 * kk + 8 * g;
-    uint4 v = *(const uint4*)(qrow + d0);
-    if (d0 + 8 > first) {
-      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int d = d0 + 2 * p;
-        if (d >= first) {
-          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu)), bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
-          const double2 c = cs[(d - first) >> 1];
-          rot64(a, bb, c.x, c.y);
-          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
-        }
-      }
-      v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  // bit r of vmask[c - c0]: row r of chunk c takes part in the softmax
+  for (int j0 = 64 * wv; j0 < r1 - r0; j0 += 64 * NW) {
+    const bool ok = j0 + lane < r1 - r0 && rid[j0 + lane] != -1;
+    const unsigned long long bal = __ballot(ok);
+    if (lane == 0) {
+      vmask[j0 >> 5] = (uint32_t)bal;
+      vmask[(j0 >> 5) + 1] = (uint32_t)(bal >> 32);
     }
-    Qf[kk] = v;
   }
+  __syncthreads();
 
-  f32x4 O[32];
+  // gather of chunk c into dst: this wave moves rows RPW*wv .. +RPW-1
+  auto issue = [&](int c, bf16_t* dst) {
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) O[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = scale * kLog2e;
-
-  const int rg = tid & 3, d0s = 8 * (tid >> 2);
-  for (int c = c0; c < c1; ++c) {
-    // ---- stage 32 rows: row-major copy and transposed copy
-    uint4 rv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int rr = e < 4 ? 4 * rg + e : 16 + 4 * rg + (e - 4);
+    for (int e = 0; e < RPW; ++e) {
+      const int rr = RPW * wv + e;
       const int jr = c * kCH + rr;
-      const int id = jr < r1 ? rid[jr - r0] : -1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (id >= 0)
-        v = *(const uint4*)(win + (int64_t)id * kAD + d0s);
-      else if (id <= -2)
-        v = *(const uint4*)(pool + (int64_t)(-2 - id) * kAD + d0s);
-      rv[e] = v;
-      *(uint4*)(Kt + rr * kKRow + d0s) = v;
+      int id = jr < r1 ? rid[jr - r0] : -1;
+      if (id == -1) id = self_id;  // masked below; any finite row will do
+      const bf16_t* src = id >= 0 ? win + (int64_t)id * kAD : pool + (int64_t)(-2 - id) * kAD;
+      src += 8 * (lane ^ swz(rr));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + rr * kAD), 16, 0, 0);
     }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      uint32_t o4[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint4 x0 = rv[2 * p], x1 = rv[2 * p + 1];
-        const uint32_t w0 = (dd >> 1) == 0 ? x0.x : (dd >> 1) == 1 ? x0.y : (dd >> 1) == 2 ? x0.z : x0.w;
-        const uint32_t w1 = (dd >> 1) == 0 ? x1.x : (dd >> 1) == 1 ? x1.y : (dd >> 1) == 2 ? x1.z : x1.w;
-        const uint32_t e0 = (dd & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        const uint32_t e1 = (dd & 1) ? (w1 >> 16) : (w1 & 0xffffu);
-        o4[p] = e0 | (e1 << 16);
-      }
-      *(uint4*)(Vt + (d0s + dd) * kVRow + 8 * rg) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-    }
-    __syncthreads();
+  };
+  if (c0 < c1) issue(c0, kbuf0);
 
-    // ---- S^T = K Q^T for 32 rows x 16 heads
-    f32x4 S[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+  // rotated query fragments: heads 16*NT*wv + 16*nt + r16, channels 32*kk + 8*g + 0..7
+  const int first = kAD - R;
+  const int hw0 = 16 * NT * wv;  // first head of this wave
+  uint4 Qf[NT][16];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bf16_t* qrow = q + (tok * kAH + hw0 + 16 * nt + r16) * kAD;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
+      const int d0 = 32 * kk + 8 * g;
+      uint4 v = *(const uint4*)(qrow + d0);
+      if (d0 + 8 > first) {
+        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const uint4 a = *(const uint4*)(Kt + (16 * mt + r16) * kKRow + 32 * kk + 8 * g);
-        S[mt] = mfma16(a, Qf[kk], S[mt]);
+        for (int p = 0; p < 4; ++p) {
+          const int d = d0 + 2 * p;
+          if (d >= first) {
+            double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
+            double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+            const double2 c = cs[(d - first) >> 1];
+            rot64(a, bb, c.x, c.y);
+            w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+          }
+        }
+        v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
+      Qf[nt][kk] = v;
     }
-    // ---- online softmax (log2 domain); lane column = one head
-    float s[8];
-    float cmax = -INFINITY;
+  }
+
+  f32x4 O[NT][32];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt) O[nt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
+  const float sl2 = scale * kLog2e;
+
+  // LDS byte offsets (constant per lane).  The swizzle only touches the low
+  // four chunk bits, so every read is a per-lane base plus a compile-time
+  // multiple of 256 bytes (16 chunks):
+  //  * QK^T: row r16 (+16 for the second row tile), chunk 4kk + g; with
+  //    kk = 4u + v the chunk is 16u + ((4v + g) ^ swz(r16)): bases kb_v[v];
+  //  * transpose read: source lane s = r16 of group g supplies row 4g + s/4
+  //    (+16 for the upper 4 rows) and channels 4 (s mod 4) .. +3 of the
+  //    16-channel tile mt = 8u + v, i.e. chunk 16u + ((2v + (s mod 4)/2) ^
+  //    swz(row)) plus 8 bytes for odd s: bases tr_v[v] (row + 16 adds 16 KB).
+  int kb_v[4], tr_v[8];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) kb_v[v] = r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
+  {
+    const int trA = 4 * g + (r16 >> 2);
+    const int trc = (r16 & 3) >> 1, trh = (r16 & 1) * 8;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh;
+  }
+
+  auto chunk = [&](int c, const bf16_t* cur) {
+    const char* kb = (const char*)cur;
+
+    // ---- S^T = K Q^T: 32 rows x 16*NT heads
+    f32x4 S[2][NT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int jr = c * kCH + 16 * mt + 4 * g + ii;
-        const bool ok = jr < r1 && rid[jr - r0] != -1;
-        const float v = ok ? S[mt][ii] * sl2 : -INFINITY;
-        s[4 * mt + ii] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    uint32_t pk[4];
+      for (int nt = 0; nt < NT; ++nt) S[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // swz(16*mt + r16) == swz(r16): the second row tile is 16 KB further
+    auto kfrag = [&](int kk, int mt) {
+      return *(const uint4*)(kb + kb_v[kk & 3] + (kk >> 2) * 256 + mt * 16384);
+    };
+    uint4 acur0 = kfrag(0, 0), acur1 = kfrag(0, 1);
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const float pa = m_new == -INFINITY ? 0.f : exp2f(s[j] - m_new);
-      const float pb = m_new == -INFINITY ? 0.f : exp2f(s[j + 1] - m_new);
-      psum += pa + pb;
-      pk[j >> 1] = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
+    for (int kk = 0; kk < 16; ++kk) {
+      uint4 anx0 = acur0, anx1 = acur1;
+      if (kk + 1 < 16) {
+        anx0 = kfrag(kk + 1, 0);
+        anx1 = kfrag(kk + 1, 1);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        S[0][nt] = mfma16(acur0, Qf[nt][kk], S[0][nt]);
+        S[1][nt] = mfma16(acur1, Qf[nt][kk], S[1][nt]);
+      }
+      acur0 = anx0;
+      acur1 = anx1;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const uint4 Pf = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    // ---- O^T += V^T P^T
+    // ---- online softmax (log2 domain); lane column = one head per nt
+    const uint32_t vm = vmask[c - c0] >> (4 * g);
+    uint4 Pf[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float sv[8];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float v = (vm >> (16 * mt + ii)) & 1u ? S[mt][nt][ii] * sl2 : -INFINITY;
+          sv[4 * mt + ii] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      if (__any(cmax > m_run[nt] + kLazy)) {
+        const float m_new = fmaxf(m_run[nt], cmax);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+#pragma unroll
+        for (int mt = 0; mt < 32; ++mt) O[nt][mt] *= alpha;
+        l_run[nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+      const float mr = m_run[nt];
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        // exp2(-inf) = 0 for masked rows; mr is finite once any row was seen
+        const float pa = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j] - mr);
+        const float pb = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j + 1] - mr);
+        psum += pa + pb;
+        pk[j >> 1] = pack_bf16x2(pa, pb);
+      }
+      l_run[nt] += psum;
+      Pf[nt] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+    // ---- O^T += V^T P^T, V^T through the transpose read of the same rows
 #pragma unroll
     for (int mt = 0; mt < 32; ++mt) {
-      O[mt] *= alpha;
-      const uint4 a = *(const uint4*)(Vt + (16 * mt + r16) * kVRow + 8 * g);
-      O[mt] = mfma16(a, Pf, O[mt]);
+      // swz(trA + 16) == swz(trA) since trA < 16: the upper rows are 16 KB on
+      const char* pa = kb + tr_v[mt & 7] + (mt >> 3) * 256;
+      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)pa);
+      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 16384));
+      const uint4 a = make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
+                                 (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
+                                 (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
+                                 (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[nt][mt] = mfma16(a, Pf[nt], O[nt][mt]);
     }
+  };
+  for (int c = c0; c < c1; c += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (c + 1 < c1) issue(c + 1, kbuf1);
+    chunk(c, kbuf0);
+    if (c + 1 < c1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (c + 2 < c1) issue(c + 2, kbuf0);
+      chunk(c + 1, kbuf1);
+    }
   }
 
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    l_run[nt] += __shfl_xor(l_run[nt], 16, 64);
+    l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
+  }
 
   if (nsplit == 1) {
-    const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
-    const float M = fmaxf(m_run, sink);
-    const float f = exp2f(m_run - M);
-    const float lt = l_run * f + (sinks ? exp2f(sink - M) : 0.f);
-    const float inv = f / lt;
-    bf16_t* orow = out + (tok * kAH + head) * kAD;
+    __syncthreads();  // every wave is done with kbuf: reuse it to stage the output
+    // this wave's [16*NT heads][512] bf16, chunks swizzled by head
+    constexpr int kStage = 16 * NT * 1024;  // bytes per wave
+    constexpr int kPerBuf = (kCH * kAD * 2) / kStage;
+    char* ob = (wv < kPerBuf ? (char*)kbuf0 : (char*)kbuf1) + (wv % kPerBuf) * kStage;
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const int d = 16 * mt + 4 * g;
-      float o0 = O[mt][0] * inv, o1 = O[mt][1] * inv, o2 = O[mt][2] * inv, o3 = O[mt][3] * inv;
-      if (d >= first) {  // pair (d, d+1) rotated at -t
-        const double2 ca = cs[(d - first) >> 1];
-        const float c0f = (float)ca.x, s0f = (float)ca.y;
-        const float a0 = o0 * c0f + o1 * s0f, a1 = o1 * c0f - o0 * s0f;
-        o0 = a0; o1 = a1;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int hl = 16 * nt + r16, head = hw0 + hl;
+      const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
+      const float M = fmaxf(m_run[nt], sink);
+      const float f = exp2f(m_run[nt] - M);
+      const float lt = l_run[nt] * f + (sinks ? exp2f(sink - M) : 0.f);
+      const float inv = f / lt;
+#pragma unroll
+      for (int mt = 0; mt < 32; ++mt) {
+        const int d = 16 * mt + 4 * g;
+        float o0 = O[nt][mt][0] * inv, o1 = O[nt][mt][1] * inv;
+        float o2 = O[nt][mt][2] * inv, o3 = O[nt][mt][3] * inv;
+        if (d >= first) {  // pair (d, d+1) rotated at -t
+          const double2 ca = cs[(d - first) >> 1];
+          const float cf = (float)ca.x, sf = (float)ca.y;
+          const float a0 = o0 * cf + o1 * sf, a1 = o1 * cf - o0 * sf;
+          o0 = a0;
+          o1 = a1;
+        }
+        if (d + 2 >= first) {  // pair (d+2, d+3)
+          const double2 cb = cs[(d + 2 - first) >> 1];
+          const float cf = (float)cb.x, sf = (float)cb.y;
+          const float b0 = o2 * cf + o3 * sf, b1 = o3 * cf - o2 * sf;
+          o2 = b0;
+          o3 = b1;
+        }
+        uint2 st;
+        st.x = pack_bf16x2(o0, o1);
+        st.y = pack_bf16x2(o2, o3);
+        const int chunk = (d >> 3) ^ (hl & 15);
+        *(uint2*)(ob + hl * 1024 + (chunk << 4) + ((d & 7) << 1)) = st;
       }
-      if (d + 2 >= first) {  // pair (d+2, d+3)
-        const double2 cb = cs[(d + 2 - first) >> 1];
-        const float c1f = (float)cb.x, s1f = (float)cb.y;
-        const float b0 = o2 * c1f + o3 * s1f, b1 = o3 * c1f - o2 * s1f;
-        o2 = b0; o3 = b1;
-      }
-      uint2 st;
-      st.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-      st.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-      *(uint2*)(orow + d) = st;
+    }
+    __syncthreads();
+    bf16_t* orow = out + (tok * kAH + hw0) * kAD;
+#pragma unroll 4
+    for (int hl = 0; hl < 16 * NT; ++hl) {
+      const uint4 v = *(const uint4*)(ob + hl * 1024 + ((lane ^ (hl & 15)) << 4));
+      *(uint4*)(orow + hl * kAD + 8 * lane) = v;
     }
   } else {
-    float* prow = part + ((tok * nsplit + split) * kAH + head) * kPart;
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt)
-      *(f32x4*)(prow + 16 * mt + 4 * g) = O[mt];
-    if (g == 0) {
-      prow[kAD] = m_run;
-      prow[kAD + 1] = l_run;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int head = hw0 + 16 * nt + r16;
+      float* prow = part + ((tok * nsplit + split) * kAH + head) * kPart;
+#pragma unroll
+      for (int mt = 0; mt < 32; ++mt) *(f32x4*)(prow + 16 * mt + 4 * g) = O[nt][mt];
+      if (g == 0) {
+        prow[kAD] = m_run[nt];
+        prow[kAD + 1] = l_run[nt];
+      }
     }
   }
 }
@@ -473,7 +596,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
   if (attend_fast_shape(L)) {
     const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
     dim3 grid(bt.n, bt.B, ns);
-    attend_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)win, win_cap,
+    attend_mfma<kHeadTiles><<<grid, 256 / kHeadTiles, 0, s>>>((const bf16_t*)q, (const bf16_t*)win, win_cap,
                                      (const bf16_t*)pool, pool_cap, idx, L.k, sinks, (bf16_t*)out,
                                      (float*)ws, bt.pos0, bt.n, L.W, m, L.R, L.base, L.scale, ns,
                                      csa ? 1 : 0);

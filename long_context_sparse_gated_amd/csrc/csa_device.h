@@ -17,12 +17,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// float32 -> bf16, nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float32 -> bf16, nearest even (the gfx950 conversion instruction).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+// two float32 -> packed bf16 pair (low half = a), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // float64 -> float32 rounded to odd: the truncation toward zero with its last
