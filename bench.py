@@ -55,7 +55,7 @@ def cpu_baseline(spec, inp, stride):
     dt = time.perf_counter() - t0
     return {"value": len(qs) / dt, "unit": "tokens/s", "cores": int(blas),
             "kind": "oracle",
-            "sample": f"csa_prefill S={S}: full compressor passes + every {stride}th query "
+            "sample": f"csa_prefill S={S}: full compressor passes + every {stride}-th query "
                       f"({len(qs)} queries, incl. the last), {dt:.1f} s on "
                       f"{len(os.sched_getaffinity(0))} host cores"}
 
@@ -66,7 +66,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-stride", type=int, default=2)
+    ap.add_argument("--cpu-stride", type=int, default=1)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (untimed), so a "
+                         "counter run can scale HBM byte counters against a known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
@@ -118,6 +121,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]

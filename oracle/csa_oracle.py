@@ -325,9 +325,9 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
         if L.has_indexer:
             streams.append(("ipool", "ikv", "igate", "istate_kv", "istate_gate",
                             L.index_rope_dim, inorm_weight))
-        pools = {}
+        pools, fresh = {}, {}
         for pk, kk, gk, sk, sg, rd, nw in streams:
-            pool = np.asarray(cache[pk], dtype=np.float64)
+            pool = cache[pk]          # entries 0 .. t//m - 1 (any array-like)
             if (t + 1) % m == 0:
                 w = (t + 1) // m - 1
                 lo, hi = entry_tokens(w, m, ov)
@@ -336,18 +336,28 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
                 gts = np.stack([new[gk] if s == t else cache[sg][s % Ls] for s in toks])
                 ent = round_to(pool_entry(kvs, gts, w * m, rd, L.rope_theta, nw, eps), dt)
                 assert pool.shape[0] == w, "cache must hold the entries closed before t"
-                pool = np.concatenate([pool, ent[None]])
+                fresh[pk] = ent
                 res["new_" + pk] = ent
             pools[pk] = pool
+
+        def gather(pk, ids):
+            """Rows `ids` of pool pk, the entry closing at t (if any) last."""
+            ids = np.asarray(ids, dtype=np.int64)
+            P = pools[pk].shape[0]
+            old = np.asarray(pools[pk][ids[ids < P]], dtype=np.float64)
+            if pk in fresh and np.any(ids >= P):
+                old = np.concatenate([old, fresh[pk][None]])
+            return old.reshape(len(ids), -1)
+
         vis = visible_entries(t, m)
         if L.has_indexer:
-            sc = index_scores(new["qi"], new["wi"], pools["ipool"][vis.start:vis.stop], t,
-                              L.index_rope_dim, L.rope_theta, dt)
+            keys = gather("ipool", np.arange(vis.start, vis.stop))
+            sc = index_scores(new["qi"], new["wi"], keys, t, L.index_rope_dim, L.rope_theta, dt)
             idx = topk_select(sc, L.topk, first=vis.start)
             res["idx"] = idx
-            rows.append(pools["pool"][idx[idx >= 0]])
+            rows.append(gather("pool", idx[idx >= 0]))
         else:
-            rows.append(pools["pool"][vis.start:vis.stop])
+            rows.append(gather("pool", np.arange(vis.start, vis.stop)))
     rows = np.concatenate(rows)
     res["out"] = attend(new["q"], t, rows, new["sinks"], _spec_scale(L, scale), L.rope_dim,
                         L.rope_theta, dt)

@@ -5,11 +5,12 @@ dtype.  It holds none of the layer's arithmetic: RoPE, pooling, scoring,
 selection and attention live in ``oracle/`` (CPU definition) and in the HIP
 library, and neither of those is imported here.
 
-Every tensor is drawn from ``numpy.random.default_rng([seed, tensor_id, b])``
-(PCG64) as float32 normals, scaled, and rounded to bfloat16 with
-round-to-nearest-even when the workload is bf16.  Seeding per (tensor,
-sequence) lets a test regenerate one sequence of a large decode cache without
-drawing the whole batch.  bf16 tensors are returned as ``uint16`` bit patterns;
+Every tensor is drawn in blocks of 256 rows (first axis), block k of
+sequence b from ``numpy.random.default_rng([seed, tensor_id, b, k])`` (PCG64)
+as float32 normals, scaled, and rounded to bfloat16 with round-to-nearest-
+even when the workload is bf16.  Seeding per (tensor, sequence, block) lets a
+test redraw just the rows the oracle needs (``draw_rows``) and lets the full
+draw run on several threads.  bf16 tensors are returned as ``uint16`` bit patterns;
 ``bf16_bits_to_f32`` / ``to_f64`` decode them exactly.
 
 Workloads (names used by tests and the benchmark):
@@ -33,6 +34,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -184,14 +186,55 @@ def to_f64(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def _draw(seed: int, name: str, b: int, shape, std: float, dtype: str) -> np.ndarray:
-    rng = np.random.default_rng([seed, _TID[name], b])
-    x = rng.standard_normal(shape, dtype=np.float32)
+ROW_BLOCK = 256   # rows per independently seeded block
+
+
+def _draw_block(seed, name, b, blk, nrows, tail, std, dtype):
+    rng = np.random.default_rng([seed, _TID[name], b, blk])
+    x = rng.standard_normal((nrows,) + tuple(tail), dtype=np.float32)
     if std != 1.0:
         x *= np.float32(std)
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
     return x
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _draw(seed: int, name: str, b: int, shape, std: float, dtype: str) -> np.ndarray:
+    """Tensor `name` of sequence b: rows drawn in blocks of ROW_BLOCK rows, block k
+    from default_rng([seed, tensor id, b, k]) (so any row subset can be redrawn)."""
+    shape = tuple(shape)
+    rows, tail = shape[0], shape[1:]
+    nblk = (rows + ROW_BLOCK - 1) // ROW_BLOCK
+    parts = list(_pool().map(
+        lambda k: _draw_block(seed, name, b, k, min(ROW_BLOCK, rows - k * ROW_BLOCK), tail, std,
+                              dtype), range(nblk)))
+    if not parts:
+        return np.zeros(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    return np.concatenate(parts, axis=0)
+
+
+def draw_rows(seed: int, name: str, b: int, shape, std: float, dtype: str, rows) -> np.ndarray:
+    """Rows `rows` (indices along the first axis) of the tensor _draw would return."""
+    shape = tuple(shape)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows),) + shape[1:], dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for k in np.unique(rows // ROW_BLOCK):
+        n = min(ROW_BLOCK, shape[0] - k * ROW_BLOCK)
+        blk = _draw_block(seed, name, b, int(k), n, shape[1:], std, dtype)
+        sel = np.nonzero(rows // ROW_BLOCK == k)[0]
+        out[sel] = blk[rows[sel] - k * ROW_BLOCK]
+    return out
 
 
 def _stack(seed, name, batch, shape, std, dtype):
@@ -206,27 +249,62 @@ def prefill_inputs(w: Workload, seed: int = 0, layer: int = 0) -> Dict[str, np.n
     [B,S,D_I]; qi [B,S,H_I,D_I] (un-rotated); wi [B,S,H_I]; sinks [H] float32.
     """
     L = w.layers[layer]
-    B, S, H, D = w.batch, w.n_new, L.num_heads, L.head_dim
-    dt = L.dtype
     s = seed * 16 + layer
-    out = {
-        "q": _stack(s, "q", B, (S, H, D), w.q_std, dt),
-        "kv": _stack(s, "kv", B, (S, D), w.kv_std, dt),
-        "sinks": _draw(s, "sinks", 0, (H,), w.sink_std, "f32"),
-    }
-    if L.ratio > 0:
-        out["ckv"] = _stack(s, "ckv", B, (S, D), w.kv_std, dt)
-        out["cgate"] = _stack(s, "cgate", B, (S, D), 1.0, dt)
-    if L.has_indexer:
-        Hi, Di = L.index_heads, L.index_dim
-        out["ikv"] = _stack(s, "ikv", B, (S, Di), w.ikv_std, dt)
-        out["igate"] = _stack(s, "igate", B, (S, Di), 1.0, dt)
-        out["qi"] = _stack(s, "qi", B, (S, Hi, Di), w.qi_std, dt)
-        out["wi"] = _stack(s, "wi", B, (S, Hi), w.wi_std, dt)
+    out = {k: _stack(s, k, w.batch, *v) for k, v in prefill_shapes(w, layer).items()}
+    out["sinks"] = _draw(s, "sinks", 0, (L.num_heads,), w.sink_std, "f32")
     return out
 
 
-def decode_cache_seq(w: Workload, seed: int, layer: int, b: int) -> Dict[str, np.ndarray]:
+def prefill_shapes(w: Workload, layer: int = 0):
+    """name -> (shape per sequence, std, dtype) of the prefill tensors."""
+    L = w.layers[layer]
+    S, H, D, dt = w.n_new, L.num_heads, L.head_dim, L.dtype
+    out = {"q": ((S, H, D), w.q_std, dt), "kv": ((S, D), w.kv_std, dt)}
+    if L.ratio > 0:
+        out["ckv"] = ((S, D), w.kv_std, dt)
+        out["cgate"] = ((S, D), 1.0, dt)
+    if L.has_indexer:
+        Hi, Di = L.index_heads, L.index_dim
+        out["ikv"] = ((S, Di), w.ikv_std, dt)
+        out["igate"] = ((S, Di), 1.0, dt)
+        out["qi"] = ((S, Hi, Di), w.qi_std, dt)
+        out["wi"] = ((S, Hi), w.wi_std, dt)
+    return out
+
+
+def prefill_rows(w: Workload, seed: int, layer: int, b: int, name: str, rows) -> np.ndarray:
+    """Rows of one prefill tensor of sequence b (same values as prefill_inputs)."""
+    shape, std, dt = prefill_shapes(w, layer)[name]
+    return draw_rows(seed * 16 + layer, name, b, shape, std, dt, rows)
+
+
+def cache_shapes(w: Workload, layer: int = 0):
+    """name -> (shape per sequence, std, dtype) of a decode workload's caches."""
+    L = w.layers[layer]
+    D, dt, std = L.head_dim, L.dtype, w.cache_std
+    out = {"win": ((L.window, D), std, dt)}
+    if L.ratio > 0:
+        P = w.pos0 // L.ratio
+        Ls = (1 + L.overlap) * L.ratio
+        out["pool"] = ((P, D), std, dt)
+        out["cstate_kv"] = ((Ls, D), w.kv_std, dt)
+        out["cstate_gate"] = ((Ls, D), 1.0, dt)
+        if L.has_indexer:
+            Di = L.index_dim
+            out["ipool"] = ((P, Di), std, dt)
+            out["istate_kv"] = ((Ls, Di), w.ikv_std, dt)
+            out["istate_gate"] = ((Ls, Di), 1.0, dt)
+    return out
+
+
+def cache_rows(w: Workload, seed: int, layer: int, b: int, name: str, rows) -> np.ndarray:
+    """Rows of one cache tensor of sequence b (same values as decode_cache_seq)."""
+    shape, std, dt = cache_shapes(w, layer)[name]
+    return draw_rows(seed * 16 + layer, name, b, shape, std, dt, rows)
+
+
+def decode_cache_seq(w: Workload, seed: int, layer: int, b: int,
+                     names: Optional[List[str]] = None) -> Dict[str, np.ndarray]:
     """Cache contents of one sequence for a decode workload.
 
     pool [P,D] and ipool [P,D_I] hold rotated pooled entries 0..P-1 with
@@ -235,22 +313,9 @@ def decode_cache_seq(w: Workload, seed: int, layer: int, b: int) -> Dict[str, np
     the raw compressor tokens of the (1+overlap)*m positions before pos0 at
     slot (position mod (1+overlap)*m).
     """
-    L = w.layers[layer]
-    s = seed * 16 + layer
-    D, dt, std = L.head_dim, L.dtype, w.cache_std
-    out = {"win": _draw(s, "win", b, (L.window, D), std, dt)}
-    if L.ratio > 0:
-        P = w.pos0 // L.ratio
-        Ls = (1 + L.overlap) * L.ratio
-        out["pool"] = _draw(s, "pool", b, (P, D), std, dt)
-        out["cstate_kv"] = _draw(s, "cstate_kv", b, (Ls, D), w.kv_std, dt)
-        out["cstate_gate"] = _draw(s, "cstate_gate", b, (Ls, D), 1.0, dt)
-        if L.has_indexer:
-            Di = L.index_dim
-            out["ipool"] = _draw(s, "ipool", b, (P, Di), std, dt)
-            out["istate_kv"] = _draw(s, "istate_kv", b, (Ls, Di), w.ikv_std, dt)
-            out["istate_gate"] = _draw(s, "istate_gate", b, (Ls, Di), 1.0, dt)
-    return out
+    shapes = cache_shapes(w, layer)
+    names = list(shapes) if names is None else names
+    return {k: _draw(seed * 16 + layer, k, b, *shapes[k]) for k in names}
 
 
 def decode_inputs(w: Workload, seed: int = 0, layer: int = 0,

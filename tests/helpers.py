@@ -108,3 +108,20 @@ def audit_topk(gpu_idx, ref_idx, scores, absterms, Di, Hi):
 def seq_f64(inp, b):
     """Sequence b of prefill inputs as float64 (sinks shared)."""
     return {k: (to_f64(v) if k == "sinks" else to_f64(v[b])) for k, v in inp.items()}
+
+
+class LazyF64:
+    """Read-only float64 view of a stored tensor, decoded only where indexed.
+
+    Lets the oracle walk a full-size sequence while converting just the rows
+    it touches (sampled queries, gathered cache rows)."""
+
+    def __init__(self, arr):
+        self.arr = arr
+        self.shape = arr.shape
+
+    def __getitem__(self, i):
+        return to_f64(self.arr[i])
+
+    def __len__(self):
+        return self.shape[0]
