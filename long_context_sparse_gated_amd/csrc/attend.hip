@@ -87,18 +87,19 @@ __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_
 // bytes/clk/CU with any of the swizzles tried.
 __device__ __forceinline__ int swz(int r) { return r & 15; }
 
-template <int NT>
+template <int NT, int R>
 __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, int n_new, int W, int m, int R, double base, float scale,
+    const int64_t* __restrict__ pos0, int n_new, int W, int m, double base, float scale,
     int nsplit, int csa) {
+  static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   // two separate arrays (not one indexed by parity) so the compiler can tell
   // the DMA target from the tile being read and need not wait for the DMA
   __shared__ __attribute__((aligned(1024))) bf16_t kbuf0[kCH * kAD];
   __shared__ __attribute__((aligned(1024))) bf16_t kbuf1[kCH * kAD];
-  __shared__ int32_t rid[kMaxRows];
+  __shared__ __attribute__((aligned(16))) int32_t rid[kMaxRows];
   __shared__ uint32_t vmask[kMaxRows / 32 + 1];
   __shared__ double2 cs[kMaxRope / 2];
 
@@ -144,11 +145,23 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 
   // gather of chunk c into dst: this wave moves rows RPW*wv .. +RPW-1
   auto issue = [&](int c, bf16_t* dst) {
+    // the wave's RPW row ids in one go (16-byte aligned; entries past r1 are
+    // replaced below), so the DMA issues do not each wait on an LDS read
+    int ids[RPW];
+    const int base_r = (c - c0) * kCH + RPW * wv;
+#pragma unroll
+    for (int e = 0; e < RPW; e += 4) {
+      const int4 v = *(const int4*)&rid[base_r + e];
+      ids[e] = v.x;
+      ids[e + 1] = v.y;
+      ids[e + 2] = v.z;
+      ids[e + 3] = v.w;
+    }
 #pragma unroll
     for (int e = 0; e < RPW; ++e) {
       const int rr = RPW * wv + e;
       const int jr = c * kCH + rr;
-      int id = jr < r1 ? rid[jr - r0] : -1;
+      int id = jr < r1 ? ids[e] : -1;
       if (id == -1) id = self_id;  // masked below; any finite row will do
       const bf16_t* src = id >= 0 ? win + (int64_t)id * kAD : pool + (int64_t)(-2 - id) * kAD;
       src += 8 * (lane ^ swz(rr));
@@ -158,7 +171,7 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   if (c0 < c1) issue(c0, kbuf0);
 
   // rotated query fragments: heads 16*NT*wv + 16*nt + r16, channels 32*kk + 8*g + 0..7
-  const int first = kAD - R;
+  constexpr int first = kAD - R;
   const int hw0 = 16 * NT * wv;  // first head of this wave
   uint4 Qf[NT][16];
 #pragma unroll
@@ -168,7 +181,7 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     for (int kk = 0; kk < 16; ++kk) {
       const int d0 = 32 * kk + 8 * g;
       uint4 v = *(const uint4*)(qrow + d0);
-      if (d0 + 8 > first) {
+      if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
         uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -338,14 +351,14 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
         const int d = 16 * mt + 4 * g;
         float o0 = O[nt][mt][0] * inv, o1 = O[nt][mt][1] * inv;
         float o2 = O[nt][mt][2] * inv, o3 = O[nt][mt][3] * inv;
-        if (d >= first) {  // pair (d, d+1) rotated at -t
+        if (16 * mt + 16 > first && d >= first) {  // pair (d, d+1) rotated at -t
           const double2 ca = cs[(d - first) >> 1];
           const float cf = (float)ca.x, sf = (float)ca.y;
           const float a0 = o0 * cf + o1 * sf, a1 = o1 * cf - o0 * sf;
           o0 = a0;
           o1 = a1;
         }
-        if (d + 2 >= first) {  // pair (d+2, d+3)
+        if (16 * mt + 16 > first && d + 2 >= first) {  // pair (d+2, d+3)
           const double2 cb = cs[(d + 2 - first) >> 1];
           const float cf = (float)cb.x, sf = (float)cb.y;
           const float b0 = o2 * cf + o3 * sf, b1 = o3 * cf - o2 * sf;
@@ -566,7 +579,8 @@ size_t attend_generic_shm(const Layer& L) {
 // ---------------------------------------------------------------------------
 
 bool attend_fast_shape(const Layer& L) {
-  return L.dtype == 1 && L.H == kAH && L.D == kAD && L.R <= kMaxRope && L.W >= 1;
+  return L.dtype == 1 && L.H == kAH && L.D == kAD && L.W >= 1 &&
+         (L.R == 16 || L.R == 32 || L.R == 64 || L.R == 128);
 }
 
 int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
@@ -601,10 +615,17 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
   if (attend_fast_shape(L)) {
     const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
     dim3 grid(bt.n, bt.B, ns);
-    attend_mfma<kHeadTiles><<<grid, 256 / kHeadTiles, 0, s>>>((const bf16_t*)q, (const bf16_t*)win, win_cap,
-                                     (const bf16_t*)pool, pool_cap, idx, L.k, sinks, (bf16_t*)out,
-                                     (float*)ws, bt.pos0, bt.n, L.W, m, L.R, L.base, L.scale, ns,
-                                     csa ? 1 : 0);
+#define CSA_ATTN_LAUNCH(RR)                                                                 \
+  attend_mfma<kHeadTiles, RR><<<grid, 256 / kHeadTiles, 0, s>>>(                            \
+      (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k, \
+      sinks, (bf16_t*)out, (float*)ws, bt.pos0, bt.n, L.W, m, L.base, L.scale, ns, csa ? 1 : 0)
+    switch (L.R) {
+      case 16: CSA_ATTN_LAUNCH(16); break;
+      case 32: CSA_ATTN_LAUNCH(32); break;
+      case 64: CSA_ATTN_LAUNCH(64); break;
+      default: CSA_ATTN_LAUNCH(128); break;
+    }
+#undef CSA_ATTN_LAUNCH
     if (ns > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
