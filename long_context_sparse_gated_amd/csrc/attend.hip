@@ -11,23 +11,25 @@
 // (eq. 27), output rotation (eq. 26); transformers PR 45616: sink from the
 // GPT-OSS eager attention].
 //
-// attend_mfma (H = 64, D = 512, bf16) -- one block of two waves per
-// (token, split); each wave owns 32 heads:
-//  * the rotated query of a wave's 32 heads lives in VGPRs as the B operand
-//    of S^T = K Q^T (16 x 16 x 32 bf16 MFMA), so every K byte read from LDS
-//    feeds 32 heads;
+// attend_mfma (H = 64, D = 512, bf16) -- one block of four waves per
+// (token, split).  The two products are divided differently among the waves:
+//  * S^T = K Q^T by head groups: wave w scores heads 16w .. 16w+15; their
+//    rotated queries live in VGPRs as the B operand (16 x 16 x 32 bf16
+//    MFMA), so the softmax state of a lane column is one head, and P goes to
+//    LDS (32 rows x 64 heads, bf16, 4 KB per chunk);
+//  * O^T += V^T P^T by channel slices: wave w accumulates all 64 heads over
+//    channels 128w .. 128w+127, so each V^T fragment read from LDS feeds four
+//    MFMAs (one per head group) and the slow transpose reads drop fourfold;
 //  * the K = V rows are gathered 32 at a time straight from HBM/L2 into LDS
 //    by the LDS-DMA loads (one 1 KB row per wave instruction), double
 //    buffered so the next chunk's gather overlaps this chunk's MFMAs.  Each
-//    row is stored once, row-major; the V^T operand of O^T = V^T P^T comes
-//    from the same bytes through the LDS transpose read (ds_read_b64_tr_b16),
-//    so one load feeds both uses of the K = V row;
+//    row is stored once, row-major; the V^T operand comes from the same bytes
+//    through the LDS transpose read (ds_read_b64_tr_b16);
 //  * 16-byte chunks of row r sit at a per-row XOR swizzle (swz below) so the
-//    QK^T reads and the transpose reads both hit distinct banks;
-//  * S^T puts one head per lane column, so the online softmax state and the
-//    O^T accumulators of a lane all belong to one head; the running max is
-//    only raised when a chunk exceeds it by more than 2^8 (P stays <= 256,
-//    exact to bf16 precision), which skips most rescales of O;
+//    16-byte K reads run at the contiguous rate;
+//  * the running max is only raised when a chunk exceeds it by more than 2^8
+//    (P stays <= 256, exact to bf16 precision); a raise is published per head
+//    so the channel-slice waves rescale their O columns;
 //  * P is rounded to bf16 for the PV product; accumulation is float32;
 //  * the sink enters once, at the end: (m, l) -> (max(m, s), l e^(m-M) +
 //    e^(s-M)); with several splits the merge kernel does this instead;
@@ -54,19 +56,38 @@ constexpr int kMaxRope = 128;    // rope channels supported by the fast path
 constexpr int kPart = kAD + 4;   // split partial row: O[512], m, l, 2 pad (16-byte rows)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max is raised
-// Tuning (compile time): 16-head tiles per wave (1: four waves per token,
-// 2: two waves per token) and the blocks per CU the register budget targets.
-#ifndef CSA_ATTN_HEAD_TILES
-#define CSA_ATTN_HEAD_TILES 1
-#endif
+// Tuning (compile time): the blocks per CU the register budget targets.
 #ifndef CSA_ATTN_MIN_BLOCKS
 #define CSA_ATTN_MIN_BLOCKS 2
 #endif
-constexpr int kHeadTiles = CSA_ATTN_HEAD_TILES;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Reductions across lane l and l ^ 16 / l ^ 32 with the gfx950 lane-swap
+// instructions (no LDS round trip); the max / sum of the two swapped values
+// pairs every lane with its partner whichever half moves.
+__device__ __forceinline__ float xmax16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
 __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
@@ -87,8 +108,10 @@ __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_
 // bytes/clk/CU with any of the swizzles tried.
 __device__ __forceinline__ int swz(int r) { return r & 15; }
 
-template <int NT, int R>
-__global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
+constexpr int kPRow = kCH + 8;  // LDS row of P^T per head: 32 row slots + pad (bf16)
+
+template <int R>
+__global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
@@ -102,10 +125,13 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   __shared__ __attribute__((aligned(16))) int32_t rid[kMaxRows];
   __shared__ uint32_t vmask[kMaxRows / 32 + 1];
   __shared__ double2 cs[kMaxRope / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t ps[kAH * kPRow];  // P^T, row slots per head
+  __shared__ float alph[kAH];   // this chunk's rescale of O per head
+  __shared__ int resc[4];       // head group w raised its max this chunk
+  __shared__ float mlf[2][kAH];  // final running max and sum per head
 
-  constexpr int NW = 4 / NT;          // waves per block (16*NT heads each)
-  constexpr int NTH = 64 * NW;        // threads per block
-  constexpr int RPW = kCH / NW;       // rows each wave gathers per chunk
+  constexpr int NTH = 256;
+  constexpr int RPW = kCH / 4;  // rows each wave gathers per chunk
   const int i = n_new - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -133,7 +159,7 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   }
   __syncthreads();
   // bit r of vmask[c - c0]: row r of chunk c takes part in the softmax
-  for (int j0 = 64 * wv; j0 < r1 - r0; j0 += 64 * NW) {
+  for (int j0 = 64 * wv; j0 < r1 - r0; j0 += 256) {
     const bool ok = j0 + lane < r1 - r0 && rid[j0 + lane] != -1;
     const unsigned long long bal = __ballot(ok);
     if (lane == 0) {
@@ -143,40 +169,56 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   }
   __syncthreads();
 
-  // gather of chunk c into dst: this wave moves rows RPW*wv .. +RPW-1
-  auto issue = [&](int c, bf16_t* dst) {
-    // the wave's RPW row ids in one go (16-byte aligned; entries past r1 are
-    // replaced below), so the DMA issues do not each wait on an LDS read
+  // gather of chunk c into dst: this wave moves rows RPW*wv .. +RPW-1.
+  // gather_prep loads the wave's row ids in one go (16-byte aligned; entries
+  // past r1 are replaced below) so the DMA issues do not each wait on an LDS
+  // read; gather_row(e) issues row e.  The per-row source offsets come from
+  // an opaque copy of the lane id and the wave index is made scalar: hoisted
+  // out of the loop these values would be spilled, and a scratch reload
+  // waits on vmcnt, i.e. on every DMA issued before it.
+  struct Gather {
     int ids[RPW];
-    const int base_r = (c - c0) * kCH + RPW * wv;
+    int ln, wvs, c;
+    bf16_t* dst;
+  };
+  auto gather_prep = [&](Gather& G, int c, bf16_t* dst) {
+    asm volatile("v_mov_b32 %0, %1" : "=v"(G.ln) : "v"(lane));
+    G.wvs = __builtin_amdgcn_readfirstlane(wv);
+    G.c = c;
+    G.dst = dst;
+    const int base_r = (c - c0) * kCH + RPW * G.wvs;
 #pragma unroll
     for (int e = 0; e < RPW; e += 4) {
       const int4 v = *(const int4*)&rid[base_r + e];
-      ids[e] = v.x;
-      ids[e + 1] = v.y;
-      ids[e + 2] = v.z;
-      ids[e + 3] = v.w;
+      G.ids[e] = v.x;
+      G.ids[e + 1] = v.y;
+      G.ids[e + 2] = v.z;
+      G.ids[e + 3] = v.w;
     }
+  };
+  auto gather_row = [&](const Gather& G, int e) {
+    const int rr = RPW * G.wvs + e;
+    const int jr = G.c * kCH + rr;
+    int id = jr < r1 ? G.ids[e] : -1;
+    if (id == -1) id = self_id;  // masked below; any finite row will do
+    const bf16_t* src = id >= 0 ? win + (int64_t)id * kAD : pool + (int64_t)(-2 - id) * kAD;
+    src += 8 * (G.ln ^ swz(rr));
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(G.dst + rr * kAD), 16, 0, 0);
+  };
+  auto issue = [&](int c, bf16_t* dst) {
+    Gather G;
+    gather_prep(G, c, dst);
 #pragma unroll
-    for (int e = 0; e < RPW; ++e) {
-      const int rr = RPW * wv + e;
-      const int jr = c * kCH + rr;
-      int id = jr < r1 ? ids[e] : -1;
-      if (id == -1) id = self_id;  // masked below; any finite row will do
-      const bf16_t* src = id >= 0 ? win + (int64_t)id * kAD : pool + (int64_t)(-2 - id) * kAD;
-      src += 8 * (lane ^ swz(rr));
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + rr * kAD), 16, 0, 0);
-    }
+    for (int e = 0; e < RPW; ++e) gather_row(G, e);
   };
   if (c0 < c1) issue(c0, kbuf0);
 
-  // rotated query fragments: heads 16*NT*wv + 16*nt + r16, channels 32*kk + 8*g + 0..7
+  // rotated query fragments of the wave's head group: head 16*wv + r16,
+  // channels 32*kk + 8*g + 0..7
   constexpr int first = kAD - R;
-  const int hw0 = 16 * NT * wv;  // first head of this wave
-  uint4 Qf[NT][16];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const bf16_t* qrow = q + (tok * kAH + hw0 + 16 * nt + r16) * kAD;
+  uint4 Qf[16];
+  {
+    const bf16_t* qrow = q + (tok * kAH + 16 * wv + r16) * kAD;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int d0 = 32 * kk + 8 * g;
@@ -196,19 +238,18 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
         }
         v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
-      Qf[nt][kk] = v;
+      Qf[kk] = v;
     }
   }
 
-  f32x4 O[NT][32];
-  float m_run[NT], l_run[NT];
+  // O^T accumulators of the wave's channel slice: channel 128*wv + 16*dt +
+  // 4*g + e, head 16*ht + r16
+  f32x4 O[8][4];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) O[nt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-  }
+    for (int ht = 0; ht < 4; ++ht) O[dt][ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // head 16*wv + r16
   const float sl2 = scale * kLog2e;
 
   // LDS byte offsets (constant per lane).  The swizzle only touches the low
@@ -220,6 +261,7 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   //    (+16 for the upper 4 rows) and channels 4 (s mod 4) .. +3 of the
   //    16-channel tile mt = 8u + v, i.e. chunk 16u + ((2v + (s mod 4)/2) ^
   //    swz(row)) plus 8 bytes for odd s: bases tr_v[v] (row + 16 adds 16 KB).
+  //    The wave's slice is tiles mt = 8 wv + dt: base tr_v[dt] + 256 wv.
   int kb_v[4], tr_v[8];
 #pragma unroll
   for (int v = 0; v < 4; ++v) kb_v[v] = r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
@@ -227,82 +269,87 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const int trA = 4 * g + (r16 >> 2);
     const int trc = (r16 & 3) >> 1, trh = (r16 & 1) * 8;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh;
+    for (int v = 0; v < 8; ++v)
+      tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh + 256 * wv;
   }
 
-  auto chunk = [&](int c, const bf16_t* cur) {
+  auto chunk = [&](int c, const bf16_t* cur, int cn, bf16_t* nxt) {
     const char* kb = (const char*)cur;
-
-    // ---- S^T = K Q^T: 32 rows x 16*NT heads
-    f32x4 S[2][NT];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // the next chunk's gather (if any) is issued row by row between the
+    // QK^T MFMAs below
+    Gather G;
+    const bool gat = cn < c1;
+    if (gat) gather_prep(G, cn, nxt);
+    // ---- S^T = K Q^T: 32 rows x the wave's 16 heads
+    f32x4 S0 = (f32x4){0.f, 0.f, 0.f, 0.f}, S1 = S0;
     // swz(16*mt + r16) == swz(r16): the second row tile is 16 KB further
     auto kfrag = [&](int kk, int mt) {
       return *(const uint4*)(kb + kb_v[kk & 3] + (kk >> 2) * 256 + mt * 16384);
     };
-    uint4 acur0 = kfrag(0, 0), acur1 = kfrag(0, 1);
+    uint4 ka0 = kfrag(0, 0), ka1 = kfrag(0, 1);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      uint4 anx0 = acur0, anx1 = acur1;
+      const uint4 a0 = ka0, a1 = ka1;
       if (kk + 1 < 16) {
-        anx0 = kfrag(kk + 1, 0);
-        anx1 = kfrag(kk + 1, 1);
+        ka0 = kfrag(kk + 1, 0);
+        ka1 = kfrag(kk + 1, 1);
       }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        S[0][nt] = mfma16(acur0, Qf[nt][kk], S[0][nt]);
-        S[1][nt] = mfma16(acur1, Qf[nt][kk], S[1][nt]);
-      }
-      acur0 = anx0;
-      acur1 = anx1;
+      S0 = mfma16(a0, Qf[kk], S0);
+      S1 = mfma16(a1, Qf[kk], S1);
+      if (gat && (kk & 1) && (kk >> 1) < RPW) gather_row(G, kk >> 1);
     }
-    // ---- online softmax (log2 domain); lane column = one head per nt
+    // ---- online softmax (log2 domain); lane column = head 16*wv + r16
     const uint32_t vm = vmask[c - c0] >> (4 * g);
-    uint4 Pf[NT];
+    float sv[8];
+    float cmax = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float sv[8];
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float v = (vm >> (16 * mt + ii)) & 1u ? S[mt][nt][ii] * sl2 : -INFINITY;
-          sv[4 * mt + ii] = v;
-          cmax = fmaxf(cmax, v);
-        }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      if (__any(cmax > m_run[nt] + kLazy)) {
-        const float m_new = fmaxf(m_run[nt], cmax);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-#pragma unroll
-        for (int mt = 0; mt < 32; ++mt) O[nt][mt] *= alpha;
-        l_run[nt] *= alpha;
-        m_run[nt] = m_new;
-      }
-      const float mr = m_run[nt];
-      float psum = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        // exp2(-inf) = 0 for masked rows; mr is finite once any row was seen
-        const float pa = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j] - mr);
-        const float pb = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j + 1] - mr);
-        psum += pa + pb;
-        pk[j >> 1] = pack_bf16x2(pa, pb);
-      }
-      l_run[nt] += psum;
-      Pf[nt] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    for (int ii = 0; ii < 4; ++ii) {
+      sv[ii] = (vm >> ii) & 1u ? S0[ii] * sl2 : -INFINITY;
+      sv[4 + ii] = (vm >> (16 + ii)) & 1u ? S1[ii] * sl2 : -INFINITY;
+      cmax = fmaxf(cmax, fmaxf(sv[ii], sv[4 + ii]));
     }
-    // ---- O^T += V^T P^T, V^T through the transpose read of the same rows
+    cmax = xmax32(xmax16(cmax));
+    const bool raise = __any(cmax > m_run + kLazy);
+    float alpha = 1.f;
+    if (raise) {
+      const float m_new = fmaxf(m_run, cmax);
+      alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    float psum = 0.f;
+    uint32_t pk[4];
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      // swz(trA + 16) == swz(trA) since trA < 16: the upper rows are 16 KB on
-      const char* pa = kb + tr_v[mt & 7] + (mt >> 3) * 256;
+    for (int j = 0; j < 8; j += 2) {
+      // exp2(-inf) = 0 for masked rows; m_run is finite once a row was seen
+      const float pa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_run);
+      const float pb = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[j + 1] - m_run);
+      psum += pa + pb;
+      pk[j >> 1] = pack_bf16x2(pa, pb);
+    }
+    l_run += psum;
+    // P^T slots of lane group g hold rows 4g..4g+3 and 16+4g..16+4g+3
+    *(uint4*)&ps[(16 * wv + r16) * kPRow + 8 * g] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (g == 0) alph[16 * wv + r16] = alpha;
+    if (lane == 0) resc[wv] = raise ? 1 : 0;
+    __syncthreads();
+
+    // ---- O^T += V^T P^T over the wave's channel slice, all 64 heads
+    if (resc[0] | resc[1] | resc[2] | resc[3]) {
+      float a4[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) a4[ht] = alph[16 * ht + r16];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) O[dt][ht] *= a4[ht];
+    }
+    uint4 Pf[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) Pf[ht] = *(const uint4*)&ps[(16 * ht + r16) * kPRow + 8 * g];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const char* pa = kb + tr_v[dt];
       const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)pa);
       const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 16384));
       const uint4 a = make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
@@ -310,55 +357,57 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
                                  (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
                                  (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[nt][mt] = mfma16(a, Pf[nt], O[nt][mt]);
+      for (int ht = 0; ht < 4; ++ht) O[dt][ht] = mfma16(a, Pf[ht], O[dt][ht]);
     }
   };
   for (int c = c0; c < c1; c += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (c + 1 < c1) issue(c + 1, kbuf1);
-    chunk(c, kbuf0);
+    chunk(c, kbuf0, c + 1, kbuf1);
     if (c + 1 < c1) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (c + 2 < c1) issue(c + 2, kbuf0);
-      chunk(c + 1, kbuf1);
+      chunk(c + 1, kbuf1, c + 2, kbuf0);
     }
   }
 
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    l_run[nt] += __shfl_xor(l_run[nt], 16, 64);
-    l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
+  l_run = xsum32(xsum16(l_run));
+  if (g == 0) {
+    mlf[0][16 * wv + r16] = m_run;
+    mlf[1][16 * wv + r16] = l_run;
   }
+  __syncthreads();  // every wave is done with kbuf; m, l of every head published
 
   if (nsplit == 1) {
-    __syncthreads();  // every wave is done with kbuf: reuse it to stage the output
-    // this wave's [16*NT heads][512] bf16, chunks swizzled by head
-    constexpr int kStage = 16 * NT * 1024;  // bytes per wave
-    constexpr int kPerBuf = (kCH * kAD * 2) / kStage;
-    char* ob = (wv < kPerBuf ? (char*)kbuf0 : (char*)kbuf1) + (wv % kPerBuf) * kStage;
+    // the whole [64 heads][512] bf16 output, chunks swizzled by head: heads
+    // 0..31 in kbuf0, 32..63 in kbuf1
+    float inv[4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int hl = 16 * nt + r16, head = hw0 + hl;
+    for (int ht = 0; ht < 4; ++ht) {
+      const int head = 16 * ht + r16;
+      const float mh = mlf[0][head], lh = mlf[1][head];
       const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
-      const float M = fmaxf(m_run[nt], sink);
-      const float f = exp2f(m_run[nt] - M);
-      const float lt = l_run[nt] * f + (sinks ? exp2f(sink - M) : 0.f);
-      const float inv = f / lt;
+      const float M = fmaxf(mh, sink);
+      const float f = __builtin_amdgcn_exp2f(mh - M);
+      const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
+      inv[ht] = f / lt;
+    }
 #pragma unroll
-      for (int mt = 0; mt < 32; ++mt) {
-        const int d = 16 * mt + 4 * g;
-        float o0 = O[nt][mt][0] * inv, o1 = O[nt][mt][1] * inv;
-        float o2 = O[nt][mt][2] * inv, o3 = O[nt][mt][3] * inv;
-        if (16 * mt + 16 > first && d >= first) {  // pair (d, d+1) rotated at -t
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 128 * wv + 16 * dt + 4 * g;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const int head = 16 * ht + r16;
+        float o0 = O[dt][ht][0] * inv[ht], o1 = O[dt][ht][1] * inv[ht];
+        float o2 = O[dt][ht][2] * inv[ht], o3 = O[dt][ht][3] * inv[ht];
+        if (d >= first) {  // pair (d, d+1) rotated at -t
           const double2 ca = cs[(d - first) >> 1];
           const float cf = (float)ca.x, sf = (float)ca.y;
           const float a0 = o0 * cf + o1 * sf, a1 = o1 * cf - o0 * sf;
           o0 = a0;
           o1 = a1;
         }
-        if (16 * mt + 16 > first && d + 2 >= first) {  // pair (d+2, d+3)
+        if (d + 2 >= first) {  // pair (d+2, d+3)
           const double2 cb = cs[(d + 2 - first) >> 1];
           const float cf = (float)cb.x, sf = (float)cb.y;
           const float b0 = o2 * cf + o3 * sf, b1 = o3 * cf - o2 * sf;
@@ -368,28 +417,30 @@ __global__ void __launch_bounds__(256 / NT, CSA_ATTN_MIN_BLOCKS) attend_mfma(
         uint2 st;
         st.x = pack_bf16x2(o0, o1);
         st.y = pack_bf16x2(o2, o3);
-        const int chunk = (d >> 3) ^ (hl & 15);
-        *(uint2*)(ob + hl * 1024 + (chunk << 4) + ((d & 7) << 1)) = st;
+        char* ob = (head < 32 ? (char*)kbuf0 : (char*)kbuf1) + (head & 31) * 1024;
+        *(uint2*)(ob + ((((d >> 3) ^ (head & 15))) << 4) + ((d & 7) << 1)) = st;
       }
     }
     __syncthreads();
-    bf16_t* orow = out + (tok * kAH + hw0) * kAD;
+    bf16_t* orow = out + tok * kAH * kAD;
 #pragma unroll 4
-    for (int hl = 0; hl < 16 * NT; ++hl) {
-      const uint4 v = *(const uint4*)(ob + hl * 1024 + ((lane ^ (hl & 15)) << 4));
-      *(uint4*)(orow + hl * kAD + 8 * lane) = v;
+    for (int hh = 0; hh < 16; ++hh) {
+      const int head = 16 * wv + hh;
+      const char* ob = (head < 32 ? (const char*)kbuf0 : (const char*)kbuf1) + (head & 31) * 1024;
+      const uint4 v = *(const uint4*)(ob + ((lane ^ (head & 15)) << 4));
+      *(uint4*)(orow + head * kAD + 8 * lane) = v;
     }
   } else {
+    float* pbase = part + (tok * nsplit + split) * kAH * kPart;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int head = hw0 + 16 * nt + r16;
-      float* prow = part + ((tok * nsplit + split) * kAH + head) * kPart;
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int mt = 0; mt < 32; ++mt) *(f32x4*)(prow + 16 * mt + 4 * g) = O[nt][mt];
-      if (g == 0) {
-        prow[kAD] = m_run[nt];
-        prow[kAD + 1] = l_run[nt];
-      }
+      for (int ht = 0; ht < 4; ++ht)
+        *(f32x4*)(pbase + (16 * ht + r16) * kPart + 128 * wv + 16 * dt + 4 * g) = O[dt][ht];
+    if (g == 0) {
+      float* prow = pbase + (16 * wv + r16) * kPart;
+      prow[kAD] = m_run;
+      prow[kAD + 1] = l_run;
     }
   }
 }
@@ -616,7 +667,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
     const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
     dim3 grid(bt.n, bt.B, ns);
 #define CSA_ATTN_LAUNCH(RR)                                                                 \
-  attend_mfma<kHeadTiles, RR><<<grid, 256 / kHeadTiles, 0, s>>>(                            \
+  attend_mfma<RR><<<grid, 256, 0, s>>>(                                                     \
       (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k, \
       sinks, (bf16_t*)out, (float*)ws, bt.pos0, bt.n, L.W, m, L.base, L.scale, ns, csa ? 1 : 0)
     switch (L.R) {
