@@ -1,19 +1,32 @@
-"""Throughput of the CSA layer hot path on one MI355X.
+"""Throughput of the compressed-attention layer hot path on one MI355X.
 
-Workload: the CSA prefill layer, bf16, B=1, S=8192, 64 query heads, one shared
-K=V head, head_dim 512 (64 rope channels, base 160000), window 128,
-compressor m=4 with overlapping windows (2048 entries), indexer 64 heads x
-128 with top-512.  Inputs are seeded synthetic tensors (synth.prefill_inputs,
-seed 0), resident in HBM before timing starts.
+Headline (``value``): the CSA prefill layer, bf16, B=1, S=8192, 64 query
+heads, one shared K=V head, head_dim 512 (64 rope channels, base 160000),
+window 128, compressor m=4 with overlapping windows (2048 entries), indexer
+64 heads x 128 with top-512.  One step = the whole hot path for the 8192
+tokens: window append (RoPE of the K=V rows), the main and indexer
+compressors, indexer scores + top-k, and the sparse attention with sink and
+output un-rotation.
 
-One step = the whole hot path for the 8192 tokens: window append (RoPE of the
-K=V rows), the main and indexer compressors, indexer scores + top-k, and the
-sparse attention with sink and output un-rotation.
+The same JSON line carries, under ``workloads``, the other layer shapes timed
+the same way (one step = every call of the layer(s) for one batch):
 
-Printed JSON (one line): tokens/s of the step; the roofline of the dominant
-kernel (the attention launch, timed with HIP events on its stream inside the
-timed region; algorithmic FLOPs = 4 * H * D * sum over queries of attended
-rows); the CPU oracle's rate on a bounded sample (``cpu_baseline``).
+* ``hca_prefill``  S=65536, m'=128 non-overlapping pooling, dense attention
+                   over the window and every visible entry;
+* ``csa_decode``   64 sequences x 1 token at position 131072 (32768 entries);
+* ``mixed_decode`` 4 sequences x 1 token at position 1048576 through a CSA
+                   layer (262144 entries), an HCA layer (8192 entries) and a
+                   sliding-only layer.
+
+Prefill steps are priced in MFMA FLOPs (4 H D per attended (query, row)
+pair, plus 2 H_I D_I per scored (query, key) pair); decode steps in the HBM
+bytes the step must move at least once (new-token inputs and outputs, cache
+rows read, cache slots written).  A decode step is replayed as one captured
+HIP graph (its eager time is reported beside it).  Inputs are seeded synthetic tensors
+(``synth``), resident in HBM before timing starts.  The attention launch of
+the headline step is timed with HIP events on its stream inside the timed
+region (``roofline``); ``cpu_baseline`` is the CPU oracle's rate on a bounded
+sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -31,11 +44,48 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
 def attended_rows(S, W, m, k):
-    """Sum over queries t < S of (window rows + selected entries)."""
+    """Sum over queries t < S of (window rows + attended entries); k=0: all visible."""
     tot = 0
     for t in range(S):
-        tot += min(W, t + 1) + min(k, (t + 1) // m)
+        nv = (t + 1) // m if m else 0
+        tot += min(W, t + 1) + (min(k, nv) if k else nv)
     return tot
+
+
+def scored_pairs(S, m):
+    return sum((t + 1) // m for t in range(S))
+
+
+def prefill_flops(spec, S):
+    attn = 4.0 * spec.num_heads * spec.head_dim * attended_rows(
+        S, spec.window, spec.ratio, spec.topk if spec.has_indexer else 0)
+    idx = (2.0 * spec.index_heads * spec.index_dim * scored_pairs(S, spec.ratio)
+           if spec.has_indexer else 0.0)
+    return attn, idx
+
+
+def decode_bytes(spec, B, t):
+    """HBM bytes one decode call of one token per sequence must move."""
+    e = 2 if spec.dtype == "bf16" else 4
+    H, D = spec.num_heads, spec.head_dim
+    per = 2 * H * D * e + 2 * D * e + min(spec.window, t + 1) * D * e + H * 4
+    if spec.ratio:
+        Ls = (1 + spec.overlap) * spec.ratio
+        emit = (t + 1) % spec.ratio == 0
+        widths = [D] + ([spec.index_dim] if spec.has_indexer else [])
+        for wd in widths:
+            per += 4 * wd * e                       # new kv+gate read, state slot written
+            if emit:
+                per += 2 * (Ls - 1) * wd * e + wd * e   # state rows read, entry written
+        nv = (t + 1) // spec.ratio
+        if spec.has_indexer:
+            Hi, Di = spec.index_heads, spec.index_dim
+            per += Hi * Di * e + Hi * e + nv * Di * e   # indexer query, weights, keys
+            per += 2 * spec.topk * 4                    # ids written, read back
+            per += min(spec.topk, nv) * D * e          # selected entries
+        else:
+            per += nv * D * e                          # every visible entry
+    return B * per
 
 
 def cpu_baseline(spec, inp, stride):
@@ -60,6 +110,165 @@ def cpu_baseline(spec, inp, stride):
                       f"{len(os.sched_getaffinity(0))} host cores"}
 
 
+def _dev(torch, a):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def _time_steps(torch, step, steps, warmup, attn_events=False):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)] if attn_events else [None] * steps)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    attn = (sum(a.elapsed_time(b) for a, b in evs) / steps) if attn_events else None
+    return ms, attn
+
+
+def prefill_leg(torch, m, name, steps, warmup, attn_events=False):
+    import synth
+    from long_context_sparse_gated_amd.layer import LayerCache
+    w = synth.workload(name)
+    spec, S = w.layers[0], w.n_new
+    inp = synth.prefill_inputs(w, 0)
+    L = m.Layer.from_spec(spec)
+    a = {k: _dev(torch, v) for k, v in inp.items()}
+    cache = LayerCache(L, 1, S, S // spec.ratio)
+    pos0 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(a["q"])
+    stream = torch.cuda.current_stream()
+    if spec.has_indexer:
+        idx = torch.empty(1, S, spec.topk, dtype=torch.int32, device="cuda")
+        ws_i = cache.workspace(S, m.CSA_OP_INDEX_TOPK)
+        ws_a = cache.workspace(S, m.CSA_OP_ATTEND)
+    else:
+        ws_a = cache.workspace(S, m.CSA_OP_HCA_ATTEND)
+
+    # every step prefills the same sequence from position 0 (a prefill from 0
+    # never reads the compressor state, so steps are identical)
+    def step(ev):
+        m.csa_window_append(L, pos0, 0, a["kv"], cache.ring)
+        m.csa_compress(L, pos0, 0, a["ckv"], a["cgate"], cache.cstate_kv, cache.cstate_gate,
+                       cache.pool, spec.rope_dim)
+        if spec.has_indexer:
+            m.csa_compress(L, pos0, 0, a["ikv"], a["igate"], cache.istate_kv,
+                           cache.istate_gate, cache.ipool, spec.index_rope_dim)
+            m.csa_index_topk(L, pos0, 0, a["qi"], a["wi"], cache.ipool, idx, workspace=ws_i)
+        if ev is not None:
+            ev[0].record(stream)
+        if spec.has_indexer:
+            m.csa_attend(L, pos0, 0, a["q"], cache.ring, cache.pool, idx, a["sinks"], out, ws_a)
+        else:
+            m.hca_attend(L, pos0, 0, a["q"], cache.ring, cache.pool, a["sinks"], out, ws_a)
+        if ev is not None:
+            ev[1].record(stream)
+
+    ms, attn_ms = _time_steps(torch, step, steps, warmup, attn_events)
+    f_attn, f_idx = prefill_flops(spec, S)
+    res = {"ms_per_step": ms, "tokens_per_s": S / (ms * 1e-3),
+           "step_tflops": (f_attn + f_idx) / (ms * 1e-3) / 1e12,
+           "step_frac_bf16_peak": (f_attn + f_idx) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "attend_flop": f_attn, "index_flop": f_idx}
+    if attn_ms is not None:
+        res["attend_ms"] = attn_ms
+    del a, cache, out
+    return spec, inp, res
+
+
+def decode_leg(torch, m, name, steps, warmup):
+    import synth
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    w = synth.workload(name)
+    t, B = w.pos0, w.batch
+    layers, total_bytes = [], 0
+    for li, spec in enumerate(w.layers):
+        L = m.Layer.from_spec(spec)
+        pool_cap = (t + 1) // spec.ratio if spec.ratio else 1
+        cache = LayerCache(L, B, spec.window, pool_cap)
+        for b in range(B):  # one sequence at a time keeps host memory bounded
+            c = synth.decode_cache_seq(w, 0, li, b)
+            cache.ring[b].copy_(_dev(torch, c["win"]))
+            if spec.ratio:
+                P = t // spec.ratio
+                cache.pool[b, :P].copy_(_dev(torch, c["pool"]))
+                cache.cstate_kv[b].copy_(_dev(torch, c["cstate_kv"]))
+                cache.cstate_gate[b].copy_(_dev(torch, c["cstate_gate"]))
+                if spec.has_indexer:
+                    cache.ipool[b, :P].copy_(_dev(torch, c["ipool"]))
+                    cache.istate_kv[b].copy_(_dev(torch, c["istate_kv"]))
+                    cache.istate_gate[b].copy_(_dev(torch, c["istate_gate"]))
+            del c
+        a = {k: _dev(torch, v) for k, v in synth.prefill_inputs(w, 0, li).items()}
+        out = torch.empty_like(a["q"])
+        idx = (torch.empty(B, 1, spec.topk, dtype=torch.int32, device="cuda")
+               if spec.has_indexer else None)
+        layers.append((cache, a, out, idx))
+        total_bytes += decode_bytes(spec, B, t)
+    p0 = torch.full((B,), t, dtype=torch.int64, device="cuda")
+
+    # every step decodes the same token at the same position: the window slot,
+    # the compressor state slot and (when an entry closes) the pool entry are
+    # rewritten with the same values, so steps are identical
+    def step(_ev):
+        for cache, a, out, idx in layers:
+            layer_step(cache, p0, t, a["q"], a["kv"], a.get("ckv"), a.get("cgate"),
+                       a.get("ikv"), a.get("igate"), a.get("qi"), a.get("wi"), a["sinks"],
+                       out=out, topk_idx=idx)
+
+    eager_ms, _ = _time_steps(torch, step, steps, warmup)
+    # a decode step is a short chain of small launches: replay it as one HIP
+    # graph (captured after the warmup above, which also sized the workspaces)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None)
+    torch.cuda.synchronize()
+    ms, _ = _time_steps(torch, lambda _ev: graph.replay(), steps, warmup)
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    del graph, layers
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": total_bytes,
+            "achieved_GBs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "hip_graph": True,
+            "eager_ms_per_step": eager_ms}
+
+
+def calib_copy(torch, mib):
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_leg(torch, m, name, args):
+    if name in ("csa_prefill", "hca_prefill"):
+        steps = args.steps if name == "csa_prefill" else max(2, args.steps // 4)
+        _, _, r = prefill_leg(torch, m, name, steps, min(args.warmup, 1 if
+                              name == "hca_prefill" else args.warmup), attn_events=True)
+        r["roofline"] = {"bound": "mfma", "kernel": "attend_mfma",
+                         "achieved": r["attend_flop"] / (r["attend_ms"] * 1e-3) / 1e12,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        r["roofline"]["frac"] = r["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+        return r
+    if name in ("csa_decode", "mixed_decode"):
+        return decode_leg(torch, m, name, 5 * args.steps, args.warmup)
+    raise SystemExit(f"unknown workload {name}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,6 +276,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1)
+    ap.add_argument("--legs", default="hca_prefill,csa_decode,mixed_decode",
+                    help="comma list of further workloads to time after the headline "
+                         "(hca_prefill, csa_decode, mixed_decode; empty for none)")
+    ap.add_argument("--only", default="",
+                    help="time just this one workload and print its object (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), so a "
                          "counter run can scale HBM byte counters against a known size")
@@ -77,83 +291,35 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
     import long_context_sparse_gated_amd as m
-    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
-
-    w = synth.workload("csa_prefill")
-    spec = w.layers[0]
-    S = w.n_new
-    inp = synth.prefill_inputs(w, 0)
     m.load_library()
-    L = m.Layer.from_spec(spec)
 
-    def dev(a):
-        import numpy as np
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
+    if args.only:
+        r = run_leg(torch, m, args.only, args)
+        calib_copy(torch, args.calib_copy_mib)
+        print(json.dumps({"workload": args.only, **r}), flush=True)
+        return
 
-    a = {k: dev(v) for k, v in inp.items()}
-    cache = LayerCache(L, 1, S, S // spec.ratio)
-    pos0 = torch.zeros(1, dtype=torch.int64, device="cuda")
-    out = torch.empty_like(a["q"])
-    idx = torch.empty(1, S, spec.topk, dtype=torch.int32, device="cuda")
-    ws_i = cache.workspace(S, m.CSA_OP_INDEX_TOPK)
-    ws_a = cache.workspace(S, m.CSA_OP_ATTEND)
-    stream = torch.cuda.current_stream()
+    spec, inp, head = prefill_leg(torch, m, "csa_prefill", args.steps, args.warmup,
+                                  attn_events=True)
+    calib_copy(torch, args.calib_copy_mib)
+    torch.cuda.empty_cache()
 
-    def step(ev=None):
-        m.csa_window_append(L, pos0, 0, a["kv"], cache.ring)
-        m.csa_compress(L, pos0, 0, a["ckv"], a["cgate"], cache.cstate_kv, cache.cstate_gate,
-                       cache.pool, spec.rope_dim)
-        m.csa_compress(L, pos0, 0, a["ikv"], a["igate"], cache.istate_kv, cache.istate_gate,
-                       cache.ipool, spec.index_rope_dim)
-        m.csa_index_topk(L, pos0, 0, a["qi"], a["wi"], cache.ipool, idx, workspace=ws_i)
-        if ev is not None:
-            ev[0].record(stream)
-        m.csa_attend(L, pos0, 0, a["q"], cache.ring, cache.pool, idx, a["sinks"], out, ws_a)
-        if ev is not None:
-            ev[1].record(stream)
+    legs = {}
+    for name in [x for x in args.legs.split(",") if x]:
+        legs[name] = run_leg(torch, m, name, args)
+        torch.cuda.empty_cache()
 
-    # every step prefills the same sequence from position 0 (a prefill from 0
-    # never reads the compressor state, so steps are identical)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    attn_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
-
-    rows = attended_rows(S, spec.window, spec.ratio, spec.topk)
-    flops = 4.0 * spec.num_heads * spec.head_dim * rows
-    achieved = flops / (attn_ms * 1e-3) / 1e12
+    S = 8192
+    achieved = head["attend_flop"] / (head["attend_ms"] * 1e-3) / 1e12
     res = {
         "metric": "CSA prefill tokens/s @S=8192",
-        "value": S / (ms_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -165,8 +331,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attend_mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "launch_ms": attn_ms, "algorithmic_flop": flops},
-        "attend_share_of_step": attn_ms / ms_step,
+                     "launch_ms": head["attend_ms"], "algorithmic_flop": head["attend_flop"]},
+        "attend_share_of_step": head["attend_ms"] / head["ms_per_step"],
+        "step_frac_bf16_peak": head["step_frac_bf16_peak"],
+        "workloads": legs,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_stride)

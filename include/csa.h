@@ -195,6 +195,8 @@ csa_status csa_attend(const csa_layer* layer, const csa_batch* batch,
 /* HCA / sliding-only attention: as csa_attend, but the pooled rows of query t
  * are every visible entry w < (t+1)/m; compress_ratio == 0 attends to the
  * window alone.  workspace: csa_workspace_bytes(..., CSA_OP_HCA_ATTEND).
+ * With H = 64, D = 512 in bf16, a query attends to at most 262144 rows
+ * (window + pool_cap); beyond that the call returns CSA_ERR_UNSUPPORTED.
  * Source: model page, sec. 2.3 (HCA has no indexer, every pool entry takes
  * part; sliding_attention layers have no long-range branch). */
 csa_status hca_attend(const csa_layer* layer, const csa_batch* batch,

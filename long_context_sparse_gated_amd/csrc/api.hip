@@ -11,7 +11,6 @@ namespace {
 using csa::Batch;
 using csa::Layer;
 
-constexpr int kMaxTopk = 4096;
 constexpr int kMaxWidth = 2048;   // compressor row width (LDS row buffer)
 constexpr int64_t kMaxRowId = 2147483000LL;
 
@@ -55,7 +54,7 @@ csa_status to_batch(const csa_batch* in, Batch* b) {
 
 csa_status indexer_ok(const Layer& L) {
   if (L.m < 1 || L.Hi < 1 || L.Di < 2 || (L.Di & 1) || L.Ri < 0 || (L.Ri & 1) || L.Ri > L.Di ||
-      L.k < 1 || L.k > kMaxTopk)
+      L.k < 1 || L.k > csa::kMaxTopK)
     return CSA_ERR_SHAPE;
   return CSA_OK;
 }
@@ -96,7 +95,7 @@ csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const v
   if ((st = to_batch(batch, &b)) != CSA_OK) return st;
   if (!q || !win || !out) return CSA_ERR_NULL;
   if (csa_layer_kind) {
-    if (L.m < 1 || L.k < 1 || L.k > kMaxTopk) return CSA_ERR_SHAPE;
+    if (L.m < 1 || L.k < 1 || L.k > csa::kMaxTopK) return CSA_ERR_SHAPE;
     if (!topk_idx || !pool) return CSA_ERR_NULL;
   }
   if (L.m > 0) {
@@ -106,6 +105,8 @@ csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const v
   }
   if ((st = window_ok(L, b, win_cap)) != CSA_OK) return st;
   if (!csa::attend_fast_shape(L) && !generic_attend_limit_ok(L)) return CSA_ERR_UNSUPPORTED;
+  if (csa::attend_splits(L, b.B, b.n, L.m > 0 ? pool_cap : 0, csa_layer_kind) < 1)
+    return CSA_ERR_UNSUPPORTED;  // more rows per token than the split grid covers
   const size_t need = csa::attend_workspace_bytes(L, b.B, b.n, L.m > 0 ? pool_cap : 0,
                                                   csa_layer_kind);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
@@ -210,7 +211,7 @@ size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
       if (indexer_ok(L) != CSA_OK) return (size_t)-1;
       return csa::index_workspace_bytes(L, batch, n_new, pool_cap);
     case CSA_OP_ATTEND:
-      if (L.m < 1 || L.k < 1 || L.k > kMaxTopk) return (size_t)-1;
+      if (L.m < 1 || L.k < 1 || L.k > csa::kMaxTopK) return (size_t)-1;
       return csa::attend_workspace_bytes(L, batch, n_new, pool_cap, true);
     case CSA_OP_HCA_ATTEND:
       return csa::attend_workspace_bytes(L, batch, n_new, L.m > 0 ? pool_cap : 0, false);

@@ -446,61 +446,77 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 }
 
 // Merge of split partials (m in log2 units, l, unnormalised O) with the sink,
-// then the -t rotation of the rope slice and the store.
-__global__ void __launch_bounds__(256) attend_merge(const float* __restrict__ part,
-                                                    const float* __restrict__ sinks,
-                                                    bf16_t* __restrict__ out,
-                                                    const int64_t* __restrict__ pos0, int n_new,
-                                                    int R, double base, int nsplit) {
+// then the -t rotation of the rope slice and the store.  One wave per
+// (token, head): lane s first reads split s's (m, l), then every lane merges
+// 8 channels over all splits.
+constexpr int kMergeHeads = 4;  // heads (waves) per merge block
+constexpr int kMaxSplits = 256;
+
+__global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
+    const float* __restrict__ part, const float* __restrict__ sinks, bf16_t* __restrict__ out,
+    const int64_t* __restrict__ pos0, int n_new, int R, double base, int nsplit) {
   __shared__ double2 cs[kAD / 2];
+  __shared__ float fs[kMergeHeads][kMaxSplits];
   const int64_t tok = blockIdx.x;
+  const int lane = threadIdx.x & 63, hh = threadIdx.x >> 6;
+  const int h = blockIdx.y * kMergeHeads + hh;
   const int b = (int)(tok / n_new), i = (int)(tok % n_new);
   const int64_t t = pos0[b] + i;
-  for (int j = threadIdx.x; j < R / 2; j += 256) {
+  for (int j = threadIdx.x; j < R / 2; j += 64 * kMergeHeads) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
-  __syncthreads();
-  const int h = threadIdx.x >> 2, dq = (threadIdx.x & 3) * (kAD / 4);
   const float sink = sinks ? sinks[h] * kLog2e : -INFINITY;
+  const float* ph = part + (tok * nsplit * kAH + h) * kPart;  // split s at + s * kAH * kPart
   float M = sink;
-  for (int s = 0; s < nsplit; ++s)
-    M = fmaxf(M, part[((tok * nsplit + s) * kAH + h) * kPart + kAD]);
-  float lt = sinks ? exp2f(sink - M) : 0.f;
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ph[(int64_t)s * kAH * kPart + kAD]);
+  M = wave_max(M);
+  float lt = 0.f;
+  for (int s = lane; s < nsplit; s += 64) {
+    const float* pr = ph + (int64_t)s * kAH * kPart;
+    const float ms = pr[kAD];
+    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    fs[hh][s] = f;
+    lt += f * pr[kAD + 1];
+  }
+  lt = wave_sum(lt);
+  if (sinks) lt += exp2f(sink - M);
+  __syncthreads();
+  const int d0 = 8 * lane;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // a split without rows holds O = 0 and f = 0, so every split is summed
+#pragma unroll 4
   for (int s = 0; s < nsplit; ++s) {
-    const float* pr = part + ((tok * nsplit + s) * kAH + h) * kPart;
-    if (pr[kAD] != -INFINITY) lt += pr[kAD + 1] * exp2f(pr[kAD] - M);
+    const float f = fs[hh][s];
+    const float* pr = ph + (int64_t)s * kAH * kPart + d0;
+    const f32x4 v0 = *(const f32x4*)pr, v1 = *(const f32x4*)(pr + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] += f * v0[e];
+      o[4 + e] += f * v1[e];
+    }
   }
+  const float inv = 1.f / lt;
   const int first = kAD - R;
-  bf16_t* orow = out + (tok * kAH + h) * kAD;
-  for (int d = dq; d < dq + kAD / 4; d += 4) {
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pr = part + ((tok * nsplit + s) * kAH + h) * kPart;
-      if (pr[kAD] == -INFINITY) continue;
-      const float f = exp2f(pr[kAD] - M);
-      const f32x4 v = *(const f32x4*)(pr + d);
-      o[0] += f * v[0]; o[1] += f * v[1]; o[2] += f * v[2]; o[3] += f * v[3];
-    }
-    const float inv = 1.f / lt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] *= inv;
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
 #pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      if (d + e >= first) {
-        const double2 c = cs[(d + e - first) >> 1];
-        const float cf = (float)c.x, sf = (float)c.y;
-        const float a = o[e] * cf + o[e + 1] * sf, bb = o[e + 1] * cf - o[e] * sf;
-        o[e] = a;
-        o[e + 1] = bb;
-      }
+  for (int e = 0; e < 8; e += 2) {
+    if (d0 + e >= first) {
+      const double2 c = cs[(d0 + e - first) >> 1];
+      const float cf = (float)c.x, sf = (float)c.y;
+      const float a = o[e] * cf + o[e + 1] * sf, bb = o[e + 1] * cf - o[e] * sf;
+      o[e] = a;
+      o[e + 1] = bb;
     }
-    uint2 st;
-    st.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    st.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    *(uint2*)(orow + d) = st;
   }
+  uint4 st;
+  st.x = pack_bf16x2(o[0], o[1]);
+  st.y = pack_bf16x2(o[2], o[3]);
+  st.z = pack_bf16x2(o[4], o[5]);
+  st.w = pack_bf16x2(o[6], o[7]);
+  *(uint4*)(out + (tok * kAH + h) * kAD + d0) = st;
 }
 
 // ---------------------------------------------------------------------------
@@ -641,15 +657,17 @@ int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
   const int64_t rows = (int64_t)L.W + npool;
   const int64_t nch = (rows + kCH - 1) / kCH;
   const int64_t tokens = (int64_t)B * n;
-  // No block above kMaxRows rows.  Beyond that, split only while a split
-  // keeps >= 256 rows (its float32 partial, 64 x 514 words, costs about as
-  // much traffic as 128 rows) and the grid is short of ~256 blocks.
+  // No block above kMaxRows rows.  Beyond that, calls of fewer than 256
+  // tokens split while the grid is short of ~2 blocks per CU and each split
+  // keeps >= 4 chunks (128 rows: its float32 partial, 64 x 516 words, costs
+  // about as much traffic as the rows).
   const int64_t need = (nch * kCH + kMaxRows - 1) / kMaxRows;
-  int64_t s = (256 + tokens - 1) / tokens;
-  const int64_t cap = nch / 8 > 1 ? nch / 8 : 1;
+  int64_t s = tokens >= 256 ? 1 : (512 + tokens - 1) / tokens;
+  const int64_t cap = nch / 4 > 1 ? nch / 4 : 1;
   if (s > cap) s = cap;
   if (s < need) s = need;
   if (s < 1) s = 1;
+  if (s > kMaxSplits) s = need <= kMaxSplits ? kMaxSplits : -1;  // -1: too many rows
   return (int)s;
 }
 
@@ -680,8 +698,8 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
     if (ns > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      attend_merge<<<bt.B * bt.n, 256, 0, s>>>((const float*)ws, sinks, (bf16_t*)out, bt.pos0,
-                                               bt.n, L.R, L.base, ns);
+      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
+          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
     }
     return hipGetLastError();
   }

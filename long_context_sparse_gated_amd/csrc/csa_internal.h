@@ -7,6 +7,8 @@
 
 namespace csa {
 
+constexpr int kMaxTopK = 4096;  // largest index_topk the library accepts
+
 struct Layer {
   int dtype;       // 0 float32, 1 bf16
   int H, D, R;     // heads, head_dim, rope channels

@@ -15,12 +15,19 @@
 //    the four waves: 64 x 16 x 32 bf16 MFMA tiles, then ReLU, head weights and
 //    the head sum in registers (16 heads in-lane, 4 lane groups by shuffles).
 //    Per tile a wave reads 16 KB of keys from LDS for 128 MFMAs.
-//  * index_decode_mfma: one query per block row and 256 keys per block, keys
-//    streamed from HBM straight into MFMA B fragments (the decode bottleneck:
-//    each key is read once).
+//  * index_decode_mfma (few queries per sequence): queries rotated once
+//    (rotate_queries_bf16), then each block streams a run of one query's keys
+//    from HBM through LDS (LDS-DMA, two tiles in flight per wave) into MFMA B
+//    fragments; each key is read once.  It also counts the query's scores in
+//    a histogram of the top 12 bits of their order keys.
+//  * topk_collect / topk_final (same path): the histogram names the bin
+//    holding the k-th best score; per 1024-key slice the ids above that bin
+//    and inside it are compacted in id order; a radix select inside the bin
+//    settles the last places and both id lists are merged in id order.
 //  * index_generic: any head count / width, float or bf16, VALU float32.
-//  * topk_radix: per query, four 8-bit radix-select passes find the k-th
-//    largest ordered key; one ordered pass emits ids by ballot prefix counts.
+//  * topk_radix (prefill path): per query, four 8-bit radix-select passes
+//    find the k-th largest ordered key; one ordered pass emits ids by ballot
+//    prefix counts.
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -158,22 +165,43 @@ __global__ void __launch_bounds__(256) index_prefill_mfma(
 
 // ---------------------------------------------------------------------------
 // decode: rotate queries once, then stream keys from HBM into MFMA fragments
+//
+// Selection of the k best among up to millions of visible keys runs in three
+// steps spread over the whole chip: the scoring kernel also counts each
+// token's scores in a histogram of the top kHBits bits of their order keys;
+// topk_collect finds from the histogram the bin holding the k-th best score
+// and compacts, per 1024-key slice, the ids of the keys above that bin and of
+// those inside it; topk_final settles the bin by radix select over the few
+// keys in it and merges both id lists in ascending order.
+
+constexpr int kHBits = 12, kHBins = 1 << kHBits, kHShift = 32 - kHBits;
+constexpr int kSlice = 1024;         // keys per collect wave
+constexpr int kMaxSlices = 2048;     // topk_final keeps slice offsets in LDS
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;  // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 __global__ void __launch_bounds__(256) rotate_queries_bf16(const bf16_t* __restrict__ q,
                                                            bf16_t* __restrict__ qr,
+                                                           uint32_t* __restrict__ hist,
                                                            const int64_t* __restrict__ pos0,
                                                            int n_new, int Hi, int Di, int Ri,
                                                            double base) {
   __shared__ double2 cs[128];
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t t = pos0[b] + i;
+  const int64_t tok = (int64_t)b * n_new + i;
+  for (int j = threadIdx.x; j < kHBins; j += blockDim.x) hist[tok * kHBins + j] = 0u;
   for (int j = threadIdx.x; j < Ri / 2; j += blockDim.x) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, Ri), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
   __syncthreads();
-  const int64_t off = ((int64_t)b * n_new + i) * Hi * Di;
+  const int64_t off = tok * Hi * Di;
   const int chunks = Hi * Di / 8;
   for (int e = threadIdx.x; e < chunks; e += blockDim.x) {
     const int d0 = (e * 8) % Di;
@@ -182,22 +210,65 @@ __global__ void __launch_bounds__(256) rotate_queries_bf16(const bf16_t* __restr
   }
 }
 
-constexpr int kDecKeys = 256;  // keys per block (64 per wave)
+typedef __attribute__((address_space(3))) void lds_void;
 
+constexpr int kDecTile = 128;  // keys per LDS tile: 32 per wave, 32 KB
+
+// Sum over lanes l, l^16, l^32, l^48 with the gfx950 lane swaps.
+__device__ __forceinline__ float sum_g4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One block scores a run of keys of one token, 128-key tiles at a time.  The
+// keys reach LDS through the LDS-DMA loads (no VGPRs held while in flight)
+// into two arrays; each wave fetches and scores its own 32 rows of a tile, so
+// waves only meet at the start and at the histogram.  Per tile a wave copies
+// its B fragments to VGPRs, refills the same array with the tile two ahead,
+// then runs the MFMAs: two tiles stay in flight.  The 16-byte chunk c of tile
+// row r sits at slot c ^ (r & 15) so that the 16 rows of a fragment read hit
+// distinct bank groups.  The histogram of the block's scores is built after
+// the loop from the scores it stored.
 __global__ void __launch_bounds__(256) index_decode_mfma(const bf16_t* __restrict__ qr,
                                                          const bf16_t* __restrict__ wts,
                                                          const bf16_t* __restrict__ keys,
                                                          float* __restrict__ scores,
+                                                         float* __restrict__ discard,
+                                                         uint32_t* __restrict__ hist,
                                                          const int64_t* __restrict__ pos0,
-                                                         int n_new, int m, int64_t pool_cap) {
+                                                         int n_new, int m, int64_t pool_cap,
+                                                         int block_keys) {
   constexpr int Hi = 64, Di = 128;
+  __shared__ __attribute__((aligned(1024))) bf16_t kt0[kDecTile * Di];
+  __shared__ __attribute__((aligned(1024))) bf16_t kt1[kDecTile * Di];
   const int tok = blockIdx.y;  // b * n_new + i
   const int b = tok / n_new, i = tok % n_new;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t nv = (pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
-  const int64_t k0 = (int64_t)blockIdx.x * kDecKeys + 64 * wv;
-  if (k0 >= nv) return;
+  const int64_t kb = (int64_t)blockIdx.x * block_keys;
+  if (kb >= nv) return;  // block-uniform, before any barrier
+  const int64_t ke = kb + block_keys < nv ? kb + block_keys : nv;
+  const int ntile = (int)((ke - kb + kDecTile - 1) / kDecTile);
+  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
+  // DMA of this wave's 32 rows of tile `tile` (8 instructions of 4 rows);
+  // rows past the run re-read its last row (already in cache, never scored)
+  const int lrow = lane >> 4, slot = lane & 15;
+  auto issue = [&](int tile, bf16_t* dst) {
+    const int64_t t0 = kb + (int64_t)tile * kDecTile;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 32 * wv + 4 * j + lrow;
+      int64_t key = t0 + r;
+      if (key > ke - 1) key = ke - 1;
+      const bf16_t* src = kbase + key * Di + 8 * (slot ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
+                                       16, 0, 0);
+    }
+  };
   const bf16_t* qrow = qr + (int64_t)tok * Hi * Di;
   uint4 A[4][4];
   float wr[4][4];
@@ -210,33 +281,401 @@ __global__ void __launch_bounds__(256) index_decode_mfma(const bf16_t* __restric
     for (int ii = 0; ii < 4; ++ii)
       wr[mt][ii] = bf16_to_f32(wts[(int64_t)tok * Hi + 16 * mt + 4 * g + ii]);
   }
-  uint4 B[4][4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t key = k0 + 16 * nt + r16;
-    const bf16_t* krow = keys + ((int64_t)b * pool_cap + (key < nv ? key : 0)) * Di;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) B[nt][kk] = *(const uint4*)(krow + 32 * kk + 8 * g);
-  }
+  issue(0, kt0);
+  issue(1, kt1);
   float* srow = scores + (int64_t)tok * pool_cap;
+  // fragment reads in one asm block that also waits for them: the compiler
+  // then sees no LDS load to order after the in-flight DMA of other tiles
+  auto frags = [&](const bf16_t* buf, uint4 (&Bf)[2][4]) {
+    uint32_t a[2][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    f32x4 acc[4];
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = 32 * wv + 16 * nt + r16;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 4; ++kk)
+        a[nt][kk] = (uint32_t)(size_t)(lds_void*)(buf + r * Di + 8 * ((4 * kk + g) ^ (r & 15)));
+    }
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %9\n"
+        "ds_read_b128 %2, %10\n"
+        "ds_read_b128 %3, %11\n"
+        "ds_read_b128 %4, %12\n"
+        "ds_read_b128 %5, %13\n"
+        "ds_read_b128 %6, %14\n"
+        "ds_read_b128 %7, %15\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(Bf[0][0]), "=v"(Bf[0][1]), "=v"(Bf[0][2]), "=v"(Bf[0][3]), "=v"(Bf[1][0]),
+          "=v"(Bf[1][1]), "=v"(Bf[1][2]), "=v"(Bf[1][3])
+        : "v"(a[0][0]), "v"(a[0][1]), "v"(a[0][2]), "v"(a[0][3]), "v"(a[1][0]), "v"(a[1][1]),
+          "v"(a[1][2]), "v"(a[1][3])
+        : "memory");
+  };
+  auto compute = [&](int tile, const uint4 (&Bf)[2][4]) {
+    f32x4 acc[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(A[mt][kk], B[nt][kk], acc[mt]);
-    float v = 0.f;
+      for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) v += wr[mt][ii] * fmaxf(acc[mt][ii], 0.f);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    const int64_t key = k0 + 16 * nt + r16;
-    if (g == 0 && key < nv) srow[key] = v;
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mfma16(A[mt][kk], Bf[nt][kk], acc[nt][mt]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = 32 * wv + 16 * nt + r16;
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) v += wr[mt][ii] * fmaxf(acc[nt][mt][ii], 0.f);
+      v = sum_g4(v);
+      // the four lane groups hold the same sum: all store it (keys past the
+      // run go to a discard slot)
+      const int64_t key = kb + (int64_t)tile * kDecTile + r;
+      *(key < ke ? srow + key : discard) = v;
+    }
+  };
+  // Two tiles in flight per wave: the fragments of tile t are copied to
+  // VGPRs (the asm read waits for them), then tile t+2 is fetched into the
+  // same array while tile t is scored.  After `vmcnt(8)` only the newest
+  // tile's 8 DMA rows may be in flight (score stores issued after an older
+  // tile only make the wait longer).  Prefetches are unconditional.
+  uint4 Bf[2][4];
+  for (int tile = 0;;) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    frags(kt0, Bf);
+    issue(tile + 2, kt0);
+    compute(tile, Bf);
+    if (++tile >= ntile) break;
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    frags(kt1, Bf);
+    issue(tile + 2, kt1);
+    compute(tile, Bf);
+    if (++tile >= ntile) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA outlives the block
+  // histogram of the block's scores (read back from the cache)
+  uint32_t* lh = (uint32_t*)kt0;  // kHBins words, free now
+  __syncthreads();
+  for (int j = threadIdx.x; j < kHBins; j += 256) lh[j] = 0u;
+  __threadfence_block();
+  __syncthreads();
+  for (int64_t j = kb + threadIdx.x; j < ke; j += 256)
+    atomicAdd(&lh[order_key(srow[j]) >> kHShift], 1u);
+  __syncthreads();
+  uint32_t* h = hist + (int64_t)tok * kHBins;
+  for (int j = threadIdx.x; j < kHBins; j += 256) {
+    const uint32_t c = lh[j];
+    if (c) atomicAdd(&h[j], c);
+  }
+}
+
+// Block-wide (256 threads): the bin holding the k-th largest key of a
+// histogram whose total exceeds k, and the number of keys in the bins above.
+__device__ void hist_cut(const uint32_t* __restrict__ h, uint32_t k, uint32_t* wsum,
+                         uint32_t* res) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int per = kHBins / 256;
+  if (tid == 0) {  // kept if no bin qualifies (a histogram of <= k keys)
+    res[0] = 0u;
+    res[1] = 0u;
+  }
+  uint32_t c[per], s = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    c[e] = h[kHBins - 1 - per * tid - e];  // thread 0 holds the top bins
+    s += c[e];
+  }
+  uint32_t x = s;  // inclusive scan in thread order
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  uint32_t before = x - s;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  if (before < k && before + s >= k) {
+    uint32_t acc = before;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+      if (acc + c[e] >= k) {
+        res[0] = (uint32_t)(kHBins - 1 - per * tid - e);
+        res[1] = acc;
+        break;
+      }
+      acc += c[e];
+    }
+  }
+  __syncthreads();
+}
+
+// Per 1024-key slice (one wave): ids of keys above the cut bin and of keys
+// inside it, each list compacted in id order at the slice's own offset.
+__global__ void __launch_bounds__(256) topk_collect(const float* __restrict__ scores,
+                                                    const uint32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ cand_hi,
+                                                    int32_t* __restrict__ cand_tie,
+                                                    uint32_t* __restrict__ counts,
+                                                    const int64_t* __restrict__ pos0, int n_new,
+                                                    int m, int k, int64_t pool_cap, int nslice) {
+  __shared__ uint32_t wsum[4], res[2];
+  const int tok = blockIdx.y;
+  const int b = tok / n_new, i = tok % n_new;
+  int64_t nv = (pos0[b] + i + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  const int64_t c0b = (int64_t)blockIdx.x * 4 * kSlice;
+  if (nv <= k || c0b >= nv) return;  // block-uniform
+  hist_cut(hist + (int64_t)tok * kHBins, (uint32_t)k, wsum, res);
+  const uint32_t T = res[0];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t c0 = c0b + (int64_t)wv * kSlice;
+  if (c0 >= nv) return;
+  const int64_t c1 = c0 + kSlice < nv ? c0 + kSlice : nv;
+  const float* sc = scores + (int64_t)tok * pool_cap;
+  int32_t* hi = cand_hi + (int64_t)tok * pool_cap + c0;
+  int32_t* ti = cand_tie + (int64_t)tok * pool_cap + c0;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  constexpr int U = kSlice / 64;
+  uint32_t bin[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {  // all loads first: one latency per slice
+    const int64_t j = c0 + 64 * u + lane;
+    bin[u] = j < c1 ? (order_key(sc[j]) >> kHShift) : 0u;
+  }
+  uint32_t nh = 0, nt = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = c0 + 64 * u + lane;
+    const bool above = j < c1 && bin[u] > T, in = j < c1 && bin[u] == T;
+    const unsigned long long ba = __ballot(above), bi = __ballot(in);
+    if (above) hi[nh + __popcll(ba & lt)] = (int32_t)j;
+    if (in) ti[nt + __popcll(bi & lt)] = (int32_t)j;
+    nh += (uint32_t)__popcll(ba);
+    nt += (uint32_t)__popcll(bi);
+  }
+  if (lane == 0) {
+    const int64_t sl = c0 / kSlice;
+    counts[((int64_t)tok * nslice + sl) * 2] = nh;
+    counts[((int64_t)tok * nslice + sl) * 2 + 1] = nt;
+  }
+}
+
+// Position of the first element >= x in an ascending LDS array.
+__device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int slice_of(const uint32_t* off, int ns, uint32_t i) {
+  int lo = 0, hi = ns;  // last slice with off[s] <= i
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+constexpr int kTieCap = 4096;  // keys of the cut bin held in LDS (more: read from L2)
+
+// Per token: radix select inside the cut bin for the k - above keys still
+// needed (ties to the lower id), then the ascending merge of both id lists.
+__global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ cand_hi,
+                                                  const int32_t* __restrict__ cand_tie,
+                                                  const uint32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ out,
+                                                  const int64_t* __restrict__ pos0, int n_new,
+                                                  int m, int k, int64_t pool_cap, int nslice) {
+  __shared__ uint32_t off_hi[kMaxSlices + 1], off_tie[kMaxSlices + 1];
+  __shared__ int32_t sel_hi[kMaxTopK], sel_tie[kMaxTopK];
+  __shared__ int32_t tie_id[kTieCap];
+  __shared__ uint32_t tie_key[kTieCap];
+  __shared__ uint32_t bins[256], wsum[4], wcnt[4], sh_prefix, sh_rem;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tok = blockIdx.x;
+  const int b = tok / n_new, i = tok % n_new;
+  int64_t nv = (pos0[b] + i + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  int32_t* o = out + (int64_t)tok * k;
+  if (nv <= k) {
+    for (int j = tid; j < k; j += 256) o[j] = j < nv ? j : -1;
+    return;
+  }
+  const int ns = (int)((nv + kSlice - 1) / kSlice);
+  // exclusive prefix sums of the per-slice counts, 256 slices at a time
+  uint32_t carry_h = 0, carry_t = 0;
+  for (int s0 = 0; s0 < ns; s0 += 256) {
+    const int s = s0 + tid;
+    uint32_t ch = 0, ct = 0;
+    if (s < ns) {
+      ch = counts[((int64_t)tok * nslice + s) * 2];
+      ct = counts[((int64_t)tok * nslice + s) * 2 + 1];
+    }
+    uint32_t xh = ch, xt = ct;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t yh = __shfl_up(xh, d, 64), yt = __shfl_up(xt, d, 64);
+      if (lane >= d) { xh += yh; xt += yt; }
+    }
+    if (lane == 63) { wsum[wv] = xh; wcnt[wv] = xt; }
+    __syncthreads();
+    uint32_t bh = carry_h + xh - ch, bt = carry_t + xt - ct;
+    for (int w = 0; w < wv; ++w) { bh += wsum[w]; bt += wcnt[w]; }
+    if (s < ns) { off_hi[s] = bh; off_tie[s] = bt; }
+    for (int w = 0; w < 4; ++w) { carry_h += wsum[w]; carry_t += wcnt[w]; }
+    __syncthreads();
+  }
+  if (tid == 0) { off_hi[ns] = carry_h; off_tie[ns] = carry_t; }
+  __syncthreads();
+  // by construction 0 <= A < k <= A + C; the clamps below only keep every
+  // index in bounds should the counts ever disagree
+  const uint32_t A = carry_h < (uint32_t)k ? carry_h : (uint32_t)k;
+  const uint32_t C = carry_t < (uint32_t)nv ? carry_t : (uint32_t)nv;
+  const uint32_t need = (uint32_t)k - A < C ? (uint32_t)k - A : C;
+  const bool in_lds = C <= (uint32_t)kTieCap;
+  // id of list entry e of a slice list (offsets `off`), clamped into the token's rows
+  auto list_id = [&](const int32_t* base, const uint32_t* off, uint32_t e) -> int32_t {
+    const int s = slice_of(off, ns, e);
+    uint32_t d = e - off[s];
+    if (d > (uint32_t)kSlice - 1u) d = (uint32_t)kSlice - 1u;
+    int64_t p = (int64_t)s * kSlice + d;
+    if (p > pool_cap - 1) p = pool_cap - 1;
+    int32_t id = base[p];
+    return id < 0 ? 0 : (id >= nv ? (int32_t)(nv - 1) : id);
+  };
+  const float* sc = scores + (int64_t)tok * pool_cap;
+  const int32_t* hb = cand_hi + (int64_t)tok * pool_cap;
+  const int32_t* tb = cand_tie + (int64_t)tok * pool_cap;
+  // the cut bin's keys share their top kHBits bits: keep the low ones
+  constexpr uint32_t kLow = (1u << kHShift) - 1u;
+  // gather both id lists (4 items per thread in flight)
+  for (uint32_t e0 = 0; e0 < (A > C ? A : C); e0 += 1024) {
+    int32_t ida[4], idt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t e = e0 + 256 * u + tid;
+      ida[u] = -1;
+      idt[u] = -1;
+      if (e < A) ida[u] = list_id(hb, off_hi, e);
+      if (in_lds && e < C) idt[u] = list_id(tb, off_tie, e);
+    }
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = idt[u] >= 0 ? sc[idt[u]] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t e = e0 + 256 * u + tid;
+      if (e < A) sel_hi[e] = ida[u];
+      if (idt[u] >= 0) {
+        tie_id[e] = idt[u];
+        tie_key[e] = order_key(v[u]) & kLow;
+      }
+    }
+  }
+  __syncthreads();
+  auto tie_at = [&](uint32_t e, int32_t& id) -> uint32_t {
+    if (in_lds) {
+      id = tie_id[e];
+      return tie_key[e];
+    }
+    id = list_id(tb, off_tie, e);
+    return order_key(sc[id]) & kLow;
+  };
+  // radix select over the low bits: 8 + 8 + 4
+  uint32_t prefix = 0, mask = 0, rem = need;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? kHShift - 8 : (pass == 1 ? kHShift - 16 : 0);
+    const uint32_t nb = pass == 2 ? (1u << (kHShift - 16)) : 256u;
+    bins[tid] = 0u;
+    __syncthreads();
+    for (uint32_t e = tid; e < C; e += 256) {
+      int32_t id;
+      const uint32_t key = tie_at(e, id);
+      if ((key & mask) == prefix) atomicAdd(&bins[(key >> shift) & (nb - 1u)], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t c0 = bins[4 * lane], c1 = bins[4 * lane + 1], c2 = bins[4 * lane + 2],
+                     c3 = bins[4 * lane + 3];
+      const uint32_t sum = c0 + c1 + c2 + c3;
+      uint32_t suf = sum;  // inclusive suffix sum over lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t x = __shfl_down(suf, d, 64);
+        if (lane + d < 64) suf += x;
+      }
+      const unsigned long long bal = __ballot(suf >= rem);
+      const int Lb = 63 - __clzll(bal);
+      if (lane == Lb) {
+        uint32_t above = suf - sum;
+        const uint32_t cnt[4] = {c0, c1, c2, c3};
+        int d = 3;
+        for (; d > 0; --d) {
+          if (above + cnt[d] >= rem) break;
+          above += cnt[d];
+        }
+        sh_prefix = prefix | ((uint32_t)(4 * Lb + d) << shift);
+        sh_rem = rem - above;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    rem = sh_rem;
+    mask |= (nb - 1u) << shift;
+  }
+  // every cut-bin key above `prefix`, and the first `rem` equal to it, in id order
+  uint32_t base_sel = 0, base_eq = 0;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (uint32_t e0 = 0; e0 < C; e0 += 256) {
+    const uint32_t e = e0 + tid;
+    int32_t id = -1;
+    uint32_t key = 0u;
+    if (e < C) key = tie_at(e, id);
+    const bool gt = e < C && key > prefix, eq = e < C && key == prefix;
+    const unsigned long long be = __ballot(eq);
+    if (lane == 0) wcnt[wv] = (uint32_t)__popcll(be);
+    __syncthreads();
+    uint32_t eq_off = base_eq, eq_tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) eq_off += wcnt[w];
+      eq_tot += wcnt[w];
+    }
+    const bool sel = gt || (eq && eq_off + (uint32_t)__popcll(be & lt) < rem);
+    const unsigned long long bs = __ballot(sel);
+    if (lane == 0) wsum[wv] = (uint32_t)__popcll(bs);
+    __syncthreads();
+    uint32_t off = base_sel, tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) off += wsum[w];
+      tot += wsum[w];
+    }
+    const uint32_t pos = off + (uint32_t)__popcll(bs & lt);
+    if (sel && pos < need) sel_tie[pos] = id;
+    base_sel += tot;
+    base_eq += eq_tot;
+    __syncthreads();
+    if (base_sel >= need) break;  // block-uniform: every later key is unselected
+  }
+  // both lists ascend; an id's output slot is its rank in its own list plus
+  // the number of smaller ids in the other one
+  for (uint32_t a = tid; a < A; a += 256) {
+    const int32_t x = sel_hi[a];
+    o[a + lower_bound_lds(sel_tie, (int)need, x)] = x;
+  }
+  for (uint32_t j = tid; j < need; j += 256) {
+    const int32_t y = sel_tie[j];
+    o[j + lower_bound_lds(sel_hi, (int)A, y)] = y;
   }
 }
 
@@ -294,12 +733,6 @@ __global__ void __launch_bounds__(256) index_generic(const T* __restrict__ q,
 
 // ---------------------------------------------------------------------------
 // top-k by radix select
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u << 1) == 0u) u = 0u;  // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 template <int BS>
 __global__ void __launch_bounds__(BS) topk_radix(const float* __restrict__ scores,
@@ -401,11 +834,24 @@ static bool index_fast_shape(const Layer& L) {
   return L.dtype == 1 && L.Hi == 64 && L.Di == 128 && L.Ri <= 128;
 }
 
+// Few new tokens per sequence over a pool the selection buffers can index.
+static bool index_decode_path(const Layer& L, int n, int64_t pool_cap) {
+  return index_fast_shape(L) && n < kIdxQPB &&
+         (pool_cap + kSlice - 1) / kSlice <= kMaxSlices;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
-  size_t s = align256((size_t)B * n * pool_cap * sizeof(float));
-  if (index_fast_shape(L) && n < kIdxQPB) s += align256((size_t)B * n * L.Hi * L.Di * 2);
+  const size_t bn = (size_t)B * n;
+  size_t s = align256(bn * pool_cap * sizeof(float));
+  if (index_decode_path(L, n, pool_cap)) {
+    const size_t nslice = (size_t)((pool_cap + kSlice - 1) / kSlice);
+    s += align256(bn * L.Hi * L.Di * 2);              // rotated queries
+    s += align256(bn * kHBins * sizeof(uint32_t));    // score histograms
+    s += 2 * align256(bn * pool_cap * sizeof(int32_t));  // candidate ids
+    s += align256(bn * nslice * 2 * sizeof(uint32_t) + 64);  // per-slice counts, discard
+  }
   return s;
 }
 
@@ -413,26 +859,50 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
                              const void* keys, int64_t pool_cap, int32_t* idx, float* scores_out,
                              void* ws, hipStream_t s) {
   char* wsp = (char*)ws;
+  const size_t bn = (size_t)bt.B * bt.n;
   float* scores = (float*)wsp;
-  wsp += align256((size_t)bt.B * bt.n * pool_cap * sizeof(float));
+  wsp += align256(bn * pool_cap * sizeof(float));
   if (scores_out) scores = scores_out;
-  if (index_fast_shape(L)) {
-    if (bt.n >= kIdxQPB) {
-      dim3 grid((bt.n + kIdxQPB - 1) / kIdxQPB, bt.B);
-      index_prefill_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
-                                              (const bf16_t*)keys, scores, bt.pos0, bt.n, L.Ri,
-                                              L.base, L.m, pool_cap);
-    } else {
-      bf16_t* qr = (bf16_t*)wsp;
-      rotate_queries_bf16<<<dim3(bt.n, bt.B), 256, 0, s>>>((const bf16_t*)q, qr, bt.pos0, bt.n,
-                                                           L.Hi, L.Di, L.Ri, L.base);
-      int64_t nv = (bt.pos0_max + bt.n) / L.m;
-      if (nv > pool_cap) nv = pool_cap;
-      dim3 grid((unsigned)((nv + kDecKeys - 1) / kDecKeys), bt.B * bt.n);
-      if (grid.x > 0)
-        index_decode_mfma<<<grid, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
-                                               bt.pos0, bt.n, L.m, pool_cap);
+  if (index_decode_path(L, bt.n, pool_cap)) {
+    const int nslice = (int)((pool_cap + kSlice - 1) / kSlice);
+    bf16_t* qr = (bf16_t*)wsp;
+    wsp += align256(bn * L.Hi * L.Di * 2);
+    uint32_t* hist = (uint32_t*)wsp;
+    wsp += align256(bn * kHBins * sizeof(uint32_t));
+    int32_t* cand_hi = (int32_t*)wsp;
+    wsp += align256(bn * pool_cap * sizeof(int32_t));
+    int32_t* cand_tie = (int32_t*)wsp;
+    wsp += align256(bn * pool_cap * sizeof(int32_t));
+    uint32_t* counts = (uint32_t*)wsp;
+    rotate_queries_bf16<<<dim3(bt.n, bt.B), 256, 0, s>>>((const bf16_t*)q, qr, hist, bt.pos0,
+                                                         bt.n, L.Hi, L.Di, L.Ri, L.base);
+    int64_t nv = (bt.pos0_max + bt.n) / L.m;
+    if (nv > pool_cap) nv = pool_cap;
+    const unsigned tokens = (unsigned)bn;
+    if (nv > 0) {
+      // ~512 blocks over the call (two per CU), runs of whole tiles
+      const int64_t per_tok = (512 + tokens - 1) / tokens;
+      int64_t bk = (nv + per_tok - 1) / per_tok;
+      bk = (bk + kDecTile - 1) / kDecTile * kDecTile;
+      dim3 g1((unsigned)((nv + bk - 1) / bk), tokens);
+      index_decode_mfma<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
+                                           (float*)(counts + bn * nslice * 2), hist, bt.pos0,
+                                           bt.n, L.m, pool_cap, (int)bk);
     }
+    if (nv > L.k) {
+      dim3 g2((unsigned)((nv + 4 * kSlice - 1) / (4 * kSlice)), tokens);
+      topk_collect<<<g2, 256, 0, s>>>(scores, hist, cand_hi, cand_tie, counts, bt.pos0, bt.n,
+                                      L.m, L.k, pool_cap, nslice);
+    }
+    topk_final<<<tokens, 256, 0, s>>>(scores, cand_hi, cand_tie, counts, idx, bt.pos0, bt.n,
+                                      L.m, L.k, pool_cap, nslice);
+    return hipGetLastError();
+  }
+  if (index_fast_shape(L)) {
+    dim3 grid((bt.n + kIdxQPB - 1) / kIdxQPB, bt.B);
+    index_prefill_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
+                                            (const bf16_t*)keys, scores, bt.pos0, bt.n, L.Ri,
+                                            L.base, L.m, pool_cap);
   } else {
     const size_t shm = ((size_t)L.Hi * L.Di + L.Hi) * sizeof(float);
     dim3 grid(bt.n, bt.B);
