@@ -38,77 +38,19 @@
 // shapes.
 #include "csa_device.h"
 #include "csa_internal.h"
+#include "attend_common.h"
 
 namespace csa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-constexpr int kAH = 64, kAD = 512, kCH = 32;
-constexpr int kMaxRows = 1024;   // rows handled by one block
-constexpr int kMaxRope = 128;    // rope channels supported by the fast path
-constexpr int kPart = kAD + 4;   // split partial row: O[512], m, l, 2 pad (16-byte rows)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;    // log2 headroom before the running max is raised
-// Tuning (compile time): the blocks per CU the register budget targets.
-#ifndef CSA_ATTN_MIN_BLOCKS
-#define CSA_ATTN_MIN_BLOCKS 2
-#endif
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Reductions across lane l and l ^ 16 / l ^ 32 with the gfx950 lane-swap
-// instructions (no LDS round trip); the max / sum of the two swapped values
-// pairs every lane with its partner whichever half moves.
-__device__ __forceinline__ float xmax16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xmax32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xsum16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xsum32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
-__device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
-                                      int64_t pool_cap, const int32_t* idx_row, int csa,
-                                      int64_t nvis) {
-  if (jr < nwin) return (int)((int64_t)b * win_cap + (lo + jr) % win_cap);
-  const int e = jr - nwin;
-  const int64_t w = csa ? (int64_t)idx_row[e] : (int64_t)e;
-  if (w < 0 || w >= nvis) return -1;
-  return (int)(-2 - ((int64_t)b * pool_cap + w));
-}
-
-// Chunk swizzle of LDS row r (16-byte chunks, 64 per row; only the low four
-// chunk bits move): the 16 rows of a QK^T read get 16 distinct chunk slots.
-// Measured on gfx950 with the read patterns of this kernel: 16-byte reads
-// run at the contiguous rate with this swizzle (about 300+ bytes/clk/CU,
-// against about 120 with no swizzle); the transpose reads run at about 115
-// bytes/clk/CU with any of the swizzles tried.
-__device__ __forceinline__ int swz(int r) { return r & 15; }
-
 constexpr int kPRow = kCH + 8;  // LDS row of P^T per head: 32 row slots + pad (bf16)
+// Software-pipeline depths of the LDS fragment reads (steps ahead).
+#ifndef CSA_ATTN_QD
+#define CSA_ATTN_QD 2
+#endif
+#ifndef CSA_ATTN_PD
+#define CSA_ATTN_PD 2
+#endif
+constexpr int kQD = CSA_ATTN_QD, kPD = CSA_ATTN_PD;
 
 template <int R>
 __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
@@ -217,30 +159,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   // channels 32*kk + 8*g + 0..7
   constexpr int first = kAD - R;
   uint4 Qf[16];
-  {
-    const bf16_t* qrow = q + (tok * kAH + 16 * wv + r16) * kAD;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int d0 = 32 * kk + 8 * g;
-      uint4 v = *(const uint4*)(qrow + d0);
-      if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int d = d0 + 2 * p;
-          if (d >= first) {
-            double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
-            double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
-            const double2 c = cs[(d - first) >> 1];
-            rot64(a, bb, c.x, c.y);
-            w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
-          }
-        }
-        v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      }
-      Qf[kk] = v;
-    }
-  }
+  load_qfrag<R>(q + (tok * kAH + 16 * wv + r16) * kAD, cs, g, Qf);
 
   // O^T accumulators of the wave's channel slice: channel 128*wv + 16*dt +
   // 4*g + e, head 16*ht + r16
@@ -286,17 +205,26 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     auto kfrag = [&](int kk, int mt) {
       return *(const uint4*)(kb + kb_v[kk & 3] + (kk >> 2) * 256 + mt * 16384);
     };
-    uint4 ka0 = kfrag(0, 0), ka1 = kfrag(0, 1);
+    // K fragments are read kQD steps ahead of their MFMAs (an LDS read takes
+    // longer than the two MFMAs of one step); the scheduling barriers keep
+    // the compiler from sinking the reads next to their use
+    uint4 kf[kQD][2];
+#pragma unroll
+    for (int j = 0; j < kQD; ++j) {
+      kf[j][0] = kfrag(j, 0);
+      kf[j][1] = kfrag(j, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      const uint4 a0 = ka0, a1 = ka1;
-      if (kk + 1 < 16) {
-        ka0 = kfrag(kk + 1, 0);
-        ka1 = kfrag(kk + 1, 1);
+      S0 = mfma16(kf[kk % kQD][0], Qf[kk], S0);
+      S1 = mfma16(kf[kk % kQD][1], Qf[kk], S1);
+      if (kk + kQD < 16) {
+        kf[kk % kQD][0] = kfrag(kk + kQD, 0);
+        kf[kk % kQD][1] = kfrag(kk + kQD, 1);
       }
-      S0 = mfma16(a0, Qf[kk], S0);
-      S1 = mfma16(a1, Qf[kk], S1);
       if (gat && (kk & 1) && (kk >> 1) < RPW) gather_row(G, kk >> 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- online softmax (log2 domain); lane column = head 16*wv + r16
     const uint32_t vm = vmask[c - c0] >> (4 * g);
@@ -347,17 +275,27 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     uint4 Pf[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) Pf[ht] = *(const uint4*)&ps[(16 * ht + r16) * kPRow + 8 * g];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    // V^T fragments (two transpose reads each) kPD channel tiles ahead
+    auto vfrag = [&](int dt) {
       const char* pa = kb + tr_v[dt];
       const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)pa);
       const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 16384));
-      const uint4 a = make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
-                                 (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
-                                 (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
-                                 (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
+      return make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
+                        (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
+                        (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
+                        (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
+    };
+    uint4 vf[kPD];
+#pragma unroll
+    for (int j = 0; j < kPD; ++j) vf[j] = vfrag(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint4 a = vf[dt % kPD];
+      if (dt + kPD < 8) vf[dt % kPD] = vfrag(dt + kPD);
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) O[dt][ht] = mfma16(a, Pf[ht], O[dt][ht]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int c = c0; c < c1; c += 2) {
@@ -650,25 +588,37 @@ bool attend_fast_shape(const Layer& L) {
          (L.R == 16 || L.R == 32 || L.R == 64 || L.R == 128);
 }
 
-int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
-  if (!attend_fast_shape(L)) return 1;
+static int64_t attend_rows(const Layer& L, int64_t pool_cap, bool csa) {
   int64_t npool = 0;
   if (L.m > 0) npool = csa ? (pool_cap < L.k ? pool_cap : (int64_t)L.k) : pool_cap;
-  const int64_t rows = (int64_t)L.W + npool;
-  const int64_t nch = (rows + kCH - 1) / kCH;
+  return (int64_t)L.W + npool;
+}
+
+// Calls of fewer than 256 tokens run attend_decode (rows and head groups
+// spread over the chip), except a few tokens with long row lists: there
+// attend_mfma's 64-head blocks, each splitting a list over many blocks, keep
+// more rows in flight per block.
+static bool attend_dec(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
   const int64_t tokens = (int64_t)B * n;
-  // No block above kMaxRows rows.  Beyond that, calls of fewer than 256
-  // tokens split while the grid is short of ~2 blocks per CU and each split
-  // keeps >= 4 chunks (128 rows: its float32 partial, 64 x 516 words, costs
-  // about as much traffic as the rows).
+  return tokens < 256 && (tokens >= 16 || attend_rows(L, pool_cap, csa) <= 256);
+}
+
+int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
+  if (!attend_fast_shape(L)) return 1;
+  if (attend_dec(L, B, n, pool_cap, csa)) return attend_decode_splits(L, B, n, pool_cap, csa);
+  const int64_t nch = (attend_rows(L, pool_cap, csa) + kCH - 1) / kCH;
+  const int64_t tokens = (int64_t)B * n;
+  // no block above kMaxRows rows; calls of fewer than 256 tokens also split
+  // while the grid is short of ~2 blocks per CU and every split keeps >= 4
+  // chunks (128 rows: its float32 partial, 64 x 516 words, costs about as
+  // much traffic as the rows)
   const int64_t need = (nch * kCH + kMaxRows - 1) / kMaxRows;
   int64_t s = tokens >= 256 ? 1 : (512 + tokens - 1) / tokens;
   const int64_t cap = nch / 4 > 1 ? nch / 4 : 1;
   if (s > cap) s = cap;
   if (s < need) s = need;
   if (s < 1) s = 1;
-  if (s > kMaxSplits) s = need <= kMaxSplits ? kMaxSplits : -1;  // -1: too many rows
-  return (int)s;
+  return s > kMaxSplits ? -1 : (int)s;  // -1: too many rows
 }
 
 size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
@@ -683,6 +633,14 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
   const int m = L.m;
   if (attend_fast_shape(L)) {
     const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
+    if (attend_dec(L, bt.B, bt.n, pool_cap, csa)) {
+      hipError_t e = launch_attend_decode(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
+                                          ws, csa, ns, s);
+      if (e != hipSuccess || ns == 1) return e;
+      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
+          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
+      return hipGetLastError();
+    }
     dim3 grid(bt.n, bt.B, ns);
 #define CSA_ATTN_LAUNCH(RR)                                                                 \
   attend_mfma<RR><<<grid, 256, 0, s>>>(                                                     \

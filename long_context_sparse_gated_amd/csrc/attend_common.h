@@ -1,0 +1,108 @@
+// Shared pieces of the attention kernels (H = 64, D = 512, bf16 fast paths):
+// MFMA and lane-swap wrappers, the row-id encoding of the row list, the LDS
+// chunk swizzle and the rotated query fragments.
+#pragma once
+
+#include "csa_device.h"
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kAH = 64, kAD = 512, kCH = 32;
+constexpr int kMaxRows = 1024;   // rows handled by one block
+constexpr int kMaxRope = 128;    // rope channels supported by the fast path
+constexpr int kPart = kAD + 4;   // split partial row: O[512], m, l, 2 pad (16-byte rows)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;    // log2 headroom before the running max is raised
+// Tuning (compile time): the blocks per CU the register budget targets.
+#ifndef CSA_ATTN_MIN_BLOCKS
+#define CSA_ATTN_MIN_BLOCKS 2
+#endif
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Reductions across lane l and l ^ 16 / l ^ 32 with the gfx950 lane-swap
+// instructions (no LDS round trip); the max / sum of the two swapped values
+// pairs every lane with its partner whichever half moves.
+__device__ __forceinline__ float xmax16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
+__device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
+                                      int64_t pool_cap, const int32_t* idx_row, int csa,
+                                      int64_t nvis) {
+  if (jr < nwin) return (int)((int64_t)b * win_cap + (lo + jr) % win_cap);
+  const int e = jr - nwin;
+  const int64_t w = csa ? (int64_t)idx_row[e] : (int64_t)e;
+  if (w < 0 || w >= nvis) return -1;
+  return (int)(-2 - ((int64_t)b * pool_cap + w));
+}
+
+// Chunk swizzle of LDS row r (16-byte chunks, 64 per row; only the low four
+// chunk bits move): the 16 rows of a QK^T read get 16 distinct chunk slots.
+// Measured on gfx950 with the read patterns of this kernel: 16-byte reads
+// run at the contiguous rate with this swizzle (about 300+ bytes/clk/CU,
+// against about 120 with no swizzle); the transpose reads run at about 115
+// bytes/clk/CU with any of the swizzles tried.
+__device__ __forceinline__ int swz(int r) { return r & 15; }
+
+// Query fragments of head row `qrow` (512 channels) for a 16 x 16 x 32 MFMA B
+// operand: fragment kk holds channels 32 kk + 8 g .. +7; the last R channels
+// are rotated at the query's position (cs[j] = (cos, sin) of pair j) in
+// float64 and rounded to bf16 once.
+template <int R>
+__device__ __forceinline__ void load_qfrag(const bf16_t* __restrict__ qrow, const double2* cs,
+                                           int g, uint4 (&Qf)[16]) {
+  constexpr int first = kAD - R;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int d0 = 32 * kk + 8 * g;
+    uint4 v = *(const uint4*)(qrow + d0);
+    if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
+      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int d = d0 + 2 * p;
+        if (d >= first) {
+          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
+          double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+          const double2 c = cs[(d - first) >> 1];
+          rot64(a, bb, c.x, c.y);
+          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+        }
+      }
+      v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    Qf[kk] = v;
+  }
+}
+
+}  // namespace csa

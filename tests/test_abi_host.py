@@ -60,7 +60,10 @@ def test_workspace_sizes(lib):
     L = csa_layer()
     assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 8192, 2048, m.CSA_OP_INDEX_TOPK) >= 8192 * 2048 * 4
     assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 8192, 2048, m.CSA_OP_ATTEND) == 0
-    assert lib.csa_workspace_bytes(ctypes.byref(L), 64, 1, 32768, m.CSA_OP_ATTEND) > 0
+    # 64 one-token sequences fill the chip without splitting a row list; four
+    # of them split each list over several blocks (float32 partials)
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 64, 1, 32768, m.CSA_OP_ATTEND) == 0
+    assert lib.csa_workspace_bytes(ctypes.byref(L), 4, 1, 262144, m.CSA_OP_ATTEND) >= 4 * 2 * 64 * 516 * 4
     assert lib.csa_workspace_bytes(ctypes.byref(L), 1, 1, 1, 99) == ctypes.c_size_t(-1).value
     bad = csa_layer(dtype=7)
     assert lib.csa_workspace_bytes(ctypes.byref(bad), 1, 1, 1, 1) == ctypes.c_size_t(-1).value
@@ -88,8 +91,8 @@ def test_rejections_return_before_launch(lib):
     assert call_attend(lib, L, B, win_cap=8191) == SHAPE           # needs min(128+8191, 8192)
     assert call_attend(lib, L, batch(n_new=0)) == SHAPE
     # decode shapes need split partials: missing workspace
-    Bd = batch(batch=64, n_new=1, pos0_max=131072)
-    assert call_attend(lib, L, Bd, win_cap=128, pool_cap=32768) == WS
+    Bd = batch(batch=4, n_new=1, pos0_max=1048576)
+    assert call_attend(lib, L, Bd, win_cap=128, pool_cap=262144) == WS
     # generic path limits: a large float32 layer is not implemented
     assert call_attend(lib, csa_layer(dtype=0), B) == UNSUP
     # compressor

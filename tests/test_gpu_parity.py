@@ -226,6 +226,16 @@ def test_csa_decode_entry_closes(csa):
     _decode_case(csa, "csa_decode", 4099, 2, 1)
 
 
+def test_csa_decode_b20_head_group_path(csa):
+    say("case: csa decode B=20 pos0=3001 (row slices x head groups, merged)")
+    _decode_case(csa, "csa_decode", 3001, 20, 5)
+
+
+def test_hca_decode_b16(csa):
+    say("case: mixed decode B=16 pos0=40000, HCA layer only (row slices x head groups)")
+    _decode_case(csa, "mixed_decode", 40000, 16, 6, layers=[1])
+
+
 def test_mixed_decode_small(csa):
     say("case: mixed decode B=2 pos0=40959 (HCA entry closes) three layers")
     _decode_case(csa, "mixed_decode", 40959, 2, 2)
