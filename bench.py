@@ -88,6 +88,27 @@ def decode_bytes(spec, B, t):
     return B * per
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_csa_prefill_S8192_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter profile, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return rec["read_bytes"] + rec["write_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(spec, inp, stride):
     """The oracle as it stands, on every `stride`-th query of the same layer."""
     from oracle import csa_oracle as O
@@ -330,7 +351,7 @@ def main():
                    "index_heads": 64, "index_dim": 128, "index_topk": 512},
         "roofline": {"bound": "mfma", "kernel": "attend_mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "launch_ms": head["attend_ms"], "algorithmic_flop": head["attend_flop"]},
         "attend_share_of_step": head["attend_ms"] / head["ms_per_step"],
         "step_frac_bf16_peak": head["step_frac_bf16_peak"],
