@@ -27,11 +27,19 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]
+# Per-file additions.  attend_wide8's eight-wave blocks give each wave 256
+# registers; with accumulators in AGPRs the compiler would split them 128/128
+# and spill the VGPR half, so its MFMA accumulators live in VGPRs.
+FILE_FLAGS = {
+    "attend_wide8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+# Extra flags for every file (e.g. -DCSA_ATTN_PREFILL=2), space separated.
+EXTRA = os.environ.get("CSA_HIPCC_EXTRA", "").split()
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -36,6 +36,8 @@
 //  * the bf16 output is staged through LDS and written as whole 1 KB rows.
 // attend_generic: any H, D; float32 VALU; used for float32 layers and small
 // shapes.
+#include <cstdlib>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 #include "attend_common.h"
@@ -51,6 +53,40 @@ constexpr int kPRow = kCH + 8;  // LDS row of P^T per head: 32 row slots + pad (
 #define CSA_ATTN_PD 2
 #endif
 constexpr int kQD = CSA_ATTN_QD, kPD = CSA_ATTN_PD;
+// O^T += V^T P^T on 32 x 32 x 16 tiles (about twice the 16 x 16 x 32 rate
+// on gfx950) instead of 16 x 16 x 32 ones.
+#ifndef CSA_ATTN_PV32
+#define CSA_ATTN_PV32 1
+#endif
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// Four 16-byte loads at a + i*SA + j*SB (i, j < 2) and two 4-byte loads at b
+// and b + SC (byte offsets), complete on return.
+template <int SA, int SB, int SC>
+__device__ __forceinline__ void lds_ld_2x2x128_2x32(const void* a, const void* b,
+                                                    uint4 (&o)[2][2], uint32_t (&w)[2]) {
+  static_assert(SA + SB < 65536 && SC < 65536, "immediate LDS offsets are 16-bit");
+  u32x4 x[4];
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:%9\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %6 offset:%10\n\t"
+      "ds_read_b32 %4, %7\n\t"
+      "ds_read_b32 %5, %7 offset:%11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(w[0]), "=&v"(w[1])
+      : "v"(lds_addr(a)), "v"(lds_addr(b)), "i"(SA), "i"(SB), "i"(SA + SB), "i"(SC)
+      : "memory");
+  o[0][0] = __builtin_bit_cast(uint4, x[0]);
+  o[0][1] = __builtin_bit_cast(uint4, x[1]);
+  o[1][0] = __builtin_bit_cast(uint4, x[2]);
+  o[1][1] = __builtin_bit_cast(uint4, x[3]);
+}
 
 template <int R>
 __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
@@ -69,7 +105,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   __shared__ double2 cs[kMaxRope / 2];
   __shared__ __attribute__((aligned(16))) bf16_t ps[kAH * kPRow];  // P^T, row slots per head
   __shared__ float alph[kAH];   // this chunk's rescale of O per head
-  __shared__ int resc[4];       // head group w raised its max this chunk
   __shared__ float mlf[2][kAH];  // final running max and sum per head
 
   constexpr int NTH = 256;
@@ -161,6 +196,19 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   uint4 Qf[16];
   load_qfrag<R>(q + (tok * kAH + 16 * wv + r16) * kAD, cs, g, Qf);
 
+#if CSA_ATTN_PV32
+  // O^T tiles of the wave's channel slice (channel tile ct, head tile hh):
+  // lane (l32, h32) holds channels 128*wv + 32*ct + 8*(v/4) + 4*h32 + v%4 of
+  // head 32*hh + l32
+  const int l32 = lane & 31, h32 = lane >> 5;
+  f32x16 O[4][2];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[ct][hh][v] = 0.f;
+#else
   // O^T accumulators of the wave's channel slice: channel 128*wv + 16*dt +
   // 4*g + e, head 16*ht + r16
   f32x4 O[8][4];
@@ -168,6 +216,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) O[dt][ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#endif
   float m_run = -INFINITY, l_run = 0.f;  // head 16*wv + r16
   const float sl2 = scale * kLog2e;
 
@@ -184,6 +233,24 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   int kb_v[4], tr_v[8];
 #pragma unroll
   for (int v = 0; v < 4; ++v) kb_v[v] = r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
+#if CSA_ATTN_PV32
+  // 32 x 32 x 16 V^T fragment of channel tile ct, row step ks, half h2: the
+  // address lane a = 4 j + q of 16-lane group (sub, h32) names row
+  // 16 ks + 8 h32 + 4 h2 + j and channels 32 ct + 16 sub + 4 q .. +3 of the
+  // wave's slice; lane a receives channel 16 sub + a of the tile for rows
+  // j = 0..3: tr_v[2 ct + h2] + ks * 16 KB
+  {
+    const int sub = g & 1, j4 = r16 >> 2, q4 = r16 & 3;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = 8 * h32 + 4 * h2 + j4;
+        tr_v[2 * ct + h2] =
+            r * 1024 + (((4 * ct + 2 * sub + (q4 >> 1)) ^ swz(r)) << 4) + (q4 & 1) * 8 + 256 * wv;
+      }
+  }
+#else
   {
     const int trA = 4 * g + (r16 >> 2);
     const int trc = (r16 & 3) >> 1, trh = (r16 & 1) * 8;
@@ -191,9 +258,12 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     for (int v = 0; v < 8; ++v)
       tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh + 256 * wv;
   }
+#endif
 
   auto chunk = [&](int c, const bf16_t* cur, int cn, bf16_t* nxt) {
     const char* kb = (const char*)cur;
+    // read before this chunk's gather is issued (no DMA in flight yet)
+    const uint32_t vm = vmask[c - c0] >> (4 * g);
     // the next chunk's gather (if any) is issued row by row between the
     // QK^T MFMAs below
     Gather G;
@@ -227,7 +297,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- online softmax (log2 domain); lane column = head 16*wv + r16
-    const uint32_t vm = vmask[c - c0] >> (4 * g);
     float sv[8];
     float cmax = -INFINITY;
 #pragma unroll
@@ -256,25 +325,77 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       pk[j >> 1] = pack_bf16x2(pa, pb);
     }
     l_run += psum;
-    // P^T slots of lane group g hold rows 4g..4g+3 and 16+4g..16+4g+3
-    *(uint4*)&ps[(16 * wv + r16) * kPRow + 8 * g] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    if (g == 0) alph[16 * wv + r16] = alpha;
-    if (lane == 0) resc[wv] = raise ? 1 : 0;
-    __syncthreads();
+    // P^T slots of lane group g hold rows 4g..4g+3 and 16+4g..16+4g+3; the
+    // next chunk's gather is in flight, so these LDS accesses and the
+    // barrier go through lds_* (they must not wait for it)
+#if CSA_ATTN_PV32
+    // rows in natural order: slots 4g..4g+3 and 16+4g..16+4g+3
+    lds_st64(&ps[(16 * wv + r16) * kPRow + 4 * g], pk[0], pk[1]);
+    lds_st64(&ps[(16 * wv + r16) * kPRow + 16 + 4 * g], pk[2], pk[3]);
+#else
+    lds_st128(&ps[(16 * wv + r16) * kPRow + 8 * g], make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#endif
+    if (g == 0) lds_st32(&alph[16 * wv + r16], __float_as_uint(alpha));
+    lds_barrier();
 
     // ---- O^T += V^T P^T over the wave's channel slice, all 64 heads
-    if (resc[0] | resc[1] | resc[2] | resc[3]) {
+#if CSA_ATTN_PV32
+    // P^T fragment (head tile hh, row step ks): rows 16 ks + 8 h32 .. +7 of
+    // head 32 hh + l32
+    uint4 Pf[2][2];
+    uint32_t a2u[2];
+    lds_ld_2x2x128_2x32<32 * kPRow * 2, 32, 32 * 4>(&ps[l32 * kPRow + 8 * h32], &alph[l32], Pf,
+                                                    a2u);
+    {
+      const float a0 = __uint_as_float(a2u[0]), a1 = __uint_as_float(a2u[1]);
+      // a head whose maximum was not raised has alpha exactly 1
+      if (__any(a0 != 1.f || a1 != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          O[ct][0] *= a0;
+          O[ct][1] *= a1;
+        }
+      }
+    }
+    auto vfrag = [&](int ct, int ks) {
+      const char* pa = kb + ks * 16384;
+      const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + tr_v[2 * ct]));
+      const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + tr_v[2 * ct + 1]));
+      return make_uint4((uint32_t)(uint16_t)x0[0] | ((uint32_t)(uint16_t)x0[1] << 16),
+                        (uint32_t)(uint16_t)x0[2] | ((uint32_t)(uint16_t)x0[3] << 16),
+                        (uint32_t)(uint16_t)x1[0] | ((uint32_t)(uint16_t)x1[1] << 16),
+                        (uint32_t)(uint16_t)x1[2] | ((uint32_t)(uint16_t)x1[3] << 16));
+    };
+    uint4 vf[2];
+    vf[0] = vfrag(0, 0);
+    vf[1] = vfrag(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {  // step st: row step st / 4, channel tile st % 4
+      const int ks = st >> 2, ct = st & 3;
+      const uint4 a = vf[st & 1];
+      if (st + 2 < 8) vf[st & 1] = vfrag((st + 2) & 3, (st + 2) >> 2);
+      O[ct][0] = mfma32x(a, Pf[0][ks], O[ct][0]);
+      O[ct][1] = mfma32x(a, Pf[1][ks], O[ct][1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#else
+    uint4 Pf[4];
+    uint32_t a4u[4];
+    lds_ld_4x128_4x32<16 * kPRow * 2, 16 * 4>(&ps[r16 * kPRow + 8 * g], &alph[r16], Pf, a4u);
+    {
       float a4[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) a4[ht] = alph[16 * ht + r16];
+      for (int ht = 0; ht < 4; ++ht) a4[ht] = __uint_as_float(a4u[ht]);
+      // a head whose maximum was not raised has alpha exactly 1
+      if (__any(a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) O[dt][ht] *= a4[ht];
+          for (int ht = 0; ht < 4; ++ht) O[dt][ht] *= a4[ht];
+      }
     }
-    uint4 Pf[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) Pf[ht] = *(const uint4*)&ps[(16 * ht + r16) * kPRow + 8 * g];
     // V^T fragments (two transpose reads each) kPD channel tiles ahead
     auto vfrag = [&](int dt) {
       const char* pa = kb + tr_v[dt];
@@ -298,13 +419,14 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+#endif
   for (int c = c0; c < c1; c += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this chunk's rows are in LDS
+    lds_barrier();
     chunk(c, kbuf0, c + 1, kbuf1);
     if (c + 1 < c1) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      lds_barrier();
       chunk(c + 1, kbuf1, c + 2, kbuf0);
     }
   }
@@ -319,6 +441,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   if (nsplit == 1) {
     // the whole [64 heads][512] bf16 output, chunks swizzled by head: heads
     // 0..31 in kbuf0, 32..63 in kbuf1
+#if !CSA_ATTN_PV32
     float inv[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -330,6 +453,41 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
       inv[ht] = f / lt;
     }
+#endif
+#if CSA_ATTN_PV32
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int head = 32 * hh + l32;
+      const float mh = mlf[0][head], lh = mlf[1][head];
+      const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
+      const float M = fmaxf(mh, sink);
+      const float f = __builtin_amdgcn_exp2f(mh - M);
+      const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
+      const float iv = f / lt;
+      char* ob = (hh == 0 ? (char*)kbuf0 : (char*)kbuf1) + (head & 31) * 1024;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = 128 * wv + 32 * ct + 8 * a + 4 * h32;
+          float o[4];
+#pragma unroll
+          for (int bq = 0; bq < 4; ++bq) o[bq] = O[ct][hh][4 * a + bq] * iv;
+#pragma unroll
+          for (int bq = 0; bq < 4; bq += 2) {
+            if (d + bq >= first) {  // pair (d + bq, d + bq + 1) rotated at -t
+              const double2 cz = cs[(d + bq - first) >> 1];
+              const float cf = (float)cz.x, sf = (float)cz.y;
+              const float x0 = o[bq] * cf + o[bq + 1] * sf, x1 = o[bq + 1] * cf - o[bq] * sf;
+              o[bq] = x0;
+              o[bq + 1] = x1;
+            }
+          }
+          *(uint2*)(ob + (((d >> 3) ^ (head & 15)) << 4) + ((d & 7) << 1)) =
+              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
+    }
+#else
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 128 * wv + 16 * dt + 4 * g;
@@ -359,6 +517,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
         *(uint2*)(ob + ((((d >> 3) ^ (head & 15))) << 4) + ((d & 7) << 1)) = st;
       }
     }
+#endif
     __syncthreads();
     bf16_t* orow = out + tok * kAH * kAD;
 #pragma unroll 4
@@ -370,11 +529,23 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     }
   } else {
     float* pbase = part + (tok * nsplit + split) * kAH * kPart;
+#if CSA_ATTN_PV32
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *(f32x4*)(pbase + (32 * hh + l32) * kPart + 128 * wv + 32 * ct + 8 * a + 4 * h32) =
+              f32x4{O[ct][hh][4 * a], O[ct][hh][4 * a + 1], O[ct][hh][4 * a + 2],
+                    O[ct][hh][4 * a + 3]};
+#else
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht)
         *(f32x4*)(pbase + (16 * ht + r16) * kPart + 128 * wv + 16 * dt + 4 * g) = O[dt][ht];
+#endif
     if (g == 0) {
       float* prow = pbase + (16 * wv + r16) * kPart;
       prow[kAD] = m_run;
@@ -603,9 +774,26 @@ static bool attend_dec(const Layer& L, int B, int n, int64_t pool_cap, bool csa)
   return tokens < 256 && (tokens >= 16 || attend_rows(L, pool_cap, csa) <= 256);
 }
 
+// Prefill kernel: 0 attend_mfma (QK^T on 16 x 16 tiles, 32-row chunks),
+// 1 attend_x32 (32 x 32 tiles, one wave per SIMD, 64-row chunks), 2 attend_w8
+// (32 x 32 tiles, eight waves per block, 64-row chunks), 3 attend_h32 (32 x 32
+// tiles, two blocks per CU, 32-row chunks).  The environment variable
+// CSA_ATTN_PREFILL ("0" .. "3"), read at each call, overrides the compiled
+// default.
+#ifndef CSA_ATTN_PREFILL
+#define CSA_ATTN_PREFILL 0
+#endif
+static int prefill_kernel() {
+  const char* e = getenv("CSA_ATTN_PREFILL");
+  if (e && e[0] >= '0' && e[0] <= '3' && e[1] == 0) return e[0] - '0';
+  return CSA_ATTN_PREFILL;
+}
+
 int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
   if (!attend_fast_shape(L)) return 1;
   if (attend_dec(L, B, n, pool_cap, csa)) return attend_decode_splits(L, B, n, pool_cap, csa);
+  const int pk = prefill_kernel();
+  const int kCH = pk == 1 || pk == 2 ? 64 : csa::kCH;
   const int64_t nch = (attend_rows(L, pool_cap, csa) + kCH - 1) / kCH;
   const int64_t tokens = (int64_t)B * n;
   // no block above kMaxRows rows; calls of fewer than 256 tokens also split
@@ -614,7 +802,7 @@ int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
   // much traffic as the rows)
   const int64_t need = (nch * kCH + kMaxRows - 1) / kMaxRows;
   int64_t s = tokens >= 256 ? 1 : (512 + tokens - 1) / tokens;
-  const int64_t cap = nch / 4 > 1 ? nch / 4 : 1;
+  const int64_t cap = nch / (128 / kCH) > 1 ? nch / (128 / kCH) : 1;
   if (s > cap) s = cap;
   if (s < need) s = need;
   if (s < 1) s = 1;
@@ -636,6 +824,20 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
     if (attend_dec(L, bt.B, bt.n, pool_cap, csa)) {
       hipError_t e = launch_attend_decode(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
                                           ws, csa, ns, s);
+      if (e != hipSuccess || ns == 1) return e;
+      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
+          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
+      return hipGetLastError();
+    }
+    const int pk = prefill_kernel();
+    if (pk) {
+      hipError_t e =
+          pk == 3   ? launch_attend_h32(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
+                                        ws, csa, ns, s)
+          : pk == 2 ? launch_attend_w8(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
+                                       ws, csa, ns, s)
+                    : launch_attend_x32(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
+                                        ws, csa, ns, s);
       if (e != hipSuccess || ns == 1) return e;
       attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
           (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
