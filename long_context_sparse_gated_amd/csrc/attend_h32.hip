@@ -49,6 +49,12 @@ __device__ __forceinline__ void lds_st2x128_mfma(void* a, f32x4 v0, f32x4 v1) {
       "i"(S)
       : "memory");
 }
+// One 16-byte load, complete on return.
+__device__ __forceinline__ u32x4 lds_ld128(const void* a) {
+  u32x4 x;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(lds_addr(a)) : "memory");
+  return x;
+}
 // Two 16-byte loads at a and a + S (byte offset), complete on return.
 template <int S>
 __device__ __forceinline__ void lds_ld_2x128(const void* a, f32x4& o0, f32x4& o1) {
@@ -132,6 +138,7 @@ __global__ void __launch_bounds__(256, 2) attend_h32(
   __shared__ uint32_t vmask[kMaxRows / 32 + 1];
   __shared__ double2 cs[kMaxRope / 2];
   __shared__ float cmx[4][32];   // each wave's chunk maximum per head of its tile
+  __shared__ __attribute__((aligned(16))) uint32_t flg[4];  // wave's rows exceed its maximum
   __shared__ float alph[kAH];    // this chunk's rescale of O per head
   __shared__ float lfin[4][32];  // each wave's running sum per head of its tile
   __shared__ float mfin[kAH];    // final running maximum per head
@@ -208,15 +215,33 @@ __global__ void __launch_bounds__(256, 2) attend_h32(
   // chunk's gather): head h at kb1[h * R ..]
   constexpr int first = kAD - R;
   {
+    // 16-byte pieces (4 pairs); the loads of a thread's pieces are issued
+    // together
+    constexpr int kPieces = kAH * R / 8, kPer = (kPieces + 255) / 256;
     const bf16_t* qt = q + tok * kAH * kAD;
-    for (int e = tid; e < kAH * (R / 2); e += 256) {
-      const int h = e / (R / 2), pr = e % (R / 2);
-      const uint32_t w = *(const uint32_t*)(qt + h * kAD + first + 2 * pr);
-      double a = bf16_to_f32((bf16_t)(w & 0xffffu)), bb = bf16_to_f32((bf16_t)(w >> 16));
-      const double2 c = cs[pr];
-      rot64(a, bb, c.x, c.y);
-      *(uint32_t*)(kb1 + h * R + 2 * pr) =
-          (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+    uint4 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      v[u] = e < kPieces ? *(const uint4*)(qt + (e / (R / 8)) * kAD + first + 8 * (e % (R / 8)))
+                         : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      if (e < kPieces) {
+        const int h = e / (R / 8), pc = e % (R / 8);
+        uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
+          double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+          const double2 c = cs[4 * pc + p];
+          rot64(a, bb, c.x, c.y);
+          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+        }
+        *(uint4*)(kb1 + h * R + 8 * pc) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
     }
   }
   __syncthreads();
@@ -330,32 +355,49 @@ __global__ void __launch_bounds__(256, 2) attend_h32(
       mx = fmaxf(mx, sv[j]);
     }
     mx = xmax32(mx);
+    // P with the running maximum of the earlier chunks.  A kept row above it
+    // by more than 2^8 (always in a split's first chunk) sends every wave
+    // through the second pass below, which takes the decision of the lazy
+    // rescale on the pair's combined maximum and rewrites P: the result is
+    // the same as exchanging the maxima up front, without that barrier in
+    // the common case.
+    const bool need = __any(mx > m_run + kLazy);
     if (hi == 0) lds_st32(&cmx[wv][lo], __float_as_uint(mx));
-    lds_barrier();
-    const float cmax = fmaxf(mx, __uint_as_float(lds_ld32(&cmx[wv ^ 2][lo])));
-    float alpha = 1.f;
-    if (__any(cmax > m_run + kLazy)) {  // the same decision in both waves of the head tile
-      const float m_new = fmaxf(m_run, cmax);
-      alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    float psum = 0.f;
+    if (ln == 0) lds_st32(&flg[wv], need ? 1u : 0u);
     bf16_t* prow = ps + (32 * ht + lo) * kHPRow + 4 * hi;
+    auto write_p = [&]() {
+      float psum = 0.f;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      float p[4];
+      for (int g = 0; g < 2; ++g) {
+        float p[4];
 #pragma unroll
-      for (int bq = 0; bq < 4; ++bq) {
-        // exp2(-inf) = 0 for masked rows; m_run is finite once a row was seen
-        p[bq] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[4 * g + bq] - m_run);
-        psum += p[bq];
+        for (int bq = 0; bq < 4; ++bq) {
+          // exp2(-inf) = 0 for masked rows; m_run is finite once a row was seen
+          p[bq] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[4 * g + bq] - m_run);
+          psum += p[bq];
+        }
+        lds_st64(prow + 8 * (g == 0 ? ka : kb), pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
-      lds_st64(prow + 8 * (g == 0 ? ka : kb), pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    }
-    l_run += psum;
-    if (kh == 0 && hi == 0) lds_st32(&alph[32 * ht + lo], __float_as_uint(alpha));
+      return psum;
+    };
+    const float l_prev = l_run;
+    l_run += write_p();
+    if (kh == 0 && hi == 0) lds_st32(&alph[32 * ht + lo], __float_as_uint(1.f));
     lds_barrier();
+    {
+      const u32x4 f4 = lds_ld128(flg);
+      if ((f4[0] | f4[1] | f4[2] | f4[3]) != 0) {  // the same in every wave
+        const float cmax = fmaxf(mx, __uint_as_float(lds_ld32(&cmx[wv ^ 2][lo])));
+        if (__any(cmax > m_run + kLazy)) {  // the same in both waves of the head tile
+          const float m_new = fmaxf(m_run, cmax);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run = l_prev * alpha + write_p();
+          if (kh == 0 && hi == 0) lds_st32(&alph[32 * ht + lo], __float_as_uint(alpha));
+        }
+        lds_barrier();
+      }
+    }
     // ---- O^T += V^T P^T over the wave's channel slice, all 64 heads; P^T
     // fragment (head tile hh, row step ks): rows 16 ks + 8 hi .. +7 of head
     // 32 hh + lo
