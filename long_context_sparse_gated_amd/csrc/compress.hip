@@ -21,18 +21,13 @@ namespace csa {
 
 constexpr int kMaxWidth = 2048;
 
+// Entry w of sequence b (one 256-thread block; pooled and red in LDS).
 template <typename T>
-__global__ void __launch_bounds__(256) compress_kernel(
+__device__ __forceinline__ void pool_entry(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, int n_new, int width, int R, double base, int m,
-    int overlap, int64_t pool_cap) {
-  __shared__ double pooled[kMaxWidth];
-  __shared__ double red[256 / 64];
-  const int b = blockIdx.y;
-  const int64_t p0 = pos0[b];
-  const int64_t w = p0 / m + blockIdx.x;
-  if (w >= (p0 + n_new) / m || w >= pool_cap) return;
+    int b, int64_t p0, int64_t w, int n_new, int width, int R, double base, int m, int overlap,
+    int64_t pool_cap, double* pooled, double* red) {
   const int Ls = (1 + overlap) * m;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
   const T* kv_b = kv + (int64_t)b * n_new * width;
@@ -82,6 +77,51 @@ __global__ void __launch_bounds__(256) compress_kernel(
   }
 }
 
+template <typename T>
+__global__ void __launch_bounds__(256) compress_kernel(
+    const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
+    float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
+    const int64_t* __restrict__ pos0, int n_new, int width, int R, double base, int m,
+    int overlap, int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double red[256 / 64];
+  const int b = blockIdx.y;
+  const int64_t p0 = pos0[b];
+  const int64_t w = p0 / m + blockIdx.x;
+  if (w >= (p0 + n_new) / m || w >= pool_cap) return;
+  pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, n_new, width, R, base, m,
+                overlap, pool_cap, pooled, red);
+}
+
+// One new token per sequence (decode): the entry that closes at it, if any,
+// then the token's raw row into its state slot, in one launch.  The entry's
+// earlier tokens sit in the other Ls - 1 slots, so the slot written here
+// (p0 mod Ls, holding position p0 - Ls) is never one the entry reads.
+template <typename T>
+__global__ void __launch_bounds__(256) compress_one_kernel(
+    const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
+    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
+    const int64_t* __restrict__ pos0, int width, int R, double base, int m, int overlap,
+    int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double red[256 / 64];
+  const int b = blockIdx.x;
+  const int64_t p0 = pos0[b];
+  const int Ls = (1 + overlap) * m;
+  const int64_t w = p0 / m;
+  if ((p0 + 1) % m == 0 && w < pool_cap)  // uniform per block
+    pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, 1, width, R, base, m,
+                  overlap, pool_cap, pooled, red);
+  const T* src_kv = kv + (int64_t)b * width;
+  const T* src_g = gate + (int64_t)b * width;
+  T* dk = st_kv + ((int64_t)b * Ls + p0 % Ls) * width;
+  T* dg = st_gate + ((int64_t)b * Ls + p0 % Ls) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) {
+    dk[c] = src_kv[c];
+    dg[c] = src_g[c];
+  }
+}
+
 // Keep the raw rows of the last (1 + overlap) m positions for later calls.
 // Runs after compress_kernel on the same stream (it overwrites slots that
 // kernel reads).
@@ -113,6 +153,17 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
   const int m = L.m, Ls = (1 + L.overlap) * m;
   const int max_entries = bt.n / m + 1;
   dim3 g1(max_entries, bt.B), g2(Ls, bt.B);
+  if (bt.n == 1) {
+    if (L.dtype == 1)
+      compress_one_kernel<bf16_t><<<bt.B, 256, 0, s>>>(
+          (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (bf16_t*)st_kv, (bf16_t*)st_gate,
+          (bf16_t*)pool, bt.pos0, width, rope_dim, L.base, m, L.overlap, pool_cap);
+    else
+      compress_one_kernel<float><<<bt.B, 256, 0, s>>>(
+          (const float*)kv, (const float*)gate, norm_w, eps, (float*)st_kv, (float*)st_gate,
+          (float*)pool, bt.pos0, width, rope_dim, L.base, m, L.overlap, pool_cap);
+    return hipGetLastError();
+  }
   if (L.dtype == 1) {
     compress_kernel<bf16_t><<<g1, 256, 0, s>>>(
         (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
