@@ -9,7 +9,8 @@
 // rotary_emb].
 //
 // Kernels:
-//  * index_prefill_mfma: H_I = 64, D_I = 128, bf16.  A block takes 8
+//  * index_prefill_mfma: H_I = 64, D_I = 128, bf16 (other rope widths, or
+//    CSA_INDEX_PREFILL=1).  A block takes 8
 //    consecutive queries (2 per wave, rotated query fragments held in VGPRs)
 //    and streams the visible keys through LDS in tiles of 64 keys shared by
 //    the four waves: 64 x 16 x 32 bf16 MFMA tiles, then ReLU, head weights and
@@ -24,10 +25,15 @@
 //    holding the k-th best score; per 1024-key slice the ids above that bin
 //    and inside it are compacted in id order; a radix select inside the bin
 //    settles the last places and both id lists are merged in id order.
+//  * index_prefill_x32 (default for H_I = 64, D_I = 128, rope width 64, bf16):
+//    one query per wave on 32 x 32 x 16 MFMA tiles, 128-key LDS tiles shared
+//    by the block's four waves; see its comment below.
 //  * index_generic: any head count / width, float or bf16, VALU float32.
 //  * topk_radix (prefill path): per query, four 8-bit radix-select passes
 //    find the k-th largest ordered key; one ordered pass emits ids by ballot
 //    prefix counts.
+#include <cstdlib>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -37,6 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -60,6 +68,43 @@ __device__ __forceinline__ uint4 rope8_bf16(uint4 v, int d0, int width, int R,
       w[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(b) << 16);
     }
   }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The same rotation with a float32 fast path, for 8 channels that are all
+// rope channels; c[p] holds the float32 images (ch, sh) of the float64 (cos,
+// sin) of pair p.  With S = |a| + |b|, x1 = fma(a, ch, -(b sh)) differs from
+// a cos - b sin by at most 2^-24 (|a| + 2|b| + |x1|) (1 + 2^-23) < 3.01 2^-24 S
+// (the cos/sin roundings, the rounded product and the fma), and the same
+// bound holds for y1 = fma(a, sh, b ch) against a sin + b cos.  The float64
+// evaluation is that close to the exact value too, so both round to the same
+// bf16 unless a rounding boundary (a bf16 midpoint) lies within e = 2^-22 S
+// of x1, or e is not below a quarter of x1's bf16 spacing (|x1| <= 1024 e);
+// a floor of 2^-120 on e covers float32 underflow.  A lane meeting either
+// case for any value redoes its 8 channels in float64 (rope8_bf16), so the
+// result is always that of the float64 path.
+__device__ __forceinline__ bool near_bf16_mid(float v, float e) {
+  const float mid = __uint_as_float((__float_as_uint(v) & 0xffff0000u) | 0x8000u);
+  return fabsf(v - mid) <= e;  // exact difference: same binade
+}
+
+__device__ __forceinline__ uint4 rope4_fast(uint4 v, const float2 (&c)[4], int d0, int width,
+                                            int R, const double2* cs) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  bool hard = false;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = __uint_as_float(w[p] << 16), b = __uint_as_float(w[p] & 0xffff0000u);
+    const float x = fmaf(a, c[p].x, -(b * c[p].y));
+    const float y = fmaf(a, c[p].y, b * c[p].x);
+    const float S = fabsf(a) + fabsf(b);
+    const float e = fmaxf(S * 0x1p-22f, 0x1p-120f), e10 = e * 1024.f;
+    const bool h = (int)near_bf16_mid(x, e) | (int)near_bf16_mid(y, e) |
+                   (int)(fminf(fabsf(x), fabsf(y)) <= e10);
+    hard = hard | (h & (S != 0.f));
+    w[p] = pack_bf16x2(x, y);
+  }
+  if (hard) return rope8_bf16(v, d0, width, R, cs);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -164,6 +209,235 @@ __global__ void __launch_bounds__(256) index_prefill_mfma(
 }
 
 // ---------------------------------------------------------------------------
+// prefill on 32 x 32 x 16 MFMA tiles: one query per wave, four per block
+//
+// For one query the scores of 32 keys come from a 64 x 32 product (heads x
+// keys) over 128 channels: two 32 x 32 output tiles of eight 16-deep steps.
+// A wave keeps its query's rotated fragments (64 VGPRs, heads as rows) and
+// the weights of the heads its lanes receive; the four waves of a block share
+// 128-key tiles that reach LDS through LDS-DMA, two buffers deep, and each
+// tile is scored in four 32-key steps.  In a 32 x 32 result each lane holds
+// 16 heads of one key, so ReLU, weights and the sum over them stay in-lane;
+// one lane-half swap then adds the other 16 heads and packs two steps so that
+// lane l holds key l of the pair.  The query itself arrives by whole-row DMA
+// through the tile buffers (coalesced, unlike fragment-shaped global loads)
+// and is rotated with the float32 fast path.  Blocks take the longest query
+// groups first.  Rope width 64 only (a template parameter; other widths use
+// index_prefill_mfma).
+
+constexpr int kX32Q = 4;     // queries per block, one per wave
+constexpr int kX32KT = 128;  // keys per LDS tile (32 KB): four 32-key steps
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// max(x, 0) for a finite float (-0 -> +0) by its bits: a single integer max.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Eight 16-byte LDS reads at a[i] + OFF, waited for in the same block (the
+// compiler then sees no LDS load to order after the DMA in flight).
+template <int OFF>
+__device__ __forceinline__ void lds_frag8(const uint32_t (&a)[8], uint4 (&o)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%16\n"
+      "ds_read_b128 %1, %9 offset:%16\n"
+      "ds_read_b128 %2, %10 offset:%16\n"
+      "ds_read_b128 %3, %11 offset:%16\n"
+      "ds_read_b128 %4, %12 offset:%16\n"
+      "ds_read_b128 %5, %13 offset:%16\n"
+      "ds_read_b128 %6, %14 offset:%16\n"
+      "ds_read_b128 %7, %15 offset:%16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "n"(OFF)
+      : "memory");
+}
+
+template <int RI>
+__global__ void __launch_bounds__(256, 2) index_prefill_x32(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
+    float* __restrict__ scores, float* __restrict__ discard, const int64_t* __restrict__ pos0,
+    int n_new, int B, double base, int m, int64_t pool_cap) {
+  constexpr int Hi = 64, Di = 128, kFirst = Di - RI, kK0 = kFirst / 16;
+  static_assert(RI > 0 && RI <= Di && RI % 16 == 0, "rope channels: whole 16-channel steps");
+  __shared__ __attribute__((aligned(1024))) bf16_t kt0[kX32KT * Di];
+  __shared__ __attribute__((aligned(1024))) bf16_t kt1[kX32KT * Di];
+  __shared__ double2 cs[kX32Q][RI / 2];
+  __shared__ float2 csf[kX32Q][RI / 2];
+  __shared__ float wsh[kX32Q][Hi];
+  const int nblk = (n_new + kX32Q - 1) / kX32Q;
+  const int b = blockIdx.x % B, i0 = (nblk - 1 - (int)(blockIdx.x / B)) * kX32Q;
+  const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t p0 = pos0[b];
+  const int nq = min(kX32Q, n_new - i0);
+  int64_t nv_last = (p0 + i0 + nq) / m;  // the block's last query sees the most keys
+  if (nv_last > pool_cap) nv_last = pool_cap;
+  const int nkeys = (int)nv_last;
+  if (nkeys == 0) return;  // block-uniform
+  const int ntile = (nkeys + kX32KT - 1) / kX32KT;
+
+  // DMA of this wave's 32 rows of a tile (8 instructions of 4 rows); chunk c
+  // of row r sits at slot c ^ (r & 15); rows past the keys re-read the last.
+  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
+  const int lrow = lane >> 4, slot = lane & 15;
+  auto issue = [&](int tile, bf16_t* dst) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 32 * wv + 4 * j + lrow;
+      const int key = min(tile * kX32KT + r, nkeys - 1);
+      const bf16_t* src = kbase + (int64_t)key * Di + 8 * (slot ^ ((4 * j + lrow) & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
+                                       16, 0, 0);
+    }
+  };
+  const int ql = wv < nq ? wv : 0;
+  int64_t nv = (p0 + i0 + wv + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  const int nvis = wv < nq ? (int)nv : 0;
+  const bf16_t* qrow = q + ((int64_t)b * n_new + i0 + ql) * Hi * Di;
+  const bf16_t wt_raw = wts[((int64_t)b * n_new + i0 + min(tid / Hi, nq - 1)) * Hi + tid % Hi];
+  // The query reaches registers through LDS: head rows 0-31 go to this
+  // wave's 32 rows of kt0, rows 32-63 to its rows of kt1 (whole-row DMA in
+  // the keys' layout), and are read back as A fragments like the keys.  The
+  // wave's own DMA of key tile 0 then refills its rows of kt0; kt1 is free
+  // until tile 1, which is issued after a barrier.
+  auto issue_q = [&](int mt, bf16_t* dst) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + lrow;
+      const bf16_t* src = qrow + (32 * mt + r) * Di + 8 * (slot ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
+                                       16, 0, 0);
+    }
+  };
+  // lane address of step kk = 0 in a 32-row block of the keys' layout; step
+  // kk adds nothing but an XOR of 32 kk (bits 5-7)
+  auto frag_addr = [&](const bf16_t* rows, uint32_t (&a)[8]) {
+    int ln;  // opaque copy: keeps the per-lane addresses out of loop-invariant registers
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int l = ln & 31, h = ln >> 5;
+    const uint32_t a0 = (uint32_t)(size_t)(lds_void*)rows +
+                        (uint32_t)(l * Di * 2 + 16 * (h ^ (l & 1)) + 32 * ((l >> 1) & 7));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) a[kk] = a0 ^ (32u * kk);
+  };
+  issue_q(0, kt0);
+  issue_q(1, kt1);  // both overlap the tables
+  for (int e = tid; e < kX32Q * (RI / 2); e += 256) {
+    const int qq = e / (RI / 2), j = e % (RI / 2);
+    double sn, c;
+    sincos((double)(p0 + i0 + qq) * rope_freq(base, j, RI), &sn, &c);
+    cs[qq][j] = make_double2(c, sn);
+    csf[qq][j] = make_float2((float)c, (float)sn);
+  }
+  wsh[tid / Hi][tid % Hi] = tid / Hi < nq ? bf16_to_f32(wt_raw) : 0.f;
+  __syncthreads();  // the tables are written
+  uint4 A[2][8];  // this wave's query, head 32 mt + l32, channels 16 kk + 8 h32 .. + 7
+  float wr[2][16];
+  // (cos, sin) of the lane's rope pairs, read before the key DMA (LDS reads
+  // after it would wait for it)
+  float2 c[8 - kK0][4];
+#pragma unroll
+  for (int kk = kK0; kk < 8; ++kk)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c[kk - kK0][p] = csf[ql][8 * kk + 4 * h32 + p - kFirst / 2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[mt][r] = wsh[ql][32 * mt + 8 * (r / 4) + 4 * h32 + r % 4];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's query rows landed
+  {
+    uint32_t a[8];
+    frag_addr(kt0 + 32 * wv * Di, a);
+    lds_frag8<0>(a, A[0]);
+    frag_addr(kt1 + 32 * wv * Di, a);
+    lds_frag8<0>(a, A[1]);
+  }
+  issue(0, kt0);  // this wave's rows only: its own staging reads are done
+  if (wv < nq) {  // waves past the last query score nothing that is kept
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kk = kK0; kk < 8; ++kk)
+        A[mt][kk] = rope4_fast(A[mt][kk], c[kk - kK0], 16 * kk + 8 * h32, Di, RI, cs[wv]);
+  }
+
+  // The B fragment of step kk for the 32 keys of step st: row 32 st + l32,
+  // channels 16 kk + 8 h32, i.e. chunk 2 kk + h32 at slot (2 kk + h32) ^ (l32 & 15):
+  // byte offset (row base) + 16 (h32 ^ (l32 & 1)) + 32 (kk ^ ((l32 >> 1) & 7)),
+  // an XOR of 32 kk into the lane's kk = 0 offset.
+  float* srow = scores + ((int64_t)b * n_new + i0 + ql) * pool_cap;
+  auto step = [&](uint4 (&Bf)[8]) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(A[mt][kk], Bf[kk], acc[mt]);
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r & 3] += wr[mt][r] * relu_bits(acc[mt][r]);
+    return (p[0] + p[1]) + (p[2] + p[3]);
+  };
+  // lanes 0-31: keys 0-31 of the pair of steps, lanes 32-63: keys 32-63;
+  // every path stores (the loop's wait counts the stores)
+  auto store = [&](int key0, float v0, float v1) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false,
+                                               false);
+    const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int key = key0 + lane;
+    *(key < nvis ? srow + key : discard + lane) = sc;
+  };
+  auto compute = [&](int tile, const bf16_t* kt) {
+    uint32_t a[8];
+    frag_addr(kt, a);
+    const int k0 = tile * kX32KT;
+    uint4 Bf[8];
+    lds_frag8<0>(a, Bf);
+    const float v0 = step(Bf);
+    lds_frag8<32 * Di * 2>(a, Bf);
+    const float v1 = step(Bf);
+    store(k0, v0, v1);
+    float v2 = 0.f, v3 = 0.f;
+    if (k0 + 64 < nkeys) {  // block-uniform: skip the steps past the keys
+      lds_frag8<64 * Di * 2>(a, Bf);
+      v2 = step(Bf);
+      lds_frag8<96 * Di * 2>(a, Bf);
+      v3 = step(Bf);
+    }
+    store(k0 + 64, v2, v3);
+  };
+  // Tile t is in kt0 for even t, kt1 for odd t.  At the top of each tile
+  // this wave's DMA of it is done once at most two later VMEM operations (the
+  // previous tile's two score stores) are outstanding; the barrier then
+  // publishes every wave's rows and retires every read of the other array.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int tile = 0;;) {
+    if (tile + 1 < ntile) issue(tile + 1, kt1);
+    compute(tile, kt0);
+    if (++tile >= ntile) break;
+    asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+    if (tile + 1 < ntile) issue(tile + 1, kt0);
+    compute(tile, kt1);
+    if (++tile >= ntile) break;
+    asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// ---------------------------------------------------------------------------
 // decode: rotate queries once, then stream keys from HBM into MFMA fragments
 //
 // Selection of the k best among up to millions of visible keys runs in three
@@ -210,7 +484,6 @@ __global__ void __launch_bounds__(256) rotate_queries_bf16(const bf16_t* __restr
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kDecTile = 128;  // keys per LDS tile: 32 per wave, 32 KB
 
@@ -840,6 +1113,16 @@ static bool index_decode_path(const Layer& L, int n, int64_t pool_cap) {
          (pool_cap + kSlice - 1) / kSlice <= kMaxSlices;
 }
 
+// Prefill scoring kernel: 0 index_prefill_x32 (32 x 32 tiles, one query per
+// wave), 1 index_prefill_mfma (16 x 16 tiles, two queries per wave).  The
+// environment variable CSA_INDEX_PREFILL ("0" or "1"), read at each call,
+// overrides the default.
+static int index_prefill_kernel() {
+  const char* e = getenv("CSA_INDEX_PREFILL");
+  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
+  return 0;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
@@ -851,6 +1134,8 @@ size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
     s += align256(bn * kHBins * sizeof(uint32_t));    // score histograms
     s += 2 * align256(bn * pool_cap * sizeof(int32_t));  // candidate ids
     s += align256(bn * nslice * 2 * sizeof(uint32_t) + 64);  // per-slice counts, discard
+  } else if (index_fast_shape(L)) {
+    s += 256;  // discard slots of index_prefill_x32
   }
   return s;
 }
@@ -898,7 +1183,13 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
                                       L.m, L.k, pool_cap, nslice);
     return hipGetLastError();
   }
-  if (index_fast_shape(L)) {
+  if (index_fast_shape(L) && L.Ri == 64 && index_prefill_kernel() == 0) {
+    const unsigned nblk = (unsigned)((bt.n + kX32Q - 1) / kX32Q);
+    index_prefill_x32<64><<<nblk * bt.B, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
+                                                      (const bf16_t*)keys, scores, (float*)wsp,
+                                                      bt.pos0, bt.n, bt.B, L.base, L.m,
+                                                      pool_cap);
+  } else if (index_fast_shape(L)) {
     dim3 grid((bt.n + kIdxQPB - 1) / kIdxQPB, bt.B);
     index_prefill_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
                                             (const bf16_t*)keys, scores, bt.pos0, bt.n, L.Ri,

@@ -103,6 +103,19 @@ def test_csa_prefill_bf16_small_topk(csa):
                                                         500, 777, 998, 999])
 
 
+@pytest.mark.parametrize("var,val", [("CSA_ATTN_PREFILL", "1"), ("CSA_ATTN_PREFILL", "2"),
+                                     ("CSA_ATTN_PREFILL", "3"), ("CSA_INDEX_PREFILL", "1")])
+def test_csa_prefill_alternative_kernels(csa, monkeypatch, var, val):
+    """The run-time selectable prefill kernels (attention and indexer) against the oracle."""
+    say(f"case: csa_prefill bf16 S=1000 k=64 B=2 with {var}={val}")
+    import dataclasses
+    monkeypatch.setenv(var, val)
+    w = synth.workload("csa_prefill", S=1000, batch=2)
+    spec = dataclasses.replace(w.layers[0], topk=64)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 5, queries_per_seq=[0, 3, 4, 63, 64, 255, 256, 511, 700, 999])
+
+
 def test_csa_prefill_bf16_k512(csa):
     say("case: csa_prefill bf16 S=2600 k=512 (mfma kernels)")
     w = synth.workload("csa_prefill", S=2600)
