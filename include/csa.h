@@ -79,6 +79,23 @@ typedef struct {
   int32_t index_topk;       /* k entries selected per query, 1..4096           */
   float softmax_scale;      /* logit scale; 0 selects 1/sqrt(head_dim).  The
                                sink logit is not scaled.                       */
+  /* YaRN rope scaling (every rope of the layer: queries, window rows, pooled
+   * entries, indexer queries and keys, the output's -t rotation).  With
+   * rope_factor = s > 1 the frequency of pair j of R rope channels,
+   * theta_j = rope_theta^(-2j/R), becomes theta_j (1 - r_j) + (theta_j / s) r_j,
+   * the ramp r_j rising linearly in j from 0 at lo to 1 at hi, where lo / hi
+   * are the pair indices, rounded down / up and clamped to [0, R - 1], at
+   * which a pair turns rope_beta_fast / rope_beta_slow times over
+   * rope_original_context positions:
+   * R ln(rope_original_context / (2 pi n)) / (2 ln rope_theta).  Only the
+   * frequencies change; any logit temperature goes through softmax_scale.
+   * rope_factor 0 (or 1) leaves the rope unscaled and the other three fields
+   * unread.  Source: optimum-intel issue 1748, "What V4-Flash adds vs V3"
+   * (YaRN factor 16, 65k -> 1M context). */
+  double rope_factor;           /* s: 0, or >= 1                              */
+  double rope_original_context; /* > 0 when rope_factor > 1                   */
+  double rope_beta_fast;        /* > rope_beta_slow > 0 when rope_factor > 1  */
+  double rope_beta_slow;
 } csa_layer;
 
 /* Geometry of one call. */

@@ -38,7 +38,9 @@ class _CLayer(ctypes.Structure):
                 ("compress_ratio", ctypes.c_int32), ("overlap", ctypes.c_int32),
                 ("index_n_heads", ctypes.c_int32), ("index_head_dim", ctypes.c_int32),
                 ("index_rope_dim", ctypes.c_int32), ("index_topk", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("rope_factor", ctypes.c_double),
+                ("rope_original_context", ctypes.c_double), ("rope_beta_fast", ctypes.c_double),
+                ("rope_beta_slow", ctypes.c_double)]
 
 
 class _CBatch(ctypes.Structure):
@@ -62,6 +64,10 @@ class Layer:
     index_rope_dim: int = 0
     index_topk: int = 0
     softmax_scale: float = 0.0
+    rope_factor: float = 0.0            # YaRN scale; 0: none
+    rope_original_context: float = 0.0
+    rope_beta_fast: float = 0.0
+    rope_beta_slow: float = 0.0
 
     @classmethod
     def from_spec(cls, spec) -> "Layer":
@@ -72,14 +78,19 @@ class Layer:
                    index_n_heads=spec.index_heads if spec.kind == "csa" else 0,
                    index_head_dim=spec.index_dim if spec.kind == "csa" else 0,
                    index_rope_dim=spec.index_rope_dim if spec.kind == "csa" else 0,
-                   index_topk=spec.topk if spec.kind == "csa" else 0)
+                   index_topk=spec.topk if spec.kind == "csa" else 0,
+                   rope_factor=getattr(spec, "rope_factor", 0.0),
+                   rope_original_context=getattr(spec, "rope_original_context", 0.0),
+                   rope_beta_fast=getattr(spec, "rope_beta_fast", 0.0),
+                   rope_beta_slow=getattr(spec, "rope_beta_slow", 0.0))
 
     def _c(self) -> _CLayer:
         return _CLayer(1 if self.dtype == "bf16" else (0 if self.dtype == "f32" else 99),
                        self.num_heads, self.head_dim, self.qk_rope_head_dim, self.rope_theta,
                        self.sliding_window, self.compress_ratio, self.overlap,
                        self.index_n_heads, self.index_head_dim, self.index_rope_dim,
-                       self.index_topk, self.softmax_scale)
+                       self.index_topk, self.softmax_scale, self.rope_factor,
+                       self.rope_original_context, self.rope_beta_fast, self.rope_beta_slow)
 
 
 _lib = None

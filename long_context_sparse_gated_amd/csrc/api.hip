@@ -23,11 +23,23 @@ csa_status to_layer(const csa_layer* in, Layer* L) {
       !(in->rope_theta > 0.0) || !isfinite(in->rope_theta) || in->softmax_scale < 0.f ||
       !isfinite(in->softmax_scale))
     return CSA_ERR_SHAPE;
+  if (!(in->rope_factor >= 0.0) || !isfinite(in->rope_factor) ||
+      (in->rope_factor > 0.0 && in->rope_factor < 1.0))
+    return CSA_ERR_SHAPE;
+  if (in->rope_factor > 1.0 &&
+      (!(in->rope_original_context > 0.0) || !isfinite(in->rope_original_context) ||
+       !(in->rope_beta_slow > 0.0) || !(in->rope_beta_fast > in->rope_beta_slow) ||
+       !isfinite(in->rope_beta_fast) || in->rope_theta == 1.0))
+    return CSA_ERR_SHAPE;
   L->dtype = in->dtype;
   L->H = in->num_heads;
   L->D = in->head_dim;
   L->R = in->qk_rope_head_dim;
-  L->base = in->rope_theta;
+  L->base.base = in->rope_theta;
+  L->base.factor = in->rope_factor > 1.0 ? in->rope_factor : 0.0;
+  L->base.orig = in->rope_original_context;
+  L->base.beta_fast = in->rope_beta_fast;
+  L->base.beta_slow = in->rope_beta_slow;
   L->W = in->sliding_window;
   L->m = in->compress_ratio;
   L->overlap = in->overlap;

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, int n_new, int W, int m, double base, float scale,
+    const int64_t* __restrict__ pos0, int n_new, int W, int m, Rope base, float scale,
     int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   // two separate arrays (not one indexed by parity) so the compiler can tell
@@ -563,7 +563,7 @@ constexpr int kMaxSplits = 256;
 
 __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
     const float* __restrict__ part, const float* __restrict__ sinks, bf16_t* __restrict__ out,
-    const int64_t* __restrict__ pos0, int n_new, int R, double base, int nsplit) {
+    const int64_t* __restrict__ pos0, int n_new, int R, Rope base, int nsplit) {
   __shared__ double2 cs[kAD / 2];
   __shared__ float fs[kMergeHeads][kMaxSplits];
   const int64_t tok = blockIdx.x;
@@ -638,7 +638,7 @@ __global__ void __launch_bounds__(256) attend_generic(
     const T* __restrict__ q, const T* __restrict__ win, int64_t win_cap, const T* __restrict__ pool,
     int64_t pool_cap, const int32_t* __restrict__ idx, int k, const float* __restrict__ sinks,
     T* __restrict__ out, const int64_t* __restrict__ pos0, int n_new, int H, int D, int R, int W,
-    int m, double base, float scale, int csa) {
+    int m, Rope base, float scale, int csa) {
   extern __shared__ float sm[];
   float* qs = sm;                      // [H*D]
   float* acc = qs + H * D;             // [H*D]

@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256, 2) attend_h32(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, int n_new, int W, int m, double base, float scale,
+    const int64_t* __restrict__ pos0, int n_new, int W, int m, Rope base, float scale,
     int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   // two separate arrays (not one indexed by parity) so the compiler can tell

@@ -26,7 +26,7 @@ template <typename T>
 __device__ __forceinline__ void pool_entry(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    int b, int64_t p0, int64_t w, int n_new, int width, int R, double base, int m, int overlap,
+    int b, int64_t p0, int64_t w, int n_new, int width, int R, Rope base, int m, int overlap,
     int64_t pool_cap, double* pooled, double* red) {
   const int Ls = (1 + overlap) * m;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
@@ -81,7 +81,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) compress_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, int n_new, int width, int R, double base, int m,
+    const int64_t* __restrict__ pos0, int n_new, int width, int R, Rope base, int m,
     int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];
@@ -101,7 +101,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) compress_one_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, int width, int R, double base, int m, int overlap,
+    const int64_t* __restrict__ pos0, int width, int R, Rope base, int m, int overlap,
     int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "csa_internal.h"
+
 namespace csa {
 
 typedef uint16_t bf16_t;
@@ -65,9 +67,27 @@ template <> struct store_t<bf16_t> {
   static __device__ __forceinline__ float cvt(bf16_t v) { return bf16_to_f32(v); }
 };
 
-// Frequency of rope pair j: base^(-2j/R), in float64.
-__device__ __forceinline__ double rope_freq(double base, int j, int R) {
-  return pow(base, (-2.0 * (double)j) / (double)R);
+// Frequency of rope pair j of R rope channels, in float64: theta_j =
+// base^(-2j/R), or with YaRN scaling by s = factor > 1,
+// theta_j (1 - r_j) + (theta_j / s) r_j.  The ramp r_j rises linearly in j
+// from 0 at lo to 1 at hi, lo and hi being the pair indices (rounded down and
+// up, clamped to [0, R - 1]) at which a pair turns beta_fast and beta_slow
+// times over the original context: c(n) = R ln(orig / (2 pi n)) / (2 ln base).
+// Pairs below lo keep their frequency, pairs from hi on are slowed by s.
+// [optimum-intel issue 1748, "What V4-Flash adds vs V3": YaRN, factor 16,
+// 65k -> 1M context; the ramp is the YaRN method's]
+__device__ __forceinline__ double rope_freq(const Rope& rp, int j, int R) {
+  const double f = pow(rp.base, (-2.0 * (double)j) / (double)R);
+  if (!(rp.factor > 1.0)) return f;
+  const double two_pi = 6.283185307179586, lb = 2.0 * log(rp.base);
+  double lo = floor((double)R * log(rp.orig / (two_pi * rp.beta_fast)) / lb);
+  double hi = ceil((double)R * log(rp.orig / (two_pi * rp.beta_slow)) / lb);
+  lo = lo > 0.0 ? lo : 0.0;
+  hi = hi < (double)(R - 1) ? hi : (double)(R - 1);
+  if (hi == lo) hi += 0.001;
+  double r = ((double)j - lo) / (hi - lo);
+  r = r < 0.0 ? 0.0 : (r > 1.0 ? 1.0 : r);
+  return f * (1.0 - r) + (f / rp.factor) * r;
 }
 
 // (a, b) <- (a cos - b sin, a sin + b cos): multiplication by cos + i sin.

@@ -9,10 +9,20 @@ namespace csa {
 
 constexpr int kMaxTopK = 4096;  // largest index_topk the library accepts
 
+// Rope frequencies of a layer: pair j of R rope channels turns at
+// base^(-2j/R) per position, remapped by YaRN when factor > 1 (rope_freq in
+// csa_device.h).
+struct Rope {
+  double base;
+  double factor;               // YaRN scale s; <= 1: none
+  double orig;                 // original context length
+  double beta_fast, beta_slow;  // turns over orig bounding the ramp
+};
+
 struct Layer {
   int dtype;       // 0 float32, 1 bf16
   int H, D, R;     // heads, head_dim, rope channels
-  double base;     // rope base
+  Rope base;       // rope frequencies (both the main and the indexer rope)
   int W;           // sliding window
   int m, overlap;  // compress ratio (0 = none), overlap flag
   int Hi, Di, Ri;  // indexer heads, dim, rope channels

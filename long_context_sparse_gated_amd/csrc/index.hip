@@ -117,7 +117,7 @@ constexpr int kIdxRow = 136;  // LDS row stride in bf16 (128 + 8 pad)
 
 __global__ void __launch_bounds__(256) index_prefill_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
-    float* __restrict__ scores, const int64_t* __restrict__ pos0, int n_new, int Ri, double base,
+    float* __restrict__ scores, const int64_t* __restrict__ pos0, int n_new, int Ri, Rope base,
     int m, int64_t pool_cap) {
   constexpr int Hi = 64, Di = 128;
   __shared__ __attribute__((aligned(16))) bf16_t ktile[2][kIdxKT * kIdxRow];
@@ -264,7 +264,7 @@ template <int RI>
 __global__ void __launch_bounds__(256, 2) index_prefill_x32(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
     float* __restrict__ scores, float* __restrict__ discard, const int64_t* __restrict__ pos0,
-    int n_new, int B, double base, int m, int64_t pool_cap) {
+    int n_new, int B, Rope base, int m, int64_t pool_cap) {
   constexpr int Hi = 64, Di = 128, kFirst = Di - RI, kK0 = kFirst / 16;
   static_assert(RI > 0 && RI <= Di && RI % 16 == 0, "rope channels: whole 16-channel steps");
   __shared__ __attribute__((aligned(1024))) bf16_t kt0[kX32KT * Di];
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(256) rotate_queries_bf16(const bf16_t* __restr
                                                            uint32_t* __restrict__ hist,
                                                            const int64_t* __restrict__ pos0,
                                                            int n_new, int Hi, int Di, int Ri,
-                                                           double base) {
+                                                           Rope base) {
   __shared__ double2 cs[128];
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t t = pos0[b] + i;
@@ -961,7 +961,7 @@ __global__ void __launch_bounds__(256) index_generic(const T* __restrict__ q,
                                                      const T* __restrict__ keys,
                                                      float* __restrict__ scores,
                                                      const int64_t* __restrict__ pos0, int n_new,
-                                                     int Hi, int Di, int Ri, double base, int m,
+                                                     int Hi, int Di, int Ri, Rope base, int m,
                                                      int64_t pool_cap) {
   extern __shared__ float qs[];  // [Hi * Di] rotated query, then [Hi] weights
   const int i = blockIdx.x, b = blockIdx.y;

@@ -15,7 +15,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict__ kv,
                                                             T* __restrict__ ring,
                                                             const int64_t* __restrict__ pos0,
-                                                            int n_new, int D, int R, double base,
+                                                            int n_new, int D, int R, Rope base,
                                                             int64_t cap) {
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t t = pos0[b] + i;
@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict_
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kernel(T* __restrict__ x,
                                                    const int64_t* __restrict__ pos0, int n_new,
-                                                   int rows, int width, int R, double base,
+                                                   int rows, int width, int R, Rope base,
                                                    int sign) {
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t t = pos0[b] + i;

@@ -40,12 +40,13 @@ Readings where the pages are silent (each is also listed in the design doc):
 from __future__ import annotations
 
 import math
-from typing import Dict, Iterable, Optional
+from typing import Dict, Iterable, NamedTuple, Optional
 
 import numpy as np
 
 __all__ = [
-    "round_to", "rope", "pool_entry", "compress", "visible_entries",
+    "round_to", "Yarn", "yarn_correction_index", "rope_frequencies", "rope_base", "rope",
+    "pool_entry", "compress", "visible_entries",
     "window_positions", "index_scores", "topk_select", "attend",
     "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step",
 ]
@@ -72,20 +73,75 @@ def round_to(x, dtype: str) -> np.ndarray:
     return np.where(np.abs(q) > _BF16_MAX, np.copysign(np.inf, x), q)
 
 
-def rope(x, pos, rope_dim: int, base: float, sign: int = 1) -> np.ndarray:
+class Yarn(NamedTuple):
+    """YaRN-scaled rope frequencies [OV "What V4-Flash adds vs V3": YaRN RoPE
+    scaling, factor 16, 65k -> 1M context].  The pages name the method and the
+    factor only; the ramp below is the YaRN method's (its published default
+    turn counts beta_fast = 32, beta_slow = 1 are the layer spec's defaults)."""
+    base: float
+    factor: float
+    original_context: float
+    beta_fast: float
+    beta_slow: float
+
+
+def yarn_correction_index(n_turns: float, rope_dim: int, base: float, context: float) -> float:
+    """The (real) pair index j at which theta_j = base^(-2j/rope_dim) makes
+    ``n_turns`` full turns over ``context`` positions: context theta_j / (2 pi)
+    = n_turns, i.e. j = rope_dim ln(context / (2 pi n_turns)) / (2 ln base)."""
+    return rope_dim * math.log(context / (2.0 * math.pi * n_turns)) / (2.0 * math.log(base))
+
+
+def rope_frequencies(rope_dim: int, base) -> np.ndarray:
+    """theta_j for the rope_dim/2 pairs: base^(-2j/rope_dim) for a float base.
+
+    For a ``Yarn`` base with factor s > 1: pairs up to lo (those turning at
+    least beta_fast times over the original context) keep theta_j, pairs from
+    hi on (at most beta_slow turns) are slowed to theta_j / s, and in between
+    theta_j (1 - r) + (theta_j / s) r with r rising linearly in j; lo and hi
+    are the correction indices of beta_fast and beta_slow rounded down and up
+    and clamped to [0, rope_dim - 1].
+    """
+    j = np.arange(rope_dim // 2, dtype=np.float64)
+    if not isinstance(base, Yarn):
+        return base ** (-2.0 * j / rope_dim)
+    theta = base.base ** (-2.0 * j / rope_dim)
+    if not base.factor > 1.0:
+        return theta
+    lo = math.floor(yarn_correction_index(base.beta_fast, rope_dim, base.base,
+                                          base.original_context))
+    hi = math.ceil(yarn_correction_index(base.beta_slow, rope_dim, base.base,
+                                         base.original_context))
+    lo, hi = max(lo, 0), min(hi, rope_dim - 1)
+    if hi == lo:
+        hi += 0.001
+    r = np.clip((j - lo) / (hi - lo), 0.0, 1.0)
+    return theta * (1.0 - r) + (theta / base.factor) * r
+
+
+def rope_base(L):
+    """The rope frequency spec of a layer spec: its base, or a ``Yarn``."""
+    f = getattr(L, "rope_factor", 0.0)
+    if f > 1.0:
+        return Yarn(L.rope_theta, f, L.rope_original_context, L.rope_beta_fast,
+                    L.rope_beta_slow)
+    return L.rope_theta
+
+
+def rope(x, pos, rope_dim: int, base, sign: int = 1) -> np.ndarray:
     """Partial interleaved-pair rotary embedding [HF-PR RoPE apply; HF-doc sec. 2.3].
 
     The last ``rope_dim`` channels of each row, taken as pairs (c, c+1), are a
     complex number x_c + i x_{c+1} multiplied by exp(i * sign * pos * theta_j),
-    theta_j = base^(-2j/rope_dim) for pair j; other channels pass unchanged.
-    ``pos`` broadcasts against the leading axes of ``x``.
+    theta_j = base^(-2j/rope_dim) for pair j (``rope_frequencies``; ``base``
+    may be a ``Yarn``); other channels pass unchanged.  ``pos`` broadcasts
+    against the leading axes of ``x``.
     """
     x = np.array(x, dtype=np.float64, copy=True)
     if rope_dim == 0:
         return x
     D = x.shape[-1]
-    j = np.arange(rope_dim // 2, dtype=np.float64)
-    theta = base ** (-2.0 * j / rope_dim)
+    theta = rope_frequencies(rope_dim, base)
     ang = sign * np.asarray(pos, dtype=np.float64)[..., None] * theta
     z = x[..., D - rope_dim::2] + 1j * x[..., D - rope_dim + 1::2]
     z = z * np.exp(1j * ang)
@@ -222,7 +278,7 @@ def _spec_scale(L, scale):
 
 def _window_rows(kv, L, p0, dtype):
     S = kv.shape[0]
-    return round_to(rope(kv, np.arange(p0, p0 + S), L.rope_dim, L.rope_theta, +1), dtype)
+    return round_to(rope(kv, np.arange(p0, p0 + S), L.rope_dim, rope_base(L), +1), dtype)
 
 
 def csa_prefill(L, inp: Dict[str, np.ndarray], queries: Optional[Iterable[int]] = None,
@@ -238,10 +294,10 @@ def csa_prefill(L, inp: Dict[str, np.ndarray], queries: Optional[Iterable[int]] 
     dt = L.dtype if dtype is None else dtype
     S = inp["q"].shape[0]
     qs = range(S) if queries is None else list(queries)
-    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, L.rope_theta,
+    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, rope_base(L),
                     dt, norm_weight, eps, p0)
     ipool = compress(inp["ikv"], inp["igate"], L.ratio, L.overlap, L.index_rope_dim,
-                     L.rope_theta, dt, inorm_weight, eps, p0)
+                     rope_base(L), dt, inorm_weight, eps, p0)
     win = _window_rows(inp["kv"], L, p0, dt)
     w0 = p0 // L.ratio
     sc_ = _spec_scale(L, scale)
@@ -251,12 +307,12 @@ def csa_prefill(L, inp: Dict[str, np.ndarray], queries: Optional[Iterable[int]] 
         t = p0 + i
         vis = visible_entries(t, L.ratio, p0)
         sc = index_scores(inp["qi"][i], inp["wi"][i], ipool[vis.start - w0:vis.stop - w0], t,
-                          L.index_rope_dim, L.rope_theta, dt)
+                          L.index_rope_dim, rope_base(L), dt)
         idx[n] = topk_select(sc, L.topk, first=vis.start)
         wp = window_positions(t, L.window, p0)
         rows = np.concatenate([win[wp.start - p0:wp.stop - p0],
                                pool[idx[n][idx[n] >= 0] - w0]])
-        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, L.rope_theta, dt)
+        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, rope_base(L), dt)
     return {"pool": pool, "ipool": ipool, "win": win, "idx": idx, "out": out}
 
 
@@ -266,7 +322,7 @@ def hca_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None,
     dt = L.dtype if dtype is None else dtype
     S = inp["q"].shape[0]
     qs = range(S) if queries is None else list(queries)
-    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, L.rope_theta,
+    pool = compress(inp["ckv"], inp["cgate"], L.ratio, L.overlap, L.rope_dim, rope_base(L),
                     dt, norm_weight, eps, p0)
     win = _window_rows(inp["kv"], L, p0, dt)
     w0 = p0 // L.ratio
@@ -277,7 +333,7 @@ def hca_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None,
         vis = visible_entries(t, L.ratio, p0)
         wp = window_positions(t, L.window, p0)
         rows = np.concatenate([win[wp.start - p0:wp.stop - p0], pool[vis.start - w0:vis.stop - w0]])
-        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, L.rope_theta, dt)
+        out[n] = attend(inp["q"][i], t, rows, inp["sinks"], sc_, L.rope_dim, rope_base(L), dt)
     return {"pool": pool, "win": win, "out": out}
 
 
@@ -293,7 +349,7 @@ def sliding_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None):
         t = p0 + i
         wp = window_positions(t, L.window, p0)
         out[n] = attend(inp["q"][i], t, win[wp.start - p0:wp.stop - p0], inp["sinks"], sc_,
-                        L.rope_dim, L.rope_theta, dt)
+                        L.rope_dim, rope_base(L), dt)
     return {"win": win, "out": out}
 
 
@@ -315,7 +371,7 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
     res = {}
     win = np.array(cache["win"], dtype=np.float64, copy=True)
     cap = win.shape[0]
-    win[t % cap] = round_to(rope(new["kv"], t, L.rope_dim, L.rope_theta, +1), dt)
+    win[t % cap] = round_to(rope(new["kv"], t, L.rope_dim, rope_base(L), +1), dt)
     wrows = np.stack([win[s % cap] for s in window_positions(t, W)])
     rows = [wrows]
     if L.ratio > 0:
@@ -334,7 +390,7 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
                 toks = list(range(lo, hi))
                 kvs = np.stack([new[kk] if s == t else cache[sk][s % Ls] for s in toks])
                 gts = np.stack([new[gk] if s == t else cache[sg][s % Ls] for s in toks])
-                ent = round_to(pool_entry(kvs, gts, w * m, rd, L.rope_theta, nw, eps), dt)
+                ent = round_to(pool_entry(kvs, gts, w * m, rd, rope_base(L), nw, eps), dt)
                 assert pool.shape[0] == w, "cache must hold the entries closed before t"
                 fresh[pk] = ent
                 res["new_" + pk] = ent
@@ -352,7 +408,7 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
         vis = visible_entries(t, m)
         if L.has_indexer:
             keys = gather("ipool", np.arange(vis.start, vis.stop))
-            sc = index_scores(new["qi"], new["wi"], keys, t, L.index_rope_dim, L.rope_theta, dt)
+            sc = index_scores(new["qi"], new["wi"], keys, t, L.index_rope_dim, rope_base(L), dt)
             idx = topk_select(sc, L.topk, first=vis.start)
             res["idx"] = idx
             rows.append(gather("pool", idx[idx >= 0]))
@@ -360,5 +416,5 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
             rows.append(gather("pool", np.arange(vis.start, vis.stop)))
     rows = np.concatenate(rows)
     res["out"] = attend(new["q"], t, rows, new["sinks"], _spec_scale(L, scale), L.rope_dim,
-                        L.rope_theta, dt)
+                        rope_base(L), dt)
     return res

@@ -68,6 +68,11 @@ class LayerSpec:
     index_dim: int = 128
     index_rope_dim: int = 64
     topk: int = 512
+    # YaRN rope scaling of every rope of the layer (0: none)
+    rope_factor: float = 0.0
+    rope_original_context: float = 65536.0
+    rope_beta_fast: float = 32.0
+    rope_beta_slow: float = 1.0
 
     @property
     def has_indexer(self) -> bool:
@@ -101,16 +106,22 @@ def _tiny_layer() -> LayerSpec:
                      index_heads=4, index_dim=32, index_rope_dim=16, topk=16)
 
 
+# The V4-shaped layers scale every rope with YaRN, factor 16 over a 65536-token
+# original context (optimum-intel issue 1748, "What V4-Flash adds vs V3").
+_V4_YARN = dict(rope_factor=16.0, rope_original_context=65536.0)
+
+
 def _csa_layer(dtype="bf16") -> LayerSpec:
-    return LayerSpec(kind="csa", dtype=dtype)
+    return LayerSpec(kind="csa", dtype=dtype, **_V4_YARN)
 
 
 def _hca_layer(dtype="bf16") -> LayerSpec:
-    return LayerSpec(kind="hca", dtype=dtype, ratio=128, overlap=0)
+    return LayerSpec(kind="hca", dtype=dtype, ratio=128, overlap=0, **_V4_YARN)
 
 
 def _sliding_layer(dtype="bf16") -> LayerSpec:
-    return LayerSpec(kind="sliding", dtype=dtype, ratio=0, overlap=0, rope_theta=10000.0)
+    return LayerSpec(kind="sliding", dtype=dtype, ratio=0, overlap=0, rope_theta=10000.0,
+                     **_V4_YARN)
 
 
 def _prefill(name, layer, S, batch=1):

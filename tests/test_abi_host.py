@@ -87,6 +87,12 @@ def test_rejections_return_before_launch(lib):
     assert call_attend(lib, csa_layer(qk_rope_head_dim=514), B) == SHAPE
     assert call_attend(lib, csa_layer(index_topk=5000), B) == SHAPE
     assert call_attend(lib, csa_layer(overlap=2), B) == SHAPE
+    # YaRN fields: a factor below 1, or a factor > 1 without a valid context or turn counts
+    assert call_attend(lib, csa_layer(rope_factor=0.5), B) == SHAPE
+    assert call_attend(lib, csa_layer(rope_factor=16.0), B) == SHAPE
+    assert call_attend(lib, csa_layer(rope_factor=16.0, rope_original_context=65536.0,
+                                      rope_beta_fast=1.0, rope_beta_slow=32.0), B) == SHAPE
+    assert call_attend(lib, csa_layer(rope_factor=float("nan")), B) == SHAPE
     assert call_attend(lib, L, B, pool_cap=2047) == SHAPE          # entries (0+8192)/4 = 2048
     assert call_attend(lib, L, B, win_cap=8191) == SHAPE           # needs min(128+8191, 8192)
     assert call_attend(lib, L, batch(n_new=0)) == SHAPE

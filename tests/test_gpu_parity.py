@@ -93,6 +93,24 @@ def test_tiny_csa_layer_f32_peaked(csa):
     _check_csa_prefill(csa, w.layers[0], w, 2)
 
 
+def test_tiny_csa_layer_f32_yarn(csa):
+    say("case: tiny_csa f32 with YaRN (factor 16 over a 64-token original context)")
+    import dataclasses
+    w = synth.workload("tiny_csa")
+    spec = dataclasses.replace(w.layers[0], rope_factor=16.0, rope_original_context=64.0)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 3)
+
+
+def test_csa_prefill_bf16_plain_rope(csa):
+    say("case: csa_prefill bf16 S=700 without YaRN")
+    import dataclasses
+    w = synth.workload("csa_prefill", S=700)
+    spec = dataclasses.replace(w.layers[0], rope_factor=0.0, topk=64)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 6, queries_per_seq=[0, 3, 64, 300, 699])
+
+
 def test_csa_prefill_bf16_small_topk(csa):
     say("case: csa_prefill bf16 S=1000 k=64 B=2 (mfma kernels)")
     import dataclasses
@@ -136,7 +154,8 @@ def _check_dense_prefill(m, kind, S, seed, queries, variant="plain"):
     spec = w.layers[0]
     if kind == "sliding":
         import dataclasses
-        spec = synth.LayerSpec(kind="sliding", dtype="bf16", ratio=0, overlap=0, rope_theta=10000.0)
+        spec = synth.LayerSpec(kind="sliding", dtype="bf16", ratio=0, overlap=0, rope_theta=10000.0,
+                               rope_factor=16.0, rope_original_context=65536.0)
         w = dataclasses.replace(w, layers=[spec])
     inp = synth.prefill_inputs(w, seed)
     L, cache, pos0, args, sinks, out, _ = _prefill_gpu(m, spec, inp, w.batch, S)

@@ -17,8 +17,19 @@ MUTATIONS = {
     "rope_half_split": ("csa_oracle.py",
                         "z = x[..., D - rope_dim::2] + 1j * x[..., D - rope_dim + 1::2]",
                         "z = x[..., D - rope_dim:D - rope_dim // 2] + 1j * x[..., D - rope_dim // 2:]"),
-    "rope_freq": ("csa_oracle.py", "theta = base ** (-2.0 * j / rope_dim)",
-                  "theta = base ** (-1.0 * j / rope_dim)"),
+    "rope_freq": ("csa_oracle.py", "return base ** (-2.0 * j / rope_dim)",
+                  "return base ** (-1.0 * j / rope_dim)"),
+    "yarn_ramp_direction": ("csa_oracle.py",
+                            "return theta * (1.0 - r) + (theta / base.factor) * r",
+                            "return theta * r + (theta / base.factor) * (1.0 - r)"),
+    "yarn_correction_half": ("csa_oracle.py",
+                             "return rope_dim * math.log(context / (2.0 * math.pi * n_turns)) / (2.0 * math.log(base))",
+                             "return rope_dim * math.log(context / (2.0 * math.pi * n_turns)) / math.log(base)"),
+    "yarn_lo_rounding": ("csa_oracle.py", "lo = math.floor(yarn_correction_index(",
+                         "lo = math.ceil(yarn_correction_index("),
+    "yarn_betas_swapped": ("csa_oracle.py",
+                           "lo = math.floor(yarn_correction_index(base.beta_fast,",
+                           "lo = math.floor(yarn_correction_index(base.beta_slow,"),
     "pool_axis": ("csa_oracle.py", "alpha = e / e.sum(axis=0, keepdims=True)",
                   "alpha = e / e.sum(axis=1, keepdims=True)"),
     "pool_window_edge": ("csa_oracle.py", "return max((w - overlap) * ratio, p0), (w + 1) * ratio",

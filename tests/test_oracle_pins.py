@@ -132,6 +132,77 @@ def test_rope_matches_independent_table_form():
 
 
 # ----------------------------------------------------------------------------
+# YaRN frequencies (the pages name YaRN and factor 16 over a 65k context; the
+# ramp is the method's, so these pins rest on the turn-count definitions)
+
+_YARN = dict(factor=16.0, original_context=65536.0, beta_fast=32.0, beta_slow=1.0)
+
+
+def test_yarn_factor_one_is_plain_rope():
+    for R, base in ((64, 10000.0), (64, 160000.0), (16, 10000.0)):
+        plain = O.rope_frequencies(R, base)
+        assert np.array_equal(plain, base ** (-2.0 * np.arange(R // 2) / R))
+        y = O.rope_frequencies(R, O.Yarn(base, 1.0, 65536.0, 32.0, 1.0))
+        assert np.array_equal(plain, y)
+
+
+def test_yarn_correction_index_counts_turns():
+    # at the real index c(n), theta = base^(-2c/R) makes n turns over the context
+    for n in (1.0, 5.0, 32.0):
+        for R, base, ctx in ((64, 10000.0, 65536.0), (64, 160000.0, 65536.0),
+                             (128, 500000.0, 4096.0)):
+            c = O.yarn_correction_index(n, R, base, ctx)
+            theta = base ** (-2.0 * c / R)
+            assert abs(ctx * theta / (2 * math.pi) - n) < 1e-9 * n
+
+
+@pytest.mark.parametrize("base", [10000.0, 160000.0])
+def test_yarn_frequencies_by_turn_count(base):
+    R, s = 64, _YARN["factor"]
+    plain = base ** (-2.0 * np.arange(R // 2) / R)
+    y = O.rope_frequencies(R, O.Yarn(base, **_YARN))
+    turns = _YARN["original_context"] * plain / (2 * math.pi)
+    # exactly the pairs that turn at least beta_fast times keep their frequency
+    assert np.array_equal(y == plain, turns >= _YARN["beta_fast"])
+    ratio = y / plain
+    assert np.all(np.diff(ratio) <= 1e-15) and ratio.min() >= 1 / s - 1e-15
+    slowed = np.isclose(ratio, 1 / s, rtol=0, atol=1e-15)
+    ramp = ~(turns >= _YARN["beta_fast"]) & ~slowed
+    # on the ramp the ratio falls linearly in the pair index
+    rj = np.nonzero(ramp)[0]
+    assert len(rj) >= 3 and np.allclose(np.diff(ratio[rj], 2), 0.0, atol=1e-13)
+    if base == 160000.0:
+        # the ramp ends inside the 32 pairs: exactly those turning at most
+        # beta_slow times (rounded to whole pair indices) run s times slower
+        assert np.array_equal(slowed, turns <= _YARN["beta_slow"])
+        assert slowed.sum() >= 2 and np.array_equal(y[slowed], plain[slowed] / s)
+    else:
+        assert not slowed.any()  # the ramp would end past the last pair
+
+
+def test_yarn_slowed_pairs_at_s_times_the_position_turn_like_plain_rope():
+    rng = np.random.default_rng(6)
+    R, base, s = 64, 160000.0, _YARN["factor"]
+    x = rng.standard_normal(R)
+    y = O.rope_frequencies(R, O.Yarn(base, **_YARN))
+    slowed = np.isclose(y, base ** (-2.0 * np.arange(R // 2) / R) / s, rtol=0, atol=1e-18)
+    a = O.rope(x, 1000 * s, R, O.Yarn(base, **_YARN))
+    b = O.rope(x, 1000, R, base)
+    ch = np.repeat(slowed, 2)
+    assert ch.sum() >= 4 and np.allclose(a[ch], b[ch], atol=1e-9)
+    # the pairs that keep their frequency turn like plain rope at the same position
+    kept = np.repeat(y == base ** (-2.0 * np.arange(R // 2) / R), 2)
+    assert kept.sum() >= 4 and np.allclose(O.rope(x, 777, R, O.Yarn(base, **_YARN))[kept],
+                                           O.rope(x, 777, R, base)[kept], atol=1e-12)
+
+
+def test_yarn_layer_spec_selects_the_scaled_frequencies():
+    L = LayerSpec(kind="csa", dtype="f64", rope_factor=16.0)
+    assert isinstance(O.rope_base(L), O.Yarn) and O.rope_base(L).factor == 16.0
+    assert O.rope_base(LayerSpec(kind="csa", dtype="f64")) == 160000.0
+
+
+# ----------------------------------------------------------------------------
 # compressor
 
 def test_pool_equal_gates_is_mean_over_window_tokens():
