@@ -646,6 +646,137 @@ __global__ void __launch_bounds__(256) index_decode_mfma(const bf16_t* __restric
   }
 }
 
+// The same scan on 32 x 32 x 16 MFMA tiles, with index_prefill_x32's
+// operands (the rotated query as A, heads as rows; keys as B): per tile each
+// wave scores its 32 rows in one step of 16 MFMAs, ReLU, weights and the sum
+// over a lane's 16 heads stay in-lane, and one lane-half swap adds the other
+// 16.  Each score also goes into the block's LDS histogram as it is made, so
+// no pass over the stored scores follows the loop.
+__global__ void __launch_bounds__(256, 2) index_decode_x32(
+    const bf16_t* __restrict__ qr, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
+    float* __restrict__ scores, float* __restrict__ discard, uint32_t* __restrict__ hist,
+    const int64_t* __restrict__ pos0, int n_new, int m, int64_t pool_cap, int block_keys) {
+  constexpr int Hi = 64, Di = 128;
+  __shared__ __attribute__((aligned(1024))) bf16_t kt0[kDecTile * Di];
+  __shared__ __attribute__((aligned(1024))) bf16_t kt1[kDecTile * Di];
+  __shared__ uint32_t lh[kHBins];
+  const int tok = blockIdx.y;  // b * n_new + i
+  const int b = tok / n_new, i = tok % n_new;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h32 = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t nv = (pos0[b] + i + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  const int64_t kb = (int64_t)blockIdx.x * block_keys;
+  if (kb >= nv) return;  // block-uniform, before any barrier
+  const int64_t ke = kb + block_keys < nv ? kb + block_keys : nv;
+  const int ntile = (int)((ke - kb + kDecTile - 1) / kDecTile);
+  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
+  // DMA of this wave's 32 rows of tile `tile` (8 instructions of 4 rows);
+  // rows past the run re-read its last row (already in cache, never scored)
+  const int lrow = lane >> 4, slot = lane & 15;
+  auto issue = [&](int tile, bf16_t* dst) {
+    const int64_t t0 = kb + (int64_t)tile * kDecTile;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 32 * wv + 4 * j + lrow;
+      int64_t key = t0 + r;
+      if (key > ke - 1) key = ke - 1;
+      const bf16_t* src = kbase + key * Di + 8 * (slot ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
+                                       16, 0, 0);
+    }
+  };
+  // query fragments and weights first: their loads then complete before the
+  // tiles' DMA, so the first wait on them leaves the DMA in flight
+  const bf16_t* qrow = qr + (int64_t)tok * Hi * Di;
+  uint4 A[2][8];  // head 32 mt + l32, channels 16 kk + 8 h32 .. + 7
+  float wr[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      A[mt][kk] = *(const uint4*)(qrow + (32 * mt + l32) * Di + 16 * kk + 8 * h32);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wr[mt][r] = bf16_to_f32(wts[(int64_t)tok * Hi + 32 * mt + 8 * (r / 4) + 4 * h32 + r % 4]);
+  }
+  asm volatile("" ::: "memory");  // keeps those loads ahead of the DMA
+  issue(0, kt0);
+  issue(1, kt1);
+  for (int j = threadIdx.x; j < kHBins; j += 256) lh[j] = 0u;
+  // the histogram is clear before any wave adds to it (LDS stores only: the
+  // DMA in flight need not land here)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // B fragment of step kk: row 32 wv + l32 of the tile, chunk 2 kk + h32 at
+  // slot (2 kk + h32) ^ (l32 & 15): the lane's kk = 0 offset XOR 32 kk
+  auto frags = [&](const bf16_t* buf, uint4 (&Bf)[8]) {
+    int ln;  // opaque copy: keeps the per-lane addresses out of loop-invariant registers
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int l = ln & 31, h = ln >> 5;
+    const uint32_t a0 = (uint32_t)(size_t)(lds_void*)buf +
+                        (uint32_t)((32 * wv + l) * Di * 2 + 16 * (h ^ (l & 1)) + 32 * ((l >> 1) & 7));
+    uint32_t a[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) a[kk] = a0 ^ (32u * kk);
+    lds_frag8<0>(a, Bf);
+  };
+  float* srow = scores + (int64_t)tok * pool_cap;
+  auto compute = [&](int tile, const uint4 (&Bf)[8]) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(A[mt][kk], Bf[kk], acc[mt]);
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r & 3] += wr[mt][r] * relu_bits(acc[mt][r]);
+    const float v = (p[0] + p[1]) + (p[2] + p[3]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                               false);
+    const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // all 64 heads
+    const int64_t key = kb + (int64_t)tile * kDecTile + 32 * wv + l32;
+    const bool ok = key < ke;
+    // both lane halves hold the score: all store it (one store per tile on
+    // every path; keys past the run go to a discard slot)
+    *(ok ? srow + key : discard) = sc;
+    // histogram add by asm: a compiler-visible LDS atomic would first wait
+    // for every DMA in flight (it cannot tell lh from the tiles); the next
+    // fragment read's lgkmcnt wait orders it
+    if (ok && h32 == 0) {
+      const uint32_t ha = (uint32_t)(size_t)(lds_void*)&lh[order_key(sc) >> kHShift];
+      asm volatile("ds_add_u32 %0, %1" ::"v"(ha), "v"(1u) : "memory");
+    }
+  };
+  // Two tiles in flight per wave, as in index_decode_mfma: after vmcnt(8)
+  // only the newest tile's 8 DMA rows may be in flight.
+  uint4 Bf[8];
+  for (int tile = 0;;) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    frags(kt0, Bf);
+    issue(tile + 2, kt0);
+    compute(tile, Bf);
+    if (++tile >= ntile) break;
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    frags(kt1, Bf);
+    issue(tile + 2, kt1);
+    compute(tile, Bf);
+    if (++tile >= ntile) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA outlives the block
+  __syncthreads();  // every wave's histogram adds are in
+  uint32_t* h = hist + (int64_t)tok * kHBins;
+  for (int j = threadIdx.x; j < kHBins; j += 256) {
+    const uint32_t c = lh[j];
+    if (c) atomicAdd(&h[j], c);
+  }
+}
+
 // Block-wide (256 threads): the bin holding the k-th largest key of a
 // histogram whose total exceeds k, and the number of keys in the bins above.
 __device__ void hist_cut(const uint32_t* __restrict__ h, uint32_t k, uint32_t* wsum,
@@ -1123,6 +1254,16 @@ static int index_prefill_kernel() {
   return 0;
 }
 
+// Decode key scan: 0 index_decode_x32 (32 x 32 tiles, histogram built in
+// LDS as scores are made), 1 index_decode_mfma (16 x 16 tiles).  The
+// environment variable CSA_INDEX_DECODE ("0" or "1"), read at each call,
+// overrides the default.
+static int index_decode_kernel() {
+  const char* e = getenv("CSA_INDEX_DECODE");
+  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
+  return 0;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
@@ -1170,9 +1311,14 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
       int64_t bk = (nv + per_tok - 1) / per_tok;
       bk = (bk + kDecTile - 1) / kDecTile * kDecTile;
       dim3 g1((unsigned)((nv + bk - 1) / bk), tokens);
-      index_decode_mfma<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
-                                           (float*)(counts + bn * nslice * 2), hist, bt.pos0,
-                                           bt.n, L.m, pool_cap, (int)bk);
+      if (index_decode_kernel() == 0)
+        index_decode_x32<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
+                                            (float*)(counts + bn * nslice * 2), hist, bt.pos0,
+                                            bt.n, L.m, pool_cap, (int)bk);
+      else
+        index_decode_mfma<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
+                                             (float*)(counts + bn * nslice * 2), hist, bt.pos0,
+                                             bt.n, L.m, pool_cap, (int)bk);
     }
     if (nv > L.k) {
       dim3 g2((unsigned)((nv + 4 * kSlice - 1) / (4 * kSlice)), tokens);
