@@ -37,9 +37,13 @@ csa_status to_layer(const csa_layer* in, Layer* L) {
   L->R = in->qk_rope_head_dim;
   L->base.base = in->rope_theta;
   L->base.factor = in->rope_factor > 1.0 ? in->rope_factor : 0.0;
-  L->base.orig = in->rope_original_context;
-  L->base.beta_fast = in->rope_beta_fast;
-  L->base.beta_slow = in->rope_beta_slow;
+  L->base.ln_fast = L->base.ln_slow = L->base.ln_base2 = 0.0;
+  if (L->base.factor > 1.0) {
+    const double two_pi = 2.0 * 3.141592653589793;
+    L->base.ln_fast = log(in->rope_original_context / (two_pi * in->rope_beta_fast));
+    L->base.ln_slow = log(in->rope_original_context / (two_pi * in->rope_beta_slow));
+    L->base.ln_base2 = 2.0 * log(in->rope_theta);
+  }
   L->W = in->sliding_window;
   L->m = in->compress_ratio;
   L->overlap = in->overlap;

@@ -21,7 +21,8 @@ namespace csa {
 
 constexpr int kMaxWidth = 2048;
 
-// Entry w of sequence b (one 256-thread block; pooled and red in LDS).
+// Entry w of sequence b, one block serially over the window (the one-token
+// decode call; pooled and red in LDS).
 template <typename T>
 __device__ __forceinline__ void pool_entry(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
@@ -77,20 +78,150 @@ __device__ __forceinline__ void pool_entry(
   }
 }
 
+// Prefill pooling, one 512-thread block per entry.  With P = width / 2
+// channel pairs below 512, thread (g, p) takes the pair (2p, 2p + 1) and the
+// window's tokens lo + g, lo + g + G, ... (G = 512 / P token groups): first
+// the per-channel window maximum (the groups' maxima merged through LDS), then
+// exp(gate - max) and the weighted sums over the same tokens (merged through
+// LDS).  These are the float64 terms of a serial pass, summed in another
+// order.  Wider rows take G = 1 and several pairs per thread.  Then the
+// optional RMSNorm over the entry and the rotation at position w m.
+constexpr int kCmpT = 512;
+
 template <typename T>
-__global__ void __launch_bounds__(256) compress_kernel(
+__device__ __forceinline__ void ld2(const T* p, double& a, double& b);
+template <>
+__device__ __forceinline__ void ld2<bf16_t>(const bf16_t* p, double& a, double& b) {
+  const uint32_t u = *(const uint32_t*)p;
+  a = bf16_to_f32((bf16_t)(u & 0xffffu));
+  b = bf16_to_f32((bf16_t)(u >> 16));
+}
+template <>
+__device__ __forceinline__ void ld2<float>(const float* p, double& a, double& b) {
+  const float2 f = *(const float2*)p;
+  a = f.x;
+  b = f.y;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
     const int64_t* __restrict__ pos0, int n_new, int width, int R, Rope base, int m,
     int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
-  __shared__ double red[256 / 64];
+  __shared__ double pa[kCmpT][2], pb[kCmpT][2];
+  __shared__ double red[kCmpT / 64];
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
   const int64_t w = p0 / m + blockIdx.x;
-  if (w >= (p0 + n_new) / m || w >= pool_cap) return;
-  pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, n_new, width, R, base, m,
-                overlap, pool_cap, pooled, red);
+  if (w >= (p0 + n_new) / m || w >= pool_cap) return;  // block-uniform
+  const int Ls = (1 + overlap) * m, tid = threadIdx.x;
+  const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
+  const T* kv_b = kv + (int64_t)b * n_new * width;
+  const T* g_b = gate + (int64_t)b * n_new * width;
+  const T* skv_b = st_kv + (int64_t)b * Ls * width;
+  const T* sg_b = st_gate + (int64_t)b * Ls * width;
+  auto row = [&](const T* cur, const T* st, int64_t s) {
+    return s >= p0 ? cur + (s - p0) * width : st + (int64_t)(s % Ls) * width;
+  };
+  const int P = width / 2;
+  if (P < kCmpT) {
+    const int G = kCmpT / P, p = tid % P, g = tid / P;
+    const bool act = g < G;
+    double mx0 = -INFINITY, mx1 = -INFINITY;
+    if (act)
+      for (int64_t s = lo + g; s < hi; s += G) {
+        double a, c;
+        ld2<T>(row(g_b, sg_b, s) + 2 * p, a, c);
+        mx0 = fmax(mx0, a);
+        mx1 = fmax(mx1, c);
+      }
+    pa[tid][0] = mx0;
+    pa[tid][1] = mx1;
+    __syncthreads();
+    double M0 = -INFINITY, M1 = -INFINITY;
+    for (int k = 0; k < G; ++k) {
+      M0 = fmax(M0, pa[p + k * P][0]);
+      M1 = fmax(M1, pa[p + k * P][1]);
+    }
+    double l0 = 0.0, l1 = 0.0, n0 = 0.0, n1 = 0.0;
+    if (act)
+      for (int64_t s = lo + g; s < hi; s += G) {
+        double ga, gc, va, vc;
+        ld2<T>(row(g_b, sg_b, s) + 2 * p, ga, gc);
+        ld2<T>(row(kv_b, skv_b, s) + 2 * p, va, vc);
+        const double e0 = exp(ga - M0), e1 = exp(gc - M1);
+        l0 += e0;
+        l1 += e1;
+        n0 += e0 * va;
+        n1 += e1 * vc;
+      }
+    __syncthreads();  // the maxima are read
+    pa[tid][0] = l0;
+    pa[tid][1] = l1;
+    pb[tid][0] = n0;
+    pb[tid][1] = n1;
+    __syncthreads();
+    if (tid < P) {
+      double L0 = 0.0, L1 = 0.0, N0 = 0.0, N1 = 0.0;
+      for (int k = 0; k < G; ++k) {
+        L0 += pa[p + k * P][0];
+        L1 += pa[p + k * P][1];
+        N0 += pb[p + k * P][0];
+        N1 += pb[p + k * P][1];
+      }
+      pooled[2 * p] = N0 / L0;
+      pooled[2 * p + 1] = N1 / L1;
+    }
+  } else {
+    for (int p = tid; p < P; p += kCmpT) {
+      double mx0 = -INFINITY, mx1 = -INFINITY;
+      for (int64_t s = lo; s < hi; ++s) {
+        double a, c;
+        ld2<T>(row(g_b, sg_b, s) + 2 * p, a, c);
+        mx0 = fmax(mx0, a);
+        mx1 = fmax(mx1, c);
+      }
+      double l0 = 0.0, l1 = 0.0, n0 = 0.0, n1 = 0.0;
+      for (int64_t s = lo; s < hi; ++s) {
+        double ga, gc, va, vc;
+        ld2<T>(row(g_b, sg_b, s) + 2 * p, ga, gc);
+        ld2<T>(row(kv_b, skv_b, s) + 2 * p, va, vc);
+        const double e0 = exp(ga - mx0), e1 = exp(gc - mx1);
+        l0 += e0;
+        l1 += e1;
+        n0 += e0 * va;
+        n1 += e1 * vc;
+      }
+      pooled[2 * p] = n0 / l0;
+      pooled[2 * p + 1] = n1 / l1;
+    }
+  }
+  __syncthreads();
+  if (norm_w != nullptr) {
+    double ss = 0.0;
+    for (int c = tid; c < width; c += kCmpT) ss += pooled[c] * pooled[c];
+    ss = wave_sum64(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int k = 0; k < kCmpT / 64; ++k) tot += red[k];
+    const double inv = 1.0 / sqrt(tot / (double)width + (double)eps);
+    for (int c = tid; c < width; c += kCmpT) pooled[c] = pooled[c] * inv * (double)norm_w[c];
+    __syncthreads();
+  }
+  T* dst = pool + ((int64_t)b * pool_cap + w) * width;
+  for (int c = tid; c < width - R; c += kCmpT) store_t<T>::st64(dst + c, pooled[c]);
+  for (int j = tid; j < R / 2; j += kCmpT) {
+    const int c = width - R + 2 * j;
+    double sn, cs;
+    sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
+    double a = pooled[c], bb = pooled[c + 1];
+    rot64(a, bb, cs, sn);
+    store_t<T>::st64(dst + c, a);
+    store_t<T>::st64(dst + c + 1, bb);
+  }
 }
 
 // One new token per sequence (decode): the entry that closes at it, if any,
@@ -123,7 +254,7 @@ __global__ void __launch_bounds__(256) compress_one_kernel(
 }
 
 // Keep the raw rows of the last (1 + overlap) m positions for later calls.
-// Runs after compress_kernel on the same stream (it overwrites slots that
+// Runs after compress_entry_kernel on the same stream (it overwrites slots that
 // kernel reads).
 template <typename T>
 __global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__ kv,
@@ -165,7 +296,7 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
     return hipGetLastError();
   }
   if (L.dtype == 1) {
-    compress_kernel<bf16_t><<<g1, 256, 0, s>>>(
+    compress_entry_kernel<bf16_t><<<g1, kCmpT, 0, s>>>(
         (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
         (const bf16_t*)st_gate, (bf16_t*)pool, bt.pos0, bt.n, width, rope_dim, L.base, m,
         L.overlap, pool_cap);
@@ -173,7 +304,7 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
                                                    (bf16_t*)st_kv, (bf16_t*)st_gate, bt.pos0,
                                                    bt.n, width, Ls);
   } else {
-    compress_kernel<float><<<g1, 256, 0, s>>>((const float*)kv, (const float*)gate, norm_w, eps,
+    compress_entry_kernel<float><<<g1, kCmpT, 0, s>>>((const float*)kv, (const float*)gate, norm_w, eps,
                                               (const float*)st_kv, (const float*)st_gate,
                                               (float*)pool, bt.pos0, bt.n, width, rope_dim,
                                               L.base, m, L.overlap, pool_cap);

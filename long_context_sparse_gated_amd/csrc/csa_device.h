@@ -79,9 +79,8 @@ template <> struct store_t<bf16_t> {
 __device__ __forceinline__ double rope_freq(const Rope& rp, int j, int R) {
   const double f = pow(rp.base, (-2.0 * (double)j) / (double)R);
   if (!(rp.factor > 1.0)) return f;
-  const double two_pi = 6.283185307179586, lb = 2.0 * log(rp.base);
-  double lo = floor((double)R * log(rp.orig / (two_pi * rp.beta_fast)) / lb);
-  double hi = ceil((double)R * log(rp.orig / (two_pi * rp.beta_slow)) / lb);
+  double lo = floor((double)R * rp.ln_fast / rp.ln_base2);
+  double hi = ceil((double)R * rp.ln_slow / rp.ln_base2);
   lo = lo > 0.0 ? lo : 0.0;
   hi = hi < (double)(R - 1) ? hi : (double)(R - 1);
   if (hi == lo) hi += 0.001;

@@ -14,9 +14,11 @@ constexpr int kMaxTopK = 4096;  // largest index_topk the library accepts
 // csa_device.h).
 struct Rope {
   double base;
-  double factor;               // YaRN scale s; <= 1: none
-  double orig;                 // original context length
-  double beta_fast, beta_slow;  // turns over orig bounding the ramp
+  double factor;  // YaRN scale s; <= 1: none
+  // YaRN ramp terms (host-computed): ln(orig / (2 pi beta_fast)),
+  // ln(orig / (2 pi beta_slow)) and 2 ln(base), orig being the original
+  // context; the correction index of n turns is R ln(orig / (2 pi n)) / (2 ln base)
+  double ln_fast, ln_slow, ln_base2;
 };
 
 struct Layer {

@@ -10,22 +10,49 @@
 
 namespace csa {
 
-// One block per (token, sequence); threads stride over the row's channels.
+// A block takes kWaTok consecutive tokens of one sequence: the channels
+// before the rope slice are copied with 16-byte moves where rows allow it,
+// then each (token, pair) of the slice is rotated by one thread, with the
+// pair frequencies computed once per block.
+constexpr int kWaTok = 8;
+
 template <typename T>
 __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict__ kv,
                                                             T* __restrict__ ring,
                                                             const int64_t* __restrict__ pos0,
                                                             int n_new, int D, int R, Rope base,
                                                             int64_t cap) {
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t t = pos0[b] + i;
-  const T* src = kv + ((int64_t)b * n_new + i) * D;
-  T* dst = ring + ((int64_t)b * cap + (t % cap)) * D;
-  for (int c = threadIdx.x; c < D - R; c += blockDim.x) dst[c] = src[c];
-  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) {
-    const int c = D - R + 2 * j;
+  extern __shared__ double freq[];  // R / 2 pair frequencies
+  const int i0 = blockIdx.x * kWaTok, b = blockIdx.y;
+  const int nt = min(kWaTok, n_new - i0);
+  const int64_t p0 = pos0[b];
+  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) freq[j] = rope_freq(base, j, R);
+  const int plain = D - R;  // channels copied unchanged
+  constexpr int V = 16 / (int)sizeof(T);
+  if ((D % V) == 0 && (plain % V) == 0) {
+    const int per = plain / V;
+    for (int e = threadIdx.x; e < nt * per; e += blockDim.x) {
+      const int k = e / per, c = (e % per) * V;
+      const int64_t t = p0 + i0 + k;
+      *(uint4*)(ring + ((int64_t)b * cap + t % cap) * D + c) =
+          *(const uint4*)(kv + ((int64_t)b * n_new + i0 + k) * D + c);
+    }
+  } else {
+    for (int e = threadIdx.x; e < nt * plain; e += blockDim.x) {
+      const int k = e / plain, c = e % plain;
+      const int64_t t = p0 + i0 + k;
+      ring[((int64_t)b * cap + t % cap) * D + c] = kv[((int64_t)b * n_new + i0 + k) * D + c];
+    }
+  }
+  __syncthreads();
+  const int np = R / 2;
+  for (int e = threadIdx.x; e < nt * np; e += blockDim.x) {
+    const int k = e / np, j = e % np, c = D - R + 2 * j;
+    const int64_t t = p0 + i0 + k;
+    const T* src = kv + ((int64_t)b * n_new + i0 + k) * D;
+    T* dst = ring + ((int64_t)b * cap + t % cap) * D;
     double sn, cs;
-    sincos((double)t * rope_freq(base, j, R), &sn, &cs);
+    sincos((double)t * freq[j], &sn, &cs);
     double a = store_t<T>::ld(src + c), bb = store_t<T>::ld(src + c + 1);
     rot64(a, bb, cs, sn);
     store_t<T>::st64(dst + c, a);
@@ -59,13 +86,14 @@ __global__ void __launch_bounds__(256) rope_kernel(T* __restrict__ x,
 
 hipError_t launch_window_append(const Layer& L, const Batch& bt, const void* kv, void* ring,
                                 int64_t cap, hipStream_t s) {
-  dim3 grid(bt.n, bt.B);
+  dim3 grid((bt.n + kWaTok - 1) / kWaTok, bt.B);
+  const size_t shm = (size_t)(L.R / 2) * sizeof(double);
   if (L.dtype == 1)
-    window_append_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)kv, (bf16_t*)ring, bt.pos0,
-                                                      bt.n, L.D, L.R, L.base, cap);
+    window_append_kernel<bf16_t><<<grid, 256, shm, s>>>((const bf16_t*)kv, (bf16_t*)ring,
+                                                        bt.pos0, bt.n, L.D, L.R, L.base, cap);
   else
-    window_append_kernel<float><<<grid, 256, 0, s>>>((const float*)kv, (float*)ring, bt.pos0,
-                                                     bt.n, L.D, L.R, L.base, cap);
+    window_append_kernel<float><<<grid, 256, shm, s>>>((const float*)kv, (float*)ring, bt.pos0,
+                                                       bt.n, L.D, L.R, L.base, cap);
   return hipGetLastError();
 }
 

@@ -134,6 +134,46 @@ def test_csa_prefill_alternative_kernels(csa, monkeypatch, var, val):
     _check_csa_prefill(csa, spec, w, 5, queries_per_seq=[0, 3, 4, 63, 64, 255, 256, 511, 700, 999])
 
 
+@pytest.mark.parametrize("name,S,pos0", [("csa_prefill", 600, 0), ("csa_prefill", 301, 1000),
+                                         ("hca_prefill", 700, 0), ("tiny_csa", 200, 37)])
+def test_compress_with_rmsnorm(csa, name, S, pos0):
+    """The compressor's optional RMSNorm (both streams of a CSA layer, HCA, float32) against
+    the oracle, also from a nonzero position with the state ring carrying earlier tokens."""
+    import torch
+    say(f"case: compress with RMSNorm {name} S={S} pos0={pos0}")
+    m = csa
+    w = synth.workload(name, S=S + pos0)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 9)
+    x = seq_f64(inp, 0)
+    L = m.Layer.from_spec(spec)
+    rng = np.random.default_rng(10)
+    streams = [("ckv", "cgate", spec.head_dim, spec.rope_dim)]
+    if spec.kind == "csa":
+        streams.append(("ikv", "igate", spec.index_dim, spec.index_rope_dim))
+    for kk, gk, width, rd in streams:
+        nw = (1.0 + 0.25 * rng.standard_normal(width)).astype(np.float32)
+        cap = (S + pos0) // spec.ratio
+        Ls = (1 + spec.overlap) * spec.ratio
+        tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        st_kv = torch.zeros(1, Ls, width, dtype=tdt, device="cuda")
+        st_g = torch.zeros(1, Ls, width, dtype=tdt, device="cuda")
+        pool = torch.zeros(1, cap, width, dtype=tdt, device="cuda")
+        kv_all, g_all = dev(inp[kk][:1]), dev(inp[gk][:1])
+        nwd = torch.from_numpy(nw).cuda()
+        # the earlier tokens (if any) in one call, then the S new ones
+        for a, n in ((0, pos0), (pos0, S)):
+            if n == 0:
+                continue
+            p0 = torch.full((1,), a, dtype=torch.int64, device="cuda")
+            m.csa_compress(L, p0, a, kv_all[:, a:a + n].contiguous(), g_all[:, a:a + n].contiguous(),
+                           st_kv, st_g, pool, rd, norm_weight=nwd, norm_eps=1e-6)
+        torch.cuda.synchronize()
+        ref = O.compress(x[kk], x[gk], spec.ratio, spec.overlap, rd, O.rope_base(spec),
+                         spec.dtype, nw.astype(np.float64), 1e-6, 0)
+        ulp_diff_ok(host(pool[0]), ref, spec.dtype, f"{kk} pool with RMSNorm")
+
+
 def test_csa_prefill_bf16_k512(csa):
     say("case: csa_prefill bf16 S=2600 k=512 (mfma kernels)")
     w = synth.workload("csa_prefill", S=2600)
