@@ -1232,6 +1232,96 @@ __global__ void __launch_bounds__(BS) topk_radix(const float* __restrict__ score
   }
 }
 
+// Per query one wave (four per block) for rows of at most 2048 scores: the
+// row stays in registers (32 scores per lane, id 64 u + lane) through the
+// same four 8-bit radix passes as topk_radix and the emit in id order by
+// ballots; no block barriers.  Each pass counts into four copies of a
+// 256-bin histogram private to the wave (copy = lane mod 4): the row's
+// scores share few leading bits, and adds of equal bins from one instruction
+// serialize.
+constexpr int kTkPer = 32;
+
+__global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ scores, int64_t stride,
+                                                 int32_t* __restrict__ out,
+                                                 const int64_t* __restrict__ pos0, int n_new,
+                                                 int m, int k, int64_t pool_cap) {
+  __shared__ uint32_t hist_all[4][4][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * 4 + wv, b = blockIdx.y;
+  if (i >= n_new) return;  // wave-uniform; the waves never meet at a barrier
+  uint32_t (*hist)[256] = hist_all[wv];
+  const int64_t tok = (int64_t)b * n_new + i;
+  int64_t nv = (pos0[b] + i + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  const int n = (int)nv;
+  const float* sc = scores + tok * stride;
+  int32_t* o = out + tok * k;
+  if (n <= k) {
+    for (int j = lane; j < k; j += 64) o[j] = j < n ? j : -1;
+    return;
+  }
+  uint32_t key[kTkPer];
+#pragma unroll
+  for (int u = 0; u < kTkPer; ++u) {
+    const int j = 64 * u + lane;
+    key[u] = j < n ? order_key(sc[j]) : 0u;
+  }
+  uint32_t* myh = hist[lane & 3];
+  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hist[c][64 * e + lane] = 0u;
+#pragma unroll
+    for (int u = 0; u < kTkPer; ++u)
+      if (64 * u + lane < n && (key[u] & mask) == prefix)
+        atomicAdd(&myh[(key[u] >> shift) & 255u], 1u);
+    uint32_t cnt[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      cnt[e] = hist[0][4 * lane + e] + hist[1][4 * lane + e] + hist[2][4 * lane + e] +
+               hist[3][4 * lane + e];
+    const uint32_t sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint32_t suf = sum;  // inclusive suffix sum over lanes (lane 63: the largest keys)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += v;
+    }
+    const unsigned long long bal = __ballot(suf >= rem);
+    const int L = 63 - __clzll(bal);
+    uint32_t above = suf - sum;
+    int d = 3;
+    for (; d > 0; --d) {
+      if (above + cnt[d] >= rem) break;
+      above += cnt[d];
+    }
+    const uint32_t np = prefix | ((uint32_t)(4 * L + d) << shift), nr = rem - above;
+    prefix = (uint32_t)__builtin_amdgcn_readlane((int)np, L);
+    rem = (uint32_t)__builtin_amdgcn_readlane((int)nr, L);
+    mask |= 255u << shift;
+  }
+  // prefix is the k-th largest key: every larger key and the first `rem`
+  // keys equal to it, in id order
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t base_sel = 0, base_eq = 0;
+#pragma unroll
+  for (int u = 0; u < kTkPer; ++u) {
+    const int j = 64 * u + lane;
+    const bool gt = j < n && key[u] > prefix, eq = j < n && key[u] == prefix;
+    const unsigned long long be = __ballot(eq);
+    const bool sel = gt || (eq && base_eq + (uint32_t)__popcll(be & lt) < rem);
+    const unsigned long long bs = __ballot(sel);
+    if (sel) o[base_sel + (uint32_t)__popcll(bs & lt)] = j;
+    base_sel += (uint32_t)__popcll(bs);
+    base_eq += (uint32_t)__popcll(be);
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 static bool index_fast_shape(const Layer& L) {
@@ -1354,6 +1444,11 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((bt.pos0_max + bt.n) / L.m <= 64 * kTkPer) {  // every row fits in one wave's registers
+    dim3 gw((bt.n + 3) / 4, bt.B);
+    topk_wave<<<gw, 256, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.n, L.m, L.k, pool_cap);
+    return hipGetLastError();
+  }
   dim3 grid(bt.n, bt.B);
   if ((bt.pos0_max + bt.n) / L.m > 16384)
     topk_radix<1024><<<grid, 1024, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.n, L.m, L.k,
