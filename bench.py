@@ -16,7 +16,10 @@ the same way (one step = every call of the layer(s) for one batch):
 * ``csa_decode``   64 sequences x 1 token at position 131072 (32768 entries);
 * ``mixed_decode`` 4 sequences x 1 token at position 1048576 through a CSA
                    layer (262144 entries), an HCA layer (8192 entries) and a
-                   sliding-only layer.
+                   sliding-only layer;
+* ``output_projection`` the grouped low-rank output projection of the 8192
+                   prefill tokens (8 groups of 8 heads x 512 -> rank 1024 each
+                   -> hidden 4096), priced in its two products' MFMA FLOPs.
 
 Prefill steps are priced in MFMA FLOPs (4 H D per attended (query, row)
 pair, plus 2 H_I D_I per scored (query, key) pair); decode steps in the HBM
@@ -263,6 +266,25 @@ def decode_leg(torch, m, name, steps, warmup):
             "eager_ms_per_step": eager_ms}
 
 
+def oproj_leg(torch, m, steps, warmup):
+    import synth
+    s = synth.OPROJ_SHAPE
+    T, H, D, G, R, hidden = s["T"], s["H"], s["D"], s["G"], s["R"], s["hidden"]
+    inp = synth.oproj_inputs(T, H, D, G, R, hidden, seed=0)
+    x, wa, wb = (_dev(torch, inp[k]) for k in ("x", "w_a", "w_b"))
+    out = torch.empty(T, hidden, dtype=torch.bfloat16, device="cuda")
+    need = m.load_library().csa_output_projection_workspace_bytes(
+        m._COproj(T, H, D, G, R, hidden))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ms, _ = _time_steps(torch, lambda _ev: m.csa_output_projection(x, wa, wb, out, G, ws), steps,
+                        warmup)
+    flop = 2.0 * T * G * R * ((H // G) * D + hidden)
+    tf = flop / (ms * 1e-3) / 1e12
+    del x, wa, wb, out, ws
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_flop": flop,
+            "achieved_TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, **s}
+
+
 def calib_copy(torch, mib):
     if mib <= 0:
         return
@@ -287,6 +309,8 @@ def run_leg(torch, m, name, args):
         return r
     if name in ("csa_decode", "mixed_decode"):
         return decode_leg(torch, m, name, 5 * args.steps, args.warmup)
+    if name == "output_projection":
+        return oproj_leg(torch, m, args.steps, args.warmup)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -297,9 +321,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1)
-    ap.add_argument("--legs", default="hca_prefill,csa_decode,mixed_decode",
+    ap.add_argument("--legs", default="hca_prefill,csa_decode,mixed_decode,output_projection",
                     help="comma list of further workloads to time after the headline "
-                         "(hca_prefill, csa_decode, mixed_decode; empty for none)")
+                         "(hca_prefill, csa_decode, mixed_decode, output_projection; empty "
+                         "for none)")
     ap.add_argument("--only", default="",
                     help="time just this one workload and print its object (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

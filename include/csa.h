@@ -230,6 +230,45 @@ enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
 size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
                            int64_t pool_cap, int32_t op);
 
+/* Grouped low-rank output projection, the step after the attention.
+ * Source: model page, sec. 2.3 ("Grouped Output Projection": o_groups groups
+ * of heads -> o_lora_rank per group -> hidden_size, o_a_proj then o_b_proj);
+ * transformers PR 45616 notes (DeepseekV4GroupedLinear keeps an (out, in)
+ * weight and runs a per-group bmm).  The pages give no sizes.
+ *  attn_out [tokens, num_heads, head_dim] bf16: the attention output (after
+ *           the -t rotation), heads of group g = g H/G .. (g+1) H/G - 1.
+ *  w_a      [o_groups * o_lora_rank, (num_heads / o_groups) * head_dim] bf16:
+ *           o_a_proj's weight; rows g R .. g R + R - 1 belong to group g.
+ *  w_b      [hidden_size, o_groups * o_lora_rank] bf16: o_b_proj's weight.
+ *  out      [tokens, hidden_size] bf16 out:
+ *           y[t, g, r] = sum_i attn_out[t, group g, i] w_a[g R + r, i] (bf16),
+ *           out[t, h] = sum_j y[t, j] w_b[h, j]; float32 accumulation, each
+ *           stored value rounded once; no bias.
+ *  workspace >= csa_output_projection_workspace_bytes(p) bytes (holds y).
+ * Requires o_groups to divide num_heads (else CSA_ERR_SHAPE),
+ * (num_heads / o_groups) * head_dim and o_groups * o_lora_rank to be
+ * multiples of 32, tokens <= 2^23, and attn_out, w_a and w_b to be 16-byte
+ * aligned (else CSA_ERR_UNSUPPORTED).  The caller owns every buffer; the two
+ * products are queued on `stream` in order and the call returns without
+ * waiting.  attn_out, w_a, w_b, out and workspace must not overlap. */
+typedef struct {
+  int32_t tokens;       /* T >= 1 rows                                       */
+  int32_t num_heads;    /* H                                                 */
+  int32_t head_dim;     /* D                                                 */
+  int32_t o_groups;     /* G, divides H                                      */
+  int32_t o_lora_rank;  /* R >= 1                                            */
+  int32_t hidden_size;  /* >= 1                                              */
+} csa_oproj;
+
+csa_status csa_output_projection(const csa_oproj* p, const void* attn_out,
+                                 const void* w_a, const void* w_b, void* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Workspace bytes of csa_output_projection (256-byte aligned pointer), or
+ * (size_t)-1 for invalid sizes. */
+size_t csa_output_projection_workspace_bytes(const csa_oproj* p);
+
 /* Static description of a status code. */
 const char* csa_status_str(csa_status status);
 

@@ -22,13 +22,14 @@ __all__ = [
     "Layer", "load_library", "library_path", "csa_window_append", "csa_rope", "csa_compress",
     "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
     "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
+    "csa_output_projection",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 CSA_OP_INDEX_TOPK, CSA_OP_ATTEND, CSA_OP_HCA_ATTEND = 1, 2, 3
 EXPORTED_SYMBOLS = ("csa_window_append", "csa_rope", "csa_compress", "csa_index_topk",
                     "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
-                    "csa_version")
+                    "csa_version", "csa_output_projection", "csa_output_projection_workspace_bytes")
 
 
 class _CLayer(ctypes.Structure):
@@ -41,6 +42,12 @@ class _CLayer(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("rope_factor", ctypes.c_double),
                 ("rope_original_context", ctypes.c_double), ("rope_beta_fast", ctypes.c_double),
                 ("rope_beta_slow", ctypes.c_double)]
+
+
+class _COproj(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("o_groups", ctypes.c_int32),
+                ("o_lora_rank", ctypes.c_int32), ("hidden_size", ctypes.c_int32)]
 
 
 class _CBatch(ctypes.Structure):
@@ -123,6 +130,7 @@ def load_library():
         "csa_index_topk": [LP, BP, P, P, P, I64, P, P, P, SZ, P],
         "csa_attend": [LP, BP, P, P, I64, P, I64, P, P, P, P, SZ, P],
         "hca_attend": [LP, BP, P, P, I64, P, I64, P, P, P, SZ, P],
+        "csa_output_projection": [ctypes.POINTER(_COproj), P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -134,6 +142,8 @@ def load_library():
     lib.csa_status_str.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
     lib.csa_version.restype = I32
+    lib.csa_output_projection_workspace_bytes.argtypes = [ctypes.POINTER(_COproj)]
+    lib.csa_output_projection_workspace_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -281,3 +291,26 @@ def hca_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, sinks, out, work
         ctypes.byref(lay), ctypes.byref(bt), _ptr(q, "q", dt), _ptr(win, "win", dt), win.shape[1],
         _ptr(pool, "pool", dt), pcap, _ptr(sinks, "sinks", torch.float32), _ptr(out, "out", dt),
         _ptr(ws, "workspace"), wsb, _stream()), "hca_attend")
+
+
+def csa_output_projection(attn_out, w_a, w_b, out, o_groups: int, workspace=None):
+    """attn_out [T, H, D], w_a [G*R, (H/G)*D], w_b [hidden, G*R] (bf16) -> out [T, hidden]."""
+    torch = _torch()
+    T, H, D = attn_out.shape
+    R = w_a.shape[0] // o_groups
+    shape = _COproj(T, H, D, o_groups, R, w_b.shape[0])
+    if tuple(w_a.shape) != (o_groups * R, (H // o_groups) * D) or w_b.shape[1] != o_groups * R \
+            or tuple(out.shape) != (T, w_b.shape[0]):
+        raise ValueError("csa_output_projection: inconsistent shapes")
+    lib = load_library()
+    need = lib.csa_output_projection_workspace_bytes(ctypes.byref(shape))
+    if need == ctypes.c_size_t(-1).value:
+        raise RuntimeError("csa_output_projection: invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=attn_out.device)
+    bf = torch.bfloat16
+    _check(lib.csa_output_projection(
+        ctypes.byref(shape), _ptr(attn_out, "attn_out", bf), _ptr(w_a, "w_a", bf),
+        _ptr(w_b, "w_b", bf), _ptr(out, "out", bf), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()), "csa_output_projection")
+

@@ -236,6 +236,41 @@ size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
   }
 }
 
+static csa_status oproj_ok(const csa_oproj* p) {
+  if (!p) return CSA_ERR_NULL;
+  if (p->tokens < 1 || p->num_heads < 1 || p->head_dim < 1 || p->o_groups < 1 ||
+      p->o_lora_rank < 1 || p->hidden_size < 1 || p->num_heads % p->o_groups != 0)
+    return CSA_ERR_SHAPE;
+  const int64_t ig = (int64_t)(p->num_heads / p->o_groups) * p->head_dim;
+  const int64_t gr = (int64_t)p->o_groups * p->o_lora_rank;
+  if (ig % 32 != 0 || gr % 32 != 0 || ig > (1 << 30) || gr > (1 << 30) ||
+      (int64_t)p->num_heads * p->head_dim > (1 << 30) || p->tokens > (1 << 23))
+    return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+size_t csa_output_projection_workspace_bytes(const csa_oproj* p) {
+  if (oproj_ok(p) != CSA_OK) return (size_t)-1;
+  return (size_t)p->tokens * p->o_groups * p->o_lora_rank * sizeof(csa::bf16_t);
+}
+
+csa_status csa_output_projection(const csa_oproj* p, const void* attn_out, const void* w_a,
+                                 const void* w_b, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const csa_status st = oproj_ok(p);
+  if (st != CSA_OK) return st;
+  if (!attn_out || !w_a || !w_b || !out) return CSA_ERR_NULL;
+  // the products stage 16-byte chunks of their operands
+  if (((uintptr_t)attn_out | (uintptr_t)w_a | (uintptr_t)w_b) & 15u) return CSA_ERR_UNSUPPORTED;
+  const size_t need = csa_output_projection_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return CSA_ERR_WORKSPACE;
+  hipError_t e = csa::launch_output_projection(
+      p->tokens, p->num_heads, p->head_dim, p->o_groups, p->o_lora_rank, p->hidden_size,
+      (const csa::bf16_t*)attn_out, (const csa::bf16_t*)w_a, (const csa::bf16_t*)w_b,
+      (csa::bf16_t*)workspace, (csa::bf16_t*)out, stream);
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
 const char* csa_status_str(csa_status s) {
   switch (s) {
     case CSA_OK: return "CSA_OK";

@@ -13,8 +13,6 @@
 
 namespace csa {
 
-typedef uint16_t bf16_t;
-
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

@@ -7,6 +7,8 @@
 
 namespace csa {
 
+typedef uint16_t bf16_t;  // bfloat16 carried as its raw bits
+
 constexpr int kMaxTopK = 4096;  // largest index_topk the library accepts
 
 // Rope frequencies of a layer: pair j of R rope channels turns at
@@ -37,6 +39,11 @@ struct Batch {
   const int64_t* pos0;  // device [B]
   int64_t pos0_max;     // host bound
 };
+
+// oproj.hip
+hipError_t launch_output_projection(int T, int H, int D, int G, int R, int hidden,
+                                    const bf16_t* x, const bf16_t* wa, const bf16_t* wb,
+                                    bf16_t* y1, bf16_t* out, hipStream_t s);
 
 // rope.hip
 hipError_t launch_window_append(const Layer& L, const Batch& b, const void* kv, void* ring,

@@ -48,7 +48,7 @@ __all__ = [
     "round_to", "Yarn", "yarn_correction_index", "rope_frequencies", "rope_base", "rope",
     "pool_entry", "compress", "visible_entries",
     "window_positions", "index_scores", "topk_select", "attend",
-    "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step",
+    "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step", "output_projection",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -418,3 +418,29 @@ def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarr
     res["out"] = attend(new["q"], t, rows, new["sinks"], _spec_scale(L, scale), L.rope_dim,
                         rope_base(L), dt)
     return res
+
+
+def output_projection(attn_out, w_a, w_b, o_groups: int, dtype: str) -> np.ndarray:
+    """Grouped low-rank output projection [HF-doc sec. 2.3, "Grouped Output
+    Projection"; HF-PR notes on DeepseekV4GroupedLinear].
+
+    attn_out [T, H, D] (the attention output after the -t rotation); w_a
+    [G R, (H / G) D], o_a_proj's (out, in) weight, rows g R .. g R + R - 1 for
+    group g; w_b [hidden, G R], o_b_proj's weight.  Group g takes the heads
+    g H/G .. (g+1) H/G - 1 of a token: y[t, g] = w_a[g] x[t, g], stored at
+    ``dtype`` like the module output; out[t] = w_b y[t], stored at ``dtype``.
+    The pages give no bias; none is added.
+    """
+    x = np.asarray(attn_out, dtype=np.float64)
+    T, H, D = x.shape
+    G = o_groups
+    ig = (H // G) * D
+    R = np.asarray(w_a).shape[0] // G
+    xg = x.reshape(T, G, ig)
+    wa = np.asarray(w_a, dtype=np.float64).reshape(G, R, ig)
+    y = np.empty((T, G, R))
+    for g in range(G):
+        y[:, g, :] = xg[:, g, :] @ wa[g].T
+    y = round_to(y, dtype)
+    return round_to(y.reshape(T, G * R) @ np.asarray(w_b, dtype=np.float64).T, dtype)
+

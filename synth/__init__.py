@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "Workload", "WORKLOADS", "workload", "prefill_inputs",
     "decode_inputs", "bf16_bits_to_f32", "f32_to_bf16_bits", "to_f64",
-    "grid_index_inputs",
+    "grid_index_inputs", "OPROJ_SHAPE", "oproj_inputs",
 ]
 
 # Tensor ids keep streams independent of draw order.
@@ -50,6 +50,7 @@ _TID = {
     "q": 1, "kv": 2, "ckv": 3, "cgate": 4, "ikv": 5, "igate": 6, "qi": 7,
     "wi": 8, "sinks": 9, "pool": 10, "ipool": 11, "win": 12, "cstate_kv": 13,
     "cstate_gate": 14, "istate_kv": 15, "istate_gate": 16, "norm": 17,
+    "attn_out": 18, "o_a": 19, "o_b": 20,
 }
 
 
@@ -367,3 +368,26 @@ def grid_index_inputs(n_q: int, pool: int, Hi: int, Di: int, Ri: int, seed: int 
     k[:, Di - Ri:] = 0
     wt = rng.integers(-4, 5, size=(n_q, Hi)).astype(np.float32) / 4
     return q, k, wt
+
+
+# Output projection after the attention of the csa_prefill workload: 8192
+# tokens x 64 heads x 512, eight groups of eight heads, rank 1024 per group,
+# hidden size 4096 (sizes chosen here; the pages name the fields only).
+OPROJ_SHAPE = dict(T=8192, H=64, D=512, G=8, R=1024, hidden=4096)
+
+
+def oproj_inputs(T: int, H: int, D: int, G: int, R: int, hidden: int, seed: int = 0,
+                 rows=None) -> Dict[str, np.ndarray]:
+    """bf16 bits of the output projection's inputs: x [T, H, D] ~ N(0, 1),
+    w_a [G R, (H/G) D] ~ N(0, 1/((H/G) D)), w_b [hidden, G R] ~ N(0, 1/(G R))
+    (so that both products stay near unit scale).  ``rows`` draws only those
+    token rows of x (the weights are always whole)."""
+    ig = (H // G) * D
+    if rows is None:
+        x = _draw(seed, "attn_out", 0, (T, H, D), 1.0, "bf16")
+    else:
+        x = draw_rows(seed, "attn_out", 0, (T, H, D), 1.0, "bf16", rows)
+    return {"x": x,
+            "w_a": _draw(seed, "o_a", 0, (G * R, ig), 1.0 / math.sqrt(ig), "bf16"),
+            "w_b": _draw(seed, "o_b", 0, (hidden, G * R), 1.0 / math.sqrt(G * R), "bf16")}
+

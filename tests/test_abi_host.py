@@ -132,3 +132,25 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         m.csa_window_append(L, torch.zeros(1, dtype=torch.int64), 0, x, x)
+
+
+def test_output_projection_sizes_and_rejections(lib):
+    NULL, SHAPE, WS, UNSUP = 1, 2, 5, 4
+    P = m._COproj(300, 8, 64, 2, 96, 200)
+    assert lib.csa_output_projection_workspace_bytes(ctypes.byref(P)) == 300 * 2 * 96 * 2
+
+    def call(p, x=FAKE, wa=FAKE, ws=FAKE, wsb=1 << 40):
+        return lib.csa_output_projection(ctypes.byref(p), x, wa, FAKE, FAKE, ws, wsb, None)
+
+    assert lib.csa_output_projection(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == NULL
+    assert call(P, x=None) == NULL
+    assert call(m._COproj(300, 8, 64, 3, 96, 200)) == SHAPE          # 3 does not divide 8
+    assert call(m._COproj(0, 8, 64, 2, 96, 200)) == SHAPE
+    assert call(m._COproj(300, 8, 60, 2, 96, 200)) == UNSUP          # 4 * 60 not a multiple of 32
+    assert call(m._COproj(300, 8, 64, 2, 95, 200)) == UNSUP          # 2 * 95 not a multiple of 32
+    assert lib.csa_output_projection_workspace_bytes(
+        ctypes.byref(m._COproj(300, 8, 64, 3, 96, 200))) == ctypes.c_size_t(-1).value
+    assert call(P, x=ctypes.c_void_p(0x1008)) == UNSUP               # not 16-byte aligned
+    assert call(P, ws=None) == WS
+    assert call(P, wsb=300 * 2 * 96 * 2 - 1) == WS
+    assert call(P, ws=ctypes.c_void_p(0x1010)) == WS                  # not 256-byte aligned

@@ -467,3 +467,46 @@ def test_repeat_runs_are_bitwise_identical(csa):
     r2 = _prefill_gpu(csa, w.layers[0], inp, 1, 900)
     assert torch.equal(r1[6], r2[6])
     assert torch.equal(r1[5].view(torch.int16), r2[5].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# grouped output projection
+
+def _oproj_gpu(m, inp, G, T, hidden):
+    import torch
+    x, wa, wb = dev(inp["x"]), dev(inp["w_a"]), dev(inp["w_b"])
+    out = torch.full((T, hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    m.csa_output_projection(x, wa, wb, out, G)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("T,H,D,G,R,hidden", [
+    (300, 8, 64, 2, 96, 200),      # ragged in every dimension of both products
+    (1, 4, 64, 4, 32, 256),        # one token
+    (129, 16, 32, 1, 64, 513),     # one group: two plain products
+    (257, 8, 64, 4, 40, 96),       # rank below one tile, G R = 160
+])
+def test_output_projection_small(csa, T, H, D, G, R, hidden):
+    say(f"output projection T={T} H={H} D={D} G={G} R={R} hidden={hidden}")
+    inp = synth.oproj_inputs(T, H, D, G, R, hidden, seed=5)
+    got = _oproj_gpu(csa, inp, G, T, hidden)
+    ref = O.output_projection(to_f64(inp["x"]), to_f64(inp["w_a"]), to_f64(inp["w_b"]), G, "bf16")
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", "output projection")
+
+
+def test_output_projection_full_size_sampled(csa):
+    s = synth.OPROJ_SHAPE
+    T, H, D, G, R, hidden = s["T"], s["H"], s["D"], s["G"], s["R"], s["hidden"]
+    say(f"output projection full size {s}, sampled rows")
+    inp = synth.oproj_inputs(T, H, D, G, R, hidden, seed=7)
+    got = _oproj_gpu(csa, inp, G, T, hidden)
+    assert np.isfinite(got).all()
+    rows = np.r_[0:3, 127:130, 4095:4097, T - 3:T, np.random.default_rng(3).integers(0, T, 40)]
+    ref = O.output_projection(to_f64(inp["x"][rows]), to_f64(inp["w_a"]), to_f64(inp["w_b"]), G,
+                              "bf16")
+    assert_close(got[rows], ref, "bf16", "output projection rows")
+    # the same rows drawn alone match the whole draw
+    part = synth.oproj_inputs(T, H, D, G, R, hidden, seed=7, rows=rows)
+    assert np.array_equal(part["x"], inp["x"][rows])

@@ -50,6 +50,13 @@ MUTATIONS = {
                     "o = rope(o, t, rope_dim, base, +1)"),
     "query_unrotated": ("csa_oracle.py", "q = round_to(rope(q_t, t, rope_dim, base, +1), dtype)",
                         "q = round_to(np.asarray(q_t, np.float64), dtype)"),
+    "oproj_group_order": ("csa_oracle.py", "xg = x.reshape(T, G, ig)",
+                          "xg = x.reshape(T, ig, G).transpose(0, 2, 1)"),
+    "oproj_weight_transposed": ("csa_oracle.py",
+                                "wa = np.asarray(w_a, dtype=np.float64).reshape(G, R, ig)",
+                                "wa = np.asarray(w_a, dtype=np.float64).reshape(G, ig, R).transpose(0, 2, 1)"),
+    "oproj_no_intermediate_rounding": ("csa_oracle.py", "    y = round_to(y, dtype)\n",
+                                       "    y = y\n"),
     "round_bits": ("csa_oracle.py", "q = np.ldexp(np.round(np.ldexp(x, 8 - e)), e - 8)",
                    "q = np.ldexp(np.round(np.ldexp(x, 9 - e)), e - 9)"),
     "round_double": ("csa_oracle.py", "_, e = np.frexp(x)",

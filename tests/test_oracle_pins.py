@@ -512,3 +512,69 @@ def test_decode_step_equals_prefill_row(kind):
             assert np.array_equal(res["idx"], full["idx"][t])
         if L.ratio > 0 and (t + 1) % L.ratio == 0:
             assert np.allclose(res["new_pool"], full["pool"][(t + 1) // L.ratio - 1], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# grouped output projection
+
+def _oproj_inputs(T, H, D, G, R, hidden, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H, D))
+    wa = rng.standard_normal((G * R, (H // G) * D))
+    wb = rng.standard_normal((hidden, G * R))
+    return x, wa, wb
+
+
+def test_output_projection_matches_loops_on_tiny_sizes():
+    T, H, D, G, R, hidden = 3, 4, 2, 2, 3, 5
+    x, wa, wb = _oproj_inputs(T, H, D, G, R, hidden, 11)
+    out = O.output_projection(x, wa, wb, G, "f64")
+    ref = np.zeros((T, hidden))
+    hp = H // G
+    for t in range(T):
+        y = np.zeros(G * R)
+        for g in range(G):
+            for r in range(R):
+                for hh in range(hp):
+                    for d in range(D):
+                        y[g * R + r] += x[t, g * hp + hh, d] * wa[g * R + r, hh * D + d]
+        for o in range(hidden):
+            ref[t, o] = sum(y[j] * wb[o, j] for j in range(G * R))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_equals_dense_block_diagonal_product():
+    T, H, D, G, R, hidden = 7, 8, 4, 4, 5, 6
+    x, wa, wb = _oproj_inputs(T, H, D, G, R, hidden, 12)
+    ig = (H // G) * D
+    full = np.zeros((G * R, H * D))
+    for g in range(G):
+        full[g * R:(g + 1) * R, g * ig:(g + 1) * ig] = wa[g * R:(g + 1) * R]
+    dense = (x.reshape(T, H * D) @ full.T) @ wb.T
+    assert np.allclose(O.output_projection(x, wa, wb, G, "f64"), dense, rtol=1e-12, atol=1e-12)
+    # one group is two plain products
+    assert np.allclose(O.output_projection(x, full, wb, 1, "f64"), dense, rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_group_locality_and_stored_intermediate():
+    T, H, D, G, R, hidden = 4, 6, 3, 3, 2, 5
+    x, wa, wb = _oproj_inputs(T, H, D, G, R, hidden, 13)
+    g = 1
+    wb_g = np.zeros_like(wb)
+    wb_g[:, g * R:(g + 1) * R] = wb[:, g * R:(g + 1) * R]
+    x2 = x.copy()
+    hp = H // G
+    x2[:, :g * hp] += 1.0
+    x2[:, (g + 1) * hp:] -= 2.0
+    # only group g's heads reach the output through group g's block of w_b
+    assert np.allclose(O.output_projection(x, wa, wb_g, G, "f64"),
+                       O.output_projection(x2, wa, wb_g, G, "f64"), atol=1e-12)
+    assert not np.allclose(O.output_projection(x, wa, wb, G, "f64"),
+                           O.output_projection(x2, wa, wb, G, "f64"))
+    # the intermediate is stored at the dtype: rounding it first is the same result
+    xb = O.round_to(x, "bf16")
+    out = O.output_projection(xb, wa, wb, G, "bf16")
+    y = O.round_to(np.einsum("tgi,gri->tgr", xb.reshape(T, G, hp * D), wa.reshape(G, R, hp * D)),
+                   "bf16")
+    assert np.array_equal(out, O.round_to(y.reshape(T, G * R) @ wb.T, "bf16"))
+
