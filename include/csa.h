@@ -247,7 +247,8 @@ size_t csa_workspace_bytes(const csa_layer* layer, int32_t batch, int32_t n_new,
  *  workspace >= csa_output_projection_workspace_bytes(p) bytes (holds y).
  * Requires o_groups to divide num_heads (else CSA_ERR_SHAPE),
  * (num_heads / o_groups) * head_dim and o_groups * o_lora_rank to be
- * multiples of 32, tokens <= 2^23, and attn_out, w_a and w_b to be 16-byte
+ * multiples of 32, num_heads * head_dim and o_groups * o_lora_rank to be at
+ * most 2^22, tokens <= 2^23, and attn_out, w_a and w_b to be 16-byte
  * aligned (else CSA_ERR_UNSUPPORTED).  The caller owns every buffer; the two
  * products are queued on `stream` in order and the call returns without
  * waiting.  attn_out, w_a, w_b, out and workspace must not overlap. */

@@ -243,8 +243,10 @@ static csa_status oproj_ok(const csa_oproj* p) {
     return CSA_ERR_SHAPE;
   const int64_t ig = (int64_t)(p->num_heads / p->o_groups) * p->head_dim;
   const int64_t gr = (int64_t)p->o_groups * p->o_lora_rank;
-  if (ig % 32 != 0 || gr % 32 != 0 || ig > (1 << 30) || gr > (1 << 30) ||
-      (int64_t)p->num_heads * p->head_dim > (1 << 30) || p->tokens > (1 << 23))
+  // row strides stay below 2^22 elements: a block's 256 rows are addressed
+  // with 32-bit byte offsets
+  if (ig % 32 != 0 || gr % 32 != 0 || gr > (1 << 22) ||
+      (int64_t)p->num_heads * p->head_dim > (1 << 22) || p->tokens > (1 << 23))
     return CSA_ERR_UNSUPPORTED;
   return CSA_OK;
 }

@@ -15,12 +15,20 @@
 // gemm_nt_bf16: C[b][m, n] = sum_k A[b][m, k] B[b][n, k], all row-major
 // with k contiguous in A and B (a weight in (out, in) layout is B as it is),
 // bf16 inputs, float32 accumulation, bf16 output rounded to nearest even.
-// A block computes a 128 x 256 tile with four waves of 64 x 128 (2 x 4
-// tiles of v_mfma_f32_32x32x16_bf16); K advances in 32-wide stages that
-// reach LDS by LDS-DMA, three buffers deep (two stages in flight while one
-// is multiplied).  In LDS a row is 64 bytes (four 16-byte chunks) and chunk
-// c of row r sits at slot c ^ ((r >> 1) & 3), so that the eight rows of a
-// 16-byte fragment read hit distinct bank groups.
+// A block of four waves computes a 256 x 256 tile, each wave a 128 x 128
+// part as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs,
+// one wave per SIMD): per 16-deep step 16 MFMAs from eight 16-byte fragment
+// reads.  K advances 32 per stage; stages reach LDS by LDS-DMA into four
+// buffers.  One barrier per stage, between its two steps: after it the next
+// stage is complete in LDS and the buffer just read is free, so the wave
+// issues the DMA four stages ahead into it and reads the next stage's
+// fragments while the second step's MFMAs run.
+// The DMA is issued from inline asm (it has no register results): the
+// kernel counts its completions itself, and the compiler, which then sees
+// only the LDS reads, orders those by the LDS counter alone instead of
+// draining every DMA in flight before each read.  In LDS a row is 64 bytes
+// (four 16-byte chunks) and chunk c of row r sits at slot c ^ ((r >> 2) & 3),
+// so that the sixteen rows of a fragment read fill all 64 banks.
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -30,119 +38,164 @@ namespace {
 
 typedef __bf16 bf16x8g __attribute__((ext_vector_type(8)));
 typedef float f32x16g __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_vg;
 
-constexpr int kGM = 128, kGN = 256, kGK = 32, kGStages = 3;
-constexpr int kGRowB = kGK * 2;  // bytes per LDS row
+constexpr int kGM = 256, kGN = 256, kGK = 32;
+constexpr int kGRows = 256;  // rows per operand per stage
+
+typedef __attribute__((address_space(3))) void lds_vg;
 
 __device__ __forceinline__ f32x16g mfma32g(uint4 a, uint4 b, f32x16g c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8g, a),
                                                  __builtin_bit_cast(bf16x8g, b), c, 0, 0, 0);
 }
 
-// Four 16-byte LDS reads, waited for in the same block (the compiler then
-// sees no LDS load to order after the DMA in flight).
-__device__ __forceinline__ void lds_rd4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                        uint4& o0, uint4& o1, uint4& o2, uint4& o3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n"
-      "ds_read_b128 %1, %5\n"
-      "ds_read_b128 %2, %6\n"
-      "ds_read_b128 %3, %7\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
-}
-
 }  // namespace
 
-__global__ void __launch_bounds__(256, 2) gemm_nt_bf16(
+__global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M,
     int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sa, int64_t sb, int64_t sc) {
-  __shared__ __attribute__((aligned(1024))) bf16_t As[kGStages][kGM * kGK];
-  __shared__ __attribute__((aligned(1024))) bf16_t Bs[kGStages][kGN * kGK];
-  const int64_t bz = blockIdx.z;
+  // [stage buffer][operand][row * 4 + slot]
+  __shared__ __attribute__((aligned(1024))) uint4 lds[4][2][kGRows * 4];
+  // Tile order: consecutive blocks are dealt round-robin to the eight XCDs
+  // (each with its own L2), so block L runs on XCD L % 8.  When the tile
+  // count is a multiple of 8, XCD c takes tiles c T/8 .. (c+1) T/8 - 1 in
+  // order, and tiles are numbered group by group of 8 row tiles (column
+  // tile fastest within a group's 8 rows), so the blocks an XCD runs at once
+  // cover a compact patch and share their A and B tiles in that L2.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int ntile = gx * gy * (int)gridDim.z;
+  int t = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  if ((ntile & 7) == 0) t = (t & 7) * (ntile >> 3) + (t >> 3);
+  const int tz = t / (gx * gy), tr = t - tz * gx * gy;
+  const int g0 = (tr / (8 * gx)) * 8, gh = min(8, gy - g0);
+  const int tq = tr - g0 * gx;
+  const int ty = g0 + tq % gh, tx = tq / gh;
+  const int64_t bz = tz;
   A += bz * sa;
   B += bz * sb;
   C += bz * sc;
-  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
-  const int lane = threadIdx.x & 63, l32 = lane & 31, h32 = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wv & 1, wn = wv >> 1;  // the wave's 64 x 128 part of the tile
+  const int m0 = ty * kGM, n0 = tx * kGN;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv & 1, wn = wv >> 1;  // the wave's 128 x 128 part of the tile
   const int nk = K / kGK;
   // DMA of one stage: 16 rows of 64 bytes per instruction (lane = 4 row +
-  // slot); A: 2 instructions per wave, B: 4; rows past M / N re-read the last
+  // slot), four instructions per operand per wave; rows past M / N re-read
+  // the last row
   const int lr = lane >> 2, slot = lane & 3;
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * kGK;
+  const bf16_t* pa[4];
+  const bf16_t* pb[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 16 * (2 * wv + j) + lr;
-      const int row = min(m0 + r, M - 1);
-      const bf16_t* src = A + (int64_t)row * lda + k0 + 8 * (slot ^ ((r >> 1) & 3));
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (lds_vg*)(&As[buf][16 * (2 * wv + j) * kGK]), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * (4 * wv + j) + lr;
-      const int row = min(n0 + r, N - 1);
-      const bf16_t* src = B + (int64_t)row * ldb + k0 + 8 * (slot ^ ((r >> 1) & 3));
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (lds_vg*)(&Bs[buf][16 * (4 * wv + j) * kGK]), 16, 0, 0);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (4 * wv + j) + lr;
+    pa[j] = A + (int64_t)min(m0 + r, M - 1) * lda + 8 * (slot ^ ((r >> 2) & 3));
+    pb[j] = B + (int64_t)min(n0 + r, N - 1) * ldb + 8 * (slot ^ ((r >> 2) & 3));
+  }
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_vg*)&lds[0][0][0];
+  // DMA instruction i (0..7) of stage slot `st` into buffer `buf`: operand
+  // i & 1, rows 16 (4 wv + i / 2).  Every stage issues eight instructions,
+  // so the count of instructions in flight is the same at every wait; a slot
+  // past the last stage re-reads the last stage into a buffer that no wave
+  // reads again.
+  auto issue1 = [&](int st, int buf, int i) {
+    const uint32_t d = lds0 + (uint32_t)buf * (2 * kGRows * 64) + (i & 1) * (kGRows * 64) +
+                       (uint32_t)(4 * wv + (i >> 1)) * 1024;
+    const bf16_t* src = ((i & 1) ? pb[i >> 1] : pa[i >> 1]) + min(st, nk - 1) * kGK;
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(d)
+        : "memory", "m0");
   };
-  f32x16g acc[2][4];
+  f32x16g acc[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
-  // fragment of row r (tile-relative), 16-deep step s: chunk 2 s + h32
-  auto faddr = [&](const bf16_t* base, int r, int s) {
-    return (uint32_t)(size_t)(lds_vg*)base +
-           (uint32_t)(r * kGRowB + 16 * ((2 * s + h32) ^ ((r >> 1) & 3)));
+  // fragment of tile row r0 + l32 (r0 a multiple of 32), step s: chunk
+  // 2 s + h32 at slot (2 s + h32) ^ ((l32 >> 2) & 3)
+  const int fsw = (l32 >> 2) & 3;
+  const int ra = (128 * wm + l32) * 4, rb = (128 * wn + l32) * 4;
+  typedef uint4 frags_t[2][4];
+  frags_t fa0, fb0, fa1, fb1;
+  auto read_stage = [&](int kt, frags_t& fa, frags_t& fb) {
+    const uint4* la = lds[kt & 3][0];
+    const uint4* lb = lds[kt & 3][1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int sl = (2 * s + h32) ^ fsw;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[s][t] = la[ra + 128 * t + sl];
+        fb[s][t] = lb[rb + 128 * t + sl];
+      }
+    }
   };
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's DMA of stage kt is done once at most the next stage's six
-    // instructions are outstanding (none after the last issue)
-    if (kt + 1 < nk)
-      asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    // after the barrier every wave is past stage kt - 1: its buffer is free
-    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % kGStages);
-    const int buf = kt % kGStages;
-    const bf16_t* as = As[buf];
-    const bf16_t* bs = Bs[buf];
-    uint4 af[2][2], bf[4][2];
-    const int ra = 64 * wm + l32, rb = 128 * wn + l32;
-    lds_rd4(faddr(as, ra, 0), faddr(as, ra, 1), faddr(as, ra + 32, 0), faddr(as, ra + 32, 1),
-            af[0][0], af[0][1], af[1][0], af[1][1]);
-    lds_rd4(faddr(bs, rb, 0), faddr(bs, rb, 1), faddr(bs, rb + 32, 0), faddr(bs, rb + 32, 1),
-            bf[0][0], bf[0][1], bf[1][0], bf[1][1]);
-    lds_rd4(faddr(bs, rb + 64, 0), faddr(bs, rb + 64, 1), faddr(bs, rb + 96, 0),
-            faddr(bs, rb + 96, 1), bf[2][0], bf[2][1], bf[3][0], bf[3][1]);
+  auto mfma_step = [&](const frags_t& fa, const frags_t& fb, int s) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32g(fa[s][mt], fb[s][nt], acc[mt][nt]);
+  };
+  auto stage = [&](int kt, frags_t& fa, frags_t& fb, frags_t& na, frags_t& nb) {
+    mfma_step(fa, fb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // slots up to kt + 3 were issued: this wave's stage kt + 1 has landed
+      // once at most the sixteen instructions of kt + 2 and kt + 3 fly;
+      // after the barrier every wave's has, and every wave has read stage
+      // kt, so its buffer takes slot kt + 4
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    }
+    // in the last stage no barrier runs and other waves may still read
+    // stage kt: its eight instructions then go to buffer (kt + 1) & 3, whose
+    // stage was consumed three stages ago
+    const int dbuf = (kt + 1 < nk) ? (kt & 3) : ((kt + 1) & 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // (after the last stage these reads fetch a quiet buffer and are unused)
+    const uint4* la = lds[(kt + 1) & 3][0];
+    const uint4* lb = lds[(kt + 1) & 3][1];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32g(af[mt][s], bf[nt][s], acc[mt][nt]);
+    for (int i = 0; i < 16; ++i) {
+      acc[i >> 2][i & 3] = mfma32g(fa[1][i >> 2], fb[1][i & 3], acc[i >> 2][i & 3]);
+      const int st = i >> 3, t = (i >> 1) & 3;
+      const int sl = (2 * st + h32) ^ fsw;
+      if (i & 1)
+        nb[st][t] = lb[rb + 128 * t + sl];
+      else
+        na[st][t] = la[ra + 128 * t + sl];
+      if (i & 1) issue1(kt + 4, dbuf, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue1(j, j, i);
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  read_stage(0, fa0, fb0);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    stage(kt, fa0, fb0, fa1, fb1);
+    stage(kt + 1, fa1, fb1, fa0, fb0);
   }
+  if (kt < nk) stage(kt, fa0, fb0, fa1, fb1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // register v of tile (mt, nt): row 8 (v / 4) + 4 h32 + v % 4, column l32
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int col = n0 + 128 * wn + 32 * nt + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + 64 * wm + 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
+        const int row = m0 + 128 * wm + 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
         if (row < M && col < N) C[(int64_t)row * ldc + col] = f32_to_bf16(acc[mt][nt][v]);
       }
     }
