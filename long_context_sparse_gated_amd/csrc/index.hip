@@ -1083,6 +1083,190 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
   }
 }
 
+// Exclusive prefix sum of one value per thread over a 256-thread block.
+__device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  uint32_t before = x - v;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wv) before += wsum[w];
+    total += wsum[w];
+  }
+  __syncthreads();
+  return before;
+}
+
+// Decode selection in one launch for rows of at most kBlkTopK keys: one
+// block per query, thread t reading the scores of ids 128 t .. 128 t + 127.
+// The histogram the scan built names the cut bin T; a score is a candidate
+// when its order key is at least the first key of bin T, i.e. when the
+// score itself is at least the smallest float of that bin (one compare per
+// score).  The candidates' ids go to LDS in id order (a block scan of the
+// per-thread counts gives each thread its first slot; writes of non-
+// candidates land on a per-lane spare slot, so the unrolled loop has no
+// branches).  A radix select on the low 20 bits settles bin T among the
+// candidates (scores re-read from L2 by id), and an ordered pass over the
+// candidates emits the k ids ascending, ties to the lower id.
+constexpr int kBlkTopKU = 128;
+constexpr int kBlkTopK = 256 * kBlkTopKU;
+
+__global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scores,
+                                                  const uint32_t* __restrict__ hist,
+                                                  int32_t* __restrict__ out,
+                                                  const int64_t* __restrict__ pos0, int n_new,
+                                                  int m, int k, int64_t pool_cap) {
+  __shared__ int32_t cand[kBlkTopK + 64];  // candidate ids in id order (+ a spare per lane)
+  __shared__ uint32_t wsum[4], wcnt[4], res[2], bins[256], sh_prefix, sh_rem;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tok = blockIdx.x;
+  const int b = tok / n_new, i = tok % n_new;
+  int64_t nv = (pos0[b] + i + 1) / m;
+  if (nv > pool_cap) nv = pool_cap;
+  int32_t* o = out + (int64_t)tok * k;
+  if (nv <= k) {
+    for (int j = tid; j < k; j += 256) o[j] = j < nv ? j : -1;
+    return;
+  }
+  constexpr int U = kBlkTopKU;
+  const int j0 = tid * U;
+  const int nval = (int)(nv - j0 < 0 ? 0 : (nv - j0 > U ? U : nv - j0));
+  const float* row = scores + (int64_t)tok * pool_cap;
+  const float* sc = row + j0;
+  // the loads go out before the histogram is read; ids past the row get a
+  // NaN, which no comparison selects
+  float x[U];
+  if (nval == U && (pool_cap & 3) == 0) {
+#pragma unroll
+    for (int u = 0; u < U; u += 4) {
+      const float4 v = *(const float4*)(sc + u);
+      x[u] = v.x;
+      x[u + 1] = v.y;
+      x[u + 2] = v.z;
+      x[u + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = u < nval ? sc[u] : __uint_as_float(0x7fc00000u);
+  }
+  hist_cut(hist + (int64_t)tok * kHBins, (uint32_t)k, wsum, res);
+  const uint32_t T = res[0];
+  const uint32_t A = res[1];  // keys in the bins above T: all selected
+  // smallest float whose order key lies in bin T (order keys are monotonic
+  // in the score; -0 and +0 share one)
+  const uint32_t tkey = T << kHShift;
+  const float thr = __uint_as_float((tkey & 0x80000000u) ? (tkey & 0x7fffffffu) : ~tkey);
+  // candidate flags as four bit words (kept as masks, 128 of them would not
+  // fit the scalar registers)
+  uint32_t cw[U / 32];
+#pragma unroll
+  for (int w = 0; w < U / 32; ++w) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) bits |= (x[32 * w + u] >= thr ? 1u : 0u) << u;
+    cw[w] = bits;
+  }
+  uint32_t nc = 0;
+#pragma unroll
+  for (int w = 0; w < U / 32; ++w) nc += (uint32_t)__popc(cw[w]);
+  uint32_t N;
+  uint32_t pos = block_scan256(nc, wsum, N);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t c = (cw[u >> 5] >> (u & 31)) & 1u;
+    cand[c ? pos : (uint32_t)(kBlkTopK + lane)] = j0 + u;
+    pos += c;
+  }
+  __syncthreads();
+  if (N > (uint32_t)nv) N = (uint32_t)nv;  // only should the histogram disagree
+  constexpr uint32_t kLow = (1u << kHShift) - 1u;
+  auto key_of = [&](uint32_t e) -> uint32_t { return order_key(row[cand[e]]); };
+  // radix select over the low bits of the candidates in bin T: 8 + 8 + 4
+  const uint32_t need = (uint32_t)k - A;
+  uint32_t prefix = 0, mask = 0, rem = need;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? kHShift - 8 : (pass == 1 ? kHShift - 16 : 0);
+    const uint32_t nb = pass == 2 ? (1u << (kHShift - 16)) : 256u;
+    bins[tid] = 0u;
+    __syncthreads();
+    for (uint32_t e = tid; e < N; e += 256) {
+      const uint32_t key = key_of(e);
+      if ((key >> kHShift) == T && ((key & kLow) & mask) == prefix)
+        atomicAdd(&bins[((key & kLow) >> shift) & (nb - 1u)], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t c0 = bins[4 * lane], c1 = bins[4 * lane + 1], c2 = bins[4 * lane + 2],
+                     c3 = bins[4 * lane + 3];
+      const uint32_t sum = c0 + c1 + c2 + c3;
+      uint32_t suf = sum;  // inclusive suffix sum over lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_down(suf, d, 64);
+        if (lane + d < 64) suf += y;
+      }
+      const unsigned long long bal = __ballot(suf >= rem);
+      const int Lb = 63 - __clzll(bal);
+      if (lane == Lb) {
+        uint32_t above = suf - sum;
+        const uint32_t cnt[4] = {c0, c1, c2, c3};
+        int d = 3;
+        for (; d > 0; --d) {
+          if (above + cnt[d] >= rem) break;
+          above += cnt[d];
+        }
+        sh_prefix = prefix | ((uint32_t)(4 * Lb + d) << shift);
+        sh_rem = rem - above;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    rem = sh_rem;
+    mask |= (nb - 1u) << shift;
+  }
+  // the k-th best key is tk: every candidate above it, and the first `rem`
+  // equal to it in id order, go out in id order
+  const uint32_t tk = tkey | prefix;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t base_sel = 0, base_eq = 0;
+  for (uint32_t e0 = 0; e0 < N; e0 += 256) {
+    const uint32_t e = e0 + tid;
+    const uint32_t key = e < N ? key_of(e) : 0u;
+    const bool gt = e < N && key > tk, eq = e < N && key == tk;
+    const unsigned long long be = __ballot(eq);
+    if (lane == 0) wcnt[wv] = (uint32_t)__popcll(be);
+    __syncthreads();
+    uint32_t eq_off = base_eq, eq_tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) eq_off += wcnt[w];
+      eq_tot += wcnt[w];
+    }
+    const bool sel = gt || (eq && eq_off + (uint32_t)__popcll(be & lt) < rem);
+    const unsigned long long bs = __ballot(sel);
+    if (lane == 0) wsum[wv] = (uint32_t)__popcll(bs);
+    __syncthreads();
+    uint32_t off = base_sel, tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) off += wsum[w];
+      tot += wsum[w];
+    }
+    const uint32_t p = off + (uint32_t)__popcll(bs & lt);
+    if (sel && p < (uint32_t)k) o[p] = cand[e];
+    base_sel += tot;
+    base_eq += eq_tot;
+    __syncthreads();
+    if (base_sel >= (uint32_t)k) break;  // block-uniform
+  }
+}
+
 // ---------------------------------------------------------------------------
 // generic: any shape, VALU float32
 
@@ -1354,6 +1538,16 @@ static int index_decode_kernel() {
   return 0;
 }
 
+// Decode selection for rows of at most kBlkTopK keys: 0 = topk_block (one
+// launch), 1 = topk_collect + topk_final (the path longer rows always take);
+// the environment variable CSA_TOPK_DECODE ("0" or "1"), read at each call,
+// overrides the default.
+static int topk_decode_kernel() {
+  const char* e = getenv("CSA_TOPK_DECODE");
+  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
+  return 0;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
@@ -1409,6 +1603,10 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
         index_decode_mfma<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
                                              (float*)(counts + bn * nslice * 2), hist, bt.pos0,
                                              bt.n, L.m, pool_cap, (int)bk);
+    }
+    if (nv <= kBlkTopK && topk_decode_kernel() == 0) {
+      topk_block<<<tokens, 256, 0, s>>>(scores, hist, idx, bt.pos0, bt.n, L.m, L.k, pool_cap);
+      return hipGetLastError();
     }
     if (nv > L.k) {
       dim3 g2((unsigned)((nv + 4 * kSlice - 1) / (4 * kSlice)), tokens);

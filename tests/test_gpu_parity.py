@@ -382,12 +382,24 @@ def test_decode_graph_replay_matches_eager(csa):
 
 @pytest.mark.parametrize("n_q,pool,distinct,pos0", [
     (37, 700, 0, 2700), (64, 900, 5, 3000), (9, 300, 0, 0), (1, 5000, 0, 19999),
-    (1, 30000, 7, 119999), (3, 2048, 3, 8191), (7, 12000, 0, 47990), (5, 600, 0, 2048)])
+    (1, 30000, 7, 119999), (3, 2048, 3, 8191), (7, 12000, 0, 47990), (5, 600, 0, 2048),
+    (2, 3001, 0, 11990), (1, 32768, 2, 131071)])
 def test_topk_bit_exact_on_grid_inputs(csa, n_q, pool, distinct, pos0):
     """Exact-arithmetic scores: both sides must select identical ids (ties: lowest id)."""
+    _grid_topk_case(csa, n_q, pool, distinct, pos0)
+
+
+@pytest.mark.parametrize("n_q,pool,distinct,pos0", [
+    (1, 30000, 7, 119999), (3, 2048, 3, 8191), (2, 3001, 0, 11990)])
+def test_topk_decode_two_launch_path(csa, monkeypatch, n_q, pool, distinct, pos0):
+    """The collect + final selection (the path of rows beyond 32768 keys) on short rows."""
+    monkeypatch.setenv("CSA_TOPK_DECODE", "1")
+    _grid_topk_case(csa, n_q, pool, distinct, pos0)
+
+
+def _grid_topk_case(m, n_q, pool, distinct, pos0):
     import torch
     say(f"case: grid top-k n_q={n_q} pool={pool} distinct={distinct} pos0={pos0}")
-    m = csa
     spec = synth.LayerSpec(kind="csa", dtype="bf16")
     L = m.Layer.from_spec(spec)
     k = spec.topk
