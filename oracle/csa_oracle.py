@@ -49,6 +49,7 @@ __all__ = [
     "pool_entry", "compress", "visible_entries",
     "window_positions", "index_scores", "topk_select", "attend",
     "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step", "output_projection",
+    "ProjSizes", "project_inputs",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -443,4 +444,62 @@ def output_projection(attn_out, w_a, w_b, o_groups: int, dtype: str) -> np.ndarr
         y[:, g, :] = xg[:, g, :] @ wa[g].T
     y = round_to(y, dtype)
     return round_to(y.reshape(T, G * R) @ np.asarray(w_b, dtype=np.float64).T, dtype)
+
+
+class ProjSizes(NamedTuple):
+    """Widths of the producer projections (0 drops a stream: a layer without
+    compressor has comp = 0, one without indexer index_dim = index_heads = 0)."""
+    q_lora: int
+    heads: int
+    head_dim: int
+    comp: int
+    index_dim: int
+    index_heads: int
+
+
+def _rms_rows(y, weight, eps):
+    y = np.asarray(y, dtype=np.float64)
+    out = y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return out if weight is None else out * np.asarray(weight, dtype=np.float64)
+
+
+def project_inputs(x, w_x, g_qa, g_kv, w_q, sz: ProjSizes, eps: float, q_head_norm: bool,
+                   dtype: str) -> dict:
+    """Producer side of the attention block [TL, the adapter's self_attn
+    module list (q_a_proj, q_a_norm, q_b_proj, q_b_norm, kv_proj, kv_norm,
+    compressor) and ``_compressor_bridge`` (compressor kv_proj / gate_proj,
+    indexer kv_proj / gate_proj / q_b_proj / scorer.weights_proj); HF-doc
+    sec. 2.3: kv_proj makes the single shared K=V head].
+
+    x [T, hidden] are the block's normalised hidden states.  w_x stacks the
+    (out, in) weights read from x, in this row order: q_a_proj (q_lora rows),
+    kv_proj (D), compressor kv_proj (comp), compressor gate_proj (comp),
+    indexer kv_proj (index_dim), indexer gate_proj (index_dim),
+    weights_proj (index_heads).  w_q stacks the weights read from the query
+    latent: q_b_proj (H D rows) then the indexer's q_b_proj (H_I D_I rows).
+
+    Every projection output is stored at ``dtype``; the two RMSNorms
+    (q_a_norm with weight g_qa, kv_norm with weight g_kv) read the stored
+    projection and are stored in turn; with ``q_head_norm`` each head of q
+    is divided by its RMS over D (q_b_norm, read as carrying no weight), else
+    q is the stored projection.  The compressor's own kv_norm acts on pooled
+    entries (``compress``), not here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    y = round_to(x @ np.asarray(w_x, dtype=np.float64).T, dtype)
+    cuts = np.cumsum([0, sz.q_lora, sz.head_dim, sz.comp, sz.comp, sz.index_dim, sz.index_dim,
+                      sz.index_heads])
+    seg = [y[:, cuts[i]:cuts[i + 1]] for i in range(7)]
+    latent = round_to(_rms_rows(seg[0], g_qa, eps), dtype)
+    out = {"latent": latent, "kv": round_to(_rms_rows(seg[1], g_kv, eps), dtype),
+           "ckv": seg[2], "cgate": seg[3], "ikv": seg[4], "igate": seg[5], "wi": seg[6]}
+    yq = round_to(latent @ np.asarray(w_q, dtype=np.float64).T, dtype)
+    hd = sz.heads * sz.head_dim
+    q = yq[:, :hd].reshape(T, sz.heads, sz.head_dim)
+    if q_head_norm:
+        q = round_to(_rms_rows(q, None, eps), dtype)
+    out["q"] = q
+    out["qi"] = yq[:, hd:].reshape(T, sz.index_heads, sz.index_dim)
+    return out
 

@@ -57,6 +57,15 @@ MUTATIONS = {
                                 "wa = np.asarray(w_a, dtype=np.float64).reshape(G, ig, R).transpose(0, 2, 1)"),
     "oproj_no_intermediate_rounding": ("csa_oracle.py", "    y = round_to(y, dtype)\n",
                                        "    y = y\n"),
+    "proj_norm_axis": ("csa_oracle.py",
+                       "out = y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)",
+                       "out = y / np.sqrt(np.mean(y * y, axis=0, keepdims=True) + eps)"),
+    "proj_segment_order": ("csa_oracle.py",
+                           "cuts = np.cumsum([0, sz.q_lora, sz.head_dim, sz.comp,",
+                           "cuts = np.cumsum([0, sz.head_dim, sz.q_lora, sz.comp,"),
+    "proj_latent_unrounded": ("csa_oracle.py",
+                              "yq = round_to(latent @ np.asarray(w_q, dtype=np.float64).T, dtype)",
+                              "yq = round_to(_rms_rows(seg[0], g_qa, eps) @ np.asarray(w_q, dtype=np.float64).T, dtype)"),
     "round_bits": ("csa_oracle.py", "q = np.ldexp(np.round(np.ldexp(x, 8 - e)), e - 8)",
                    "q = np.ldexp(np.round(np.ldexp(x, 9 - e)), e - 9)"),
     "round_double": ("csa_oracle.py", "_, e = np.frexp(x)",

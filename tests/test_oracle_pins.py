@@ -578,3 +578,110 @@ def test_output_projection_group_locality_and_stored_intermediate():
                    "bf16")
     assert np.array_equal(out, O.round_to(y.reshape(T, G * R) @ wb.T, "bf16"))
 
+
+
+# ----------------------------------------------------------------------------
+# producer projections
+
+def _proj_case(seed, T=3, hidden=6, sz=None):
+    sz = sz or O.ProjSizes(q_lora=4, heads=2, head_dim=3, comp=2, index_dim=2, index_heads=2)
+    rng = np.random.default_rng(seed)
+    nx = sz.q_lora + sz.head_dim + 2 * sz.comp + 2 * sz.index_dim + sz.index_heads
+    nq = sz.heads * sz.head_dim + sz.index_heads * sz.index_dim
+    return (sz, rng.standard_normal((T, hidden)), rng.standard_normal((nx, hidden)),
+            rng.uniform(0.5, 1.5, sz.q_lora), rng.uniform(0.5, 1.5, sz.head_dim),
+            rng.standard_normal((nq, sz.q_lora)))
+
+
+def test_project_inputs_matches_loops_on_tiny_sizes():
+    sz, x, wx, gqa, gkv, wq = _proj_case(21)
+    eps = 1e-6
+    out = O.project_inputs(x, wx, gqa, gkv, wq, sz, eps, True, "f64")
+    T, hidden = x.shape
+
+    def dot_rows(a, w, r0, n):
+        return [[sum(a[t][i] * w[r0 + o][i] for i in range(len(a[t]))) for o in range(n)]
+                for t in range(len(a))]
+
+    def rms(v, g):
+        r = (sum(e * e for e in v) / len(v) + eps) ** 0.5
+        return [v[i] / r * (1.0 if g is None else g[i]) for i in range(len(v))]
+
+    xl = x.tolist()
+    qa = dot_rows(xl, wx, 0, sz.q_lora)
+    lat = [rms(r, gqa) for r in qa]
+    kv = [rms(r, gkv) for r in dot_rows(xl, wx, sz.q_lora, sz.head_dim)]
+    off = sz.q_lora + sz.head_dim
+    ckv = dot_rows(xl, wx, off, sz.comp)
+    cg = dot_rows(xl, wx, off + sz.comp, sz.comp)
+    ikv = dot_rows(xl, wx, off + 2 * sz.comp, sz.index_dim)
+    ig = dot_rows(xl, wx, off + 2 * sz.comp + sz.index_dim, sz.index_dim)
+    wi = dot_rows(xl, wx, off + 2 * sz.comp + 2 * sz.index_dim, sz.index_heads)
+    qfull = dot_rows(lat, wq, 0, sz.heads * sz.head_dim)
+    q = [[rms(r[h * sz.head_dim:(h + 1) * sz.head_dim], None) for h in range(sz.heads)]
+         for r in qfull]
+    qi = dot_rows(lat, wq, sz.heads * sz.head_dim, sz.index_heads * sz.index_dim)
+    for name, ref in [("latent", lat), ("kv", kv), ("ckv", ckv), ("cgate", cg), ("ikv", ikv),
+                      ("igate", ig), ("wi", wi), ("q", q)]:
+        assert np.allclose(out[name], np.array(ref), rtol=1e-12, atol=1e-12), name
+    assert np.allclose(out["qi"], np.array(qi).reshape(T, sz.index_heads, sz.index_dim),
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_project_inputs_norm_properties():
+    sz, x, wx, gqa, gkv, wq = _proj_case(22, T=5, hidden=8,
+                                         sz=O.ProjSizes(6, 3, 4, 2, 2, 3))
+    ones = np.ones
+    out = O.project_inputs(x, wx, ones(sz.q_lora), ones(sz.head_dim), wq, sz, 0.0, True, "f64")
+    # unit-weight RMSNorm rows and per-head q rows have unit RMS
+    for name in ("latent", "kv"):
+        assert np.allclose(np.sqrt(np.mean(out[name] ** 2, axis=-1)), 1.0, rtol=1e-12)
+    assert np.allclose(np.sqrt(np.mean(out["q"] ** 2, axis=-1)), 1.0, rtol=1e-12)
+    # scaling x: the normalised streams do not move, the plain ones scale with it
+    out3 = O.project_inputs(3.0 * x, wx, ones(sz.q_lora), ones(sz.head_dim), wq, sz, 0.0, True,
+                            "f64")
+    for name in ("latent", "kv", "q", "qi"):
+        assert np.allclose(out3[name], out[name], rtol=1e-11, atol=1e-12), name
+    for name in ("ckv", "cgate", "ikv", "igate", "wi"):
+        assert np.allclose(out3[name], 3.0 * out[name], rtol=1e-12), name
+    # without q_b_norm q is the plain product of the latent
+    raw = O.project_inputs(x, wx, ones(sz.q_lora), ones(sz.head_dim), wq, sz, 0.0, False, "f64")
+    hd = sz.heads * sz.head_dim
+    assert np.allclose(raw["q"].reshape(x.shape[0], hd), raw["latent"] @ wq[:hd].T, rtol=1e-12)
+
+
+def test_project_inputs_streams_are_separate_rows_of_the_stacked_weight():
+    sz, x, wx, gqa, gkv, wq = _proj_case(23)
+    base = O.project_inputs(x, wx, gqa, gkv, wq, sz, 1e-6, True, "f64")
+    off = sz.q_lora + sz.head_dim + sz.comp  # the compressor gate rows
+    wx2 = wx.copy()
+    wx2[off:off + sz.comp] *= -2.0
+    moved = O.project_inputs(x, wx2, gqa, gkv, wq, sz, 1e-6, True, "f64")
+    for name in base:
+        if name == "cgate":
+            assert np.allclose(moved[name], -2.0 * base[name], rtol=1e-12)
+        else:
+            assert np.array_equal(moved[name], base[name]), name
+    # no indexer and no compressor: those outputs are empty, the rest unchanged
+    sz0 = O.ProjSizes(sz.q_lora, sz.heads, sz.head_dim, 0, 0, 0)
+    keep = np.r_[0:sz.q_lora + sz.head_dim]
+    out0 = O.project_inputs(x, wx[keep], gqa, gkv, wq[:sz.heads * sz.head_dim], sz0, 1e-6, True,
+                            "f64")
+    for name in ("latent", "kv", "q"):
+        assert np.array_equal(out0[name], base[name]), name
+    assert out0["ckv"].shape == (x.shape[0], 0) and out0["qi"].shape == (x.shape[0], 0, 0)
+
+
+def test_project_inputs_stored_points_at_bf16():
+    sz, x, wx, gqa, gkv, wq = _proj_case(24, T=6, hidden=16, sz=O.ProjSizes(16, 2, 8, 4, 4, 2))
+    xb = O.round_to(x, "bf16")
+    out = O.project_inputs(xb, wx, gqa, gkv, wq, sz, 1e-6, False, "bf16")
+    # q reads the stored latent; the latent reads the stored projection
+    hd = sz.heads * sz.head_dim
+    assert np.array_equal(out["q"].reshape(x.shape[0], hd),
+                          O.round_to(out["latent"] @ wq[:hd].T, "bf16"))
+    y = O.round_to(xb @ wx[:sz.q_lora].T, "bf16")
+    lat = O.round_to(y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + 1e-6) * gqa, "bf16")
+    assert np.array_equal(out["latent"], lat)
+    for name in ("latent", "kv", "ckv", "q", "qi"):
+        assert np.array_equal(out[name], O.round_to(out[name], "bf16")), name
