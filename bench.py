@@ -19,7 +19,11 @@ the same way (one step = every call of the layer(s) for one batch):
                    sliding-only layer;
 * ``output_projection`` the grouped low-rank output projection of the 8192
                    prefill tokens (8 groups of 8 heads x 512 -> rank 1024 each
-                   -> hidden 4096), priced in its two products' MFMA FLOPs.
+                   -> hidden 4096), priced in its two products' MFMA FLOPs;
+* ``projections`` the producer projections of the same 8192 tokens (hidden
+                   4096 -> query latent 1024, kv 512, compressor 2 x 512, indexer
+                   2 x 128 + 64 head weights; latent -> 64 x 512 queries and 64 x
+                   128 indexer queries; the norms), priced in MFMA FLOPs.
 
 Prefill steps are priced in MFMA FLOPs (4 H D per attended (query, row)
 pair, plus 2 H_I D_I per scored (query, key) pair); decode steps in the HBM
@@ -285,6 +289,41 @@ def oproj_leg(torch, m, steps, warmup):
             "achieved_TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, **s}
 
 
+def proj_leg(torch, m, steps, warmup):
+    import synth
+    s = synth.PROJ_SHAPE
+    T, hid, ql, H, D, comp, Di, Hi = (s[k] for k in ("T", "hidden", "q_lora", "H", "D", "comp",
+                                                     "Di", "Hi"))
+    inp = synth.proj_inputs(T, hid, ql, H, D, comp, Di, Hi, seed=0)
+    a = {k: _dev(torch, v) for k, v in inp.items()}
+    bf = torch.bfloat16
+    outs = {"q": torch.empty(T, H, D, dtype=bf, device="cuda"),
+            "kv": torch.empty(T, D, dtype=bf, device="cuda"),
+            "ckv": torch.empty(T, comp, dtype=bf, device="cuda"),
+            "cgate": torch.empty(T, comp, dtype=bf, device="cuda"),
+            "ikv": torch.empty(T, Di, dtype=bf, device="cuda"),
+            "igate": torch.empty(T, Di, dtype=bf, device="cuda"),
+            "qi": torch.empty(T, Hi, Di, dtype=bf, device="cuda"),
+            "wi": torch.empty(T, Hi, dtype=bf, device="cuda")}
+    need = m.load_library().csa_project_workspace_bytes(
+        m._CProj(T, hid, ql, H, D, comp, Di, Hi, 1e-6, 1))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step(_ev):
+        m.csa_project(a["x"], a["w_x"], a["g_qa"], a["g_kv"], a["w_q"], outs, q_lora_rank=ql,
+                      num_heads=H, head_dim=D, comp_dim=comp, index_dim=Di, index_heads=Hi,
+                      eps=1e-6, q_head_norm=True, workspace=ws)
+
+    ms, _ = _time_steps(torch, step, steps, warmup)
+    nx = ql + D + 2 * comp + 2 * Di + Hi
+    nq = H * D + Hi * Di
+    flop = 2.0 * T * (nx * hid + nq * ql)
+    tf = flop / (ms * 1e-3) / 1e12
+    del a, outs, ws
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_flop": flop,
+            "achieved_TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, **s}
+
+
 def calib_copy(torch, mib):
     if mib <= 0:
         return
@@ -311,6 +350,8 @@ def run_leg(torch, m, name, args):
         return decode_leg(torch, m, name, 5 * args.steps, args.warmup)
     if name == "output_projection":
         return oproj_leg(torch, m, args.steps, args.warmup)
+    if name == "projections":
+        return proj_leg(torch, m, args.steps, args.warmup)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -321,10 +362,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1)
-    ap.add_argument("--legs", default="hca_prefill,csa_decode,mixed_decode,output_projection",
+    ap.add_argument("--legs",
+                    default="hca_prefill,csa_decode,mixed_decode,output_projection,projections",
                     help="comma list of further workloads to time after the headline "
-                         "(hca_prefill, csa_decode, mixed_decode, output_projection; empty "
-                         "for none)")
+                         "(hca_prefill, csa_decode, mixed_decode, output_projection, "
+                         "projections; empty for none)")
     ap.add_argument("--only", default="",
                     help="time just this one workload and print its object (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

@@ -270,6 +270,60 @@ csa_status csa_output_projection(const csa_oproj* p, const void* attn_out,
  * (size_t)-1 for invalid sizes. */
 size_t csa_output_projection_workspace_bytes(const csa_oproj* p);
 
+/* Producer projections: the layer's inputs from the block's normalised
+ * hidden states.
+ * Source: TransformerLens deepseek_v4 adapter, the self_attn module list
+ * (q_a_proj, q_a_norm, q_b_proj, q_b_norm, kv_proj, kv_norm, compressor) and
+ * its compressor / indexer submodules (kv_proj, gate_proj, q_b_proj,
+ * scorer.weights_proj); model page, sec. 2.3 (kv_proj makes the single K=V
+ * head).  The pages give no sizes.
+ *  x      [tokens, hidden] bf16.
+ *  w_x    [q_lora + D + 2 comp + 2 D_I + H_I, hidden] bf16, (out, in) rows
+ *         stacked in this order: q_a_proj, kv_proj, compressor kv_proj,
+ *         compressor gate_proj, indexer kv_proj, indexer gate_proj,
+ *         weights_proj (a stream of width 0 is absent).
+ *  g_qa   [q_lora] float: q_a_norm weight;  g_kv [D] float: kv_norm weight.
+ *  w_q    [H D + H_I D_I, q_lora] bf16: q_b_proj rows, then the indexer's
+ *         q_b_proj rows.
+ *  Outputs (bf16, row-major, the layout csa_window_append / csa_compress /
+ *  csa_index_topk / csa_attend take): q [tokens, H, D], kv [tokens, D],
+ *  ckv and cgate [tokens, comp], ikv and igate [tokens, D_I],
+ *  qi [tokens, H_I, D_I], wi [tokens, H_I]; pointers of absent streams may
+ *  be NULL.
+ *  latent = q_a_norm(x w_qa^T), kv = kv_norm(x w_kv^T), q = latent w_qb^T
+ *  (then, with q_head_norm, each head divided by its RMS over D), the other
+ *  streams plain products; every product and norm output is stored at bf16
+ *  (float32 accumulation; the norms in float64 over the stored values,
+ *  RMSNorm(y) = y / sqrt(mean(y^2) + eps) * g).
+ *  workspace >= csa_project_workspace_bytes(p) bytes (holds the latent).
+ * Requires hidden and q_lora to be multiples of 32, every width to be >= 0
+ * (q_lora, H, D >= 1), comp, D_I and H_I either all set or zero as the layer
+ * has them, and x, w_x, w_q 16-byte aligned (else CSA_ERR_SHAPE or
+ * CSA_ERR_UNSUPPORTED).  Buffers must not overlap; the call queues its
+ * launches on `stream` and returns. */
+typedef struct {
+  int32_t tokens;       /* T >= 1                                   */
+  int32_t hidden;       /* multiple of 32                           */
+  int32_t q_lora_rank;  /* multiple of 32                           */
+  int32_t num_heads;    /* H >= 1                                   */
+  int32_t head_dim;     /* D >= 1                                   */
+  int32_t comp_dim;     /* compressor width (D) or 0                */
+  int32_t index_dim;    /* D_I or 0                                 */
+  int32_t index_heads;  /* H_I or 0                                 */
+  float eps;            /* RMSNorm epsilon                          */
+  int32_t q_head_norm;  /* 1: q_b_norm on each head, 0: none        */
+} csa_proj;
+
+csa_status csa_project(const csa_proj* p, const void* x, const void* w_x,
+                       const float* g_qa, const float* g_kv, const void* w_q,
+                       void* q, void* kv, void* ckv, void* cgate, void* ikv,
+                       void* igate, void* qi, void* wi, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of csa_project (256-byte aligned pointer), or (size_t)-1
+ * for invalid sizes. */
+size_t csa_project_workspace_bytes(const csa_proj* p);
+
 /* Static description of a status code. */
 const char* csa_status_str(csa_status status);
 

@@ -22,14 +22,15 @@ __all__ = [
     "Layer", "load_library", "library_path", "csa_window_append", "csa_rope", "csa_compress",
     "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
     "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
-    "csa_output_projection",
+    "csa_output_projection", "csa_project",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 CSA_OP_INDEX_TOPK, CSA_OP_ATTEND, CSA_OP_HCA_ATTEND = 1, 2, 3
 EXPORTED_SYMBOLS = ("csa_window_append", "csa_rope", "csa_compress", "csa_index_topk",
                     "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
-                    "csa_version", "csa_output_projection", "csa_output_projection_workspace_bytes")
+                    "csa_version", "csa_output_projection", "csa_output_projection_workspace_bytes",
+                    "csa_project", "csa_project_workspace_bytes")
 
 
 class _CLayer(ctypes.Structure):
@@ -48,6 +49,14 @@ class _COproj(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("o_groups", ctypes.c_int32),
                 ("o_lora_rank", ctypes.c_int32), ("hidden_size", ctypes.c_int32)]
+
+
+class _CProj(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("q_lora_rank", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("comp_dim", ctypes.c_int32),
+                ("index_dim", ctypes.c_int32), ("index_heads", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("q_head_norm", ctypes.c_int32)]
 
 
 class _CBatch(ctypes.Structure):
@@ -131,6 +140,8 @@ def load_library():
         "csa_attend": [LP, BP, P, P, I64, P, I64, P, P, P, P, SZ, P],
         "hca_attend": [LP, BP, P, P, I64, P, I64, P, P, P, SZ, P],
         "csa_output_projection": [ctypes.POINTER(_COproj), P, P, P, P, P, SZ, P],
+        "csa_project": [ctypes.POINTER(_CProj), P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ,
+                        P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -144,6 +155,8 @@ def load_library():
     lib.csa_version.restype = I32
     lib.csa_output_projection_workspace_bytes.argtypes = [ctypes.POINTER(_COproj)]
     lib.csa_output_projection_workspace_bytes.restype = SZ
+    lib.csa_project_workspace_bytes.argtypes = [ctypes.POINTER(_CProj)]
+    lib.csa_project_workspace_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -313,4 +326,40 @@ def csa_output_projection(attn_out, w_a, w_b, out, o_groups: int, workspace=None
         ctypes.byref(shape), _ptr(attn_out, "attn_out", bf), _ptr(w_a, "w_a", bf),
         _ptr(w_b, "w_b", bf), _ptr(out, "out", bf), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()), "csa_output_projection")
+
+
+def csa_project(x, w_x, g_qa, g_kv, w_q, outs: dict, *, q_lora_rank: int, num_heads: int,
+                head_dim: int, comp_dim: int, index_dim: int, index_heads: int,
+                eps: float = 1e-6, q_head_norm: bool = True, workspace=None):
+    """Producer projections.  x [T, hidden], w_x and w_q stacked (out, in) bf16
+    weights, g_qa / g_kv float32 norm weights; ``outs`` holds the device
+    tensors q, kv and (as the layer has them) ckv, cgate, ikv, igate, qi, wi."""
+    torch = _torch()
+    T, hidden = x.shape
+    shape = _CProj(T, hidden, q_lora_rank, num_heads, head_dim, comp_dim, index_dim,
+                   index_heads, eps, 1 if q_head_norm else 0)
+    nx = q_lora_rank + head_dim + 2 * comp_dim + 2 * index_dim + index_heads
+    nq = num_heads * head_dim + index_heads * index_dim
+    want = {"q": (T, num_heads, head_dim), "kv": (T, head_dim), "ckv": (T, comp_dim),
+            "cgate": (T, comp_dim), "ikv": (T, index_dim), "igate": (T, index_dim),
+            "qi": (T, index_heads, index_dim), "wi": (T, index_heads)}
+    if tuple(w_x.shape) != (nx, hidden) or tuple(w_q.shape) != (nq, q_lora_rank) or \
+            tuple(g_qa.shape) != (q_lora_rank,) or tuple(g_kv.shape) != (head_dim,):
+        raise ValueError("csa_project: inconsistent weight shapes")
+    for k, shp in want.items():
+        if k in outs and outs[k] is not None and tuple(outs[k].shape) != shp:
+            raise ValueError(f"csa_project: {k} must be {shp}")
+    lib = load_library()
+    need = lib.csa_project_workspace_bytes(ctypes.byref(shape))
+    if need == ctypes.c_size_t(-1).value:
+        raise RuntimeError("csa_project: invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    bf, f32 = torch.bfloat16, torch.float32
+    o = {k: _ptr(outs.get(k), k, bf) for k in want}
+    _check(lib.csa_project(
+        ctypes.byref(shape), _ptr(x, "x", bf), _ptr(w_x, "w_x", bf), _ptr(g_qa, "g_qa", f32),
+        _ptr(g_kv, "g_kv", f32), _ptr(w_q, "w_q", bf), o["q"], o["kv"], o["ckv"], o["cgate"],
+        o["ikv"], o["igate"], o["qi"], o["wi"], _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()), "csa_project")
 

@@ -273,6 +273,50 @@ csa_status csa_output_projection(const csa_oproj* p, const void* attn_out, const
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }
 
+static csa_status proj_ok(const csa_proj* p) {
+  if (!p) return CSA_ERR_NULL;
+  if (p->tokens < 1 || p->hidden < 1 || p->q_lora_rank < 1 || p->num_heads < 1 ||
+      p->head_dim < 1 || p->comp_dim < 0 || p->index_dim < 0 || p->index_heads < 0 ||
+      (p->index_dim == 0) != (p->index_heads == 0) || !(p->eps >= 0.0f) ||
+      (p->q_head_norm != 0 && p->q_head_norm != 1))
+    return CSA_ERR_SHAPE;
+  const int64_t nx = (int64_t)p->q_lora_rank + p->head_dim + 2 * (int64_t)p->comp_dim +
+                     2 * (int64_t)p->index_dim + p->index_heads;
+  const int64_t nq = (int64_t)p->num_heads * p->head_dim +
+                     (int64_t)p->index_heads * p->index_dim;
+  // the products address a block's 256 rows with 32-bit byte offsets
+  if (p->hidden % 32 != 0 || p->q_lora_rank % 32 != 0 || p->hidden > (1 << 22) ||
+      p->q_lora_rank > (1 << 22) || nx > (1 << 30) || nq > (1 << 30) || p->tokens > (1 << 23))
+    return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+size_t csa_project_workspace_bytes(const csa_proj* p) {
+  if (proj_ok(p) != CSA_OK) return (size_t)-1;
+  return (size_t)p->tokens * p->q_lora_rank * sizeof(csa::bf16_t);
+}
+
+csa_status csa_project(const csa_proj* p, const void* x, const void* w_x, const float* g_qa,
+                       const float* g_kv, const void* w_q, void* q, void* kv, void* ckv,
+                       void* cgate, void* ikv, void* igate, void* qi, void* wi, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const csa_status st = proj_ok(p);
+  if (st != CSA_OK) return st;
+  if (!x || !w_x || !g_qa || !g_kv || !w_q || !q || !kv) return CSA_ERR_NULL;
+  if (p->comp_dim > 0 && (!ckv || !cgate)) return CSA_ERR_NULL;
+  if (p->index_dim > 0 && (!ikv || !igate || !qi || !wi)) return CSA_ERR_NULL;
+  if (((uintptr_t)x | (uintptr_t)w_x | (uintptr_t)w_q) & 15u) return CSA_ERR_UNSUPPORTED;
+  const size_t need = csa_project_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return CSA_ERR_WORKSPACE;
+  using csa::bf16_t;
+  hipError_t e = csa::launch_project(
+      p->tokens, p->hidden, p->q_lora_rank, p->num_heads, p->head_dim, p->comp_dim, p->index_dim,
+      p->index_heads, p->eps, p->q_head_norm, (const bf16_t*)x, (const bf16_t*)w_x, g_qa, g_kv,
+      (const bf16_t*)w_q, (bf16_t*)q, (bf16_t*)kv, (bf16_t*)ckv, (bf16_t*)cgate, (bf16_t*)ikv,
+      (bf16_t*)igate, (bf16_t*)qi, (bf16_t*)wi, (bf16_t*)workspace, stream);
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
 const char* csa_status_str(csa_status s) {
   switch (s) {
     case CSA_OK: return "CSA_OK";

@@ -41,6 +41,24 @@ struct Batch {
 };
 
 // oproj.hip
+// Column routing of a GEMM's output: columns col0[s] .. col0[s + 1] - 1
+// (the last segment runs to N) go to ptr[s] with row stride ld[s].
+constexpr int kGemmOutMax = 8;
+struct GemmOut {
+  bf16_t* ptr[kGemmOutMax];
+  int64_t ld[kGemmOutMax];
+  int col0[kGemmOutMax];
+  int nseg;
+};
+
+hipError_t launch_gemm_nt_routed(const bf16_t* A, const bf16_t* B, int M, int N, int K,
+                                 int64_t lda, int64_t ldb, const GemmOut& map, hipStream_t s);
+hipError_t launch_project(int T, int hidden, int q_lora, int H, int D, int comp, int Di, int Hi,
+                          float eps, int q_head_norm, const bf16_t* x, const bf16_t* w_x,
+                          const float* g_qa, const float* g_kv, const bf16_t* w_q, bf16_t* q,
+                          bf16_t* kv, bf16_t* ckv, bf16_t* cgate, bf16_t* ikv, bf16_t* igate,
+                          bf16_t* qi, bf16_t* wi, bf16_t* latent, hipStream_t s);
+
 hipError_t launch_output_projection(int T, int H, int D, int G, int R, int hidden,
                                     const bf16_t* x, const bf16_t* wa, const bf16_t* wb,
                                     bf16_t* y1, bf16_t* out, hipStream_t s);

@@ -51,9 +51,14 @@ __device__ __forceinline__ f32x16g mfma32g(uint4 a, uint4 b, f32x16g c) {
 
 }  // namespace
 
+// kRouted: the columns of C go to the outputs of `map` (columns
+// map.col0[s] .. map.col0[s + 1] - 1 to map.ptr[s], row stride map.ld[s]);
+// one batch only.  Otherwise C with row stride ldc and batch stride sc.
+template <bool kRouted>
 __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M,
-    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sa, int64_t sb, int64_t sc) {
+    int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sa, int64_t sb, int64_t sc,
+    GemmOut map) {
   // [stage buffer][operand][row * 4 + slot]
   __shared__ __attribute__((aligned(1024))) uint4 lds[4][2][kGRows * 4];
   // Tile order: consecutive blocks are dealt round-robin to the eight XCDs
@@ -193,10 +198,20 @@ __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int col = n0 + 128 * wn + 32 * nt + l32;
+      bf16_t* cp = C + col;
+      int64_t cld = ldc;
+      if (kRouted) {
+        int sg = 0;
+#pragma unroll
+        for (int q = 1; q < kGemmOutMax; ++q)
+          if (q < map.nseg && map.col0[q] <= col) sg = q;
+        cp = map.ptr[sg] + (col - map.col0[sg]);
+        cld = map.ld[sg];
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + 128 * wm + 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
-        if (row < M && col < N) C[(int64_t)row * ldc + col] = f32_to_bf16(acc[mt][nt][v]);
+        if (row < M && col < N) cp[(int64_t)row * cld] = f32_to_bf16(acc[mt][nt][v]);
       }
     }
 }
@@ -205,7 +220,15 @@ hipError_t launch_gemm_nt(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, in
                           int64_t lda, int64_t ldb, int64_t ldc, int64_t sa, int64_t sb,
                           int64_t sc, int batch, hipStream_t s) {
   dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, batch);
-  gemm_nt_bf16<<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc, sa, sb, sc);
+  gemm_nt_bf16<false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc, sa, sb, sc,
+                                           GemmOut{});
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt_routed(const bf16_t* A, const bf16_t* B, int M, int N, int K,
+                                 int64_t lda, int64_t ldb, const GemmOut& map, hipStream_t s) {
+  dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, 1);
+  gemm_nt_bf16<true><<<grid, 256, 0, s>>>(A, B, nullptr, M, N, K, lda, ldb, 0, 0, 0, 0, map);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "Workload", "WORKLOADS", "workload", "prefill_inputs",
     "decode_inputs", "bf16_bits_to_f32", "f32_to_bf16_bits", "to_f64",
-    "grid_index_inputs", "OPROJ_SHAPE", "oproj_inputs",
+    "grid_index_inputs", "OPROJ_SHAPE", "oproj_inputs", "PROJ_SHAPE", "proj_inputs",
 ]
 
 # Tensor ids keep streams independent of draw order.
@@ -50,7 +50,8 @@ _TID = {
     "q": 1, "kv": 2, "ckv": 3, "cgate": 4, "ikv": 5, "igate": 6, "qi": 7,
     "wi": 8, "sinks": 9, "pool": 10, "ipool": 11, "win": 12, "cstate_kv": 13,
     "cstate_gate": 14, "istate_kv": 15, "istate_gate": 16, "norm": 17,
-    "attn_out": 18, "o_a": 19, "o_b": 20,
+    "attn_out": 18, "o_a": 19, "o_b": 20, "hidden": 21, "w_x": 22, "w_q": 23, "g_qa": 24,
+    "g_kv": 25,
 }
 
 
@@ -390,4 +391,28 @@ def oproj_inputs(T: int, H: int, D: int, G: int, R: int, hidden: int, seed: int 
     return {"x": x,
             "w_a": _draw(seed, "o_a", 0, (G * R, ig), 1.0 / math.sqrt(ig), "bf16"),
             "w_b": _draw(seed, "o_b", 0, (hidden, G * R), 1.0 / math.sqrt(G * R), "bf16")}
+
+
+# Producer projections of the csa_prefill layer: 8192 tokens, hidden size
+# 4096, query latent of rank 1024 (sizes chosen here; the pages name the
+# modules only), 64 heads x 512, compressor width 512, indexer 64 x 128.
+PROJ_SHAPE = dict(T=8192, hidden=4096, q_lora=1024, H=64, D=512, comp=512, Di=128, Hi=64)
+
+
+def proj_inputs(T: int, hidden: int, q_lora: int, H: int, D: int, comp: int, Di: int, Hi: int,
+                seed: int = 0, rows=None) -> Dict[str, np.ndarray]:
+    """x [T, hidden] ~ N(0, 1) (bf16 bits), stacked weights w_x ~ N(0, 1/hidden)
+    and w_q ~ N(0, 1/q_lora) (bf16 bits), norm weights g_qa, g_kv ~ 1 + N(0, 0.1^2)
+    (float32).  ``rows`` draws only those token rows of x."""
+    nx = q_lora + D + 2 * comp + 2 * Di + Hi
+    nq = H * D + Hi * Di
+    if rows is None:
+        x = _draw(seed, "hidden", 0, (T, hidden), 1.0, "bf16")
+    else:
+        x = draw_rows(seed, "hidden", 0, (T, hidden), 1.0, "bf16", rows)
+    return {"x": x,
+            "w_x": _draw(seed, "w_x", 0, (nx, hidden), 1.0 / math.sqrt(hidden), "bf16"),
+            "w_q": _draw(seed, "w_q", 0, (nq, q_lora), 1.0 / math.sqrt(q_lora), "bf16"),
+            "g_qa": np.float32(1.0) + _draw(seed, "g_qa", 0, (q_lora,), 0.1, "f32"),
+            "g_kv": np.float32(1.0) + _draw(seed, "g_kv", 0, (D,), 0.1, "f32")}
 

@@ -154,3 +154,31 @@ def test_output_projection_sizes_and_rejections(lib):
     assert call(P, ws=None) == WS
     assert call(P, wsb=300 * 2 * 96 * 2 - 1) == WS
     assert call(P, ws=ctypes.c_void_p(0x1010)) == WS                  # not 256-byte aligned
+
+
+def test_project_sizes_and_rejections(lib):
+    NULL, SHAPE, WS, UNSUP = 1, 2, 5, 4
+    P = m._CProj(300, 256, 96, 4, 64, 64, 32, 8, 1e-6, 1)
+    assert lib.csa_project_workspace_bytes(ctypes.byref(P)) == 300 * 96 * 2
+
+    def call(p, x=FAKE, ckv=FAKE, qi=FAKE, ws=FAKE, wsb=1 << 40):
+        return lib.csa_project(ctypes.byref(p), x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ckv, FAKE,
+                               FAKE, FAKE, qi, FAKE, ws, wsb, None)
+
+    assert call(P, x=None) == NULL
+    assert call(P, ckv=None) == NULL                                        # compressor present
+    assert call(P, qi=None) == NULL                                         # indexer present
+    # a layer without compressor and indexer may pass NULL for those streams:
+    # the call then gets as far as the workspace check
+    assert call(m._CProj(300, 256, 96, 4, 64, 0, 0, 0, 1e-6, 1), ckv=None, qi=None,
+                ws=None) == WS
+    assert call(m._CProj(300, 250, 96, 4, 64, 64, 32, 8, 1e-6, 1)) == UNSUP  # hidden % 32
+    assert call(m._CProj(300, 256, 100, 4, 64, 64, 32, 8, 1e-6, 1)) == UNSUP  # q_lora % 32
+    assert call(m._CProj(300, 256, 96, 4, 64, 64, 32, 0, 1e-6, 1)) == SHAPE  # D_I without H_I
+    assert call(m._CProj(300, 256, 96, 4, 64, 64, 32, 8, -1.0, 1)) == SHAPE  # negative eps
+    assert call(m._CProj(0, 256, 96, 4, 64, 64, 32, 8, 1e-6, 1)) == SHAPE
+    assert call(m._CProj(300, 256, 96, 4, 64, 64, 32, 8, 1e-6, 2)) == SHAPE
+    assert call(P, x=ctypes.c_void_p(0x1008)) == UNSUP                      # not 16-byte aligned
+    assert call(P, ws=None) == WS
+    assert call(P, wsb=300 * 96 * 2 - 1) == WS
+    assert call(P, ws=ctypes.c_void_p(0x1010)) == WS

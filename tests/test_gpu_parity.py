@@ -522,3 +522,66 @@ def test_output_projection_full_size_sampled(csa):
     # the same rows drawn alone match the whole draw
     part = synth.oproj_inputs(T, H, D, G, R, hidden, seed=7, rows=rows)
     assert np.array_equal(part["x"], inp["x"][rows])
+
+
+# ----------------------------------------------------------------------------
+# producer projections
+
+def _proj_gpu(m, inp, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
+    import torch
+    bf = torch.bfloat16
+    shapes = {"q": (T, H, D), "kv": (T, D), "ckv": (T, comp), "cgate": (T, comp),
+              "ikv": (T, Di), "igate": (T, Di), "qi": (T, Hi, Di), "wi": (T, Hi)}
+    outs = {k: torch.full(v, float("nan"), dtype=bf, device="cuda") for k, v in shapes.items()
+            if (k in ("q", "kv")) or (k in ("ckv", "cgate") and comp) or
+            (k in ("ikv", "igate", "qi", "wi") and Di)}
+    need = m.load_library().csa_project_workspace_bytes(
+        m._CProj(T, hidden, q_lora, H, D, comp, Di, Hi, 1e-6, 1 if qn else 0))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    m.csa_project(dev(inp["x"]), dev(inp["w_x"]), dev(inp["g_qa"]), dev(inp["g_kv"]),
+                  dev(inp["w_q"]), outs, q_lora_rank=q_lora, num_heads=H, head_dim=D,
+                  comp_dim=comp, index_dim=Di, index_heads=Hi, eps=1e-6, q_head_norm=qn,
+                  workspace=ws)
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in outs.items()}
+    got["latent"] = host(ws.view(torch.bfloat16)[:T * q_lora].view(T, q_lora))
+    return got
+
+
+def _proj_check(got, ref, rows=None):
+    for k, g in got.items():
+        r = ref[k]
+        g = g if rows is None else g[rows]
+        assert np.isfinite(g).all(), k
+        assert_close(g, r.reshape(g.shape), "bf16", f"projection {k}")
+
+
+@pytest.mark.parametrize("T,hidden,q_lora,H,D,comp,Di,Hi,qn", [
+    (300, 256, 96, 4, 64, 64, 32, 8, True),      # ragged rows, every stream
+    (129, 128, 64, 2, 128, 0, 0, 0, False),      # sliding-only layer, no q_b_norm
+    (1, 64, 32, 3, 32, 32, 0, 0, True),          # one token, compressor without indexer
+])
+def test_project_small(csa, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
+    say(f"projections T={T} hidden={hidden} q_lora={q_lora} H={H} D={D} comp={comp} "
+        f"Di={Di} Hi={Hi} q_head_norm={qn}")
+    inp = synth.proj_inputs(T, hidden, q_lora, H, D, comp, Di, Hi, seed=9)
+    got = _proj_gpu(csa, inp, T, hidden, q_lora, H, D, comp, Di, Hi, qn)
+    ref = O.project_inputs(to_f64(inp["x"]), to_f64(inp["w_x"]), inp["g_qa"], inp["g_kv"],
+                           to_f64(inp["w_q"]), O.ProjSizes(q_lora, H, D, comp, Di, Hi), 1e-6,
+                           qn, "bf16")
+    _proj_check(got, ref)
+
+
+def test_project_full_size_sampled(csa):
+    s = synth.PROJ_SHAPE
+    args = (s["T"], s["hidden"], s["q_lora"], s["H"], s["D"], s["comp"], s["Di"], s["Hi"])
+    say(f"projections full size {s}, sampled rows")
+    inp = synth.proj_inputs(*args, seed=4)
+    got = _proj_gpu(csa, inp, *args, True)
+    T = s["T"]
+    rows = np.r_[0:2, 255:257, T - 2:T, np.random.default_rng(8).integers(0, T, 26)]
+    ref = O.project_inputs(to_f64(inp["x"][rows]), to_f64(inp["w_x"]), inp["g_qa"], inp["g_kv"],
+                           to_f64(inp["w_q"]),
+                           O.ProjSizes(s["q_lora"], s["H"], s["D"], s["comp"], s["Di"], s["Hi"]),
+                           1e-6, True, "bf16")
+    _proj_check(got, ref, rows)
