@@ -23,7 +23,9 @@ the same way (one step = every call of the layer(s) for one batch):
 * ``projections`` the producer projections of the same 8192 tokens (hidden
                    4096 -> query latent 1024, kv 512, compressor 2 x 512, indexer
                    2 x 128 + 64 head weights; latent -> 64 x 512 queries and 64 x
-                   128 indexer queries; the norms), priced in MFMA FLOPs.
+                   128 indexer queries; the norms), priced in MFMA FLOPs;
+* ``varlen_prefill`` a padded batch of four CSA sequences of 2048, 1536, 768
+                   and 256 valid tokens (padded to 2048), in valid tokens/s.
 
 Prefill steps are priced in MFMA FLOPs (4 H D per attended (query, row)
 pair, plus 2 H_I D_I per scored (query, key) pair); decode steps in the HBM
@@ -289,6 +291,38 @@ def oproj_leg(torch, m, steps, warmup):
             "achieved_TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, **s}
 
 
+VARLEN_LENS = (2048, 1536, 768, 256)
+
+
+def varlen_leg(torch, m, steps, warmup):
+    """A padded batch of four CSA sequences of different valid lengths (one
+    layer call each step, from position 0), priced in valid tokens."""
+    import synth
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    S, B = max(VARLEN_LENS), len(VARLEN_LENS)
+    w = synth.workload("csa_prefill", S=S, batch=B)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 0)
+    L = m.Layer.from_spec(spec)
+    keys = ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+    a = {k: _dev(torch, inp[k]) for k in keys}
+    sinks = _dev(torch, inp["sinks"])
+    cache = LayerCache(L, B, S, S // spec.ratio)
+    p0 = torch.zeros(B, dtype=torch.int64, device="cuda")
+    nv = torch.tensor(VARLEN_LENS, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(a["q"])
+    idx = torch.empty(B, S, spec.topk, dtype=torch.int32, device="cuda")
+    ms, _ = _time_steps(torch, lambda _ev: layer_step(
+        cache, p0, 0, *(a[k] for k in keys), sinks, out=out, topk_idx=idx, n_valid=nv), steps,
+        warmup)
+    valid = sum(VARLEN_LENS)
+    del a, cache, out, idx
+    return {"ms_per_step": ms, "valid_tokens_per_s": valid / (ms * 1e-3),
+            "lens": list(VARLEN_LENS), "padded_to": S,
+            "note": "padding rows are computed and left unspecified; the caches advance by "
+                    "the valid tokens"}
+
+
 def proj_leg(torch, m, steps, warmup):
     import synth
     s = synth.PROJ_SHAPE
@@ -352,6 +386,8 @@ def run_leg(torch, m, name, args):
         return oproj_leg(torch, m, args.steps, args.warmup)
     if name == "projections":
         return proj_leg(torch, m, args.steps, args.warmup)
+    if name == "varlen_prefill":
+        return varlen_leg(torch, m, args.steps, args.warmup)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -363,10 +399,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1)
     ap.add_argument("--legs",
-                    default="hca_prefill,csa_decode,mixed_decode,output_projection,projections",
+                    default="hca_prefill,csa_decode,mixed_decode,output_projection,projections,"
+                            "varlen_prefill",
                     help="comma list of further workloads to time after the headline "
                          "(hca_prefill, csa_decode, mixed_decode, output_projection, "
-                         "projections; empty for none)")
+                         "projections, varlen_prefill; empty for none)")
     ap.add_argument("--only", default="",
                     help="time just this one workload and print its object (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

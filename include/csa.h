@@ -105,6 +105,17 @@ typedef struct {
   const int64_t* pos0;      /* device [B]: position of each first new token    */
   int64_t pos0_max;         /* host: an upper bound of every pos0[b] (>= 0),
                                used to validate capacities                     */
+  const int32_t* n_valid;   /* device [B] or NULL: variable-length calls.
+                               Sequence b has n_valid[b] valid tokens (clamped
+                               to 0 .. n_new), the first ones of its n_new
+                               rows; the rest are padding.  csa_window_append
+                               and csa_compress advance the window ring, the
+                               pool and the compressor state by the valid
+                               tokens only (a later call continues at
+                               pos0[b] + n_valid[b]); the index and attention
+                               calls leave their outputs for padding rows
+                               unspecified (they read only in-bounds rows).
+                               NULL: every sequence has n_new tokens.        */
 } csa_batch;
 
 /* Write the window rows of the new tokens into a ring buffer.

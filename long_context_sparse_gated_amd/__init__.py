@@ -61,7 +61,8 @@ class _CProj(ctypes.Structure):
 
 class _CBatch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_new", ctypes.c_int32),
-                ("pos0", ctypes.c_void_p), ("pos0_max", ctypes.c_int64)]
+                ("pos0", ctypes.c_void_p), ("pos0_max", ctypes.c_int64),
+                ("n_valid", ctypes.c_void_p)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -193,12 +194,17 @@ def _store_dtype(layer: Layer):
     return torch.bfloat16 if layer.dtype == "bf16" else torch.float32
 
 
-def _batch(pos0, pos0_max, B, n):
+def _batch(pos0, pos0_max, B, n, n_valid=None):
     torch = _torch()
     _ptr(pos0, "pos0", torch.int64)
     if pos0.numel() != B:
         raise ValueError("pos0 must hold one position per sequence")
-    return _CBatch(B, n, pos0.data_ptr(), int(pos0_max))
+    nv = None
+    if n_valid is not None:
+        nv = _ptr(n_valid, "n_valid", torch.int32)
+        if n_valid.numel() != B:
+            raise ValueError("n_valid must hold one count per sequence")
+    return _CBatch(B, n, pos0.data_ptr(), int(pos0_max), nv)
 
 
 def _stream():
@@ -223,11 +229,12 @@ def _workspace(layer, B, n, pool_cap, op, ws, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def csa_window_append(layer: Layer, pos0, pos0_max: int, kv, ring):
-    """kv [B, n_new, D] -> ring [B, cap, D] at slot position % cap, rotated."""
+def csa_window_append(layer: Layer, pos0, pos0_max: int, kv, ring, n_valid=None):
+    """kv [B, n_new, D] -> ring [B, cap, D] at slot position % cap, rotated.
+    n_valid (int32 [B], optional): only the first n_valid[b] rows are appended."""
     dt = _store_dtype(layer)
     B, n, D = kv.shape
-    bt = _batch(pos0, pos0_max, B, n)
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
     lay = layer._c()
     _check(load_library().csa_window_append(
         ctypes.byref(lay), ctypes.byref(bt), _ptr(kv, "kv", dt), _ptr(ring, "ring", dt),
@@ -245,12 +252,13 @@ def csa_rope(layer: Layer, pos0, pos0_max: int, x, rope_dim: int, sign: int = 1)
 
 
 def csa_compress(layer: Layer, pos0, pos0_max: int, kv, gate, state_kv, state_gate, pool,
-                 rope_dim: int, norm_weight=None, norm_eps: float = 1e-6):
-    """kv, gate [B, n_new, width]; state_* [B, (1+overlap)m, width]; pool [B, cap, width]."""
+                 rope_dim: int, norm_weight=None, norm_eps: float = 1e-6, n_valid=None):
+    """kv, gate [B, n_new, width]; state_* [B, (1+overlap)m, width]; pool [B, cap, width].
+    n_valid (int32 [B], optional): only the first n_valid[b] rows are pooled and kept."""
     torch = _torch()
     dt = _store_dtype(layer)
     B, n, width = kv.shape
-    bt = _batch(pos0, pos0_max, B, n)
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
     lay = layer._c()
     _check(load_library().csa_compress(
         ctypes.byref(lay), ctypes.byref(bt), width, rope_dim, _ptr(kv, "kv", dt),

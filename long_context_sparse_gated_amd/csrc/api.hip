@@ -65,6 +65,7 @@ csa_status to_batch(const csa_batch* in, Batch* b) {
   b->n = in->n_new;
   b->pos0 = in->pos0;
   b->pos0_max = in->pos0_max;
+  b->nvalid = in->n_valid;
   return CSA_OK;
 }
 

@@ -107,15 +107,17 @@ template <typename T>
 __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, int n_new, int width, int R, Rope base, int m,
-    int overlap, int64_t pool_cap) {
+    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int n_new, int width,
+    int R, Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double pa[kCmpT][2], pb[kCmpT][2];
   __shared__ double red[kCmpT / 64];
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
   const int64_t w = p0 / m + blockIdx.x;
-  if (w >= (p0 + n_new) / m || w >= pool_cap) return;  // block-uniform
+  // entries that close within the sequence's valid tokens
+  const int nl = valid_tokens(nvalid, b, n_new);
+  if (w >= (p0 + nl) / m || w >= pool_cap) return;  // block-uniform
   const int Ls = (1 + overlap) * m, tid = threadIdx.x;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
   const T* kv_b = kv + (int64_t)b * n_new * width;
@@ -232,11 +234,12 @@ template <typename T>
 __global__ void __launch_bounds__(256) compress_one_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, int width, int R, Rope base, int m, int overlap,
-    int64_t pool_cap) {
+    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int width, int R,
+    Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];
   const int b = blockIdx.x;
+  if (valid_tokens(nvalid, b, 1) == 0) return;  // a padding token: nothing to record
   const int64_t p0 = pos0[b];
   const int Ls = (1 + overlap) * m;
   const int64_t w = p0 / m;
@@ -262,10 +265,12 @@ __global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__
                                                            T* __restrict__ st_kv,
                                                            T* __restrict__ st_gate,
                                                            const int64_t* __restrict__ pos0,
+                                                           const int32_t* __restrict__ nvalid,
                                                            int n_new, int width, int Ls) {
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
-  const int64_t s = p0 + n_new - Ls + blockIdx.x;
+  // the last Ls valid positions (padding rows are never kept)
+  const int64_t s = p0 + valid_tokens(nvalid, b, n_new) - Ls + blockIdx.x;
   if (s < p0) return;
   const T* src_kv = kv + ((int64_t)b * n_new + (s - p0)) * width;
   const T* src_g = gate + ((int64_t)b * n_new + (s - p0)) * width;
@@ -288,29 +293,29 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
     if (L.dtype == 1)
       compress_one_kernel<bf16_t><<<bt.B, 256, 0, s>>>(
           (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (bf16_t*)st_kv, (bf16_t*)st_gate,
-          (bf16_t*)pool, bt.pos0, width, rope_dim, L.base, m, L.overlap, pool_cap);
+          (bf16_t*)pool, bt.pos0, bt.nvalid, width, rope_dim, L.base, m, L.overlap, pool_cap);
     else
       compress_one_kernel<float><<<bt.B, 256, 0, s>>>(
           (const float*)kv, (const float*)gate, norm_w, eps, (float*)st_kv, (float*)st_gate,
-          (float*)pool, bt.pos0, width, rope_dim, L.base, m, L.overlap, pool_cap);
+          (float*)pool, bt.pos0, bt.nvalid, width, rope_dim, L.base, m, L.overlap, pool_cap);
     return hipGetLastError();
   }
   if (L.dtype == 1) {
     compress_entry_kernel<bf16_t><<<g1, kCmpT, 0, s>>>(
         (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
-        (const bf16_t*)st_gate, (bf16_t*)pool, bt.pos0, bt.n, width, rope_dim, L.base, m,
-        L.overlap, pool_cap);
+        (const bf16_t*)st_gate, (bf16_t*)pool, bt.pos0, bt.nvalid, bt.n, width, rope_dim, L.base,
+        m, L.overlap, pool_cap);
     state_update_kernel<bf16_t><<<g2, 256, 0, s>>>((const bf16_t*)kv, (const bf16_t*)gate,
                                                    (bf16_t*)st_kv, (bf16_t*)st_gate, bt.pos0,
-                                                   bt.n, width, Ls);
+                                                   bt.nvalid, bt.n, width, Ls);
   } else {
     compress_entry_kernel<float><<<g1, kCmpT, 0, s>>>((const float*)kv, (const float*)gate, norm_w, eps,
                                               (const float*)st_kv, (const float*)st_gate,
-                                              (float*)pool, bt.pos0, bt.n, width, rope_dim,
-                                              L.base, m, L.overlap, pool_cap);
+                                              (float*)pool, bt.pos0, bt.nvalid, bt.n, width,
+                                              rope_dim, L.base, m, L.overlap, pool_cap);
     state_update_kernel<float><<<g2, 256, 0, s>>>((const float*)kv, (const float*)gate,
-                                                  (float*)st_kv, (float*)st_gate, bt.pos0, bt.n,
-                                                  width, Ls);
+                                                  (float*)st_kv, (float*)st_gate, bt.pos0,
+                                                  bt.nvalid, bt.n, width, Ls);
   }
   return hipGetLastError();
 }

@@ -38,7 +38,15 @@ struct Batch {
   int B, n;             // sequences, new tokens per sequence
   const int64_t* pos0;  // device [B]
   int64_t pos0_max;     // host bound
+  const int32_t* nvalid;  // device [B] valid tokens per sequence, or null (all n)
 };
+
+// Valid tokens of sequence b in a call of n per sequence.
+__device__ __forceinline__ int valid_tokens(const int32_t* nvalid, int b, int n) {
+  if (!nvalid) return n;
+  const int v = nvalid[b];
+  return v < 0 ? 0 : (v > n ? n : v);
+}
 
 // oproj.hip
 // Column routing of a GEMM's output: columns col0[s] .. col0[s + 1] - 1

@@ -20,11 +20,14 @@ template <typename T>
 __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict__ kv,
                                                             T* __restrict__ ring,
                                                             const int64_t* __restrict__ pos0,
+                                                            const int32_t* __restrict__ nvalid,
                                                             int n_new, int D, int R, Rope base,
                                                             int64_t cap) {
   extern __shared__ double freq[];  // R / 2 pair frequencies
   const int i0 = blockIdx.x * kWaTok, b = blockIdx.y;
-  const int nt = min(kWaTok, n_new - i0);
+  // padding tokens of a variable-length call are not appended
+  const int nt = min(kWaTok, valid_tokens(nvalid, b, n_new) - i0);
+  if (nt <= 0) return;  // block-uniform
   const int64_t p0 = pos0[b];
   for (int j = threadIdx.x; j < R / 2; j += blockDim.x) freq[j] = rope_freq(base, j, R);
   const int plain = D - R;  // channels copied unchanged
@@ -90,10 +93,11 @@ hipError_t launch_window_append(const Layer& L, const Batch& bt, const void* kv,
   const size_t shm = (size_t)(L.R / 2) * sizeof(double);
   if (L.dtype == 1)
     window_append_kernel<bf16_t><<<grid, 256, shm, s>>>((const bf16_t*)kv, (bf16_t*)ring,
-                                                        bt.pos0, bt.n, L.D, L.R, L.base, cap);
+                                                        bt.pos0, bt.nvalid, bt.n, L.D, L.R, L.base,
+                                                        cap);
   else
     window_append_kernel<float><<<grid, 256, shm, s>>>((const float*)kv, (float*)ring, bt.pos0,
-                                                       bt.n, L.D, L.R, L.base, cap);
+                                                       bt.nvalid, bt.n, L.D, L.R, L.base, cap);
   return hipGetLastError();
 }
 

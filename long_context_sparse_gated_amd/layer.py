@@ -56,29 +56,32 @@ class LayerCache:
 
 def layer_step(cache: LayerCache, pos0, pos0_max: int, q, kv, ckv=None, cgate=None, ikv=None,
                igate=None, qi=None, wi=None, sinks=None, out=None, topk_idx=None,
-               norm_weight=None, inorm_weight=None, norm_eps: float = 1e-6):
+               norm_weight=None, inorm_weight=None, norm_eps: float = 1e-6, n_valid=None):
     """One call of the layer for q [B,n,H,D] and the new tokens' streams.
 
-    Returns (out [B,n,H,D], topk_idx [B,n,k] or None).
+    n_valid (int32 [B] on the device, optional) makes it a variable-length
+    call: sequence b has n_valid[b] valid tokens, the first of its n rows; the
+    caches advance by those only and the output rows of the padding are
+    unspecified.  Returns (out [B,n,H,D], topk_idx [B,n,k] or None).
     """
     import torch
     L = cache.layer
     B, n = q.shape[:2]
     if out is None:
         out = torch.empty_like(q)
-    csa_window_append(L, pos0, pos0_max, kv, cache.ring)
+    csa_window_append(L, pos0, pos0_max, kv, cache.ring, n_valid)
     if L.compress_ratio == 0:
         hca_attend(L, pos0, pos0_max, q, cache.ring, None, sinks, out,
                    cache.workspace(n, CSA_OP_HCA_ATTEND))
         return out, None
     csa_compress(L, pos0, pos0_max, ckv, cgate, cache.cstate_kv, cache.cstate_gate, cache.pool,
-                 L.qk_rope_head_dim, norm_weight, norm_eps)
+                 L.qk_rope_head_dim, norm_weight, norm_eps, n_valid)
     if L.index_topk == 0:
         hca_attend(L, pos0, pos0_max, q, cache.ring, cache.pool, sinks, out,
                    cache.workspace(n, CSA_OP_HCA_ATTEND))
         return out, None
     csa_compress(L, pos0, pos0_max, ikv, igate, cache.istate_kv, cache.istate_gate, cache.ipool,
-                 L.index_rope_dim, inorm_weight, norm_eps)
+                 L.index_rope_dim, inorm_weight, norm_eps, n_valid)
     if topk_idx is None:
         topk_idx = torch.empty(B, n, L.index_topk, dtype=torch.int32, device=q.device)
     csa_index_topk(L, pos0, pos0_max, qi, wi, cache.ipool, topk_idx,

@@ -225,7 +225,7 @@ def test_sliding_prefill_bf16(csa):
     _check_dense_prefill(csa, "sliding", 700, 2, [0, 1, 64, 127, 128, 129, 699])
 
 
-def _decode_case(m, name, pos0, batch, seed, layers=None):
+def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
     """One decode step at pos0 for every sequence and layer, against the oracle."""
     import torch
     from long_context_sparse_gated_amd.layer import LayerCache, layer_step
@@ -251,11 +251,24 @@ def _decode_case(m, name, pos0, batch, seed, layers=None):
         p0 = torch.full((batch,), pos0, dtype=torch.int64, device="cuda")
         a = {k: dev(inp[k]) for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
              if k in inp}
+        nvd = None if valid is None else torch.tensor(valid, dtype=torch.int32, device="cuda")
         out, idx = layer_step(cache, p0, pos0, a["q"], a["kv"], a.get("ckv"), a.get("cgate"),
                               a.get("ikv"), a.get("igate"), a.get("qi"), a.get("wi"),
-                              dev(inp["sinks"]))
+                              dev(inp["sinks"]), n_valid=nvd)
         torch.cuda.synchronize()
         for b in range(batch):
+            if valid is not None and valid[b] == 0:
+                # a padding token: every cache of the sequence is as it was
+                assert torch.equal(cache.ring[b], dev(inp["win"])[b]), f"seq {b}: ring"
+                if spec.ratio:
+                    P = pos0 // spec.ratio
+                    assert torch.equal(cache.pool[b, :P], dev(inp["pool"])[b]), f"seq {b}: pool"
+                    assert not cache.pool[b, P:].any(), f"seq {b}: no new entry"
+                    assert torch.equal(cache.cstate_kv[b], dev(inp["cstate_kv"])[b])
+                    if spec.has_indexer:
+                        assert torch.equal(cache.istate_gate[b], dev(inp["istate_gate"])[b])
+                        assert not cache.ipool[b, P:].any(), f"seq {b}: no new key"
+                continue
             new = {k: (to_f64(inp[k]) if k == "sinks" else to_f64(inp[k][b, 0]))
                    for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi", "sinks")
                    if k in inp}
@@ -296,6 +309,13 @@ def test_csa_decode_small(csa):
 def test_csa_decode_entry_closes(csa):
     say("case: csa decode B=2 pos0=4099 (entry closes at t)")
     _decode_case(csa, "csa_decode", 4099, 2, 1)
+
+
+def test_varlen_decode_step_skips_padding(csa):
+    """A one-token call where some sequences have no token: their caches stay
+    as they were, the others match the oracle (an entry closes at 4099)."""
+    say("case: varlen decode csa_decode pos0=4099 B=4 valid (1, 0, 1, 0)")
+    _decode_case(csa, "csa_decode", 4099, 4, 7, valid=(1, 0, 1, 0))
 
 
 def test_csa_decode_b20_head_group_path(csa):
@@ -585,3 +605,69 @@ def test_project_full_size_sampled(csa):
                            O.ProjSizes(s["q_lora"], s["H"], s["D"], s["comp"], s["Di"], s["Hi"]),
                            1e-6, True, "bf16")
     _proj_check(got, ref, rows)
+
+
+# ----------------------------------------------------------------------------
+# variable-length batched prefill
+
+def test_varlen_prefill_matches_separate_calls(csa):
+    """A padded batch with per-sequence valid lengths (700, 413, 0): the caches
+    advance by the valid tokens only.  Valid rows, top-k ids and caches equal
+    each sequence run alone (ids and caches bitwise); a second, full call then
+    equals a one-shot run over each sequence's concatenated tokens; one
+    sequence is also held against the oracle."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    say("case: varlen prefill, csa bf16, B=3, n_new=700, lens (700, 413, 0), then 300 more")
+    m = csa
+    S, S2, lens = 700, 300, (700, 413, 0)
+    w = synth.workload("csa_prefill", S=S, batch=3)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 11)
+    inp2 = synth.prefill_inputs(synth.workload("csa_prefill", S=S2, batch=3), 12)
+    L = m.Layer.from_spec(spec)
+    cap, pcap = S + S2, (S + S2) // 4
+    keys = ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+    a = {k: dev(inp[k]) for k in keys}
+    a2 = {k: dev(inp2[k]) for k in keys}
+    sinks = dev(inp["sinks"])
+    cache = LayerCache(L, 3, cap, pcap)
+    p0 = torch.zeros(3, dtype=torch.int64, device="cuda")
+    nv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, idx = layer_step(cache, p0, 0, *(a[k] for k in keys), sinks, n_valid=nv)
+    torch.cuda.synchronize()
+    out, idx = out.clone(), idx.clone()
+    # an empty sequence leaves its caches untouched (they start at zero)
+    assert not cache.ring[2].any() and not cache.pool[2].any() and not cache.ipool[2].any()
+    assert not cache.cstate_kv[2].any() and not cache.istate_kv[2].any()
+    # second call: every sequence continues with 300 valid tokens
+    p1 = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    out2, idx2 = layer_step(cache, p1, max(lens), *(a2[k] for k in keys), sinks)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        # the sequence alone: its valid tokens, then the same 300
+        one = LayerCache(L, 1, cap, pcap)
+        z = torch.zeros(1, dtype=torch.int64, device="cuda")
+        cat = {k: torch.cat([a[k][b:b + 1, :n], a2[k][b:b + 1]], 1).contiguous() for k in keys}
+        o1, i1 = layer_step(one, z, 0, *(cat[k] for k in keys), sinks)
+        torch.cuda.synchronize()
+        if n:
+            assert torch.equal(idx[b, :n], i1[0, :n]), f"sequence {b}: first-call ids"
+            assert_close(host(out[b, :n]), host(o1[0, :n]), "bf16", f"sequence {b} first call")
+        assert torch.equal(idx2[b], i1[0, n:]), f"sequence {b}: second-call ids"
+        assert_close(host(out2[b]), host(o1[0, n:]), "bf16", f"sequence {b} second call")
+        ne = (n + S2) // 4
+        assert torch.equal(cache.pool[b, :ne], one.pool[0, :ne]), f"sequence {b}: pool"
+        assert torch.equal(cache.ipool[b, :ne], one.ipool[0, :ne]), f"sequence {b}: indexer pool"
+        assert torch.equal(cache.ring[b], one.ring[0]), f"sequence {b}: window ring"
+        assert torch.equal(cache.cstate_kv[b], one.cstate_kv[0]), f"sequence {b}: state"
+        assert torch.equal(cache.istate_gate[b], one.istate_gate[0]), f"sequence {b}: state"
+    # the 413-token sequence against the oracle on sampled queries
+    x = seq_f64(inp, 1)
+    x = {k: (v if k == "sinks" else v[:lens[1]]) for k, v in x.items()}
+    qs = [0, 3, 4, 130, 255, 300, 411, 412]
+    ref = O.csa_prefill(spec, x, queries=qs)
+    gi = idx[1].cpu().numpy()
+    same = [j for j, t in enumerate(qs) if np.array_equal(gi[t], ref["idx"][j])]
+    assert len(same) >= len(qs) - 1, "ids differ beyond a near tie"
+    assert_close(host(out[1])[qs][same], ref["out"][same], "bf16", "varlen rows vs oracle")
