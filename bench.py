@@ -319,8 +319,8 @@ def varlen_leg(torch, m, steps, warmup):
     del a, cache, out, idx
     return {"ms_per_step": ms, "valid_tokens_per_s": valid / (ms * 1e-3),
             "lens": list(VARLEN_LENS), "padded_to": S,
-            "note": "padding rows are computed and left unspecified; the caches advance by "
-                    "the valid tokens"}
+            "note": "the prefill scoring, selection and attention kernels skip padding rows "
+                    "(left unspecified); the caches advance by the valid tokens"}
 
 
 def proj_leg(torch, m, steps, warmup):

@@ -268,12 +268,12 @@ def csa_compress(layer: Layer, pos0, pos0_max: int, kv, gate, state_kv, state_ga
 
 
 def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,
-                   scores_out=None, workspace=None):
+                   scores_out=None, workspace=None, n_valid=None):
     """q_idx [B,n,H_I,D_I], weights [B,n,H_I], k_pool [B,cap,D_I] -> topk_idx [B,n,k] int32."""
     torch = _torch()
     dt = _store_dtype(layer)
     B, n = q_idx.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n)
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
     ws, wsb = _workspace(layer, B, n, k_pool.shape[1], CSA_OP_INDEX_TOPK, workspace, q_idx.device)
     lay = layer._c()
     _check(load_library().csa_index_topk(
@@ -284,12 +284,12 @@ def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, to
 
 
 def csa_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, topk_idx, sinks, out,
-               workspace=None):
+               workspace=None, n_valid=None):
     """q [B,n,H,D], win [B,cap,D], pool [B,pcap,D], topk_idx [B,n,k], sinks [H] -> out."""
     torch = _torch()
     dt = _store_dtype(layer)
     B, n = q.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n)
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
     ws, wsb = _workspace(layer, B, n, pool.shape[1], CSA_OP_ATTEND, workspace, q.device)
     lay = layer._c()
     _check(load_library().csa_attend(
@@ -299,12 +299,13 @@ def csa_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, topk_idx, sinks,
         _stream()), "csa_attend")
 
 
-def hca_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, sinks, out, workspace=None):
+def hca_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, sinks, out, workspace=None,
+               n_valid=None):
     """As csa_attend with every visible entry (compress_ratio 0: window only; pool may be None)."""
     torch = _torch()
     dt = _store_dtype(layer)
     B, n = q.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n)
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
     pcap = pool.shape[1] if pool is not None else 0
     ws, wsb = _workspace(layer, B, n, pcap, CSA_OP_HCA_ATTEND, workspace, q.device)
     lay = layer._c()

@@ -93,8 +93,8 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, int n_new, int W, int m, Rope base, float scale,
-    int nsplit, int csa) {
+    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int n_new, int W,
+    int m, Rope base, float scale, int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   // two separate arrays (not one indexed by parity) so the compiler can tell
   // the DMA target from the tile being read and need not wait for the DMA
@@ -111,6 +111,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   constexpr int RPW = kCH / 4;  // rows each wave gathers per chunk
   const int i = n_new - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y, split = blockIdx.z;
+  if (i >= valid_tokens(nvalid, b, n_new)) return;  // a padding row: left as it is
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int64_t t = pos0[b] + i;
   const int64_t tok = (int64_t)b * n_new + i;
@@ -847,7 +848,8 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
 #define CSA_ATTN_LAUNCH(RR)                                                                 \
   attend_mfma<RR><<<grid, 256, 0, s>>>(                                                     \
       (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k, \
-      sinks, (bf16_t*)out, (float*)ws, bt.pos0, bt.n, L.W, m, L.base, L.scale, ns, csa ? 1 : 0)
+      sinks, (bf16_t*)out, (float*)ws, bt.pos0, bt.nvalid, bt.n, L.W, m, L.base, L.scale, ns, \
+      csa ? 1 : 0)
     switch (L.R) {
       case 16: CSA_ATTN_LAUNCH(16); break;
       case 32: CSA_ATTN_LAUNCH(32); break;

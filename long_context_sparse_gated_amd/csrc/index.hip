@@ -264,7 +264,7 @@ template <int RI>
 __global__ void __launch_bounds__(256, 2) index_prefill_x32(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
     float* __restrict__ scores, float* __restrict__ discard, const int64_t* __restrict__ pos0,
-    int n_new, int B, Rope base, int m, int64_t pool_cap) {
+    const int32_t* __restrict__ nvalid, int n_new, int B, Rope base, int m, int64_t pool_cap) {
   constexpr int Hi = 64, Di = 128, kFirst = Di - RI, kK0 = kFirst / 16;
   static_assert(RI > 0 && RI <= Di && RI % 16 == 0, "rope channels: whole 16-channel steps");
   __shared__ __attribute__((aligned(1024))) bf16_t kt0[kX32KT * Di];
@@ -278,6 +278,9 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t p0 = pos0[b];
   const int nq = min(kX32Q, n_new - i0);
+  // padding queries (a suffix of the sequence's rows) are not scored; a block
+  // whose first query is padding has no other
+  if (i0 >= valid_tokens(nvalid, b, n_new)) return;  // block-uniform
   int64_t nv_last = (p0 + i0 + nq) / m;  // the block's last query sees the most keys
   if (nv_last > pool_cap) nv_last = pool_cap;
   const int nkeys = (int)nv_last;
@@ -1427,13 +1430,16 @@ constexpr int kTkPer = 32;
 
 __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ scores, int64_t stride,
                                                  int32_t* __restrict__ out,
-                                                 const int64_t* __restrict__ pos0, int n_new,
+                                                 const int64_t* __restrict__ pos0,
+                                                 const int32_t* __restrict__ nvalid, int n_new,
                                                  int m, int k, int64_t pool_cap) {
   __shared__ uint32_t hist_all[4][4][256];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x * 4 + wv, b = blockIdx.y;
-  if (i >= n_new) return;  // wave-uniform; the waves never meet at a barrier
+  // wave-uniform (padding rows are left as they are); the waves never meet
+  // at a barrier
+  if (i >= valid_tokens(nvalid, b, n_new)) return;
   uint32_t (*hist)[256] = hist_all[wv];
   const int64_t tok = (int64_t)b * n_new + i;
   int64_t nv = (pos0[b] + i + 1) / m;
@@ -1621,8 +1627,8 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
     const unsigned nblk = (unsigned)((bt.n + kX32Q - 1) / kX32Q);
     index_prefill_x32<64><<<nblk * bt.B, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
                                                       (const bf16_t*)keys, scores, (float*)wsp,
-                                                      bt.pos0, bt.n, bt.B, L.base, L.m,
-                                                      pool_cap);
+                                                      bt.pos0, bt.nvalid, bt.n, bt.B, L.base,
+                                                      L.m, pool_cap);
   } else if (index_fast_shape(L)) {
     dim3 grid((bt.n + kIdxQPB - 1) / kIdxQPB, bt.B);
     index_prefill_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
@@ -1644,7 +1650,8 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
   if (e != hipSuccess) return e;
   if ((bt.pos0_max + bt.n) / L.m <= 64 * kTkPer) {  // every row fits in one wave's registers
     dim3 gw((bt.n + 3) / 4, bt.B);
-    topk_wave<<<gw, 256, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.n, L.m, L.k, pool_cap);
+    topk_wave<<<gw, 256, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.nvalid, bt.n, L.m, L.k,
+                                 pool_cap);
     return hipGetLastError();
   }
   dim3 grid(bt.n, bt.B);

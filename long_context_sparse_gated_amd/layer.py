@@ -72,20 +72,20 @@ def layer_step(cache: LayerCache, pos0, pos0_max: int, q, kv, ckv=None, cgate=No
     csa_window_append(L, pos0, pos0_max, kv, cache.ring, n_valid)
     if L.compress_ratio == 0:
         hca_attend(L, pos0, pos0_max, q, cache.ring, None, sinks, out,
-                   cache.workspace(n, CSA_OP_HCA_ATTEND))
+                   cache.workspace(n, CSA_OP_HCA_ATTEND), n_valid=n_valid)
         return out, None
     csa_compress(L, pos0, pos0_max, ckv, cgate, cache.cstate_kv, cache.cstate_gate, cache.pool,
                  L.qk_rope_head_dim, norm_weight, norm_eps, n_valid)
     if L.index_topk == 0:
         hca_attend(L, pos0, pos0_max, q, cache.ring, cache.pool, sinks, out,
-                   cache.workspace(n, CSA_OP_HCA_ATTEND))
+                   cache.workspace(n, CSA_OP_HCA_ATTEND), n_valid=n_valid)
         return out, None
     csa_compress(L, pos0, pos0_max, ikv, igate, cache.istate_kv, cache.istate_gate, cache.ipool,
                  L.index_rope_dim, inorm_weight, norm_eps, n_valid)
     if topk_idx is None:
         topk_idx = torch.empty(B, n, L.index_topk, dtype=torch.int32, device=q.device)
     csa_index_topk(L, pos0, pos0_max, qi, wi, cache.ipool, topk_idx,
-                   workspace=cache.workspace(n, CSA_OP_INDEX_TOPK))
+                   workspace=cache.workspace(n, CSA_OP_INDEX_TOPK), n_valid=n_valid)
     csa_attend(L, pos0, pos0_max, q, cache.ring, cache.pool, topk_idx, sinks, out,
-               cache.workspace(n, CSA_OP_ATTEND))
+               cache.workspace(n, CSA_OP_ATTEND), n_valid=n_valid)
     return out, topk_idx
