@@ -192,28 +192,64 @@ __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
   }
   if (kt < nk) stage(kt, fa0, fb0, fa1, fb1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // register v of tile (mt, nt): row 8 (v / 4) + 4 h32 + v % 4, column l32
+  // Epilogue through LDS (free once every wave is past its last reads): each
+  // wave writes its 128 x 128 part as bf16 rows of 256 bytes into its own
+  // 32 KB, then reads 16-byte pieces back, 16 lanes per row, and stores them
+  // (four 256-byte row pieces per instruction instead of two 64-byte ones
+  // per 2-byte store).  Register v of tile (mt, nt) is row
+  // 8 (v / 4) + 4 h32 + v % 4, column l32.
+  __syncthreads();
+  bf16_t* st = (bf16_t*)&lds[0][0][0] + (size_t)wv * 128 * 128;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int col = n0 + 128 * wn + 32 * nt + l32;
-      bf16_t* cp = C + col;
-      int64_t cld = ldc;
-      if (kRouted) {
-        int sg = 0;
-#pragma unroll
-        for (int q = 1; q < kGemmOutMax; ++q)
-          if (q < map.nseg && map.col0[q] <= col) sg = q;
-        cp = map.ptr[sg] + (col - map.col0[sg]);
-        cld = map.ld[sg];
-      }
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + 128 * wm + 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
-        if (row < M && col < N) cp[(int64_t)row * cld] = f32_to_bf16(acc[mt][nt][v]);
+        const int r = 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
+        st[r * 128 + 32 * nt + l32] = f32_to_bf16(acc[mt][nt][v]);
+      }
+  const int rbase = m0 + 128 * wm, cbase = n0 + 128 * wn;
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    const int qd = lane + 64 * j, r = qd >> 4, c8 = (qd & 15) * 8;
+    const uint4 v = *(const uint4*)(st + r * 128 + c8);
+    const int row = rbase + r, col = cbase + c8;
+    if (row >= M || col >= N) continue;
+    bf16_t* cp = C + col;
+    int64_t cld = ldc;
+    int cend = N;  // first column past this output
+    if (kRouted) {
+      int sg = 0;
+#pragma unroll
+      for (int q = 1; q < kGemmOutMax; ++q)
+        if (q < map.nseg && map.col0[q] <= col) sg = q;
+      cp = map.ptr[sg] + (col - map.col0[sg]);
+      cld = map.ld[sg];
+      if (sg + 1 < map.nseg) cend = min(cend, map.col0[sg + 1]);
+    }
+    bf16_t* dst = cp + (int64_t)row * cld;
+    if (col + 7 < cend && ((uintptr_t)dst & 15u) == 0) {
+      *(uint4*)dst = v;
+    } else {
+      // edge of the matrix, of an output, or an unaligned row: one value at
+      // a time, each routed on its own
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ce = col + e;
+        if (ce >= N) break;
+        bf16_t* de = C + (int64_t)row * ldc + ce;
+        if (kRouted) {
+          int sg = 0;
+          for (int q = 1; q < map.nseg; ++q)
+            if (map.col0[q] <= ce) sg = q;
+          de = map.ptr[sg] + (int64_t)row * map.ld[sg] + (ce - map.col0[sg]);
+        }
+        *de = (bf16_t)(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
+  }
 }
 
 hipError_t launch_gemm_nt(const bf16_t* A, const bf16_t* B, bf16_t* C, int M, int N, int K,

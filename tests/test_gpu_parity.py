@@ -580,6 +580,7 @@ def _proj_check(got, ref, rows=None):
     (300, 256, 96, 4, 64, 64, 32, 8, True),      # ragged rows, every stream
     (129, 128, 64, 2, 128, 0, 0, 0, False),      # sliding-only layer, no q_b_norm
     (1, 64, 32, 3, 32, 32, 0, 0, True),          # one token, compressor without indexer
+    (77, 96, 32, 2, 36, 20, 12, 4, True),        # stream widths off 8-column pieces
 ])
 def test_project_small(csa, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
     say(f"projections T={T} hidden={hidden} q_lora={q_lora} H={H} D={D} comp={comp} "
