@@ -1086,8 +1086,9 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
   }
 }
 
-// Exclusive prefix sum of one value per thread over a 256-thread block.
-__device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* wsum, uint32_t& total) {
+// Exclusive prefix sum of one value per thread over a block of NW waves.
+template <int NW>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -1100,12 +1101,53 @@ __device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* wsum, ui
   uint32_t before = x - v;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wv) before += wsum[w];
     total += wsum[w];
   }
   __syncthreads();
   return before;
+}
+
+// hist_cut for a 1024-thread block: res[0] = the bin holding the k-th best
+// key of histogram h, res[1] = the number of keys in the bins above it.
+__device__ void hist_cut1024(const uint32_t* __restrict__ h, uint32_t k, uint32_t* wsum,
+                             uint32_t* res) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int per = kHBins / 1024;
+  if (tid == 0) {
+    res[0] = 0u;
+    res[1] = 0u;
+  }
+  uint32_t c[per], s = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    c[e] = h[kHBins - 1 - per * tid - e];  // thread 0 holds the top bins
+    s += c[e];
+  }
+  uint32_t x = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  uint32_t before = x - s;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  if (before < k && before + s >= k) {
+    uint32_t acc = before;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+      if (acc + c[e] >= k) {
+        res[0] = (uint32_t)(kHBins - 1 - per * tid - e);
+        res[1] = acc;
+        break;
+      }
+      acc += c[e];
+    }
+  }
+  __syncthreads();
 }
 
 // Decode selection in one launch for rows of at most kBlkTopK keys: one
@@ -1119,16 +1161,18 @@ __device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* wsum, ui
 // branches).  A radix select on the low 20 bits settles bin T among the
 // candidates (scores re-read from L2 by id), and an ordered pass over the
 // candidates emits the k ids ascending, ties to the lower id.
-constexpr int kBlkTopKU = 128;
-constexpr int kBlkTopK = 256 * kBlkTopKU;
+constexpr int kBlkTopKT = 1024;  // threads: four waves per SIMD hide VALU latency
+constexpr int kBlkTopKU = 32;    // scores per thread
+constexpr int kBlkTopK = kBlkTopKT * kBlkTopKU;
 
-__global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scores,
+__global__ void __launch_bounds__(kBlkTopKT) topk_block(const float* __restrict__ scores,
                                                   const uint32_t* __restrict__ hist,
                                                   int32_t* __restrict__ out,
                                                   const int64_t* __restrict__ pos0, int n_new,
                                                   int m, int k, int64_t pool_cap) {
   __shared__ int32_t cand[kBlkTopK + 64];  // candidate ids in id order (+ a spare per lane)
-  __shared__ uint32_t wsum[4], wcnt[4], res[2], bins[256], sh_prefix, sh_rem;
+  __shared__ uint32_t wsum[kBlkTopKT / 64], wcnt[kBlkTopKT / 64], res[2], bins[256], sh_prefix,
+      sh_rem;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tok = blockIdx.x;
   const int b = tok / n_new, i = tok % n_new;
@@ -1136,7 +1180,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
   if (nv > pool_cap) nv = pool_cap;
   int32_t* o = out + (int64_t)tok * k;
   if (nv <= k) {
-    for (int j = tid; j < k; j += 256) o[j] = j < nv ? j : -1;
+    for (int j = tid; j < k; j += kBlkTopKT) o[j] = j < nv ? j : -1;
     return;
   }
   constexpr int U = kBlkTopKU;
@@ -1160,7 +1204,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
 #pragma unroll
     for (int u = 0; u < U; ++u) x[u] = u < nval ? sc[u] : __uint_as_float(0x7fc00000u);
   }
-  hist_cut(hist + (int64_t)tok * kHBins, (uint32_t)k, wsum, res);
+  hist_cut1024(hist + (int64_t)tok * kHBins, (uint32_t)k, wsum, res);
   const uint32_t T = res[0];
   const uint32_t A = res[1];  // keys in the bins above T: all selected
   // smallest float whose order key lies in bin T (order keys are monotonic
@@ -1181,7 +1225,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
 #pragma unroll
   for (int w = 0; w < U / 32; ++w) nc += (uint32_t)__popc(cw[w]);
   uint32_t N;
-  uint32_t pos = block_scan256(nc, wsum, N);
+  uint32_t pos = block_scan<kBlkTopKT / 64>(nc, wsum, N);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t c = (cw[u >> 5] >> (u & 31)) & 1u;
@@ -1198,9 +1242,9 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? kHShift - 8 : (pass == 1 ? kHShift - 16 : 0);
     const uint32_t nb = pass == 2 ? (1u << (kHShift - 16)) : 256u;
-    bins[tid] = 0u;
+    if (tid < 256) bins[tid] = 0u;
     __syncthreads();
-    for (uint32_t e = tid; e < N; e += 256) {
+    for (uint32_t e = tid; e < N; e += kBlkTopKT) {
       const uint32_t key = key_of(e);
       if ((key >> kHShift) == T && ((key & kLow) & mask) == prefix)
         atomicAdd(&bins[((key & kLow) >> shift) & (nb - 1u)], 1u);
@@ -1240,7 +1284,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
   const uint32_t tk = tkey | prefix;
   const unsigned long long lt = (1ull << lane) - 1ull;
   uint32_t base_sel = 0, base_eq = 0;
-  for (uint32_t e0 = 0; e0 < N; e0 += 256) {
+  for (uint32_t e0 = 0; e0 < N; e0 += kBlkTopKT) {
     const uint32_t e = e0 + tid;
     const uint32_t key = e < N ? key_of(e) : 0u;
     const bool gt = e < N && key > tk, eq = e < N && key == tk;
@@ -1248,7 +1292,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
     if (lane == 0) wcnt[wv] = (uint32_t)__popcll(be);
     __syncthreads();
     uint32_t eq_off = base_eq, eq_tot = 0;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kBlkTopKT / 64; ++w) {
       if (w < wv) eq_off += wcnt[w];
       eq_tot += wcnt[w];
     }
@@ -1257,7 +1301,7 @@ __global__ void __launch_bounds__(256) topk_block(const float* __restrict__ scor
     if (lane == 0) wsum[wv] = (uint32_t)__popcll(bs);
     __syncthreads();
     uint32_t off = base_sel, tot = 0;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kBlkTopKT / 64; ++w) {
       if (w < wv) off += wsum[w];
       tot += wsum[w];
     }
@@ -1611,7 +1655,8 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
                                              bt.n, L.m, pool_cap, (int)bk);
     }
     if (nv <= kBlkTopK && topk_decode_kernel() == 0) {
-      topk_block<<<tokens, 256, 0, s>>>(scores, hist, idx, bt.pos0, bt.n, L.m, L.k, pool_cap);
+      topk_block<<<tokens, kBlkTopKT, 0, s>>>(scores, hist, idx, bt.pos0, bt.n, L.m, L.k,
+                                              pool_cap);
       return hipGetLastError();
     }
     if (nv > L.k) {
