@@ -461,7 +461,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(256) rotate_queries_bf16(const bf16_t* __restrict__ q,
+__global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __restrict__ q,
                                                            bf16_t* __restrict__ qr,
                                                            uint32_t* __restrict__ hist,
                                                            const int64_t* __restrict__ pos0,
@@ -1634,7 +1634,9 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
     int32_t* cand_tie = (int32_t*)wsp;
     wsp += align256(bn * pool_cap * sizeof(int32_t));
     uint32_t* counts = (uint32_t*)wsp;
-    rotate_queries_bf16<<<dim3(bt.n, bt.B), 256, 0, s>>>((const bf16_t*)q, qr, hist, bt.pos0,
+    // 1024 threads: one 16-byte chunk of the query each (64 x 128 channels),
+    // many waves per SIMD to cover the float64 rotation's latency
+    rotate_queries_bf16<<<dim3(bt.n, bt.B), 1024, 0, s>>>((const bf16_t*)q, qr, hist, bt.pos0,
                                                          bt.n, L.Hi, L.Di, L.Ri, L.base);
     int64_t nv = (bt.pos0_max + bt.n) / L.m;
     if (nv > pool_cap) nv = pool_cap;
