@@ -331,6 +331,6 @@ const char* csa_status_str(csa_status s) {
   return "unknown csa_status";
 }
 
-int32_t csa_version(void) { return 100; }
+int32_t csa_version(void) { return 200; }  // 0.2.0: projections, variable-length batches
 
 }  // extern "C"

@@ -39,7 +39,7 @@ def test_every_declared_entry_point_is_exported(lib):
 def test_status_strings_and_version(lib):
     for code in range(7):
         assert m.csa_status_str(code).startswith("CSA_")
-    assert lib.csa_version() >= 100
+    assert lib.csa_version() >= 200
 
 
 def csa_layer(**kw):
