@@ -182,3 +182,12 @@ def test_project_sizes_and_rejections(lib):
     assert call(P, ws=None) == WS
     assert call(P, wsb=300 * 96 * 2 - 1) == WS
     assert call(P, ws=ctypes.c_void_p(0x1010)) == WS
+
+
+def test_binding_checks_variable_length_counts():
+    torch = pytest.importorskip("torch")
+    # host tensors are refused before any call; a wrong dtype or count too
+    pos0 = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        m._batch(pos0, 0, 2, 8, torch.zeros(2, dtype=torch.int32))      # not on the device
+    assert m._CBatch(2, 8, 0x1000, 0).n_valid is None                  # NULL by default

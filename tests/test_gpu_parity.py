@@ -672,3 +672,71 @@ def test_varlen_prefill_matches_separate_calls(csa):
     same = [j for j, t in enumerate(qs) if np.array_equal(gi[t], ref["idx"][j])]
     assert len(same) >= len(qs) - 1, "ids differ beyond a near tie"
     assert_close(host(out[1])[qs][same], ref["out"][same], "bf16", "varlen rows vs oracle")
+
+
+@pytest.mark.parametrize("kind", ["hca", "sliding"])
+def test_varlen_prefill_dense_layers(csa, kind):
+    """Variable-length prefill through an HCA layer (compressor, no indexer)
+    and a sliding-only layer (window only): caches bitwise equal to each
+    sequence run alone, outputs within tolerance, an empty sequence leaves
+    its caches untouched, one sequence against the oracle."""
+    import dataclasses
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    say(f"case: varlen prefill, {kind} bf16, B=3, n_new=700, lens (700, 413, 0), then 300 more")
+    m = csa
+    S, S2, lens = 700, 300, (700, 413, 0)
+    w = synth.workload("hca_prefill", S=S, batch=3)
+    w2 = synth.workload("hca_prefill", S=S2, batch=3)
+    if kind == "sliding":
+        spec = synth.LayerSpec(kind="sliding", dtype="bf16", ratio=0, overlap=0,
+                               rope_theta=10000.0, rope_factor=16.0,
+                               rope_original_context=65536.0)
+        w = dataclasses.replace(w, layers=[spec])
+        w2 = dataclasses.replace(w2, layers=[spec])
+    spec = w.layers[0]
+    inp, inp2 = synth.prefill_inputs(w, 13), synth.prefill_inputs(w2, 14)
+    keys = ("q", "kv") if kind == "sliding" else ("q", "kv", "ckv", "cgate")
+    a = {k: dev(inp[k]) for k in keys}
+    a2 = {k: dev(inp2[k]) for k in keys}
+    sinks = dev(inp["sinks"])
+    L = m.Layer.from_spec(spec)
+    cap = S + S2
+    pcap = cap // spec.ratio if spec.ratio else 1
+
+    def run(cache, p0, pmax, t, nv=None):
+        return layer_step(cache, p0, pmax, t["q"], t["kv"], t.get("ckv"), t.get("cgate"),
+                          sinks=sinks, n_valid=nv)[0]
+
+    cache = LayerCache(L, 3, cap, pcap)
+    p0 = torch.zeros(3, dtype=torch.int64, device="cuda")
+    nv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = run(cache, p0, 0, a, nv).clone()
+    torch.cuda.synchronize()
+    assert not cache.ring[2].any()
+    if spec.ratio:
+        assert not cache.pool[2].any() and not cache.cstate_kv[2].any()
+    p1 = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    out2 = run(cache, p1, max(lens), a2)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        one = LayerCache(L, 1, cap, pcap)
+        z = torch.zeros(1, dtype=torch.int64, device="cuda")
+        cat = {k: torch.cat([a[k][b:b + 1, :n], a2[k][b:b + 1]], 1).contiguous() for k in keys}
+        o1 = run(one, z, 0, cat)
+        torch.cuda.synchronize()
+        if n:
+            assert_close(host(out[b, :n]), host(o1[0, :n]), "bf16", f"sequence {b} first call")
+        assert_close(host(out2[b]), host(o1[0, n:]), "bf16", f"sequence {b} second call")
+        assert torch.equal(cache.ring[b], one.ring[0]), f"sequence {b}: window ring"
+        if spec.ratio:
+            ne = (n + S2) // spec.ratio
+            assert torch.equal(cache.pool[b, :ne], one.pool[0, :ne]), f"sequence {b}: pool"
+            assert torch.equal(cache.cstate_kv[b], one.cstate_kv[0]), f"sequence {b}: state"
+            assert torch.equal(cache.cstate_gate[b], one.cstate_gate[0]), f"sequence {b}: state"
+    x = seq_f64(inp, 1)
+    x = {k: (v if k == "sinks" else v[:lens[1]]) for k, v in x.items()}
+    qs = [0, 1, 127, 128, 255, 256, 400, 412]
+    ref = O.sliding_prefill(spec, x, queries=qs) if kind == "sliding" else \
+        O.hca_prefill(spec, x, queries=qs)
+    assert_close(host(out[1])[qs], ref["out"], "bf16", f"varlen {kind} rows vs oracle")
