@@ -518,6 +518,7 @@ def _oproj_gpu(m, inp, G, T, hidden):
     (1, 4, 64, 4, 32, 256),        # one token
     (129, 16, 32, 1, 64, 513),     # one group: two plain products
     (257, 8, 64, 4, 40, 96),       # rank below one tile, G R = 160
+    (64, 4, 64, 4, 8, 96),         # one head per group, the smallest G R (32)
 ])
 def test_output_projection_small(csa, T, H, D, G, R, hidden):
     say(f"output projection T={T} H={H} D={D} G={G} R={R} hidden={hidden}")
