@@ -775,26 +775,9 @@ static bool attend_dec(const Layer& L, int B, int n, int64_t pool_cap, bool csa)
   return tokens < 256 && (tokens >= 16 || attend_rows(L, pool_cap, csa) <= 256);
 }
 
-// Prefill kernel: 0 attend_mfma (QK^T on 16 x 16 tiles, 32-row chunks),
-// 1 attend_x32 (32 x 32 tiles, one wave per SIMD, 64-row chunks), 2 attend_w8
-// (32 x 32 tiles, eight waves per block, 64-row chunks), 3 attend_h32 (32 x 32
-// tiles, two blocks per CU, 32-row chunks).  The environment variable
-// CSA_ATTN_PREFILL ("0" .. "3"), read at each call, overrides the compiled
-// default.
-#ifndef CSA_ATTN_PREFILL
-#define CSA_ATTN_PREFILL 0
-#endif
-static int prefill_kernel() {
-  const char* e = getenv("CSA_ATTN_PREFILL");
-  if (e && e[0] >= '0' && e[0] <= '3' && e[1] == 0) return e[0] - '0';
-  return CSA_ATTN_PREFILL;
-}
-
 int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
   if (!attend_fast_shape(L)) return 1;
   if (attend_dec(L, B, n, pool_cap, csa)) return attend_decode_splits(L, B, n, pool_cap, csa);
-  const int pk = prefill_kernel();
-  const int kCH = pk == 1 || pk == 2 ? 64 : csa::kCH;
   const int64_t nch = (attend_rows(L, pool_cap, csa) + kCH - 1) / kCH;
   const int64_t tokens = (int64_t)B * n;
   // no block above kMaxRows rows; calls of fewer than 256 tokens also split
@@ -825,20 +808,6 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
     if (attend_dec(L, bt.B, bt.n, pool_cap, csa)) {
       hipError_t e = launch_attend_decode(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
                                           ws, csa, ns, s);
-      if (e != hipSuccess || ns == 1) return e;
-      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
-          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
-      return hipGetLastError();
-    }
-    const int pk = prefill_kernel();
-    if (pk) {
-      hipError_t e =
-          pk == 3   ? launch_attend_h32(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
-                                        ws, csa, ns, s)
-          : pk == 2 ? launch_attend_w8(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
-                                       ws, csa, ns, s)
-                    : launch_attend_x32(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
-                                        ws, csa, ns, s);
       if (e != hipSuccess || ns == 1) return e;
       attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
           (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);

@@ -89,19 +89,6 @@ hipError_t launch_index_topk(const Layer& L, const Batch& b, const void* q, cons
 bool attend_fast_shape(const Layer& L);
 int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
 size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
-// attend_wide.hip
-hipError_t launch_attend_x32(const Layer& L, const Batch& b, const void* q, const void* win,
-                             int64_t win_cap, const void* pool, int64_t pool_cap,
-                             const int32_t* idx, const float* sinks, void* out, void* ws, bool csa,
-                             int nsplit, hipStream_t s);
-hipError_t launch_attend_w8(const Layer& L, const Batch& b, const void* q, const void* win,
-                             int64_t win_cap, const void* pool, int64_t pool_cap,
-                             const int32_t* idx, const float* sinks, void* out, void* ws, bool csa,
-                             int nsplit, hipStream_t s);
-hipError_t launch_attend_h32(const Layer& L, const Batch& b, const void* q, const void* win,
-                             int64_t win_cap, const void* pool, int64_t pool_cap,
-                             const int32_t* idx, const float* sinks, void* out, void* ws, bool csa,
-                             int nsplit, hipStream_t s);
 // attend_decode.hip
 int attend_decode_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
 hipError_t launch_attend_decode(const Layer& L, const Batch& b, const void* q, const void* win,

@@ -9,25 +9,26 @@
 // rotary_emb].
 //
 // Kernels:
-//  * index_prefill_mfma: H_I = 64, D_I = 128, bf16 (other rope widths, or
-//    CSA_INDEX_PREFILL=1).  A block takes 8
-//    consecutive queries (2 per wave, rotated query fragments held in VGPRs)
-//    and streams the visible keys through LDS in tiles of 64 keys shared by
-//    the four waves: 64 x 16 x 32 bf16 MFMA tiles, then ReLU, head weights and
-//    the head sum in registers (16 heads in-lane, 4 lane groups by shuffles).
-//    Per tile a wave reads 16 KB of keys from LDS for 128 MFMAs.
-//  * index_decode_mfma (few queries per sequence): queries rotated once
+//  * index_prefill_mfma: H_I = 64, D_I = 128, bf16, rope widths other than
+//    64.  A block takes 8 consecutive queries (2 per wave, rotated query
+//    fragments held in VGPRs) and streams the visible keys through LDS in
+//    tiles of 64 keys shared by the four waves: 64 x 16 x 32 bf16 MFMA tiles,
+//    then ReLU, head weights and the head sum in registers (16 heads in-lane,
+//    4 lane groups by shuffles).
+//  * index_decode_x32 (few queries per sequence): queries rotated once
 //    (rotate_queries_bf16), then each block streams a run of one query's keys
-//    from HBM through LDS (LDS-DMA, two tiles in flight per wave) into MFMA B
+//    from HBM through LDS (LDS-DMA, two tiles in flight per wave) into MFMA
 //    fragments; each key is read once.  It also counts the query's scores in
 //    a histogram of the top 12 bits of their order keys.
-//  * topk_collect / topk_final (same path): the histogram names the bin
-//    holding the k-th best score; per 1024-key slice the ids above that bin
-//    and inside it are compacted in id order; a radix select inside the bin
-//    settles the last places and both id lists are merged in id order.
-//  * index_prefill_x32 (default for H_I = 64, D_I = 128, rope width 64, bf16):
-//    one query per wave on 32 x 32 x 16 MFMA tiles, 128-key LDS tiles shared
-//    by the block's four waves; see its comment below.
+//  * topk_block (decode rows of at most 32768 keys): one block per query
+//    selects with the histogram's cut bin and a radix select inside it.
+//  * topk_collect / topk_final (decode rows beyond that): the histogram names
+//    the bin holding the k-th best score; per 1024-key slice the ids above
+//    that bin and inside it are compacted in id order; a radix select inside
+//    the bin settles the last places and both id lists are merged in id order.
+//  * index_prefill_x32 (H_I = 64, D_I = 128, rope width 64, bf16): one query
+//    per wave on 32 x 32 x 16 MFMA tiles, 128-key LDS tiles shared by the
+//    block's four waves; see its comment below.
 //  * index_generic: any head count / width, float or bf16, VALU float32.
 //  * topk_radix (prefill path): per query, four 8-bit radix-select passes
 //    find the k-th largest ordered key; one ordered pass emits ids by ballot
@@ -487,174 +488,17 @@ __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __rest
   }
 }
 
-
 constexpr int kDecTile = 128;  // keys per LDS tile: 32 per wave, 32 KB
 
-// Sum over lanes l, l^16, l^32, l^48 with the gfx950 lane swaps.
-__device__ __forceinline__ float sum_g4(float v) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One block scores a run of keys of one token, 128-key tiles at a time.  The
-// keys reach LDS through the LDS-DMA loads (no VGPRs held while in flight)
-// into two arrays; each wave fetches and scores its own 32 rows of a tile, so
-// waves only meet at the start and at the histogram.  Per tile a wave copies
-// its B fragments to VGPRs, refills the same array with the tile two ahead,
-// then runs the MFMAs: two tiles stay in flight.  The 16-byte chunk c of tile
-// row r sits at slot c ^ (r & 15) so that the 16 rows of a fragment read hit
-// distinct bank groups.  The histogram of the block's scores is built after
-// the loop from the scores it stored.
-__global__ void __launch_bounds__(256) index_decode_mfma(const bf16_t* __restrict__ qr,
-                                                         const bf16_t* __restrict__ wts,
-                                                         const bf16_t* __restrict__ keys,
-                                                         float* __restrict__ scores,
-                                                         float* __restrict__ discard,
-                                                         uint32_t* __restrict__ hist,
-                                                         const int64_t* __restrict__ pos0,
-                                                         int n_new, int m, int64_t pool_cap,
-                                                         int block_keys) {
-  constexpr int Hi = 64, Di = 128;
-  __shared__ __attribute__((aligned(1024))) bf16_t kt0[kDecTile * Di];
-  __shared__ __attribute__((aligned(1024))) bf16_t kt1[kDecTile * Di];
-  const int tok = blockIdx.y;  // b * n_new + i
-  const int b = tok / n_new, i = tok % n_new;
-  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int64_t nv = (pos0[b] + i + 1) / m;
-  if (nv > pool_cap) nv = pool_cap;
-  const int64_t kb = (int64_t)blockIdx.x * block_keys;
-  if (kb >= nv) return;  // block-uniform, before any barrier
-  const int64_t ke = kb + block_keys < nv ? kb + block_keys : nv;
-  const int ntile = (int)((ke - kb + kDecTile - 1) / kDecTile);
-  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
-  // DMA of this wave's 32 rows of tile `tile` (8 instructions of 4 rows);
-  // rows past the run re-read its last row (already in cache, never scored)
-  const int lrow = lane >> 4, slot = lane & 15;
-  auto issue = [&](int tile, bf16_t* dst) {
-    const int64_t t0 = kb + (int64_t)tile * kDecTile;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 32 * wv + 4 * j + lrow;
-      int64_t key = t0 + r;
-      if (key > ke - 1) key = ke - 1;
-      const bf16_t* src = kbase + key * Di + 8 * (slot ^ (r & 15));
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
-                                       16, 0, 0);
-    }
-  };
-  const bf16_t* qrow = qr + (int64_t)tok * Hi * Di;
-  uint4 A[4][4];
-  float wr[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      A[mt][kk] = *(const uint4*)(qrow + (16 * mt + r16) * Di + 32 * kk + 8 * g);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      wr[mt][ii] = bf16_to_f32(wts[(int64_t)tok * Hi + 16 * mt + 4 * g + ii]);
-  }
-  issue(0, kt0);
-  issue(1, kt1);
-  float* srow = scores + (int64_t)tok * pool_cap;
-  // fragment reads in one asm block that also waits for them: the compiler
-  // then sees no LDS load to order after the in-flight DMA of other tiles
-  auto frags = [&](const bf16_t* buf, uint4 (&Bf)[2][4]) {
-    uint32_t a[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = 32 * wv + 16 * nt + r16;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        a[nt][kk] = (uint32_t)(size_t)(lds_void*)(buf + r * Di + 8 * ((4 * kk + g) ^ (r & 15)));
-    }
-    asm volatile(
-        "ds_read_b128 %0, %8\n"
-        "ds_read_b128 %1, %9\n"
-        "ds_read_b128 %2, %10\n"
-        "ds_read_b128 %3, %11\n"
-        "ds_read_b128 %4, %12\n"
-        "ds_read_b128 %5, %13\n"
-        "ds_read_b128 %6, %14\n"
-        "ds_read_b128 %7, %15\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(Bf[0][0]), "=v"(Bf[0][1]), "=v"(Bf[0][2]), "=v"(Bf[0][3]), "=v"(Bf[1][0]),
-          "=v"(Bf[1][1]), "=v"(Bf[1][2]), "=v"(Bf[1][3])
-        : "v"(a[0][0]), "v"(a[0][1]), "v"(a[0][2]), "v"(a[0][3]), "v"(a[1][0]), "v"(a[1][1]),
-          "v"(a[1][2]), "v"(a[1][3])
-        : "memory");
-  };
-  auto compute = [&](int tile, const uint4 (&Bf)[2][4]) {
-    f32x4 acc[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mfma16(A[mt][kk], Bf[nt][kk], acc[nt][mt]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = 32 * wv + 16 * nt + r16;
-      float v = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) v += wr[mt][ii] * fmaxf(acc[nt][mt][ii], 0.f);
-      v = sum_g4(v);
-      // the four lane groups hold the same sum: all store it (keys past the
-      // run go to a discard slot)
-      const int64_t key = kb + (int64_t)tile * kDecTile + r;
-      *(key < ke ? srow + key : discard) = v;
-    }
-  };
-  // Two tiles in flight per wave: the fragments of tile t are copied to
-  // VGPRs (the asm read waits for them), then tile t+2 is fetched into the
-  // same array while tile t is scored.  After `vmcnt(8)` only the newest
-  // tile's 8 DMA rows may be in flight (score stores issued after an older
-  // tile only make the wait longer).  Prefetches are unconditional.
-  uint4 Bf[2][4];
-  for (int tile = 0;;) {
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    frags(kt0, Bf);
-    issue(tile + 2, kt0);
-    compute(tile, Bf);
-    if (++tile >= ntile) break;
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    frags(kt1, Bf);
-    issue(tile + 2, kt1);
-    compute(tile, Bf);
-    if (++tile >= ntile) break;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA outlives the block
-  // histogram of the block's scores (read back from the cache)
-  uint32_t* lh = (uint32_t*)kt0;  // kHBins words, free now
-  __syncthreads();
-  for (int j = threadIdx.x; j < kHBins; j += 256) lh[j] = 0u;
-  __threadfence_block();
-  __syncthreads();
-  for (int64_t j = kb + threadIdx.x; j < ke; j += 256)
-    atomicAdd(&lh[order_key(srow[j]) >> kHShift], 1u);
-  __syncthreads();
-  uint32_t* h = hist + (int64_t)tok * kHBins;
-  for (int j = threadIdx.x; j < kHBins; j += 256) {
-    const uint32_t c = lh[j];
-    if (c) atomicAdd(&h[j], c);
-  }
-}
-
-// The same scan on 32 x 32 x 16 MFMA tiles, with index_prefill_x32's
-// operands (the rotated query as A, heads as rows; keys as B): per tile each
-// wave scores its 32 rows in one step of 16 MFMAs, ReLU, weights and the sum
-// over a lane's 16 heads stay in-lane, and one lane-half swap adds the other
-// 16.  Each score also goes into the block's LDS histogram as it is made, so
-// no pass over the stored scores follows the loop.
+// Decode key scan on 32 x 32 x 16 MFMA tiles, with index_prefill_x32's
+// operands (the rotated query as A, heads as rows; keys as B).  One block
+// scores a run of keys of one token, 128-key tiles at a time; the keys reach
+// LDS through LDS-DMA loads (no VGPRs held while in flight), two tiles in
+// flight per wave, each wave fetching and scoring its own 32 rows of a tile
+// in one step of 16 MFMAs.  ReLU, weights and the sum over a lane's 16 heads
+// stay in-lane, and one lane-half swap adds the other 16.  Each score also
+// goes into the block's LDS histogram as it is made, so no pass over the
+// stored scores follows the loop.
 __global__ void __launch_bounds__(256, 2) index_decode_x32(
     const bf16_t* __restrict__ qr, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
     float* __restrict__ scores, float* __restrict__ discard, uint32_t* __restrict__ hist,
@@ -756,8 +600,11 @@ __global__ void __launch_bounds__(256, 2) index_decode_x32(
       asm volatile("ds_add_u32 %0, %1" ::"v"(ha), "v"(1u) : "memory");
     }
   };
-  // Two tiles in flight per wave, as in index_decode_mfma: after vmcnt(8)
-  // only the newest tile's 8 DMA rows may be in flight.
+  // Two tiles in flight per wave: the fragments of tile t are copied to
+  // VGPRs (the asm read waits for them), then tile t+2 is fetched into the
+  // same array while tile t is scored.  After vmcnt(8) only the newest
+  // tile's 8 DMA rows may be in flight (score stores issued after an older
+  // tile only make the wait longer).  Prefetches are unconditional.
   uint4 Bf[8];
   for (int tile = 0;;) {
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -1568,36 +1415,6 @@ static bool index_decode_path(const Layer& L, int n, int64_t pool_cap) {
          (pool_cap + kSlice - 1) / kSlice <= kMaxSlices;
 }
 
-// Prefill scoring kernel: 0 index_prefill_x32 (32 x 32 tiles, one query per
-// wave), 1 index_prefill_mfma (16 x 16 tiles, two queries per wave).  The
-// environment variable CSA_INDEX_PREFILL ("0" or "1"), read at each call,
-// overrides the default.
-static int index_prefill_kernel() {
-  const char* e = getenv("CSA_INDEX_PREFILL");
-  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
-  return 0;
-}
-
-// Decode key scan: 0 index_decode_x32 (32 x 32 tiles, histogram built in
-// LDS as scores are made), 1 index_decode_mfma (16 x 16 tiles).  The
-// environment variable CSA_INDEX_DECODE ("0" or "1"), read at each call,
-// overrides the default.
-static int index_decode_kernel() {
-  const char* e = getenv("CSA_INDEX_DECODE");
-  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
-  return 0;
-}
-
-// Decode selection for rows of at most kBlkTopK keys: 0 = topk_block (one
-// launch), 1 = topk_collect + topk_final (the path longer rows always take);
-// the environment variable CSA_TOPK_DECODE ("0" or "1"), read at each call,
-// overrides the default.
-static int topk_decode_kernel() {
-  const char* e = getenv("CSA_TOPK_DECODE");
-  if (e && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] - '0';
-  return 0;
-}
-
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
@@ -1647,16 +1464,11 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
       int64_t bk = (nv + per_tok - 1) / per_tok;
       bk = (bk + kDecTile - 1) / kDecTile * kDecTile;
       dim3 g1((unsigned)((nv + bk - 1) / bk), tokens);
-      if (index_decode_kernel() == 0)
-        index_decode_x32<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
-                                            (float*)(counts + bn * nslice * 2), hist, bt.pos0,
-                                            bt.n, L.m, pool_cap, (int)bk);
-      else
-        index_decode_mfma<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
-                                             (float*)(counts + bn * nslice * 2), hist, bt.pos0,
-                                             bt.n, L.m, pool_cap, (int)bk);
+      index_decode_x32<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
+                                          (float*)(counts + bn * nslice * 2), hist, bt.pos0,
+                                          bt.n, L.m, pool_cap, (int)bk);
     }
-    if (nv <= kBlkTopK && topk_decode_kernel() == 0) {
+    if (nv <= kBlkTopK) {
       topk_block<<<tokens, kBlkTopKT, 0, s>>>(scores, hist, idx, bt.pos0, bt.n, L.m, L.k,
                                               pool_cap);
       return hipGetLastError();
@@ -1670,7 +1482,7 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
                                       L.m, L.k, pool_cap, nslice);
     return hipGetLastError();
   }
-  if (index_fast_shape(L) && L.Ri == 64 && index_prefill_kernel() == 0) {
+  if (index_fast_shape(L) && L.Ri == 64) {
     const unsigned nblk = (unsigned)((bt.n + kX32Q - 1) / kX32Q);
     index_prefill_x32<64><<<nblk * bt.B, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
                                                       (const bf16_t*)keys, scores, (float*)wsp,

@@ -73,11 +73,21 @@ def ulp_diff_ok(gpu, ref, dtype, what="", max_frac=1e-4):
     return int(diff.sum())
 
 
-def score_bounds(qi_t, wi_t, keys, t, rope_dim, base, dtype):
-    """|terms| sums of the index score of every key (for the float32 error bound)."""
+def index_exact(spec, qi_t, wi_t, keys, t, dtype=None):
+    """Exact (float64) index scores of query t against ``keys`` and the sum of
+    |terms| of each score, for the float32 error bound of ``audit_topk``.
+
+    Both use the layer's own rope frequencies (``O.rope_base(spec)``: the
+    plain base, or the YaRN-scaled frequencies the layer's keys were rotated
+    with), so the exact scores are those of the stored keys."""
     from oracle import csa_oracle as O
-    q = O.round_to(O.rope(qi_t, t, rope_dim, base, +1), dtype)
-    return (np.abs(wi_t)[:, None] * (np.abs(q) @ np.abs(np.asarray(keys)).T)).sum(axis=0)
+    dt = spec.dtype if dtype is None else dtype
+    base = O.rope_base(spec)
+    keys = np.asarray(keys, dtype=np.float64)
+    sc = O.index_scores(qi_t, wi_t, keys, t, spec.index_rope_dim, base, dt)
+    q = O.round_to(O.rope(qi_t, t, spec.index_rope_dim, base, +1), dt)
+    ab = (np.abs(wi_t)[:, None] * (np.abs(q) @ np.abs(keys).T)).sum(axis=0)
+    return sc, ab
 
 
 def audit_topk(gpu_idx, ref_idx, scores, absterms, Di, Hi):
@@ -107,7 +117,8 @@ def audit_topk(gpu_idx, ref_idx, scores, absterms, Di, Hi):
 
 def seq_f64(inp, b):
     """Sequence b of prefill inputs as float64 (sinks shared)."""
-    return {k: (to_f64(v) if k == "sinks" else to_f64(v[b])) for k, v in inp.items()}
+    return {k: (v if v is None else to_f64(v) if k == "sinks" else to_f64(v[b]))
+            for k, v in inp.items()}
 
 
 class LazyF64:

@@ -8,7 +8,7 @@ import pytest
 import synth
 from oracle import csa_oracle as O
 from synth import to_f64
-from tests.helpers import (LazyF64, assert_close, audit_topk, dev, host, say, score_bounds,
+from tests.helpers import (LazyF64, assert_close, audit_topk, dev, host, index_exact, say,
                            ulp_diff_ok)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -68,10 +68,7 @@ def test_csa_prefill_full_s8192(csa):
     nd = 0
     for n, t in enumerate(qs):
         keys = ref["ipool"][:(t + 1) // spec.ratio]
-        sc = O.index_scores(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim, spec.rope_theta,
-                            "bf16")
-        ab = score_bounds(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim, spec.rope_theta,
-                          "bf16")
+        sc, ab = index_exact(spec, x["qi"][t], x["wi"][t], keys, t)
         nd += audit_topk(gi[t], ref["idx"][n], sc, ab, spec.index_dim, spec.index_heads)
     say(f"  near-tie id differences: {nd} over {len(qs)} queries")
     idx2 = idx.clone()
@@ -161,10 +158,7 @@ def _decode_full(m, name, seqs_checked, layers=None):
             if spec.has_indexer:
                 nv = (pos0 + 1) // spec.ratio
                 keys = cc["ipool"][:nv]
-                sc = O.index_scores(nb["qi"], nb["wi"], keys, pos0, spec.index_rope_dim,
-                                    spec.rope_theta, "bf16")
-                ab = score_bounds(nb["qi"], nb["wi"], keys, pos0, spec.index_rope_dim,
-                                  spec.rope_theta, "bf16")
+                sc, ab = index_exact(spec, nb["qi"], nb["wi"], keys, pos0)
                 nd = audit_topk(idx[b, 0].cpu().numpy(), ref["idx"], sc, ab, spec.index_dim,
                                 spec.index_heads)
                 if nd:

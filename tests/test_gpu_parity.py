@@ -10,7 +10,7 @@ import pytest
 import synth
 from oracle import csa_oracle as O
 from synth import to_f64
-from tests.helpers import (assert_close, audit_topk, dev, host, say, score_bounds, seq_f64,
+from tests.helpers import (assert_close, audit_topk, dev, host, index_exact, say, seq_f64,
                            ulp_diff_ok)
 
 pytestmark = pytest.mark.gpu
@@ -34,16 +34,18 @@ def _prefill_gpu(m, spec, inp, B, S):
     cache = LayerCache(L, B, S, pool_cap)
     pos0 = torch.zeros(B, dtype=torch.int64, device="cuda")
     args = {k: dev(v) for k, v in inp.items() if k != "sinks"}
-    sinks = dev(inp["sinks"])
+    sinks = None if inp["sinks"] is None else dev(inp["sinks"])
     out, idx = layer_step(cache, pos0, 0, args["q"], args["kv"], args.get("ckv"), args.get("cgate"),
                           args.get("ikv"), args.get("igate"), args.get("qi"), args.get("wi"), sinks)
     torch.cuda.synchronize()
     return L, cache, pos0, args, sinks, out, idx
 
 
-def _check_csa_prefill(m, spec, w, seed, queries_per_seq=None):
+def _check_csa_prefill(m, spec, w, seed, queries_per_seq=None, sinks=True):
     import torch
     inp = synth.prefill_inputs(w, seed)
+    if not sinks:
+        inp["sinks"] = None
     B, S = w.batch, w.n_new
     L, cache, pos0, args, sinks, out, idx = _prefill_gpu(m, spec, inp, B, S)
     gidx = idx.cpu().numpy()
@@ -58,10 +60,7 @@ def _check_csa_prefill(m, spec, w, seed, queries_per_seq=None):
         for n, t in enumerate(qs):
             nv = (t + 1) // spec.ratio
             keys = ref["ipool"][:nv]
-            sc = O.index_scores(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim,
-                                spec.rope_theta, spec.dtype)
-            ab = score_bounds(x["qi"][t], x["wi"][t], keys, t, spec.index_rope_dim,
-                              spec.rope_theta, spec.dtype)
+            sc, ab = index_exact(spec, x["qi"][t], x["wi"][t], keys, t)
             ndiff += audit_topk(gidx[b, t], ref["idx"][n], sc, ab, spec.index_dim,
                                 spec.index_heads)
         go = host(out[b])[qs]
@@ -121,15 +120,14 @@ def test_csa_prefill_bf16_small_topk(csa):
                                                         500, 777, 998, 999])
 
 
-@pytest.mark.parametrize("var,val", [("CSA_ATTN_PREFILL", "1"), ("CSA_ATTN_PREFILL", "2"),
-                                     ("CSA_ATTN_PREFILL", "3"), ("CSA_INDEX_PREFILL", "1")])
-def test_csa_prefill_alternative_kernels(csa, monkeypatch, var, val):
-    """The run-time selectable prefill kernels (attention and indexer) against the oracle."""
-    say(f"case: csa_prefill bf16 S=1000 k=64 B=2 with {var}={val}")
+def test_csa_prefill_bf16_rope_width_32(csa):
+    """A CSA layer with 32 rope channels (attention and indexer): the indexer
+    runs its kernel for rope widths other than 64, the attention its R=32
+    instance."""
+    say("case: csa_prefill bf16 S=1000 k=64 B=2, rope width 32")
     import dataclasses
-    monkeypatch.setenv(var, val)
     w = synth.workload("csa_prefill", S=1000, batch=2)
-    spec = dataclasses.replace(w.layers[0], topk=64)
+    spec = dataclasses.replace(w.layers[0], topk=64, rope_dim=32, index_rope_dim=32)
     w = dataclasses.replace(w, layers=[spec])
     _check_csa_prefill(csa, spec, w, 5, queries_per_seq=[0, 3, 4, 63, 64, 255, 256, 511, 700, 999])
 
@@ -187,7 +185,7 @@ def test_csa_prefill_bf16_peaked(csa):
     _check_csa_prefill(csa, w.layers[0], w, 4, queries_per_seq=[5, 600, 2047, 2100, 2199])
 
 
-def _check_dense_prefill(m, kind, S, seed, queries, variant="plain"):
+def _check_dense_prefill(m, kind, S, seed, queries, variant="plain", sinks=True):
     import torch
     name = "hca_prefill"
     w = synth.workload(name, S=S, variant=variant)
@@ -198,7 +196,9 @@ def _check_dense_prefill(m, kind, S, seed, queries, variant="plain"):
                                rope_factor=16.0, rope_original_context=65536.0)
         w = dataclasses.replace(w, layers=[spec])
     inp = synth.prefill_inputs(w, seed)
-    L, cache, pos0, args, sinks, out, _ = _prefill_gpu(m, spec, inp, w.batch, S)
+    if not sinks:
+        inp["sinks"] = None
+    L, cache, pos0, args, sk, out, _ = _prefill_gpu(m, spec, inp, w.batch, S)
     x = seq_f64(inp, 0)
     if kind == "sliding":
         ref = O.sliding_prefill(spec, x, queries=queries)
@@ -220,16 +220,35 @@ def test_hca_prefill_bf16_peaked(csa):
     _check_dense_prefill(csa, "hca", 3000, 1, [0, 127, 1500, 2999], variant="peaked")
 
 
+def test_csa_prefill_without_sinks(csa):
+    """No sink through the prefill attention kernel (one block per query, no
+    split): plain softmax over window and selected rows."""
+    say("case: csa_prefill bf16 S=1000 k=64 sinks=None")
+    import dataclasses
+    w = synth.workload("csa_prefill", S=1000)
+    spec = dataclasses.replace(w.layers[0], topk=64)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 15, queries_per_seq=[0, 1, 5, 127, 128, 600, 999],
+                       sinks=False)
+
+
+def test_hca_prefill_without_sinks(csa):
+    say("case: hca_prefill bf16 S=1500 sinks=None")
+    _check_dense_prefill(csa, "hca", 1500, 16, [0, 127, 128, 700, 1499], sinks=False)
+
+
 def test_sliding_prefill_bf16(csa):
     say("case: sliding prefill bf16 S=700")
     _check_dense_prefill(csa, "sliding", 700, 2, [0, 1, 64, 127, 128, 129, 699])
 
 
-def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
-    """One decode step at pos0 for every sequence and layer, against the oracle."""
+def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None, variant="plain",
+                 sinks=True):
+    """One decode step at pos0 for every sequence and layer, against the oracle.
+    sinks=False runs the layer without a sink (the oracle with none)."""
     import torch
     from long_context_sparse_gated_amd.layer import LayerCache, layer_step
-    w = synth.workload(name, pos0=pos0, batch=batch)
+    w = synth.workload(name, pos0=pos0, batch=batch, variant=variant)
     for li, spec in enumerate(w.layers):
         if layers is not None and li not in layers:
             continue
@@ -252,9 +271,10 @@ def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
         a = {k: dev(inp[k]) for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
              if k in inp}
         nvd = None if valid is None else torch.tensor(valid, dtype=torch.int32, device="cuda")
+        sk = dev(inp["sinks"]) if sinks else None
         out, idx = layer_step(cache, p0, pos0, a["q"], a["kv"], a.get("ckv"), a.get("cgate"),
                               a.get("ikv"), a.get("igate"), a.get("qi"), a.get("wi"),
-                              dev(inp["sinks"]), n_valid=nvd)
+                              sk, n_valid=nvd)
         torch.cuda.synchronize()
         for b in range(batch):
             if valid is not None and valid[b] == 0:
@@ -272,6 +292,8 @@ def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
             new = {k: (to_f64(inp[k]) if k == "sinks" else to_f64(inp[k][b, 0]))
                    for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi", "sinks")
                    if k in inp}
+            if not sinks:
+                new["sinks"] = None
             cch = {k: to_f64(inp[k][b]) for k in ("win", "pool", "ipool", "cstate_kv",
                                                   "cstate_gate", "istate_kv", "istate_gate")
                    if k in inp}
@@ -285,10 +307,7 @@ def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
                 if "new_ipool" in ref:
                     keys = np.concatenate([keys, ref["new_ipool"][None]])
                 keys = keys[:nv]
-                sc = O.index_scores(new["qi"], new["wi"], keys, pos0, spec.index_rope_dim,
-                                    spec.rope_theta, "bf16")
-                ab = score_bounds(new["qi"], new["wi"], keys, pos0, spec.index_rope_dim,
-                                  spec.rope_theta, "bf16")
+                sc, ab = index_exact(spec, new["qi"], new["wi"], keys, pos0)
                 gi = idx[b, 0].cpu().numpy()
                 nd = audit_topk(gi, ref["idx"], sc, ab, spec.index_dim, spec.index_heads)
                 if nd:
@@ -296,7 +315,7 @@ def _decode_case(m, name, pos0, batch, seed, layers=None, valid=None):
                     idx2 = idx.clone()
                     idx2[b, 0] = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
                     m.csa_attend(L, p0, pos0, a["q"], cache.ring, cache.pool, idx2,
-                                 dev(inp["sinks"]), out, cache.workspace(1, m.CSA_OP_ATTEND))
+                                 sk, out, cache.workspace(1, m.CSA_OP_ATTEND))
                     torch.cuda.synchronize()
             assert_close(host(out[b, 0]), ref["out"], "bf16", f"decode out seq {b}")
 
@@ -336,6 +355,38 @@ def test_mixed_decode_small(csa):
 def test_mixed_decode_long_topk_path(csa):
     say("case: mixed decode B=2 pos0=70001, CSA layer only (1024-thread top-k)")
     _decode_case(csa, "mixed_decode", 70001, 2, 3, layers=[0])
+
+
+def test_csa_decode_peaked(csa):
+    say("case: csa decode peaked B=3 pos0=6001 (split rows, merged)")
+    _decode_case(csa, "csa_decode", 6001, 3, 8, variant="peaked")
+
+
+def test_csa_decode_peaked_b20(csa):
+    say("case: csa decode peaked B=20 pos0=3003 (row slices x head groups)")
+    _decode_case(csa, "csa_decode", 3003, 20, 9, variant="peaked")
+
+
+def test_mixed_decode_peaked(csa):
+    say("case: mixed decode peaked B=2 pos0=40959 three layers")
+    _decode_case(csa, "mixed_decode", 40959, 2, 10, variant="peaked")
+
+
+def test_decode_without_sinks_split_rows(csa):
+    """No sink: the split partials of a few tokens with long row lists
+    (attend_mfma with row splits, then the merge) against plain softmax."""
+    say("case: csa decode B=3 pos0=5000 sinks=None (split rows, merged)")
+    _decode_case(csa, "csa_decode", 5000, 3, 11, sinks=False)
+    say("case: mixed decode B=2 pos0=40000 HCA layer sinks=None (split rows, merged)")
+    _decode_case(csa, "mixed_decode", 40000, 2, 12, layers=[1], sinks=False)
+
+
+def test_decode_without_sinks_head_groups(csa):
+    """No sink through the decode attention kernel (16..255 tokens) and its merge."""
+    say("case: csa decode B=20 pos0=3001 sinks=None (row slices x head groups)")
+    _decode_case(csa, "csa_decode", 3001, 20, 13, sinks=False)
+    say("case: sliding layer B=24 sinks=None (one slice)")
+    _decode_case(csa, "mixed_decode", 40000, 24, 14, layers=[2], sinks=False)
 
 
 def test_decode_graph_replay_matches_eager(csa):
@@ -403,17 +454,11 @@ def test_decode_graph_replay_matches_eager(csa):
 @pytest.mark.parametrize("n_q,pool,distinct,pos0", [
     (37, 700, 0, 2700), (64, 900, 5, 3000), (9, 300, 0, 0), (1, 5000, 0, 19999),
     (1, 30000, 7, 119999), (3, 2048, 3, 8191), (7, 12000, 0, 47990), (5, 600, 0, 2048),
-    (2, 3001, 0, 11990), (1, 32768, 2, 131071)])
+    (2, 3001, 0, 11990), (1, 32768, 2, 131071),
+    # the mixed long-context decode row length (262144 keys), plain and tie-heavy
+    (1, 262144, 0, 1048575), (2, 262144, 3, 1048574)])
 def test_topk_bit_exact_on_grid_inputs(csa, n_q, pool, distinct, pos0):
     """Exact-arithmetic scores: both sides must select identical ids (ties: lowest id)."""
-    _grid_topk_case(csa, n_q, pool, distinct, pos0)
-
-
-@pytest.mark.parametrize("n_q,pool,distinct,pos0", [
-    (1, 30000, 7, 119999), (3, 2048, 3, 8191), (2, 3001, 0, 11990)])
-def test_topk_decode_two_launch_path(csa, monkeypatch, n_q, pool, distinct, pos0):
-    """The collect + final selection (the path of rows beyond 32768 keys) on short rows."""
-    monkeypatch.setenv("CSA_TOPK_DECODE", "1")
     _grid_topk_case(csa, n_q, pool, distinct, pos0)
 
 
@@ -440,10 +485,47 @@ def _grid_topk_case(m, n_q, pool, distinct, pos0):
         t = pos0 + i
         nv = (t + 1) // 4
         sc = O.index_scores(q[i].astype(np.float64), wt[i].astype(np.float64),
-                            keys[:nv].astype(np.float64), t, 64, spec.rope_theta, "bf16")
+                            keys[:nv].astype(np.float64), t, 64, O.rope_base(spec), "bf16")
         assert np.array_equal(gs[i, :nv].astype(np.float64), sc), "scores must be exact"
         ref = O.topk_select(sc, k)
         assert np.array_equal(gi[i], ref), f"query {i}: ids differ"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("yarn", [False, True])
+@pytest.mark.parametrize("sign", [1, -1])
+def test_csa_rope_matches_oracle(csa, dtype, yarn, sign):
+    """csa_rope rotates the last rope_dim channels of every row in place at
+    sign * position; stored bits equal the oracle's float64 rotation rounded
+    once (rows of 96 channels, 32 rope channels, three rows per token, two
+    sequences at distant positions)."""
+    import torch
+    m = csa
+    say(f"case: csa_rope dtype={dtype} yarn={yarn} sign={sign}")
+    B, n, rows, width, rd = 2, 37, 3, 96, 32
+    spec = synth.LayerSpec(kind="sliding", dtype=dtype, num_heads=4, head_dim=64, rope_dim=16,
+                           rope_theta=160000.0, ratio=0, overlap=0,
+                           rope_factor=16.0 if yarn else 0.0, rope_original_context=4096.0)
+    L = m.Layer.from_spec(spec)
+    rng = np.random.default_rng([17, sign + 1, int(yarn)])
+    x = rng.standard_normal((B, n, rows, width)).astype(np.float32)
+    if dtype == "bf16":
+        x = to_f64(synth.f32_to_bf16_bits(x))
+    x = x.astype(np.float64)
+    pos = np.array([5, 250000], dtype=np.int64)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xd = torch.from_numpy(x).to(torch.float32).to(tdt).cuda()
+    p0 = torch.from_numpy(pos).cuda()
+    m.csa_rope(L, p0, int(pos.max()), xd, rd, sign)
+    torch.cuda.synchronize()
+    got = host(xd)
+    t = pos[:, None] + np.arange(n)[None, :]                       # [B, n]
+    ref = O.round_to(O.rope(x, sign * t[:, :, None], rd, O.rope_base(spec), +1), dtype)
+    assert np.array_equal(got[..., :width - rd], x[..., :width - rd]), "channels before the slice"
+    ulp_diff_ok(got, ref, dtype, "rotated rows")
+    if yarn:  # the scaled frequencies differ from the plain ones on these positions
+        plain = O.round_to(O.rope(x, sign * t[:, :, None], rd, spec.rope_theta, +1), dtype)
+        assert not np.array_equal(plain, ref)
 
 
 def test_chunked_prefill_equals_one_shot(csa):
@@ -670,9 +752,23 @@ def test_varlen_prefill_matches_separate_calls(csa):
     qs = [0, 3, 4, 130, 255, 300, 411, 412]
     ref = O.csa_prefill(spec, x, queries=qs)
     gi = idx[1].cpu().numpy()
+    nd = 0
+    for j, t in enumerate(qs):
+        sc, ab = index_exact(spec, x["qi"][t], x["wi"][t], ref["ipool"][:(t + 1) // 4], t)
+        nd += audit_topk(gi[t], ref["idx"][j], sc, ab, spec.index_dim, spec.index_heads)
+    say(f"  near-tie id differences: {nd}")
     same = [j for j, t in enumerate(qs) if np.array_equal(gi[t], ref["idx"][j])]
-    assert len(same) >= len(qs) - 1, "ids differ beyond a near tie"
     assert_close(host(out[1])[qs][same], ref["out"][same], "bf16", "varlen rows vs oracle")
+    # every sampled row again with the oracle's ids (the second call appended
+    # positions 413..712 of this sequence: ring slots and pool rows the first
+    # call's queries read are unchanged)
+    idx_o = idx.clone()
+    idx_o[1, qs] = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+    out_o = torch.empty_like(out)
+    m.csa_attend(L, p0, 0, a["q"], cache.ring, cache.pool, idx_o, sinks, out_o,
+                 cache.workspace(S, m.CSA_OP_ATTEND), n_valid=nv)
+    torch.cuda.synchronize()
+    assert_close(host(out_o[1])[qs], ref["out"], "bf16", "varlen rows vs oracle (oracle ids)")
 
 
 @pytest.mark.parametrize("kind", ["hca", "sliding"])
