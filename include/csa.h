@@ -17,7 +17,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is DEVICE memory owned by the caller.  The library
- *    allocates nothing and keeps no mutable global state; calls on different
+ *    allocates nothing and keeps no mutable global state (the one exception
+ *    is csa_index_topk_noalloc's static scratch array); calls on different
  *    streams may run concurrently when their buffers do not overlap.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Argument errors are returned before any launch and leave all
@@ -54,7 +55,9 @@ typedef enum {
   CSA_ERR_DTYPE = 3,       /* unknown storage dtype                            */
   CSA_ERR_UNSUPPORTED = 4, /* valid request this library does not implement    */
   CSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
-  CSA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed       */
+  CSA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed       */
+  CSA_ERR_SCRATCH = 7      /* the call needs more than the static scratch of
+                              csa_index_topk_noalloc                           */
 } csa_status;
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
@@ -196,6 +199,27 @@ csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch,
                           int32_t* topk_idx, float* scores_out,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* csa_index_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus workspace), same
+ * results, same kernels.  The workspace is a static device array of the
+ * library, CSA_NOALLOC_SCRATCH_BYTES bytes, one copy per device, held until
+ * the process ends; its device address is looked up once per device (the
+ * current device at the call; `stream` must belong to it).  A call whose
+ * workspace (csa_workspace_bytes(..., CSA_OP_INDEX_TOPK)) exceeds that size
+ * returns CSA_ERR_SCRATCH before any launch, e.g. decode of 64 sequences
+ * over 32768-entry pools needs about 26 MiB.  Every call on a device shares
+ * that device's array and leaves its contents behind: calls that overlap in
+ * time on one device (different streams, or host threads racing) corrupt
+ * each other's selection; calls queued on one stream are ordered and safe.
+ * The call allocates nothing (no hipMalloc / hipFree). */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa_status csa_index_topk_noalloc(const csa_layer* layer, const csa_batch* batch,
+                                  const void* q_idx, const void* weights,
+                                  const void* k_pool, int64_t pool_cap,
+                                  int32_t* topk_idx, float* scores_out,
+                                  hipStream_t stream);
 
 /* CSA attention: per query t and head h, one softmax over the window rows of
  * t (from the ring written by csa_window_append) and the pooled rows listed in

@@ -22,15 +22,17 @@ __all__ = [
     "Layer", "load_library", "library_path", "csa_window_append", "csa_rope", "csa_compress",
     "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
     "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
-    "csa_output_projection", "csa_project",
+    "csa_output_projection", "csa_project", "csa_index_topk_noalloc",
+    "CSA_NOALLOC_SCRATCH_BYTES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 CSA_OP_INDEX_TOPK, CSA_OP_ATTEND, CSA_OP_HCA_ATTEND = 1, 2, 3
+CSA_NOALLOC_SCRATCH_BYTES = 32 << 20    # CSA_NOALLOC_SCRATCH_BYTES of csa.h
 EXPORTED_SYMBOLS = ("csa_window_append", "csa_rope", "csa_compress", "csa_index_topk",
                     "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
                     "csa_version", "csa_output_projection", "csa_output_projection_workspace_bytes",
-                    "csa_project", "csa_project_workspace_bytes")
+                    "csa_project", "csa_project_workspace_bytes", "csa_index_topk_noalloc")
 
 
 class _CLayer(ctypes.Structure):
@@ -138,6 +140,7 @@ def load_library():
         "csa_rope": [LP, BP, P, I32, I32, I32, I32, P],
         "csa_compress": [LP, BP, I32, I32, P, P, P, ctypes.c_float, P, P, P, I64, P],
         "csa_index_topk": [LP, BP, P, P, P, I64, P, P, P, SZ, P],
+        "csa_index_topk_noalloc": [LP, BP, P, P, P, I64, P, P, P],
         "csa_attend": [LP, BP, P, P, I64, P, I64, P, P, P, P, SZ, P],
         "hca_attend": [LP, BP, P, P, I64, P, I64, P, P, P, SZ, P],
         "csa_output_projection": [ctypes.POINTER(_COproj), P, P, P, P, P, SZ, P],
@@ -281,6 +284,21 @@ def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, to
         _ptr(k_pool, "k_pool", dt), k_pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
         _ptr(scores_out, "scores_out", torch.float32), _ptr(ws, "workspace"), wsb, _stream()),
         "csa_index_topk")
+
+
+def csa_index_topk_noalloc(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,
+                           scores_out=None, n_valid=None):
+    """csa_index_topk on the library's static scratch (no workspace argument,
+    nothing allocated); calls overlapping on one device race on it."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n = q_idx.shape[:2]
+    bt = _batch(pos0, pos0_max, B, n, n_valid)
+    lay = layer._c()
+    _check(load_library().csa_index_topk_noalloc(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(q_idx, "q_idx", dt), _ptr(weights, "weights", dt),
+        _ptr(k_pool, "k_pool", dt), k_pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(scores_out, "scores_out", torch.float32), _stream()), "csa_index_topk_noalloc")
 
 
 def csa_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, topk_idx, sinks, out,

@@ -3,6 +3,8 @@
 // buffer.  See include/csa.h for the contract of each entry point.
 #include <math.h>
 
+#include <mutex>
+
 #include "csa.h"
 #include "csa_internal.h"
 
@@ -132,6 +134,49 @@ csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const v
                                        topk_idx, sinks, out, workspace, csa_layer_kind, stream));
 }
 
+// Static scratch of csa_index_topk_noalloc: one array per device (each
+// device that loads the library holds its own copy until the process ends).
+// Host code never passes `scratch` itself to a kernel (in host code the name
+// is a host-side stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in scratch_dev.
+constexpr size_t kScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+csa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return CSA_OK;
+}
+
+// Argument checks of csa_index_topk (no launch); *need receives the
+// workspace bytes of the call.
+csa_status index_topk_check(const csa_layer* layer, const csa_batch* batch, const void* q_idx,
+                            const void* weights, const void* k_pool, int64_t pool_cap,
+                            const int32_t* topk_idx, Layer* L, Batch* b, size_t* need) {
+  csa_status st = to_layer(layer, L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, b)) != CSA_OK) return st;
+  if (!q_idx || !weights || !k_pool || !topk_idx) return CSA_ERR_NULL;
+  if ((st = indexer_ok(*L)) != CSA_OK) return st;
+  if (pool_cap < entries_needed(*L, *b) || pool_cap < 1) return CSA_ERR_SHAPE;
+  if (!(L->dtype == CSA_BF16 && L->Hi == 64 && L->Di == 128) && !generic_index_ok(*L))
+    return CSA_ERR_UNSUPPORTED;
+  *need = csa::index_workspace_bytes(*L, b->B, b->n, pool_cap);
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,19 +233,31 @@ csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch, const 
                           size_t workspace_bytes, hipStream_t stream) {
   Layer L;
   Batch b;
-  csa_status st = to_layer(layer, &L);
+  size_t need = 0;
+  const csa_status st = index_topk_check(layer, batch, q_idx, weights, k_pool, pool_cap, topk_idx,
+                                         &L, &b, &need);
   if (st != CSA_OK) return st;
-  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
-  if (!q_idx || !weights || !k_pool || !topk_idx) return CSA_ERR_NULL;
-  if ((st = indexer_ok(L)) != CSA_OK) return st;
-  if (pool_cap < entries_needed(L, b) || pool_cap < 1) return CSA_ERR_SHAPE;
-  if (!(L.dtype == CSA_BF16 && L.Hi == 64 && L.Di == 128) && !generic_index_ok(L))
-    return CSA_ERR_UNSUPPORTED;
-  const size_t need = csa::index_workspace_bytes(L, b.B, b.n, pool_cap);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
     return CSA_ERR_WORKSPACE;
   return hip_status(csa::launch_index_topk(L, b, q_idx, weights, k_pool, pool_cap, topk_idx,
                                            scores_out, workspace, stream));
+}
+
+csa_status csa_index_topk_noalloc(const csa_layer* layer, const csa_batch* batch,
+                                  const void* q_idx, const void* weights, const void* k_pool,
+                                  int64_t pool_cap, int32_t* topk_idx, float* scores_out,
+                                  hipStream_t stream) {
+  Layer L;
+  Batch b;
+  size_t need = 0;
+  csa_status st = index_topk_check(layer, batch, q_idx, weights, k_pool, pool_cap, topk_idx, &L,
+                                   &b, &need);
+  if (st != CSA_OK) return st;
+  if (need > kScratchBytes) return CSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != CSA_OK) return st;
+  return hip_status(csa::launch_index_topk(L, b, q_idx, weights, k_pool, pool_cap, topk_idx,
+                                           scores_out, ws, stream));
 }
 
 csa_status csa_attend(const csa_layer* layer, const csa_batch* batch, const void* q,
@@ -327,10 +384,12 @@ const char* csa_status_str(csa_status s) {
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: configuration not implemented";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing, short or misaligned";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: HIP launch failed";
+    case CSA_ERR_SCRATCH:
+      return "CSA_ERR_SCRATCH: the call needs more than the library's static scratch buffer";
   }
   return "unknown csa_status";
 }
 
-int32_t csa_version(void) { return 200; }  // 0.2.0: projections, variable-length batches
+int32_t csa_version(void) { return 300; }  // 0.3.0: allocation-free index entry point
 
 }  // extern "C"

@@ -37,9 +37,9 @@ def test_every_declared_entry_point_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         assert m.csa_status_str(code).startswith("CSA_")
-    assert lib.csa_version() >= 200
+    assert lib.csa_version() >= 300
 
 
 def csa_layer(**kw):
@@ -118,6 +118,18 @@ def test_rejections_return_before_launch(lib):
                               ctypes.c_void_p(0x1010), 1 << 40, None) == WS   # misaligned
     assert lib.csa_index_topk(ctypes.byref(csa_layer(index_rope_dim=200)), ctypes.byref(B), FAKE,
                               FAKE, FAKE, 2048, FAKE, None, FAKE, 1 << 40, None) == SHAPE
+    # the allocation-free indexer: argument errors first, then the scratch limit,
+    # all before any HIP call (a prefill of 8192 tokens needs 64 MiB of scores)
+    NOALLOC = lib.csa_index_topk_noalloc
+    assert NOALLOC(ctypes.byref(L), ctypes.byref(B), None, FAKE, FAKE, 2048, FAKE, None,
+                   None) == NULL
+    assert NOALLOC(ctypes.byref(L), ctypes.byref(B), FAKE, FAKE, FAKE, 2047, FAKE, None,
+                   None) == SHAPE
+    assert NOALLOC(ctypes.byref(L), ctypes.byref(B), FAKE, FAKE, FAKE, 2048, FAKE, None,
+                   None) == 7   # CSA_ERR_SCRATCH
+    assert m.csa_workspace_bytes(m.Layer("bf16", 64, 512, 64, 160000.0, 128, 4, 1, 64, 128, 64,
+                                         512), 1, 8192, 2048, m.CSA_OP_INDEX_TOPK) > \
+        m.CSA_NOALLOC_SCRATCH_BYTES
     # rope / window
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 64, 2, None) == SHAPE
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 65, 1, None) == SHAPE
