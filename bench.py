@@ -216,7 +216,18 @@ def prefill_leg(torch, m, name, steps, warmup, attn_events=False):
     return spec, inp, res
 
 
-def decode_leg(torch, m, name, steps, warmup):
+def _block_table(torch, B, per_seq, seed):
+    """A shuffled block table: B sequences x per_seq blocks over B per_seq blocks."""
+    import numpy as np
+    ids = np.random.default_rng(seed).permutation(B * per_seq).reshape(B, per_seq)
+    return torch.from_numpy(ids.astype(np.int32)).cuda(), ids
+
+
+def decode_leg(torch, m, name, steps, warmup, paged=False):
+    """One decode step of every layer of the workload, replayed as a HIP graph.
+    paged: each layer's pools live in blocks (256 entries for CSA layers, 128
+    for HCA layers) of one tensor per layer, mapped by a shuffled table."""
+    import numpy as np
     import synth
     from long_context_sparse_gated_amd.layer import LayerCache, layer_step
     w = synth.workload(name)
@@ -225,17 +236,32 @@ def decode_leg(torch, m, name, steps, warmup):
     for li, spec in enumerate(w.layers):
         L = m.Layer.from_spec(spec)
         pool_cap = (t + 1) // spec.ratio if spec.ratio else 1
-        cache = LayerCache(L, B, spec.window, pool_cap)
+        kw, tab_h, E = {}, None, 0
+        if paged and spec.ratio:
+            E = 256 if spec.has_indexer else 128
+            per = (pool_cap + E - 1) // E
+            tab, tab_h = _block_table(torch, B, per, seed=li)
+            kw = dict(block_entries=E, pool_blocks=B * per, block_table=tab)
+        cache = LayerCache(L, B, spec.window, pool_cap, **kw)
         for b in range(B):  # one sequence at a time keeps host memory bounded
             c = synth.decode_cache_seq(w, 0, li, b)
             cache.ring[b].copy_(_dev(torch, c["win"]))
             if spec.ratio:
                 P = t // spec.ratio
-                cache.pool[b, :P].copy_(_dev(torch, c["pool"]))
+                if tab_h is not None:
+                    j = np.arange(P)
+                    rows = torch.from_numpy(tab_h[b][j // E] * E + j % E).cuda()
+                    cache.pool[rows] = _dev(torch, c["pool"])
+                    if spec.has_indexer:
+                        cache.ipool[rows] = _dev(torch, c["ipool"])
+                    del rows
+                else:
+                    cache.pool[b, :P].copy_(_dev(torch, c["pool"]))
+                    if spec.has_indexer:
+                        cache.ipool[b, :P].copy_(_dev(torch, c["ipool"]))
                 cache.cstate_kv[b].copy_(_dev(torch, c["cstate_kv"]))
                 cache.cstate_gate[b].copy_(_dev(torch, c["cstate_gate"]))
                 if spec.has_indexer:
-                    cache.ipool[b, :P].copy_(_dev(torch, c["ipool"]))
                     cache.istate_kv[b].copy_(_dev(torch, c["istate_kv"]))
                     cache.istate_gate[b].copy_(_dev(torch, c["istate_gate"]))
             del c
@@ -267,9 +293,12 @@ def decode_leg(torch, m, name, steps, warmup):
     gbs = total_bytes / (ms * 1e-3) / 1e9
     del graph, layers
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": total_bytes,
-            "achieved_GBs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "hip_graph": True,
-            "eager_ms_per_step": eager_ms}
+    res = {"ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": total_bytes,
+           "achieved_GBs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "hip_graph": True,
+           "eager_ms_per_step": eager_ms}
+    if paged:
+        res["paged"] = "pools in shuffled blocks: 256 entries (CSA layers), 128 (HCA layers)"
+    return res
 
 
 def oproj_leg(torch, m, steps, warmup):
@@ -321,6 +350,35 @@ def varlen_leg(torch, m, steps, warmup):
             "lens": list(VARLEN_LENS), "padded_to": S,
             "note": "the prefill scoring, selection and attention kernels skip padding rows "
                     "(left unspecified); the caches advance by the valid tokens"}
+
+
+def packed_leg(torch, m, steps, warmup):
+    """The same four CSA sequences as varlen_prefill with packed rows
+    (cu_seqlens, no padding rows), priced in tokens."""
+    import numpy as np
+    import synth
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    S, B = max(VARLEN_LENS), len(VARLEN_LENS)
+    w = synth.workload("csa_prefill", S=S, batch=B)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 0)
+    L = m.Layer.from_spec(spec)
+    keys = ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+    a = {k: torch.cat([_dev(torch, inp[k][b, :n]) for b, n in enumerate(VARLEN_LENS)])
+         for k in keys}
+    sinks = _dev(torch, inp["sinks"])
+    cache = LayerCache(L, B, S, S // spec.ratio)
+    p0 = torch.zeros(B, dtype=torch.int64, device="cuda")
+    cu = torch.tensor(np.r_[0, np.cumsum(VARLEN_LENS)], dtype=torch.int32, device="cuda")
+    out = torch.empty_like(a["q"])
+    idx = torch.empty(a["q"].shape[0], spec.topk, dtype=torch.int32, device="cuda")
+    ms, _ = _time_steps(torch, lambda _ev: layer_step(
+        cache, p0, 0, *(a[k] for k in keys), sinks, out=out, topk_idx=idx, cu_seqlens=cu,
+        n_new=S), steps, warmup)
+    valid = sum(VARLEN_LENS)
+    del a, cache, out, idx
+    return {"ms_per_step": ms, "tokens_per_s": valid / (ms * 1e-3), "lens": list(VARLEN_LENS),
+            "note": "packed rows: every per-token tensor holds the sequences back to back"}
 
 
 def proj_leg(torch, m, steps, warmup):
@@ -382,6 +440,11 @@ def run_leg(torch, m, name, args):
         return r
     if name in ("csa_decode", "mixed_decode"):
         return decode_leg(torch, m, name, 5 * args.steps, args.warmup)
+    if name in ("csa_decode_paged", "mixed_decode_paged"):
+        return decode_leg(torch, m, name[:-len("_paged")], 5 * args.steps, args.warmup,
+                          paged=True)
+    if name == "packed_prefill":
+        return packed_leg(torch, m, args.steps, args.warmup)
     if name == "output_projection":
         return oproj_leg(torch, m, args.steps, args.warmup)
     if name == "projections":
@@ -399,11 +462,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1)
     ap.add_argument("--legs",
-                    default="hca_prefill,csa_decode,mixed_decode,output_projection,projections,"
-                            "varlen_prefill",
+                    default="hca_prefill,csa_decode,mixed_decode,mixed_decode_paged,"
+                            "output_projection,projections,varlen_prefill,packed_prefill",
                     help="comma list of further workloads to time after the headline "
-                         "(hca_prefill, csa_decode, mixed_decode, output_projection, "
-                         "projections, varlen_prefill; empty for none)")
+                         "(hca_prefill, csa_decode, mixed_decode, csa_decode_paged, "
+                         "mixed_decode_paged, output_projection, projections, varlen_prefill, "
+                         "packed_prefill; empty for none)")
     ap.add_argument("--only", default="",
                     help="time just this one workload and print its object (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

@@ -119,6 +119,36 @@ typedef struct {
                                calls leave their outputs for padding rows
                                unspecified (they read only in-bounds rows).
                                NULL: every sequence has n_new tokens.        */
+  /* Packed variable-length rows (NULL: rows of sequence b are b n_new .. b n_new
+   * + n_new - 1, padded).  With cu_seqlens, a device [B + 1] array of
+   * non-decreasing row offsets, sequence b has the cu_seqlens[b + 1] -
+   * cu_seqlens[b] tokens (at most n_new; n_new is then the longest sequence's
+   * length) in rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of every per-token
+   * tensor (kv, gate, q, q_idx, weights, topk_idx, out, csa_rope's x): the
+   * tensors hold no padding rows.  Mutually exclusive with n_valid.  The
+   * scores_out rows of csa_index_topk stay indexed by b n_new + i.          */
+  const int32_t* cu_seqlens;
+  /* Paged pools (NULL: every pool argument is the contiguous [B, pool_cap,
+   * width] tensor).  With block_table, a device [B, block_table_stride] int32
+   * array, entry w of sequence b lives in row
+   *   block_table[b][w / block_entries] * block_entries + w % block_entries
+   * of the pool tensor, which holds pool_blocks blocks of block_entries rows
+   * ([pool_blocks * block_entries, width]); pool_cap stays the entries per
+   * sequence and must not exceed block_table_stride * block_entries.  The main
+   * pool and the indexer pool of a layer share the entry ids and so one table
+   * (two tensors of different widths); each layer has its own table, since
+   * the layers' pools differ in ratio and size.  The table entries a call
+   * touches (blocks holding entries below (pos0[b] + n_new) / m) must lie in
+   * 0 .. pool_blocks - 1 and must not be shared between sequences that a call
+   * writes (not checked).  Window rings and compressor states do not grow with
+   * the context and stay per-sequence arrays.
+   * Source: model page, "Cache layers" (one cache type per layer, each with
+   * its own pool); optimum-intel issue 1748 ("What native registration would
+   * touch": the KV cache is not uniform across layers). */
+  const int32_t* block_table;
+  int32_t block_entries;       /* a power of two, 128 .. 2^24 (paged)          */
+  int32_t block_table_stride;  /* blocks per sequence row of block_table       */
+  int64_t pool_blocks;         /* blocks in each pool tensor (paged)          */
 } csa_batch;
 
 /* Write the window rows of the new tokens into a ring buffer.
@@ -133,10 +163,12 @@ csa_status csa_window_append(const csa_layer* layer, const csa_batch* batch,
                              const void* kv, void* ring, int64_t cap,
                              hipStream_t stream);
 
-/* Rotate rows in place: x [B, n_new, rows_per_token, width] (dtype); row r of
- * token i of sequence b is rotated at position sign * (pos0[b] + i) on its
- * last rope_dim channels, interleaved pairs (c, c+1) as complex numbers,
- * frequency base^(-2j/rope_dim) for pair j.  sign is +1 or -1.
+/* Rotate rows in place: x [B, n_new, rows_per_token, width] (dtype; packed:
+ * [rows, rows_per_token, width]); row r of token i of sequence b is rotated
+ * at position sign * (pos0[b] + i) on its last rope_dim channels, interleaved
+ * pairs (c, c+1) as complex numbers, frequency base^(-2j/rope_dim) for pair j
+ * (YaRN-scaled as the layer's rope_factor asks).  sign is +1 or -1.  Rows of
+ * padding tokens (n_valid) are left as they are.
  * Source: transformers PR 45616 notes on RoPE apply (interleaved-pair
  * rotation via complex multiplication) and the model page, sec. 2.3. */
 csa_status csa_rope(const csa_layer* layer, const csa_batch* batch, void* x,

@@ -23,7 +23,7 @@ __all__ = [
     "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
     "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
     "csa_output_projection", "csa_project", "csa_index_topk_noalloc",
-    "CSA_NOALLOC_SCRATCH_BYTES",
+    "CSA_NOALLOC_SCRATCH_BYTES", "Paged",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,7 +64,9 @@ class _CProj(ctypes.Structure):
 class _CBatch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_new", ctypes.c_int32),
                 ("pos0", ctypes.c_void_p), ("pos0_max", ctypes.c_int64),
-                ("n_valid", ctypes.c_void_p)]
+                ("n_valid", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("block_entries", ctypes.c_int32),
+                ("block_table_stride", ctypes.c_int32), ("pool_blocks", ctypes.c_int64)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -197,17 +199,58 @@ def _store_dtype(layer: Layer):
     return torch.bfloat16 if layer.dtype == "bf16" else torch.float32
 
 
-def _batch(pos0, pos0_max, B, n, n_valid=None):
+@dataclasses.dataclass(frozen=True)
+class Paged:
+    """Block table of one layer's paged pools (``csa_batch.block_table``):
+    entry w of sequence b is row ``block_table[b, w // block_entries] *
+    block_entries + w % block_entries`` of each pool tensor, which is
+    ``[blocks * block_entries, width]``; ``pool_cap`` entries per sequence."""
+    block_table: object     # int32 [B, stride] device tensor
+    block_entries: int
+    pool_cap: int
+
+
+def _batch(pos0, pos0_max, B, n, n_valid=None, cu_seqlens=None, paged=None, pool=None):
     torch = _torch()
     _ptr(pos0, "pos0", torch.int64)
     if pos0.numel() != B:
         raise ValueError("pos0 must hold one position per sequence")
-    nv = None
+    nv = cu = None
     if n_valid is not None:
         nv = _ptr(n_valid, "n_valid", torch.int32)
         if n_valid.numel() != B:
             raise ValueError("n_valid must hold one count per sequence")
-    return _CBatch(B, n, pos0.data_ptr(), int(pos0_max), nv)
+    if cu_seqlens is not None:
+        cu = _ptr(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.numel() != B + 1:
+            raise ValueError("cu_seqlens must hold B + 1 row offsets")
+    tab, E, stride, blocks = None, 0, 0, 0
+    if paged is not None:
+        tab = _ptr(paged.block_table, "block_table", torch.int32)
+        if paged.block_table.dim() != 2 or paged.block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, blocks per sequence]")
+        E, stride = int(paged.block_entries), int(paged.block_table.shape[1])
+        if pool is None or pool.dim() != 2 or pool.shape[0] % E:
+            raise ValueError("a paged pool is [blocks * block_entries, width]")
+        blocks = pool.shape[0] // E
+    return _CBatch(B, n, pos0.data_ptr(), int(pos0_max), nv, cu, tab, E, stride, blocks)
+
+
+def _lead(x, nd_tail, cu_seqlens, n_new, pos0):
+    """(B, n) of a per-token tensor: [B, n, *tail] padded, [rows, *tail] packed."""
+    if cu_seqlens is None:
+        if x.dim() != 2 + nd_tail:
+            raise ValueError("per-token tensors are [B, n_new, ...] (padded rows)")
+        return x.shape[0], x.shape[1]
+    if n_new is None or x.dim() != 1 + nd_tail:
+        raise ValueError("packed calls take [rows, ...] tensors and n_new (longest sequence)")
+    return pos0.numel(), int(n_new)
+
+
+def _pool_cap(pool, paged):
+    if pool is None:
+        return 0
+    return int(paged.pool_cap) if paged is not None else pool.shape[1]
 
 
 def _stream():
@@ -232,99 +275,115 @@ def _workspace(layer, B, n, pool_cap, op, ws, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def csa_window_append(layer: Layer, pos0, pos0_max: int, kv, ring, n_valid=None):
-    """kv [B, n_new, D] -> ring [B, cap, D] at slot position % cap, rotated.
-    n_valid (int32 [B], optional): only the first n_valid[b] rows are appended."""
+def csa_window_append(layer: Layer, pos0, pos0_max: int, kv, ring, n_valid=None,
+                      cu_seqlens=None, n_new=None):
+    """kv [B, n_new, D] (packed: [rows, D]) -> ring [B, cap, D] at slot position % cap,
+    rotated.  n_valid (int32 [B], optional): only the first n_valid[b] rows are appended."""
     dt = _store_dtype(layer)
-    B, n, D = kv.shape
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
+    B, n = _lead(kv, 1, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens)
     lay = layer._c()
     _check(load_library().csa_window_append(
         ctypes.byref(lay), ctypes.byref(bt), _ptr(kv, "kv", dt), _ptr(ring, "ring", dt),
         ring.shape[1], _stream()), "csa_window_append")
 
 
-def csa_rope(layer: Layer, pos0, pos0_max: int, x, rope_dim: int, sign: int = 1):
-    """x [B, n_new, rows, width] rotated in place at sign * position."""
+def csa_rope(layer: Layer, pos0, pos0_max: int, x, rope_dim: int, sign: int = 1, n_valid=None,
+             cu_seqlens=None, n_new=None):
+    """x [B, n_new, rows, width] (packed: [rows, rows_per_token, width]) rotated in place
+    at sign * position."""
     dt = _store_dtype(layer)
-    B, n, rows, width = x.shape
-    bt = _batch(pos0, pos0_max, B, n)
+    B, n = _lead(x, 2, cu_seqlens, n_new, pos0)
+    rows, width = x.shape[-2], x.shape[-1]
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens)
     lay = layer._c()
     _check(load_library().csa_rope(ctypes.byref(lay), ctypes.byref(bt), _ptr(x, "x", dt), rows,
                                    width, rope_dim, sign, _stream()), "csa_rope")
 
 
 def csa_compress(layer: Layer, pos0, pos0_max: int, kv, gate, state_kv, state_gate, pool,
-                 rope_dim: int, norm_weight=None, norm_eps: float = 1e-6, n_valid=None):
-    """kv, gate [B, n_new, width]; state_* [B, (1+overlap)m, width]; pool [B, cap, width].
+                 rope_dim: int, norm_weight=None, norm_eps: float = 1e-6, n_valid=None,
+                 cu_seqlens=None, n_new=None, paged: Optional[Paged] = None):
+    """kv, gate [B, n_new, width] (packed: [rows, width]); state_* [B, (1+overlap)m, width];
+    pool [B, cap, width] (paged: [blocks * block_entries, width]).
     n_valid (int32 [B], optional): only the first n_valid[b] rows are pooled and kept."""
     torch = _torch()
     dt = _store_dtype(layer)
-    B, n, width = kv.shape
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
+    B, n = _lead(kv, 1, cu_seqlens, n_new, pos0)
+    width = kv.shape[-1]
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged, pool)
     lay = layer._c()
     _check(load_library().csa_compress(
         ctypes.byref(lay), ctypes.byref(bt), width, rope_dim, _ptr(kv, "kv", dt),
         _ptr(gate, "gate", dt), _ptr(norm_weight, "norm_weight", torch.float32), norm_eps,
         _ptr(state_kv, "state_kv", dt), _ptr(state_gate, "state_gate", dt),
-        _ptr(pool, "pool", dt), pool.shape[1], _stream()), "csa_compress")
+        _ptr(pool, "pool", dt), _pool_cap(pool, paged), _stream()), "csa_compress")
 
 
 def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,
-                   scores_out=None, workspace=None, n_valid=None):
-    """q_idx [B,n,H_I,D_I], weights [B,n,H_I], k_pool [B,cap,D_I] -> topk_idx [B,n,k] int32."""
+                   scores_out=None, workspace=None, n_valid=None, cu_seqlens=None, n_new=None,
+                   paged: Optional[Paged] = None):
+    """q_idx [B,n,H_I,D_I], weights [B,n,H_I], k_pool [B,cap,D_I] -> topk_idx [B,n,k] int32
+    (packed: leading [rows] instead of [B, n]; paged: k_pool [blocks * block_entries, D_I])."""
     torch = _torch()
     dt = _store_dtype(layer)
-    B, n = q_idx.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
-    ws, wsb = _workspace(layer, B, n, k_pool.shape[1], CSA_OP_INDEX_TOPK, workspace, q_idx.device)
+    B, n = _lead(q_idx, 2, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged, k_pool)
+    pcap = _pool_cap(k_pool, paged)
+    ws, wsb = _workspace(layer, B, n, pcap, CSA_OP_INDEX_TOPK, workspace, q_idx.device)
     lay = layer._c()
     _check(load_library().csa_index_topk(
         ctypes.byref(lay), ctypes.byref(bt), _ptr(q_idx, "q_idx", dt), _ptr(weights, "weights", dt),
-        _ptr(k_pool, "k_pool", dt), k_pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(k_pool, "k_pool", dt), pcap, _ptr(topk_idx, "topk_idx", torch.int32),
         _ptr(scores_out, "scores_out", torch.float32), _ptr(ws, "workspace"), wsb, _stream()),
         "csa_index_topk")
 
 
 def csa_index_topk_noalloc(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,
-                           scores_out=None, n_valid=None):
+                           scores_out=None, n_valid=None, cu_seqlens=None, n_new=None,
+                           paged: Optional[Paged] = None):
     """csa_index_topk on the library's static scratch (no workspace argument,
     nothing allocated); calls overlapping on one device race on it."""
     torch = _torch()
     dt = _store_dtype(layer)
-    B, n = q_idx.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
+    B, n = _lead(q_idx, 2, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged, k_pool)
     lay = layer._c()
     _check(load_library().csa_index_topk_noalloc(
         ctypes.byref(lay), ctypes.byref(bt), _ptr(q_idx, "q_idx", dt), _ptr(weights, "weights", dt),
-        _ptr(k_pool, "k_pool", dt), k_pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
-        _ptr(scores_out, "scores_out", torch.float32), _stream()), "csa_index_topk_noalloc")
+        _ptr(k_pool, "k_pool", dt), _pool_cap(k_pool, paged),
+        _ptr(topk_idx, "topk_idx", torch.int32), _ptr(scores_out, "scores_out", torch.float32),
+        _stream()), "csa_index_topk_noalloc")
 
 
 def csa_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, topk_idx, sinks, out,
-               workspace=None, n_valid=None):
-    """q [B,n,H,D], win [B,cap,D], pool [B,pcap,D], topk_idx [B,n,k], sinks [H] -> out."""
+               workspace=None, n_valid=None, cu_seqlens=None, n_new=None,
+               paged: Optional[Paged] = None):
+    """q [B,n,H,D], win [B,cap,D], pool [B,pcap,D], topk_idx [B,n,k], sinks [H] -> out
+    (packed: leading [rows] instead of [B, n]; paged: pool [blocks * block_entries, D])."""
     torch = _torch()
     dt = _store_dtype(layer)
-    B, n = q.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
-    ws, wsb = _workspace(layer, B, n, pool.shape[1], CSA_OP_ATTEND, workspace, q.device)
+    B, n = _lead(q, 2, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged, pool)
+    pcap = _pool_cap(pool, paged)
+    ws, wsb = _workspace(layer, B, n, pcap, CSA_OP_ATTEND, workspace, q.device)
     lay = layer._c()
     _check(load_library().csa_attend(
         ctypes.byref(lay), ctypes.byref(bt), _ptr(q, "q", dt), _ptr(win, "win", dt), win.shape[1],
-        _ptr(pool, "pool", dt), pool.shape[1], _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(pool, "pool", dt), pcap, _ptr(topk_idx, "topk_idx", torch.int32),
         _ptr(sinks, "sinks", torch.float32), _ptr(out, "out", dt), _ptr(ws, "workspace"), wsb,
         _stream()), "csa_attend")
 
 
 def hca_attend(layer: Layer, pos0, pos0_max: int, q, win, pool, sinks, out, workspace=None,
-               n_valid=None):
+               n_valid=None, cu_seqlens=None, n_new=None, paged: Optional[Paged] = None):
     """As csa_attend with every visible entry (compress_ratio 0: window only; pool may be None)."""
     torch = _torch()
     dt = _store_dtype(layer)
-    B, n = q.shape[:2]
-    bt = _batch(pos0, pos0_max, B, n, n_valid)
-    pcap = pool.shape[1] if pool is not None else 0
+    B, n = _lead(q, 2, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged if pool is not None else None,
+                pool)
+    pcap = _pool_cap(pool, paged)
     ws, wsb = _workspace(layer, B, n, pcap, CSA_OP_HCA_ATTEND, workspace, q.device)
     lay = layer._c()
     _check(load_library().hca_attend(

@@ -57,17 +57,48 @@ csa_status to_layer(const csa_layer* in, Layer* L) {
   return CSA_OK;
 }
 
-csa_status to_batch(const csa_batch* in, Batch* b) {
+csa_status to_batch(const csa_batch* in, Batch* b, int64_t* pool_rows = nullptr) {
   if (!in) return CSA_ERR_NULL;
   if (!in->pos0) return CSA_ERR_NULL;
   if (in->batch < 1 || in->n_new < 1 || in->pos0_max < 0 ||
       in->pos0_max > (int64_t)1 << 48)
     return CSA_ERR_SHAPE;
+  if (in->n_valid && in->cu_seqlens) return CSA_ERR_SHAPE;  // one layout per call
   b->B = in->batch;
   b->n = in->n_new;
   b->pos0 = in->pos0;
   b->pos0_max = in->pos0_max;
   b->nvalid = in->n_valid;
+  b->cu = in->cu_seqlens;
+  b->table = in->block_table;
+  b->bshift = 0;
+  b->tstride = 0;
+  int64_t rows = 0;
+  if (in->block_table) {
+    const int32_t e = in->block_entries;
+    // a power of two holding whole 128-entry tiles of the key scans
+    if (e < 128 || e > (1 << 24) || (e & (e - 1)) != 0 || in->block_table_stride < 1 ||
+        in->pool_blocks < 1 || in->pool_blocks > ((int64_t)1 << 40))
+      return CSA_ERR_SHAPE;
+    while ((1 << b->bshift) < e) ++b->bshift;
+    b->tstride = in->block_table_stride;
+    rows = in->pool_blocks * (int64_t)e;
+  }
+  if (pool_rows) *pool_rows = rows;
+  return CSA_OK;
+}
+
+// A pool argument of pool_cap entries per sequence: the contiguous tensor
+// [B, pool_cap, width], or (paged) pool_rows rows addressed through the
+// block table, which must cover pool_cap entries.  Row ids of the attention
+// kernels are int32.
+csa_status pool_ok(const Batch& b, int64_t pool_cap, int64_t pool_rows) {
+  if (b.table) {
+    if (pool_cap > ((int64_t)b.tstride << b.bshift)) return CSA_ERR_SHAPE;
+    if (pool_rows > kMaxRowId) return CSA_ERR_UNSUPPORTED;
+  } else if ((int64_t)b.B * pool_cap > kMaxRowId) {
+    return CSA_ERR_UNSUPPORTED;
+  }
   return CSA_OK;
 }
 
@@ -109,9 +140,10 @@ csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const v
                          size_t workspace_bytes, hipStream_t stream, bool csa_layer_kind) {
   Layer L;
   Batch b;
+  int64_t prow = 0;
   csa_status st = to_layer(layer, &L);
   if (st != CSA_OK) return st;
-  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if ((st = to_batch(batch, &b, &prow)) != CSA_OK) return st;
   if (!q || !win || !out) return CSA_ERR_NULL;
   if (csa_layer_kind) {
     if (L.m < 1 || L.k < 1 || L.k > csa::kMaxTopK) return CSA_ERR_SHAPE;
@@ -120,7 +152,7 @@ csa_status attend_common(const csa_layer* layer, const csa_batch* batch, const v
   if (L.m > 0) {
     if (!pool) return CSA_ERR_NULL;
     if (pool_cap < entries_needed(L, b)) return CSA_ERR_SHAPE;
-    if ((int64_t)b.B * pool_cap > kMaxRowId) return CSA_ERR_UNSUPPORTED;
+    if ((st = pool_ok(b, pool_cap, prow)) != CSA_OK) return st;
   }
   if ((st = window_ok(L, b, win_cap)) != CSA_OK) return st;
   if (!csa::attend_fast_shape(L) && !generic_attend_limit_ok(L)) return CSA_ERR_UNSUPPORTED;
@@ -165,12 +197,14 @@ csa_status scratch_address(void** out) {
 csa_status index_topk_check(const csa_layer* layer, const csa_batch* batch, const void* q_idx,
                             const void* weights, const void* k_pool, int64_t pool_cap,
                             const int32_t* topk_idx, Layer* L, Batch* b, size_t* need) {
+  int64_t prow = 0;
   csa_status st = to_layer(layer, L);
   if (st != CSA_OK) return st;
-  if ((st = to_batch(batch, b)) != CSA_OK) return st;
+  if ((st = to_batch(batch, b, &prow)) != CSA_OK) return st;
   if (!q_idx || !weights || !k_pool || !topk_idx) return CSA_ERR_NULL;
   if ((st = indexer_ok(*L)) != CSA_OK) return st;
   if (pool_cap < entries_needed(*L, *b) || pool_cap < 1) return CSA_ERR_SHAPE;
+  if ((st = pool_ok(*b, pool_cap, prow)) != CSA_OK) return st;
   if (!(L->dtype == CSA_BF16 && L->Hi == 64 && L->Di == 128) && !generic_index_ok(*L))
     return CSA_ERR_UNSUPPORTED;
   *need = csa::index_workspace_bytes(*L, b->B, b->n, pool_cap);
@@ -214,15 +248,17 @@ csa_status csa_compress(const csa_layer* layer, const csa_batch* batch, int32_t 
                         void* state_gate, void* pool, int64_t pool_cap, hipStream_t stream) {
   Layer L;
   Batch b;
+  int64_t prow = 0;
   csa_status st = to_layer(layer, &L);
   if (st != CSA_OK) return st;
-  if ((st = to_batch(batch, &b)) != CSA_OK) return st;
+  if ((st = to_batch(batch, &b, &prow)) != CSA_OK) return st;
   if (!kv || !gate || !state_kv || !state_gate || !pool) return CSA_ERR_NULL;
   if (L.m < 1) return CSA_ERR_SHAPE;
   if (width < 2 || (width & 1) || width > kMaxWidth || rope_dim < 0 || (rope_dim & 1) ||
       rope_dim > width || !(norm_eps >= 0.f))
     return CSA_ERR_SHAPE;
   if (pool_cap < entries_needed(L, b)) return CSA_ERR_SHAPE;
+  if ((st = pool_ok(b, pool_cap, prow)) != CSA_OK) return st;
   return hip_status(csa::launch_compress(L, b, width, rope_dim, kv, gate, norm_weight, norm_eps,
                                          state_kv, state_gate, pool, pool_cap, stream));
 }
@@ -390,6 +426,6 @@ const char* csa_status_str(csa_status s) {
   return "unknown csa_status";
 }
 
-int32_t csa_version(void) { return 300; }  // 0.3.0: allocation-free index entry point
+int32_t csa_version(void) { return 400; }  // 0.4.0: paged pools, packed variable-length rows
 
 }  // extern "C"

@@ -92,9 +92,8 @@ template <int R>
 __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
-    const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int n_new, int W,
-    int m, Rope base, float scale, int nsplit, int csa) {
+    const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part, Seqs sq,
+    int W, int m, Rope base, float scale, int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   // two separate arrays (not one indexed by parity) so the compiler can tell
   // the DMA target from the tile being read and need not wait for the DMA
@@ -109,12 +108,13 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 
   constexpr int NTH = 256;
   constexpr int RPW = kCH / 4;  // rows each wave gathers per chunk
-  const int i = n_new - 1 - (int)blockIdx.x;  // longest rows first
+  const int i = sq.n - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y, split = blockIdx.z;
-  if (i >= valid_tokens(nvalid, b, n_new)) return;  // a padding row: left as it is
+  if (i >= sq.len(b)) return;  // a padding row: left as it is
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
-  const int64_t t = pos0[b] + i;
-  const int64_t tok = (int64_t)b * n_new + i;
+  const int64_t t = sq.pos0[b] + i;
+  const int64_t tok = sq.row(b, i);             // row of q, the ids and the output
+  const int64_t slot = (int64_t)b * sq.n + i;   // slot of the split partials
   const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int nwin = (int)(t - lo + 1);
   int64_t nvis = m > 0 ? (t + 1) / m : 0;
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
   for (int j = tid; j < r1 - r0; j += NTH)
-    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis);
+    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq);
   for (int j = tid; j < R / 2; j += NTH) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
@@ -529,7 +529,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       *(uint4*)(orow + head * kAD + 8 * lane) = v;
     }
   } else {
-    float* pbase = part + (tok * nsplit + split) * kAH * kPart;
+    float* pbase = part + (slot * nsplit + split) * kAH * kPart;
 #if CSA_ATTN_PV32
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
@@ -564,14 +564,15 @@ constexpr int kMaxSplits = 256;
 
 __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
     const float* __restrict__ part, const float* __restrict__ sinks, bf16_t* __restrict__ out,
-    const int64_t* __restrict__ pos0, int n_new, int R, Rope base, int nsplit) {
+    Seqs sq, int R, Rope base, int nsplit) {
   __shared__ double2 cs[kAD / 2];
   __shared__ float fs[kMergeHeads][kMaxSplits];
-  const int64_t tok = blockIdx.x;
+  const int64_t tok = blockIdx.x;  // the token's slot b n + i (partials)
   const int lane = threadIdx.x & 63, hh = threadIdx.x >> 6;
   const int h = blockIdx.y * kMergeHeads + hh;
-  const int b = (int)(tok / n_new), i = (int)(tok % n_new);
-  const int64_t t = pos0[b] + i;
+  const int b = (int)(tok / sq.n), i = (int)(tok % sq.n);
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  const int64_t t = sq.pos0[b] + i;
   for (int j = threadIdx.x; j < R / 2; j += 64 * kMergeHeads) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
@@ -626,7 +627,7 @@ __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
   st.y = pack_bf16x2(o[2], o[3]);
   st.z = pack_bf16x2(o[4], o[5]);
   st.w = pack_bf16x2(o[6], o[7]);
-  *(uint4*)(out + (tok * kAH + h) * kAD + d0) = st;
+  *(uint4*)(out + (sq.row(b, i) * kAH + h) * kAD + d0) = st;
 }
 
 // ---------------------------------------------------------------------------
@@ -638,8 +639,8 @@ template <typename T>
 __global__ void __launch_bounds__(256) attend_generic(
     const T* __restrict__ q, const T* __restrict__ win, int64_t win_cap, const T* __restrict__ pool,
     int64_t pool_cap, const int32_t* __restrict__ idx, int k, const float* __restrict__ sinks,
-    T* __restrict__ out, const int64_t* __restrict__ pos0, int n_new, int H, int D, int R, int W,
-    int m, Rope base, float scale, int csa) {
+    T* __restrict__ out, Seqs sq, int H, int D, int R, int W, int m, Rope base, float scale,
+    int csa) {
   extern __shared__ float sm[];
   float* qs = sm;                      // [H*D]
   float* acc = qs + H * D;             // [H*D]
@@ -650,8 +651,9 @@ __global__ void __launch_bounds__(256) attend_generic(
   float* alph = lrun + H;              // [H]
   int* ok = (int*)(alph + H);          // [kGCh]
   const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t t = pos0[b] + i;
-  const int64_t tok = (int64_t)b * n_new + i;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  const int64_t t = sq.pos0[b] + i;
+  const int64_t tok = sq.row(b, i);
   const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int nwin = (int)(t - lo + 1);
   int64_t nvis = m > 0 ? (t + 1) / m : 0;
@@ -687,7 +689,7 @@ __global__ void __launch_bounds__(256) attend_generic(
     for (int e = threadIdx.x; e < kGCh * D; e += blockDim.x) {
       const int r = e / D, d = e % D;
       const int id = c0 + r < nrows ? row_id(c0 + r, nwin, lo, win_cap, b, pool_cap, idx_row,
-                                              csa, nvis)
+                                              csa, nvis, sq)
                                     : -1;
       float v = 0.f;
       if (id >= 0) v = store_t<T>::ld(win + (int64_t)id * D + d);
@@ -803,6 +805,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
                          int64_t win_cap, const void* pool, int64_t pool_cap, const int32_t* idx,
                          const float* sinks, void* out, void* ws, bool csa, hipStream_t s) {
   const int m = L.m;
+  const Seqs sq = seqs_of(bt);
   if (attend_fast_shape(L)) {
     const int ns = attend_splits(L, bt.B, bt.n, pool_cap, csa);
     if (attend_dec(L, bt.B, bt.n, pool_cap, csa)) {
@@ -810,14 +813,14 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
                                           ws, csa, ns, s);
       if (e != hipSuccess || ns == 1) return e;
       attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
-          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
+          (const float*)ws, sinks, (bf16_t*)out, sq, L.R, L.base, ns);
       return hipGetLastError();
     }
     dim3 grid(bt.n, bt.B, ns);
 #define CSA_ATTN_LAUNCH(RR)                                                                 \
   attend_mfma<RR><<<grid, 256, 0, s>>>(                                                     \
       (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k, \
-      sinks, (bf16_t*)out, (float*)ws, bt.pos0, bt.nvalid, bt.n, L.W, m, L.base, L.scale, ns, \
+      sinks, (bf16_t*)out, (float*)ws, sq, L.W, m, L.base, L.scale, ns,                     \
       csa ? 1 : 0)
     switch (L.R) {
       case 16: CSA_ATTN_LAUNCH(16); break;
@@ -830,7 +833,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
-          (const float*)ws, sinks, (bf16_t*)out, bt.pos0, bt.n, L.R, L.base, ns);
+          (const float*)ws, sinks, (bf16_t*)out, sq, L.R, L.base, ns);
     }
     return hipGetLastError();
   }
@@ -839,11 +842,11 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
   if (L.dtype == 1)
     attend_generic<bf16_t><<<grid, 256, shm, s>>>(
         (const bf16_t*)q, (const bf16_t*)win, win_cap, (const bf16_t*)pool, pool_cap, idx, L.k,
-        sinks, (bf16_t*)out, bt.pos0, bt.n, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
+        sinks, (bf16_t*)out, sq, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
   else
     attend_generic<float><<<grid, 256, shm, s>>>(
         (const float*)q, (const float*)win, win_cap, (const float*)pool, pool_cap, idx, L.k,
-        sinks, (float*)out, bt.pos0, bt.n, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
+        sinks, (float*)out, sq, L.H, L.D, L.R, L.W, m, L.base, L.scale, csa ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -56,14 +56,16 @@ __device__ __forceinline__ float xsum32(float v) {
 }
 
 // Row id encoding in LDS: >= 0 window ring row, <= -2 pool row -(id+2), -1 none.
+// Pool rows are those of the pool tensor (through the block table when the
+// pools are paged).
 __device__ __forceinline__ int row_id(int jr, int nwin, int64_t lo, int64_t win_cap, int b,
                                       int64_t pool_cap, const int32_t* idx_row, int csa,
-                                      int64_t nvis) {
+                                      int64_t nvis, const Seqs& sq) {
   if (jr < nwin) return (int)((int64_t)b * win_cap + (lo + jr) % win_cap);
   const int e = jr - nwin;
   const int64_t w = csa ? (int64_t)idx_row[e] : (int64_t)e;
   if (w < 0 || w >= nvis) return -1;
-  return (int)(-2 - ((int64_t)b * pool_cap + w));
+  return (int)(-2 - sq.prow(b, w, pool_cap));
 }
 
 // Chunk swizzle of LDS row r (16-byte chunks, 64 per row; only the low four

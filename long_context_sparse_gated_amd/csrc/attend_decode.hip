@@ -41,8 +41,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ win, int64_t win_cap,
     const bf16_t* __restrict__ pool, int64_t pool_cap, const int32_t* __restrict__ idx, int k,
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
-    const int64_t* __restrict__ pos0, int n_new, int tokens, int W, int m, Rope base,
-    float scale, int nsplit, int csa) {
+    Seqs sq, int tokens, int W, int m, Rope base, float scale, int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
   __shared__ __attribute__((aligned(1024))) bf16_t kb0[kDCh * kAD];
   __shared__ __attribute__((aligned(1024))) bf16_t kb1[kDCh * kAD];
@@ -62,9 +61,11 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   const int hg = jg & 3, sp = jg >> 2;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
-  const int b = tq / n_new, i = tq % n_new;
-  const int64_t t = pos0[b] + i;
-  const int64_t tok = tq;
+  const int b = tq / sq.n, i = tq % sq.n;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform, before any barrier)
+  const int64_t t = sq.pos0[b] + i;
+  const int64_t tok = sq.row(b, i);  // row of q, the ids and the output
+  const int64_t slot = tq;           // slot of the split partials
   const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int nwin = (int)(t - lo + 1);
   int64_t nvis = m > 0 ? (t + 1) / m : 0;
@@ -79,7 +80,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
   for (int j = tid; j < r1 - r0; j += 256)
-    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis);
+    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq);
   for (int j = tid; j < R / 2; j += 256) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
@@ -301,7 +302,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   } else {
     // float32 partial rows staged in kb0 (2 KB per head, 16-byte chunk c of
     // head row h at slot c ^ h), then written whole
-    float* pbase = part + ((tok * nsplit + sp) * kAH + 16 * hg) * kPart;
+    float* pbase = part + ((slot * nsplit + sp) * kAH + 16 * hg) * kPart;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int ch = 32 * wv + 4 * dt + g;  // 16-byte chunk of the 512-float row
@@ -351,7 +352,7 @@ hipError_t launch_attend_decode(const Layer& L, const Batch& bt, const void* q, 
 #define CSA_DEC_LAUNCH(RR)                                                                       \
   attend_decode<RR><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)win, win_cap,          \
                                          (const bf16_t*)pool, pool_cap, idx, L.k, sinks,          \
-                                         (bf16_t*)out, (float*)ws, bt.pos0, bt.n, tokens, L.W,    \
+                                         (bf16_t*)out, (float*)ws, seqs_of(bt), tokens, L.W,     \
                                          L.m, L.base, L.scale, ns, csa ? 1 : 0)
   switch (L.R) {
     case 16: CSA_DEC_LAUNCH(16); break;

@@ -27,12 +27,12 @@ template <typename T>
 __device__ __forceinline__ void pool_entry(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    int b, int64_t p0, int64_t w, int n_new, int width, int R, Rope base, int m, int overlap,
-    int64_t pool_cap, double* pooled, double* red) {
+    int b, int64_t p0, int64_t w, int64_t row0, int64_t dst_row, int width, int R, Rope base,
+    int m, int overlap, double* pooled, double* red) {
   const int Ls = (1 + overlap) * m;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
-  const T* kv_b = kv + (int64_t)b * n_new * width;
-  const T* g_b = gate + (int64_t)b * n_new * width;
+  const T* kv_b = kv + row0 * width;  // the call's token rows of sequence b
+  const T* g_b = gate + row0 * width;
   const T* skv_b = st_kv + (int64_t)b * Ls * width;
   const T* sg_b = st_gate + (int64_t)b * Ls * width;
   double ss = 0.0;
@@ -65,7 +65,7 @@ __device__ __forceinline__ void pool_entry(
       pooled[c] = pooled[c] * inv * (double)norm_w[c];
   }
   __syncthreads();
-  T* dst = pool + ((int64_t)b * pool_cap + w) * width;
+  T* dst = pool + dst_row * width;
   for (int c = threadIdx.x; c < width - R; c += blockDim.x) store_t<T>::st64(dst + c, pooled[c]);
   for (int j = threadIdx.x; j < R / 2; j += blockDim.x) {
     const int c = width - R + 2 * j;
@@ -107,21 +107,20 @@ template <typename T>
 __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int n_new, int width,
-    int R, Rope base, int m, int overlap, int64_t pool_cap) {
+    Seqs sq, int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double pa[kCmpT][2], pb[kCmpT][2];
   __shared__ double red[kCmpT / 64];
   const int b = blockIdx.y;
-  const int64_t p0 = pos0[b];
+  const int64_t p0 = sq.pos0[b];
   const int64_t w = p0 / m + blockIdx.x;
   // entries that close within the sequence's valid tokens
-  const int nl = valid_tokens(nvalid, b, n_new);
+  const int nl = sq.len(b);
   if (w >= (p0 + nl) / m || w >= pool_cap) return;  // block-uniform
   const int Ls = (1 + overlap) * m, tid = threadIdx.x;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
-  const T* kv_b = kv + (int64_t)b * n_new * width;
-  const T* g_b = gate + (int64_t)b * n_new * width;
+  const T* kv_b = kv + sq.row(b, 0) * width;  // the call's token rows of sequence b
+  const T* g_b = gate + sq.row(b, 0) * width;
   const T* skv_b = st_kv + (int64_t)b * Ls * width;
   const T* sg_b = st_gate + (int64_t)b * Ls * width;
   auto row = [&](const T* cur, const T* st, int64_t s) {
@@ -213,7 +212,7 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     for (int c = tid; c < width; c += kCmpT) pooled[c] = pooled[c] * inv * (double)norm_w[c];
     __syncthreads();
   }
-  T* dst = pool + ((int64_t)b * pool_cap + w) * width;
+  T* dst = pool + sq.prow(b, w, pool_cap) * width;
   for (int c = tid; c < width - R; c += kCmpT) store_t<T>::st64(dst + c, pooled[c]);
   for (int j = tid; j < R / 2; j += kCmpT) {
     const int c = width - R + 2 * j;
@@ -233,21 +232,21 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
 template <typename T>
 __global__ void __launch_bounds__(256) compress_one_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
-    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
-    const int64_t* __restrict__ pos0, const int32_t* __restrict__ nvalid, int width, int R,
-    Rope base, int m, int overlap, int64_t pool_cap) {
+    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool, Seqs sq,
+    int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];
   const int b = blockIdx.x;
-  if (valid_tokens(nvalid, b, 1) == 0) return;  // a padding token: nothing to record
-  const int64_t p0 = pos0[b];
+  if (sq.len(b) == 0) return;  // a padding token: nothing to record
+  const int64_t p0 = sq.pos0[b];
   const int Ls = (1 + overlap) * m;
   const int64_t w = p0 / m;
+  const int64_t r = sq.row(b, 0);
   if ((p0 + 1) % m == 0 && w < pool_cap)  // uniform per block
-    pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, 1, width, R, base, m,
-                  overlap, pool_cap, pooled, red);
-  const T* src_kv = kv + (int64_t)b * width;
-  const T* src_g = gate + (int64_t)b * width;
+    pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, r,
+                  sq.prow(b, w, pool_cap), width, R, base, m, overlap, pooled, red);
+  const T* src_kv = kv + r * width;
+  const T* src_g = gate + r * width;
   T* dk = st_kv + ((int64_t)b * Ls + p0 % Ls) * width;
   T* dg = st_gate + ((int64_t)b * Ls + p0 % Ls) * width;
   for (int c = threadIdx.x; c < width; c += blockDim.x) {
@@ -263,17 +262,15 @@ template <typename T>
 __global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__ kv,
                                                            const T* __restrict__ gate,
                                                            T* __restrict__ st_kv,
-                                                           T* __restrict__ st_gate,
-                                                           const int64_t* __restrict__ pos0,
-                                                           const int32_t* __restrict__ nvalid,
-                                                           int n_new, int width, int Ls) {
+                                                           T* __restrict__ st_gate, Seqs sq,
+                                                           int width, int Ls) {
   const int b = blockIdx.y;
-  const int64_t p0 = pos0[b];
+  const int64_t p0 = sq.pos0[b];
   // the last Ls valid positions (padding rows are never kept)
-  const int64_t s = p0 + valid_tokens(nvalid, b, n_new) - Ls + blockIdx.x;
+  const int64_t s = p0 + sq.len(b) - Ls + blockIdx.x;
   if (s < p0) return;
-  const T* src_kv = kv + ((int64_t)b * n_new + (s - p0)) * width;
-  const T* src_g = gate + ((int64_t)b * n_new + (s - p0)) * width;
+  const T* src_kv = kv + (sq.row(b, 0) + (s - p0)) * width;
+  const T* src_g = gate + (sq.row(b, 0) + (s - p0)) * width;
   T* dk = st_kv + ((int64_t)b * Ls + (s % Ls)) * width;
   T* dg = st_gate + ((int64_t)b * Ls + (s % Ls)) * width;
   for (int c = threadIdx.x; c < width; c += blockDim.x) {
@@ -288,34 +285,33 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
                            hipStream_t s) {
   const int m = L.m, Ls = (1 + L.overlap) * m;
   const int max_entries = bt.n / m + 1;
+  const Seqs sq = seqs_of(bt);
   dim3 g1(max_entries, bt.B), g2(Ls, bt.B);
   if (bt.n == 1) {
     if (L.dtype == 1)
       compress_one_kernel<bf16_t><<<bt.B, 256, 0, s>>>(
           (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (bf16_t*)st_kv, (bf16_t*)st_gate,
-          (bf16_t*)pool, bt.pos0, bt.nvalid, width, rope_dim, L.base, m, L.overlap, pool_cap);
+          (bf16_t*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
     else
       compress_one_kernel<float><<<bt.B, 256, 0, s>>>(
           (const float*)kv, (const float*)gate, norm_w, eps, (float*)st_kv, (float*)st_gate,
-          (float*)pool, bt.pos0, bt.nvalid, width, rope_dim, L.base, m, L.overlap, pool_cap);
+          (float*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
     return hipGetLastError();
   }
   if (L.dtype == 1) {
     compress_entry_kernel<bf16_t><<<g1, kCmpT, 0, s>>>(
         (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
-        (const bf16_t*)st_gate, (bf16_t*)pool, bt.pos0, bt.nvalid, bt.n, width, rope_dim, L.base,
-        m, L.overlap, pool_cap);
+        (const bf16_t*)st_gate, (bf16_t*)pool, sq, width, rope_dim, L.base, m, L.overlap,
+        pool_cap);
     state_update_kernel<bf16_t><<<g2, 256, 0, s>>>((const bf16_t*)kv, (const bf16_t*)gate,
-                                                   (bf16_t*)st_kv, (bf16_t*)st_gate, bt.pos0,
-                                                   bt.nvalid, bt.n, width, Ls);
+                                                   (bf16_t*)st_kv, (bf16_t*)st_gate, sq, width,
+                                                   Ls);
   } else {
-    compress_entry_kernel<float><<<g1, kCmpT, 0, s>>>((const float*)kv, (const float*)gate, norm_w, eps,
-                                              (const float*)st_kv, (const float*)st_gate,
-                                              (float*)pool, bt.pos0, bt.nvalid, bt.n, width,
-                                              rope_dim, L.base, m, L.overlap, pool_cap);
+    compress_entry_kernel<float><<<g1, kCmpT, 0, s>>>(
+        (const float*)kv, (const float*)gate, norm_w, eps, (const float*)st_kv,
+        (const float*)st_gate, (float*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
     state_update_kernel<float><<<g2, 256, 0, s>>>((const float*)kv, (const float*)gate,
-                                                  (float*)st_kv, (float*)st_gate, bt.pos0,
-                                                  bt.nvalid, bt.n, width, Ls);
+                                                  (float*)st_kv, (float*)st_gate, sq, width, Ls);
   }
   return hipGetLastError();
 }

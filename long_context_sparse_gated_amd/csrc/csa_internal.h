@@ -35,11 +35,50 @@ struct Layer {
 };
 
 struct Batch {
-  int B, n;             // sequences, new tokens per sequence
+  int B, n;             // sequences, rows per sequence (packed: a bound on any length)
   const int64_t* pos0;  // device [B]
   int64_t pos0_max;     // host bound
   const int32_t* nvalid;  // device [B] valid tokens per sequence, or null (all n)
+  const int32_t* cu;      // device [B + 1] packed row offsets, or null (padded rows)
+  const int32_t* table;   // device [B, tstride] pool block table, or null (contiguous pools)
+  int bshift;             // log2 of the entries per pool block (paged pools)
+  int tstride;            // row stride of the block table
 };
+
+// The token rows and pooled entries of one call, as the kernels see them.
+//  * Token i of sequence b (i < len(b)) sits at position pos0[b] + i and in
+//    row row(b, i) of every per-token tensor: b n + i for padded calls,
+//    cu[b] + i for packed ones.  len(b) is n, n_valid[b] (padded calls) or
+//    cu[b + 1] - cu[b] (packed calls), clamped to 0 .. n.
+//  * Entry w of sequence b sits in row prow(b, w, cap) of a pool tensor:
+//    b cap + w for contiguous pools, or through the block table,
+//    table[b][w / E] E + w mod E for paged ones (E = 2^bshift entries per
+//    block).
+struct Seqs {
+  const int64_t* pos0;
+  const int32_t* nvalid;
+  const int32_t* cu;
+  const int32_t* table;
+  int n, bshift, tstride;
+  __device__ __forceinline__ int len(int b) const {
+    int v = n;
+    if (cu) v = cu[b + 1] - cu[b];
+    else if (nvalid) v = nvalid[b];
+    return v < 0 ? 0 : (v > n ? n : v);
+  }
+  __device__ __forceinline__ int64_t row(int b, int i) const {
+    return cu ? (int64_t)cu[b] + i : (int64_t)b * n + i;
+  }
+  __device__ __forceinline__ int64_t prow(int b, int64_t w, int64_t cap) const {
+    if (!table) return (int64_t)b * cap + w;
+    const int64_t blk = table[(int64_t)b * tstride + (w >> bshift)];
+    return (blk << bshift) + (w & (((int64_t)1 << bshift) - 1));
+  }
+};
+
+inline Seqs seqs_of(const Batch& b) {
+  return Seqs{b.pos0, b.nvalid, b.cu, b.table, b.n, b.bshift, b.tstride};
+}
 
 // Valid tokens of sequence b in a call of n per sequence.
 __device__ __forceinline__ int valid_tokens(const int32_t* nvalid, int b, int n) {

@@ -118,16 +118,16 @@ constexpr int kIdxRow = 136;  // LDS row stride in bf16 (128 + 8 pad)
 
 __global__ void __launch_bounds__(256) index_prefill_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
-    float* __restrict__ scores, const int64_t* __restrict__ pos0, int n_new, int Ri, Rope base,
-    int m, int64_t pool_cap) {
+    float* __restrict__ scores, Seqs sq, int Ri, Rope base, int m, int64_t pool_cap) {
   constexpr int Hi = 64, Di = 128;
   __shared__ __attribute__((aligned(16))) bf16_t ktile[2][kIdxKT * kIdxRow];
   __shared__ double2 cs[kIdxQPB][64];
   __shared__ float wsh[kIdxQPB][Hi];
   const int b = blockIdx.y, i0 = blockIdx.x * kIdxQPB;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
-  const int64_t p0 = pos0[b];
-  const int nq = min(kIdxQPB, n_new - i0);
+  const int64_t p0 = sq.pos0[b];
+  const int nq = min(kIdxQPB, sq.len(b) - i0);
+  if (nq <= 0) return;  // padding rows only (block-uniform, before any barrier)
   for (int e = tid; e < kIdxQPB * (Ri / 2); e += 256) {
     const int qq = e / (Ri / 2), j = e % (Ri / 2);
     double sn, c;
@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(256) index_prefill_mfma(
   }
   for (int e = tid; e < kIdxQPB * Hi; e += 256) {
     const int qq = e / Hi, h = e % Hi;
-    wsh[qq][h] = qq < nq ? bf16_to_f32(wts[((int64_t)b * n_new + i0 + qq) * Hi + h]) : 0.f;
+    wsh[qq][h] = qq < nq ? bf16_to_f32(wts[sq.row(b, i0 + qq) * Hi + h]) : 0.f;
   }
   __syncthreads();
 
@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(256) index_prefill_mfma(
     const int ql = 2 * wv + qq;
     int64_t nv = (p0 + i0 + ql + 1) / m;
     nvis[qq] = ql < nq ? (int)(nv < pool_cap ? nv : pool_cap) : 0;
-    const bf16_t* qrow = q + ((int64_t)b * n_new + i0 + (ql < nq ? ql : 0)) * Hi * Di;
+    const bf16_t* qrow = q + sq.row(b, i0 + (ql < nq ? ql : 0)) * Hi * Di;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -168,15 +168,16 @@ __global__ void __launch_bounds__(256) index_prefill_mfma(
     }
   }
 
-  float* srow0 = scores + ((int64_t)b * n_new + i0 + 2 * wv) * pool_cap;
+  float* srow0 = scores + ((int64_t)b * sq.n + i0 + 2 * wv) * pool_cap;
   for (int kt = 0, it = 0; kt < nkeys; kt += kIdxKT, ++it) {
     bf16_t* tile = ktile[it & 1];
+    // a 64-key tile never straddles a pool block (blocks hold a multiple of 128)
+    const int64_t kt_row = sq.prow(b, kt, pool_cap);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = tid + 256 * r, key = c >> 4, part = c & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (kt + key < nkeys)
-        v = *(const uint4*)(keys + ((int64_t)b * pool_cap + kt + key) * Di + part * 8);
+      if (kt + key < nkeys) v = *(const uint4*)(keys + (kt_row + key) * Di + part * 8);
       *(uint4*)(tile + key * kIdxRow + part * 8) = v;
     }
     __syncthreads();
@@ -264,8 +265,8 @@ __device__ __forceinline__ void lds_frag8(const uint32_t (&a)[8], uint4 (&o)[8])
 template <int RI>
 __global__ void __launch_bounds__(256, 2) index_prefill_x32(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
-    float* __restrict__ scores, float* __restrict__ discard, const int64_t* __restrict__ pos0,
-    const int32_t* __restrict__ nvalid, int n_new, int B, Rope base, int m, int64_t pool_cap) {
+    float* __restrict__ scores, float* __restrict__ discard, Seqs sq, int B, Rope base, int m,
+    int64_t pool_cap) {
   constexpr int Hi = 64, Di = 128, kFirst = Di - RI, kK0 = kFirst / 16;
   static_assert(RI > 0 && RI <= Di && RI % 16 == 0, "rope channels: whole 16-channel steps");
   __shared__ __attribute__((aligned(1024))) bf16_t kt0[kX32KT * Di];
@@ -273,15 +274,15 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
   __shared__ double2 cs[kX32Q][RI / 2];
   __shared__ float2 csf[kX32Q][RI / 2];
   __shared__ float wsh[kX32Q][Hi];
-  const int nblk = (n_new + kX32Q - 1) / kX32Q;
+  const int nblk = (sq.n + kX32Q - 1) / kX32Q;
   const int b = blockIdx.x % B, i0 = (nblk - 1 - (int)(blockIdx.x / B)) * kX32Q;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t p0 = pos0[b];
-  const int nq = min(kX32Q, n_new - i0);
+  const int64_t p0 = sq.pos0[b];
   // padding queries (a suffix of the sequence's rows) are not scored; a block
   // whose first query is padding has no other
-  if (i0 >= valid_tokens(nvalid, b, n_new)) return;  // block-uniform
+  const int nq = min(kX32Q, sq.len(b) - i0);
+  if (nq <= 0) return;  // block-uniform
   int64_t nv_last = (p0 + i0 + nq) / m;  // the block's last query sees the most keys
   if (nv_last > pool_cap) nv_last = pool_cap;
   const int nkeys = (int)nv_last;
@@ -290,14 +291,16 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
 
   // DMA of this wave's 32 rows of a tile (8 instructions of 4 rows); chunk c
   // of row r sits at slot c ^ (r & 15); rows past the keys re-read the last.
-  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
+  // A 128-key tile lies in one pool block (blocks hold a multiple of 128
+  // entries): trow is the pool row of its first key.
   const int lrow = lane >> 4, slot = lane & 15;
-  auto issue = [&](int tile, bf16_t* dst) {
+  auto tile_row = [&](int tile) { return sq.prow(b, (int64_t)tile * kX32KT, pool_cap); };
+  auto issue = [&](int tile, bf16_t* dst, int64_t trow) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = 32 * wv + 4 * j + lrow;
-      const int key = min(tile * kX32KT + r, nkeys - 1);
-      const bf16_t* src = kbase + (int64_t)key * Di + 8 * (slot ^ ((4 * j + lrow) & 15));
+      const int key = min(tile * kX32KT + r, nkeys - 1) - tile * kX32KT;
+      const bf16_t* src = keys + (trow + key) * Di + 8 * (slot ^ ((4 * j + lrow) & 15));
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
                                        16, 0, 0);
     }
@@ -306,8 +309,9 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
   int64_t nv = (p0 + i0 + wv + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   const int nvis = wv < nq ? (int)nv : 0;
-  const bf16_t* qrow = q + ((int64_t)b * n_new + i0 + ql) * Hi * Di;
-  const bf16_t wt_raw = wts[((int64_t)b * n_new + i0 + min(tid / Hi, nq - 1)) * Hi + tid % Hi];
+  const bf16_t* qrow = q + sq.row(b, i0 + ql) * Hi * Di;
+  const bf16_t wt_raw = wts[sq.row(b, i0 + min(tid / Hi, nq - 1)) * Hi + tid % Hi];
+  int64_t trow = tile_row(0);
   // The query reaches registers through LDS: head rows 0-31 go to this
   // wave's 32 rows of kt0, rows 32-63 to its rows of kt1 (whole-row DMA in
   // the keys' layout), and are read back as A fragments like the keys.  The
@@ -365,7 +369,8 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
     frag_addr(kt1 + 32 * wv * Di, a);
     lds_frag8<0>(a, A[1]);
   }
-  issue(0, kt0);  // this wave's rows only: its own staging reads are done
+  issue(0, kt0, trow);  // this wave's rows only: its own staging reads are done
+  trow = tile_row(ntile > 1 ? 1 : 0);  // the next tile's pool row, loaded ahead of its issue
   if (wv < nq) {  // waves past the last query score nothing that is kept
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
   // channels 16 kk + 8 h32, i.e. chunk 2 kk + h32 at slot (2 kk + h32) ^ (l32 & 15):
   // byte offset (row base) + 16 (h32 ^ (l32 & 1)) + 32 (kk ^ ((l32 >> 1) & 7)),
   // an XOR of 32 kk into the lane's kk = 0 offset.
-  float* srow = scores + ((int64_t)b * n_new + i0 + ql) * pool_cap;
+  float* srow = scores + ((int64_t)b * sq.n + i0 + ql) * pool_cap;
   auto step = [&](uint4 (&Bf)[8]) {
     f32x16 acc[2];
 #pragma unroll
@@ -430,11 +435,17 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
   // publishes every wave's rows and retires every read of the other array.
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   for (int tile = 0;;) {
-    if (tile + 1 < ntile) issue(tile + 1, kt1);
+    if (tile + 1 < ntile) {
+      issue(tile + 1, kt1, trow);
+      trow = tile_row(tile + 2 < ntile ? tile + 2 : tile + 1);
+    }
     compute(tile, kt0);
     if (++tile >= ntile) break;
     asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
-    if (tile + 1 < ntile) issue(tile + 1, kt0);
+    if (tile + 1 < ntile) {
+      issue(tile + 1, kt0, trow);
+      trow = tile_row(tile + 2 < ntile ? tile + 2 : tile + 1);
+    }
     compute(tile, kt1);
     if (++tile >= ntile) break;
     asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
@@ -464,14 +475,13 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __restrict__ q,
                                                            bf16_t* __restrict__ qr,
-                                                           uint32_t* __restrict__ hist,
-                                                           const int64_t* __restrict__ pos0,
-                                                           int n_new, int Hi, int Di, int Ri,
-                                                           Rope base) {
+                                                           uint32_t* __restrict__ hist, Seqs sq,
+                                                           int Hi, int Di, int Ri, Rope base) {
   __shared__ double2 cs[128];
   const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t t = pos0[b] + i;
-  const int64_t tok = (int64_t)b * n_new + i;
+  if (i >= sq.len(b)) return;  // padding slot: no query
+  const int64_t t = sq.pos0[b] + i;
+  const int64_t tok = (int64_t)b * sq.n + i;  // the query's slot in the workspace
   for (int j = threadIdx.x; j < kHBins; j += blockDim.x) hist[tok * kHBins + j] = 0u;
   for (int j = threadIdx.x; j < Ri / 2; j += blockDim.x) {
     double sn, c;
@@ -479,11 +489,11 @@ __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __rest
     cs[j] = make_double2(c, sn);
   }
   __syncthreads();
-  const int64_t off = tok * Hi * Di;
+  const int64_t off = tok * Hi * Di, qoff = sq.row(b, i) * Hi * Di;
   const int chunks = Hi * Di / 8;
   for (int e = threadIdx.x; e < chunks; e += blockDim.x) {
     const int d0 = (e * 8) % Di;
-    uint4 v = *(const uint4*)(q + off + (int64_t)e * 8);
+    uint4 v = *(const uint4*)(q + qoff + (int64_t)e * 8);
     *(uint4*)(qr + off + (int64_t)e * 8) = rope8_bf16(v, d0, Di, Ri, cs);
   }
 }
@@ -502,33 +512,41 @@ constexpr int kDecTile = 128;  // keys per LDS tile: 32 per wave, 32 KB
 __global__ void __launch_bounds__(256, 2) index_decode_x32(
     const bf16_t* __restrict__ qr, const bf16_t* __restrict__ wts, const bf16_t* __restrict__ keys,
     float* __restrict__ scores, float* __restrict__ discard, uint32_t* __restrict__ hist,
-    const int64_t* __restrict__ pos0, int n_new, int m, int64_t pool_cap, int block_keys) {
+    Seqs sq, int m, int64_t pool_cap, int block_keys) {
   constexpr int Hi = 64, Di = 128;
   __shared__ __attribute__((aligned(1024))) bf16_t kt0[kDecTile * Di];
   __shared__ __attribute__((aligned(1024))) bf16_t kt1[kDecTile * Di];
   __shared__ uint32_t lh[kHBins];
-  const int tok = blockIdx.y;  // b * n_new + i
-  const int b = tok / n_new, i = tok % n_new;
+  const int tok = blockIdx.y;  // the query's slot b n + i
+  const int b = tok / sq.n, i = tok % sq.n;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform, before any barrier)
   const int lane = threadIdx.x & 63, l32 = lane & 31, h32 = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int64_t nv = (pos0[b] + i + 1) / m;
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   const int64_t kb = (int64_t)blockIdx.x * block_keys;
   if (kb >= nv) return;  // block-uniform, before any barrier
   const int64_t ke = kb + block_keys < nv ? kb + block_keys : nv;
   const int ntile = (int)((ke - kb + kDecTile - 1) / kDecTile);
-  const bf16_t* kbase = keys + (int64_t)b * pool_cap * Di;
   // DMA of this wave's 32 rows of tile `tile` (8 instructions of 4 rows);
-  // rows past the run re-read its last row (already in cache, never scored)
+  // rows past the run re-read its last row (already in cache, never scored).
+  // A tile's keys lie in one pool block (runs and blocks are multiples of
+  // 128 entries): trow is the pool row of the tile's first key, or of the
+  // run's last key for a tile past the run (tile_row).
   const int lrow = lane >> 4, slot = lane & 15;
-  auto issue = [&](int tile, bf16_t* dst) {
+  auto tile_key = [&](int tile) {
     const int64_t t0 = kb + (int64_t)tile * kDecTile;
+    return t0 < ke - 1 ? t0 : ke - 1;
+  };
+  auto tile_row = [&](int tile) { return sq.prow(b, tile_key(tile), pool_cap); };
+  auto issue = [&](int tile, bf16_t* dst, int64_t trow) {
+    const int64_t t0 = tile_key(tile);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = 32 * wv + 4 * j + lrow;
-      int64_t key = t0 + r;
+      int64_t key = kb + (int64_t)tile * kDecTile + r;
       if (key > ke - 1) key = ke - 1;
-      const bf16_t* src = kbase + key * Di + 8 * (slot ^ (r & 15));
+      const bf16_t* src = keys + (trow + (key - t0)) * Di + 8 * (slot ^ (r & 15));
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + (32 * wv + 4 * j) * Di),
                                        16, 0, 0);
     }
@@ -536,6 +554,7 @@ __global__ void __launch_bounds__(256, 2) index_decode_x32(
   // query fragments and weights first: their loads then complete before the
   // tiles' DMA, so the first wait on them leaves the DMA in flight
   const bf16_t* qrow = qr + (int64_t)tok * Hi * Di;
+  const int64_t wrow = sq.row(b, i) * Hi;
   uint4 A[2][8];  // head 32 mt + l32, channels 16 kk + 8 h32 .. + 7
   float wr[2][16];
 #pragma unroll
@@ -545,11 +564,13 @@ __global__ void __launch_bounds__(256, 2) index_decode_x32(
       A[mt][kk] = *(const uint4*)(qrow + (32 * mt + l32) * Di + 16 * kk + 8 * h32);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      wr[mt][r] = bf16_to_f32(wts[(int64_t)tok * Hi + 32 * mt + 8 * (r / 4) + 4 * h32 + r % 4]);
+      wr[mt][r] = bf16_to_f32(wts[wrow + 32 * mt + 8 * (r / 4) + 4 * h32 + r % 4]);
   }
+  const int64_t row0 = tile_row(0), row1 = tile_row(1);
   asm volatile("" ::: "memory");  // keeps those loads ahead of the DMA
-  issue(0, kt0);
-  issue(1, kt1);
+  issue(0, kt0, row0);
+  issue(1, kt1, row1);
+  int64_t trow = tile_row(2);  // loaded a tile ahead of its issue
   for (int j = threadIdx.x; j < kHBins; j += 256) lh[j] = 0u;
   // the histogram is clear before any wave adds to it (LDS stores only: the
   // DMA in flight need not land here)
@@ -609,12 +630,14 @@ __global__ void __launch_bounds__(256, 2) index_decode_x32(
   for (int tile = 0;;) {
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     frags(kt0, Bf);
-    issue(tile + 2, kt0);
+    issue(tile + 2, kt0, trow);
+    trow = tile_row(tile + 3);
     compute(tile, Bf);
     if (++tile >= ntile) break;
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     frags(kt1, Bf);
-    issue(tile + 2, kt1);
+    issue(tile + 2, kt1, trow);
+    trow = tile_row(tile + 3);
     compute(tile, Bf);
     if (++tile >= ntile) break;
   }
@@ -674,13 +697,13 @@ __global__ void __launch_bounds__(256) topk_collect(const float* __restrict__ sc
                                                     const uint32_t* __restrict__ hist,
                                                     int32_t* __restrict__ cand_hi,
                                                     int32_t* __restrict__ cand_tie,
-                                                    uint32_t* __restrict__ counts,
-                                                    const int64_t* __restrict__ pos0, int n_new,
+                                                    uint32_t* __restrict__ counts, Seqs sq,
                                                     int m, int k, int64_t pool_cap, int nslice) {
   __shared__ uint32_t wsum[4], res[2];
-  const int tok = blockIdx.y;
-  const int b = tok / n_new, i = tok % n_new;
-  int64_t nv = (pos0[b] + i + 1) / m;
+  const int tok = blockIdx.y;  // the query's slot b n + i
+  const int b = tok / sq.n, i = tok % sq.n;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   const int64_t c0b = (int64_t)blockIdx.x * 4 * kSlice;
   if (nv <= k || c0b >= nv) return;  // block-uniform
@@ -748,8 +771,7 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
                                                   const int32_t* __restrict__ cand_hi,
                                                   const int32_t* __restrict__ cand_tie,
                                                   const uint32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ out,
-                                                  const int64_t* __restrict__ pos0, int n_new,
+                                                  int32_t* __restrict__ out, Seqs sq,
                                                   int m, int k, int64_t pool_cap, int nslice) {
   __shared__ uint32_t off_hi[kMaxSlices + 1], off_tie[kMaxSlices + 1];
   __shared__ int32_t sel_hi[kMaxTopK], sel_tie[kMaxTopK];
@@ -757,11 +779,12 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
   __shared__ uint32_t tie_key[kTieCap];
   __shared__ uint32_t bins[256], wsum[4], wcnt[4], sh_prefix, sh_rem;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tok = blockIdx.x;
-  const int b = tok / n_new, i = tok % n_new;
-  int64_t nv = (pos0[b] + i + 1) / m;
+  const int tok = blockIdx.x;  // the query's slot b n + i
+  const int b = tok / sq.n, i = tok % sq.n;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
-  int32_t* o = out + (int64_t)tok * k;
+  int32_t* o = out + sq.row(b, i) * k;
   if (nv <= k) {
     for (int j = tid; j < k; j += 256) o[j] = j < nv ? j : -1;
     return;
@@ -1014,18 +1037,18 @@ constexpr int kBlkTopK = kBlkTopKT * kBlkTopKU;
 
 __global__ void __launch_bounds__(kBlkTopKT) topk_block(const float* __restrict__ scores,
                                                   const uint32_t* __restrict__ hist,
-                                                  int32_t* __restrict__ out,
-                                                  const int64_t* __restrict__ pos0, int n_new,
+                                                  int32_t* __restrict__ out, Seqs sq,
                                                   int m, int k, int64_t pool_cap) {
   __shared__ int32_t cand[kBlkTopK + 64];  // candidate ids in id order (+ a spare per lane)
   __shared__ uint32_t wsum[kBlkTopKT / 64], wcnt[kBlkTopKT / 64], res[2], bins[256], sh_prefix,
       sh_rem;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tok = blockIdx.x;
-  const int b = tok / n_new, i = tok % n_new;
-  int64_t nv = (pos0[b] + i + 1) / m;
+  const int tok = blockIdx.x;  // the query's slot b n + i
+  const int b = tok / sq.n, i = tok % sq.n;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
-  int32_t* o = out + (int64_t)tok * k;
+  int32_t* o = out + sq.row(b, i) * k;
   if (nv <= k) {
     for (int j = tid; j < k; j += kBlkTopKT) o[j] = j < nv ? j : -1;
     return;
@@ -1168,15 +1191,16 @@ template <typename T>
 __global__ void __launch_bounds__(256) index_generic(const T* __restrict__ q,
                                                      const T* __restrict__ wts,
                                                      const T* __restrict__ keys,
-                                                     float* __restrict__ scores,
-                                                     const int64_t* __restrict__ pos0, int n_new,
+                                                     float* __restrict__ scores, Seqs sq,
                                                      int Hi, int Di, int Ri, Rope base, int m,
                                                      int64_t pool_cap) {
   extern __shared__ float qs[];  // [Hi * Di] rotated query, then [Hi] weights
   const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t t = pos0[b] + i;
-  const int64_t tok = (int64_t)b * n_new + i;
-  const T* qrow = q + tok * Hi * Di;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  const int64_t t = sq.pos0[b] + i;
+  const int64_t tok = (int64_t)b * sq.n + i;  // the query's slot (scores row)
+  const int64_t qr_ = sq.row(b, i);           // its row in q and the weights
+  const T* qrow = q + qr_ * Hi * Di;
   const int first = Di - Ri;
   for (int e = threadIdx.x; e < Hi * Di; e += blockDim.x) {
     const int d = e % Di;
@@ -1197,12 +1221,12 @@ __global__ void __launch_bounds__(256) index_generic(const T* __restrict__ q,
     }
   }
   float* wsh = qs + Hi * Di;
-  for (int h = threadIdx.x; h < Hi; h += blockDim.x) wsh[h] = store_t<T>::ld(wts + tok * Hi + h);
+  for (int h = threadIdx.x; h < Hi; h += blockDim.x) wsh[h] = store_t<T>::ld(wts + qr_ * Hi + h);
   __syncthreads();
   int64_t nv = (t + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   for (int64_t w = threadIdx.x; w < nv; w += blockDim.x) {
-    const T* krow = keys + ((int64_t)b * pool_cap + w) * Di;
+    const T* krow = keys + sq.prow(b, w, pool_cap) * Di;
     float s = 0.f;
     for (int h = 0; h < Hi; ++h) {
       float dot = 0.f;
@@ -1219,19 +1243,19 @@ __global__ void __launch_bounds__(256) index_generic(const T* __restrict__ q,
 template <int BS>
 __global__ void __launch_bounds__(BS) topk_radix(const float* __restrict__ scores,
                                                  int64_t stride, int32_t* __restrict__ out,
-                                                 const int64_t* __restrict__ pos0, int n_new,
-                                                 int m, int k, int64_t pool_cap) {
+                                                 Seqs sq, int m, int k, int64_t pool_cap) {
   constexpr int NW = BS / 64;
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_rem;
   __shared__ uint32_t wcnt[2][NW];
   const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t tok = (int64_t)b * n_new + i;
-  int64_t nv = (pos0[b] + i + 1) / m;
+  if (i >= sq.len(b)) return;  // padding slot (block-uniform)
+  const int64_t tok = (int64_t)b * sq.n + i;  // the query's slot (scores row)
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   const int n = (int)nv;
   const float* sc = scores + tok * stride;
-  int32_t* o = out + tok * k;
+  int32_t* o = out + sq.row(b, i) * k;
   if (n <= k) {
     for (int j = threadIdx.x; j < k; j += BS) o[j] = j < n ? j : -1;
     return;
@@ -1321,23 +1345,21 @@ constexpr int kTkPer = 32;
 
 __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ scores, int64_t stride,
                                                  int32_t* __restrict__ out,
-                                                 const int64_t* __restrict__ pos0,
-                                                 const int32_t* __restrict__ nvalid, int n_new,
-                                                 int m, int k, int64_t pool_cap) {
+                                                 Seqs sq, int m, int k, int64_t pool_cap) {
   __shared__ uint32_t hist_all[4][4][256];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x * 4 + wv, b = blockIdx.y;
   // wave-uniform (padding rows are left as they are); the waves never meet
   // at a barrier
-  if (i >= valid_tokens(nvalid, b, n_new)) return;
+  if (i >= sq.len(b)) return;
   uint32_t (*hist)[256] = hist_all[wv];
-  const int64_t tok = (int64_t)b * n_new + i;
-  int64_t nv = (pos0[b] + i + 1) / m;
+  const int64_t tok = (int64_t)b * sq.n + i;  // the query's slot (scores row)
+  int64_t nv = (sq.pos0[b] + i + 1) / m;
   if (nv > pool_cap) nv = pool_cap;
   const int n = (int)nv;
   const float* sc = scores + tok * stride;
-  int32_t* o = out + tok * k;
+  int32_t* o = out + sq.row(b, i) * k;
   if (n <= k) {
     for (int j = lane; j < k; j += 64) o[j] = j < n ? j : -1;
     return;
@@ -1436,6 +1458,7 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
                              const void* keys, int64_t pool_cap, int32_t* idx, float* scores_out,
                              void* ws, hipStream_t s) {
   char* wsp = (char*)ws;
+  const Seqs sq = seqs_of(bt);
   const size_t bn = (size_t)bt.B * bt.n;
   float* scores = (float*)wsp;
   wsp += align256(bn * pool_cap * sizeof(float));
@@ -1453,8 +1476,8 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
     uint32_t* counts = (uint32_t*)wsp;
     // 1024 threads: one 16-byte chunk of the query each (64 x 128 channels),
     // many waves per SIMD to cover the float64 rotation's latency
-    rotate_queries_bf16<<<dim3(bt.n, bt.B), 1024, 0, s>>>((const bf16_t*)q, qr, hist, bt.pos0,
-                                                         bt.n, L.Hi, L.Di, L.Ri, L.base);
+    rotate_queries_bf16<<<dim3(bt.n, bt.B), 1024, 0, s>>>((const bf16_t*)q, qr, hist, sq, L.Hi,
+                                                         L.Di, L.Ri, L.base);
     int64_t nv = (bt.pos0_max + bt.n) / L.m;
     if (nv > pool_cap) nv = pool_cap;
     const unsigned tokens = (unsigned)bn;
@@ -1465,61 +1488,56 @@ hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, con
       bk = (bk + kDecTile - 1) / kDecTile * kDecTile;
       dim3 g1((unsigned)((nv + bk - 1) / bk), tokens);
       index_decode_x32<<<g1, 256, 0, s>>>(qr, (const bf16_t*)w, (const bf16_t*)keys, scores,
-                                          (float*)(counts + bn * nslice * 2), hist, bt.pos0,
-                                          bt.n, L.m, pool_cap, (int)bk);
+                                          (float*)(counts + bn * nslice * 2), hist, sq, L.m,
+                                          pool_cap, (int)bk);
     }
     if (nv <= kBlkTopK) {
-      topk_block<<<tokens, kBlkTopKT, 0, s>>>(scores, hist, idx, bt.pos0, bt.n, L.m, L.k,
-                                              pool_cap);
+      topk_block<<<tokens, kBlkTopKT, 0, s>>>(scores, hist, idx, sq, L.m, L.k, pool_cap);
       return hipGetLastError();
     }
     if (nv > L.k) {
       dim3 g2((unsigned)((nv + 4 * kSlice - 1) / (4 * kSlice)), tokens);
-      topk_collect<<<g2, 256, 0, s>>>(scores, hist, cand_hi, cand_tie, counts, bt.pos0, bt.n,
-                                      L.m, L.k, pool_cap, nslice);
+      topk_collect<<<g2, 256, 0, s>>>(scores, hist, cand_hi, cand_tie, counts, sq, L.m, L.k,
+                                      pool_cap, nslice);
     }
-    topk_final<<<tokens, 256, 0, s>>>(scores, cand_hi, cand_tie, counts, idx, bt.pos0, bt.n,
-                                      L.m, L.k, pool_cap, nslice);
+    topk_final<<<tokens, 256, 0, s>>>(scores, cand_hi, cand_tie, counts, idx, sq, L.m, L.k,
+                                      pool_cap, nslice);
     return hipGetLastError();
   }
   if (index_fast_shape(L) && L.Ri == 64) {
     const unsigned nblk = (unsigned)((bt.n + kX32Q - 1) / kX32Q);
     index_prefill_x32<64><<<nblk * bt.B, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
                                                       (const bf16_t*)keys, scores, (float*)wsp,
-                                                      bt.pos0, bt.nvalid, bt.n, bt.B, L.base,
-                                                      L.m, pool_cap);
+                                                      sq, bt.B, L.base, L.m, pool_cap);
   } else if (index_fast_shape(L)) {
     dim3 grid((bt.n + kIdxQPB - 1) / kIdxQPB, bt.B);
     index_prefill_mfma<<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)w,
-                                            (const bf16_t*)keys, scores, bt.pos0, bt.n, L.Ri,
-                                            L.base, L.m, pool_cap);
+                                            (const bf16_t*)keys, scores, sq, L.Ri, L.base, L.m,
+                                            pool_cap);
   } else {
     const size_t shm = ((size_t)L.Hi * L.Di + L.Hi) * sizeof(float);
     dim3 grid(bt.n, bt.B);
     if (L.dtype == 1)
       index_generic<bf16_t><<<grid, 256, shm, s>>>((const bf16_t*)q, (const bf16_t*)w,
-                                                   (const bf16_t*)keys, scores, bt.pos0, bt.n,
-                                                   L.Hi, L.Di, L.Ri, L.base, L.m, pool_cap);
+                                                   (const bf16_t*)keys, scores, sq, L.Hi, L.Di,
+                                                   L.Ri, L.base, L.m, pool_cap);
     else
       index_generic<float><<<grid, 256, shm, s>>>((const float*)q, (const float*)w,
-                                                  (const float*)keys, scores, bt.pos0, bt.n, L.Hi,
-                                                  L.Di, L.Ri, L.base, L.m, pool_cap);
+                                                  (const float*)keys, scores, sq, L.Hi, L.Di,
+                                                  L.Ri, L.base, L.m, pool_cap);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((bt.pos0_max + bt.n) / L.m <= 64 * kTkPer) {  // every row fits in one wave's registers
     dim3 gw((bt.n + 3) / 4, bt.B);
-    topk_wave<<<gw, 256, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.nvalid, bt.n, L.m, L.k,
-                                 pool_cap);
+    topk_wave<<<gw, 256, 0, s>>>(scores, pool_cap, idx, sq, L.m, L.k, pool_cap);
     return hipGetLastError();
   }
   dim3 grid(bt.n, bt.B);
   if ((bt.pos0_max + bt.n) / L.m > 16384)
-    topk_radix<1024><<<grid, 1024, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.n, L.m, L.k,
-                                           pool_cap);
+    topk_radix<1024><<<grid, 1024, 0, s>>>(scores, pool_cap, idx, sq, L.m, L.k, pool_cap);
   else
-    topk_radix<256><<<grid, 256, 0, s>>>(scores, pool_cap, idx, bt.pos0, bt.n, L.m, L.k,
-                                         pool_cap);
+    topk_radix<256><<<grid, 256, 0, s>>>(scores, pool_cap, idx, sq, L.m, L.k, pool_cap);
   return hipGetLastError();
 }
 

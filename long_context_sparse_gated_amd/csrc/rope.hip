@@ -19,16 +19,15 @@ constexpr int kWaTok = 8;
 template <typename T>
 __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict__ kv,
                                                             T* __restrict__ ring,
-                                                            const int64_t* __restrict__ pos0,
-                                                            const int32_t* __restrict__ nvalid,
-                                                            int n_new, int D, int R, Rope base,
+                                                            Seqs sq, int D, int R, Rope base,
                                                             int64_t cap) {
   extern __shared__ double freq[];  // R / 2 pair frequencies
   const int i0 = blockIdx.x * kWaTok, b = blockIdx.y;
   // padding tokens of a variable-length call are not appended
-  const int nt = min(kWaTok, valid_tokens(nvalid, b, n_new) - i0);
+  const int nt = min(kWaTok, sq.len(b) - i0);
   if (nt <= 0) return;  // block-uniform
-  const int64_t p0 = pos0[b];
+  const int64_t p0 = sq.pos0[b];
+  const int64_t r0 = sq.row(b, i0);  // the block's tokens sit in rows r0 .. r0 + nt - 1
   for (int j = threadIdx.x; j < R / 2; j += blockDim.x) freq[j] = rope_freq(base, j, R);
   const int plain = D - R;  // channels copied unchanged
   constexpr int V = 16 / (int)sizeof(T);
@@ -38,13 +37,13 @@ __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict_
       const int k = e / per, c = (e % per) * V;
       const int64_t t = p0 + i0 + k;
       *(uint4*)(ring + ((int64_t)b * cap + t % cap) * D + c) =
-          *(const uint4*)(kv + ((int64_t)b * n_new + i0 + k) * D + c);
+          *(const uint4*)(kv + (r0 + k) * D + c);
     }
   } else {
     for (int e = threadIdx.x; e < nt * plain; e += blockDim.x) {
       const int k = e / plain, c = e % plain;
       const int64_t t = p0 + i0 + k;
-      ring[((int64_t)b * cap + t % cap) * D + c] = kv[((int64_t)b * n_new + i0 + k) * D + c];
+      ring[((int64_t)b * cap + t % cap) * D + c] = kv[(r0 + k) * D + c];
     }
   }
   __syncthreads();
@@ -52,7 +51,7 @@ __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict_
   for (int e = threadIdx.x; e < nt * np; e += blockDim.x) {
     const int k = e / np, j = e % np, c = D - R + 2 * j;
     const int64_t t = p0 + i0 + k;
-    const T* src = kv + ((int64_t)b * n_new + i0 + k) * D;
+    const T* src = kv + (r0 + k) * D;
     T* dst = ring + ((int64_t)b * cap + t % cap) * D;
     double sn, cs;
     sincos((double)t * freq[j], &sn, &cs);
@@ -65,14 +64,13 @@ __global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict_
 
 // In place; one block per (token, sequence), threads over (row, pair).
 template <typename T>
-__global__ void __launch_bounds__(256) rope_kernel(T* __restrict__ x,
-                                                   const int64_t* __restrict__ pos0, int n_new,
-                                                   int rows, int width, int R, Rope base,
-                                                   int sign) {
+__global__ void __launch_bounds__(256) rope_kernel(T* __restrict__ x, Seqs sq, int rows,
+                                                   int width, int R, Rope base, int sign) {
   const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t t = pos0[b] + i;
+  if (i >= sq.len(b)) return;  // padding rows are left as they are
+  const int64_t t = sq.pos0[b] + i;
   const double p = (double)(sign * t);
-  T* base_ptr = x + ((int64_t)b * n_new + i) * (int64_t)rows * width;
+  T* base_ptr = x + sq.row(b, i) * (int64_t)rows * width;
   const int np = R / 2;
   for (int e = threadIdx.x; e < rows * np; e += blockDim.x) {
     const int r = e / np, j = e % np;
@@ -93,11 +91,10 @@ hipError_t launch_window_append(const Layer& L, const Batch& bt, const void* kv,
   const size_t shm = (size_t)(L.R / 2) * sizeof(double);
   if (L.dtype == 1)
     window_append_kernel<bf16_t><<<grid, 256, shm, s>>>((const bf16_t*)kv, (bf16_t*)ring,
-                                                        bt.pos0, bt.nvalid, bt.n, L.D, L.R, L.base,
-                                                        cap);
+                                                        seqs_of(bt), L.D, L.R, L.base, cap);
   else
-    window_append_kernel<float><<<grid, 256, shm, s>>>((const float*)kv, (float*)ring, bt.pos0,
-                                                       bt.nvalid, bt.n, L.D, L.R, L.base, cap);
+    window_append_kernel<float><<<grid, 256, shm, s>>>((const float*)kv, (float*)ring,
+                                                       seqs_of(bt), L.D, L.R, L.base, cap);
   return hipGetLastError();
 }
 
@@ -105,10 +102,10 @@ hipError_t launch_rope(const Layer& L, const Batch& bt, void* x, int rows, int w
                        int sign, hipStream_t s) {
   dim3 grid(bt.n, bt.B);
   if (L.dtype == 1)
-    rope_kernel<bf16_t><<<grid, 256, 0, s>>>((bf16_t*)x, bt.pos0, bt.n, rows, width, rope_dim,
+    rope_kernel<bf16_t><<<grid, 256, 0, s>>>((bf16_t*)x, seqs_of(bt), rows, width, rope_dim,
                                              L.base, sign);
   else
-    rope_kernel<float><<<grid, 256, 0, s>>>((float*)x, bt.pos0, bt.n, rows, width, rope_dim,
+    rope_kernel<float><<<grid, 256, 0, s>>>((float*)x, seqs_of(bt), rows, width, rope_dim,
                                             L.base, sign);
   return hipGetLastError();
 }

@@ -49,7 +49,7 @@ __all__ = [
     "pool_entry", "compress", "visible_entries",
     "window_positions", "index_scores", "topk_select", "attend",
     "csa_prefill", "hca_prefill", "sliding_prefill", "decode_step", "output_projection",
-    "ProjSizes", "project_inputs",
+    "ProjSizes", "project_inputs", "paged_rows", "PagedPool", "page_pool",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -352,6 +352,49 @@ def sliding_prefill(L, inp, queries=None, p0: int = 0, dtype=None, scale=None):
         out[n] = attend(inp["q"][i], t, win[wp.start - p0:wp.stop - p0], inp["sinks"], sc_,
                         L.rope_dim, rope_base(L), dt)
     return {"win": win, "out": out}
+
+
+# ----------------------------------------------------------------------------
+# paged pools [HF-doc "Cache layers": one cache per layer, each holding its own
+# pool; OV "What native registration would touch": the cache layout is not
+# uniform across layers].  The pages define no paging; the reading taken: a
+# sequence's pooled entries live in fixed-size blocks of a shared pool tensor,
+# block j of sequence b at block table[b][j].  Paging moves rows only; every
+# value is the contiguous pool's.
+
+def paged_rows(ids, table, block_entries: int) -> np.ndarray:
+    """Rows of the paged pool tensor holding entries ``ids`` of one sequence:
+    table[w // E] * E + w % E for entry w (E = block_entries)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    table = np.asarray(table, dtype=np.int64)
+    return table[ids // block_entries] * block_entries + ids % block_entries
+
+
+def page_pool(pool, table, block_entries: int, blocks: int) -> np.ndarray:
+    """The paged pool tensor [blocks * E, width] holding one sequence's
+    contiguous pool [n, width] (rows of unused blocks are zero)."""
+    pool = np.asarray(pool, dtype=np.float64)
+    out = np.zeros((blocks * block_entries, pool.shape[1]))
+    out[paged_rows(np.arange(pool.shape[0]), table, block_entries)] = pool
+    return out
+
+
+class PagedPool:
+    """Read view of one sequence's entries 0 .. n-1 in a paged pool tensor, for
+    ``decode_step`` (which indexes its pool caches with id arrays)."""
+
+    def __init__(self, rows, table, block_entries: int, n: int):
+        self.rows = rows
+        self.table = np.asarray(table, dtype=np.int64)
+        self.E = block_entries
+        self.shape = (n, np.asarray(rows).shape[1])
+
+    def __getitem__(self, ids):
+        if isinstance(ids, slice):
+            ids = np.arange(*ids.indices(self.shape[0]))
+        ids = np.asarray(ids, dtype=np.int64)
+        assert ids.size == 0 or (ids.min() >= 0 and ids.max() < self.shape[0])
+        return np.asarray(self.rows, dtype=np.float64)[paged_rows(ids, self.table, self.E)]
 
 
 def decode_step(L, t: int, new: Dict[str, np.ndarray], cache: Dict[str, np.ndarray],

@@ -39,7 +39,7 @@ def test_every_declared_entry_point_is_exported(lib):
 def test_status_strings_and_version(lib):
     for code in range(8):
         assert m.csa_status_str(code).startswith("CSA_")
-    assert lib.csa_version() >= 300
+    assert lib.csa_version() >= 400
 
 
 def csa_layer(**kw):
@@ -130,6 +130,21 @@ def test_rejections_return_before_launch(lib):
     assert m.csa_workspace_bytes(m.Layer("bf16", 64, 512, 64, 160000.0, 128, 4, 1, 64, 128, 64,
                                          512), 1, 8192, 2048, m.CSA_OP_INDEX_TOPK) > \
         m.CSA_NOALLOC_SCRATCH_BYTES
+    # packed rows and paged pools: one layout per call, block sizes a power of
+    # two of at least 128 entries, a table covering pool_cap, row ids in int32
+    assert call_attend(lib, L, batch(n_valid=FAKE.value, cu_seqlens=FAKE.value)) == SHAPE
+    for E in (64, 192, 0):
+        assert call_attend(lib, L, batch(block_table=FAKE.value, block_entries=E,
+                                         block_table_stride=16, pool_blocks=16)) == SHAPE
+    assert call_attend(lib, L, batch(block_table=FAKE.value, block_entries=128,
+                                     block_table_stride=15, pool_blocks=16)) == SHAPE  # 1920 < 2048
+    assert call_attend(lib, L, batch(block_table=FAKE.value, block_entries=128,
+                                     block_table_stride=16, pool_blocks=0)) == SHAPE
+    assert call_attend(lib, L, batch(block_table=FAKE.value, block_entries=1 << 20,
+                                     block_table_stride=1, pool_blocks=4096)) == UNSUP
+    assert lib.csa_compress(ctypes.byref(L), ctypes.byref(
+        batch(block_table=FAKE.value, block_entries=128, block_table_stride=15, pool_blocks=16)),
+        512, 64, FAKE, FAKE, None, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2048, None) == SHAPE
     # rope / window
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 64, 2, None) == SHAPE
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 65, 1, None) == SHAPE

@@ -837,3 +837,271 @@ def test_varlen_prefill_dense_layers(csa, kind):
     ref = O.sliding_prefill(spec, x, queries=qs) if kind == "sliding" else \
         O.hca_prefill(spec, x, queries=qs)
     assert_close(host(out[1])[qs], ref["out"], "bf16", f"varlen {kind} rows vs oracle")
+
+
+# ----------------------------------------------------------------------------
+# paged pools and packed variable-length rows
+
+def _shuffled_table(B, per_seq, spare, seed):
+    """int32 [B, per_seq] device block table over B * per_seq + spare blocks,
+    shuffled (no two sequences share a block) -> (table, host copy, blocks)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    nb = B * per_seq + spare
+    ids = rng.permutation(nb)[:B * per_seq].reshape(B, per_seq).astype(np.int32)
+    return torch.from_numpy(ids).cuda(), ids, nb
+
+
+def _gather_paged(pool_rows, table_host, E, n):
+    """Entries 0..n-1 of each sequence from a paged pool tensor (host float64)."""
+    rows = host(pool_rows)
+    return np.stack([rows[O.paged_rows(np.arange(n), table_host[b], E)]
+                     for b in range(table_host.shape[0])])
+
+
+def test_paged_prefill_matches_contiguous(csa):
+    """A CSA prefill in two chunks with both pools paged through a shuffled
+    block table (128 entries per block): ids, outputs and every pooled entry
+    bitwise equal to the contiguous run; sampled queries of one sequence
+    against the oracle."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    say("case: paged prefill, csa bf16 B=2 S=1000 in chunks (0, 600), (600, 1000), E=128")
+    m = csa
+    B, S, E = 2, 1000, 128
+    w = synth.workload("csa_prefill", S=S, batch=B)
+    spec = w.layers[0]
+    inp = synth.prefill_inputs(w, 21)
+    L = m.Layer.from_spec(spec)
+    keys = ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+    a = {k: dev(inp[k]) for k in keys}
+    sinks = dev(inp["sinks"])
+    pcap = S // 4
+    per = (pcap + E - 1) // E
+    tab, tab_h, nb = _shuffled_table(B, per, 3, seed=4)
+    cont = LayerCache(L, B, S, pcap)
+    paged = LayerCache(L, B, S, pcap, block_entries=E, pool_blocks=nb, block_table=tab)
+    for lo, hi in ((0, 600), (600, S)):
+        p = torch.full((B,), lo, dtype=torch.int64, device="cuda")
+        sl = {k: v[:, lo:hi].contiguous() for k, v in a.items()}
+        o1, i1 = layer_step(cont, p, lo, *(sl[k] for k in keys), sinks)
+        o2, i2 = layer_step(paged, p, lo, *(sl[k] for k in keys), sinks)
+        torch.cuda.synchronize()
+        assert torch.equal(i1, i2), f"chunk {lo}: ids"
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"chunk {lo}: output"
+    assert np.array_equal(_gather_paged(paged.pool, tab_h, E, pcap), host(cont.pool))
+    assert np.array_equal(_gather_paged(paged.ipool, tab_h, E, pcap), host(cont.ipool))
+    # rows of blocks no sequence owns stay untouched
+    unused = sorted(set(range(nb)) - set(tab_h.ravel().tolist()))
+    prow = host(paged.pool).reshape(nb, E, -1)
+    assert not prow[unused].any()
+    # one sequence against the oracle (the last chunk's queries)
+    x = seq_f64(inp, 1)
+    qs = [600, 601, 777, 999]
+    ref = O.csa_prefill(spec, x, queries=qs)
+    assert np.array_equal(_gather_paged(paged.pool, tab_h, E, pcap)[1], ref["pool"])
+    gi = i2[1].cpu().numpy()
+    for j, t in enumerate(qs):
+        sc, ab = index_exact(spec, x["qi"][t], x["wi"][t], ref["ipool"][:(t + 1) // 4], t)
+        audit_topk(gi[t - 600], ref["idx"][j], sc, ab, spec.index_dim, spec.index_heads)
+    same = [j for j, t in enumerate(qs) if np.array_equal(gi[t - 600], ref["idx"][j])]
+    assert_close(host(o2[1])[[t - 600 for t in qs]][same], ref["out"][same], "bf16",
+                 "paged prefill vs oracle")
+
+
+def test_paged_decode_matches_contiguous(csa):
+    """One decode step of the mixed three-layer model (entries close in the
+    CSA and HCA layers at this position) with each layer's pools paged
+    through its own shuffled table (CSA: 256 entries per block, HCA: 128):
+    outputs, ids and the new entries bitwise equal to the contiguous run; one
+    sequence against the oracle reading the paged rows."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    m = csa
+    pos0, B = 40959, 3
+    say(f"case: paged decode, mixed_decode B={B} pos0={pos0}")
+    w = synth.workload("mixed_decode", pos0=pos0, batch=B)
+    for li, spec in enumerate(w.layers):
+        say(f"  layer {li} {spec.kind}")
+        inp = synth.decode_inputs(w, 22, li)
+        L = m.Layer.from_spec(spec)
+        pcap = (pos0 + 1) // spec.ratio if spec.ratio else 1
+        kw = {}
+        if spec.ratio:
+            E = 256 if spec.has_indexer else 128
+            tab, tab_h, nb = _shuffled_table(B, (pcap + E - 1) // E, 5, seed=li)
+            kw = dict(block_entries=E, pool_blocks=nb, block_table=tab)
+        cont = LayerCache(L, B, spec.window, pcap)
+        paged = LayerCache(L, B, spec.window, pcap, **kw)
+        P = pos0 // spec.ratio if spec.ratio else 0
+        for c in (cont, paged):
+            c.ring.copy_(dev(inp["win"]))
+            if spec.ratio:
+                c.cstate_kv.copy_(dev(inp["cstate_kv"]))
+                c.cstate_gate.copy_(dev(inp["cstate_gate"]))
+                if spec.has_indexer:
+                    c.istate_kv.copy_(dev(inp["istate_kv"]))
+                    c.istate_gate.copy_(dev(inp["istate_gate"]))
+        if spec.ratio:
+            cont.pool[:, :P].copy_(dev(inp["pool"]))
+            for b in range(B):
+                rows = torch.from_numpy(O.paged_rows(np.arange(P), tab_h[b], E)).cuda()
+                paged.pool[rows] = dev(inp["pool"][b])
+                if spec.has_indexer:
+                    paged.ipool[rows] = dev(inp["ipool"][b])
+            if spec.has_indexer:
+                cont.ipool[:, :P].copy_(dev(inp["ipool"]))
+        p0 = torch.full((B,), pos0, dtype=torch.int64, device="cuda")
+        args = [dev(inp[k]) if k in inp else None
+                for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")]
+        sk = dev(inp["sinks"])
+        o1, i1 = layer_step(cont, p0, pos0, *args, sk)
+        o2, i2 = layer_step(paged, p0, pos0, *args, sk)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "output"
+        if spec.has_indexer:
+            assert torch.equal(i1, i2), "ids"
+        if spec.ratio:
+            n = pcap
+            assert np.array_equal(_gather_paged(paged.pool, tab_h, E, n), host(cont.pool[:, :n]))
+        # sequence 2 against the oracle, its pools read through the table
+        b = 2
+        new = {k: (to_f64(inp[k]) if k == "sinks" else to_f64(inp[k][b, 0]))
+               for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi", "sinks")
+               if k in inp}
+        cch = {k: to_f64(inp[k][b]) for k in ("win", "cstate_kv", "cstate_gate", "istate_kv",
+                                              "istate_gate") if k in inp}
+        if spec.ratio:  # the paged rows as they were before the step
+            rows_before = np.zeros((nb * E, spec.head_dim))
+            rows_before[O.paged_rows(np.arange(P), tab_h[b], E)] = to_f64(inp["pool"][b])
+            cch["pool"] = O.PagedPool(rows_before, tab_h[b], E, P)
+            if spec.has_indexer:
+                irows = np.zeros((nb * E, spec.index_dim))
+                irows[O.paged_rows(np.arange(P), tab_h[b], E)] = to_f64(inp["ipool"][b])
+                cch["ipool"] = O.PagedPool(irows, tab_h[b], E, P)
+        ref = O.decode_step(spec, pos0, new, cch)
+        if spec.has_indexer:
+            keys = np.concatenate([cch["ipool"][np.arange(P)], ref["new_ipool"][None]])
+            sc, ab = index_exact(spec, new["qi"], new["wi"], keys, pos0)
+            nd = audit_topk(i2[b, 0].cpu().numpy(), ref["idx"], sc, ab, spec.index_dim,
+                            spec.index_heads)
+            if nd:  # a proven near tie: outputs differ by the rows chosen
+                say(f"  seq {b}: {nd} near-tie id differences")
+                continue
+        assert_close(host(o2[b, 0]), ref["out"], "bf16", f"layer {li} seq {b} vs oracle")
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "sliding"])
+def test_packed_varlen_prefill_matches_padded(csa, kind):
+    """Packed rows (cu_seqlens, no padding rows) against the padded
+    variable-length call of the same sequences (700, 413 and 0 tokens, then
+    300 more each): ids, outputs and caches bitwise equal."""
+    import dataclasses
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    say(f"case: packed varlen prefill, {kind} bf16, lens (700, 413, 0) then 300 each")
+    m = csa
+    S, S2, lens = 700, 300, (700, 413, 0)
+    name = "csa_prefill" if kind == "csa" else "hca_prefill"
+    w, w2 = synth.workload(name, S=S, batch=3), synth.workload(name, S=S2, batch=3)
+    if kind == "sliding":
+        spec = synth.LayerSpec(kind="sliding", dtype="bf16", ratio=0, overlap=0,
+                               rope_theta=10000.0, rope_factor=16.0,
+                               rope_original_context=65536.0)
+        w, w2 = dataclasses.replace(w, layers=[spec]), dataclasses.replace(w2, layers=[spec])
+    spec = w.layers[0]
+    inp, inp2 = synth.prefill_inputs(w, 23), synth.prefill_inputs(w2, 24)
+    keys = [k for k in ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi") if k in inp]
+    a = {k: dev(inp[k]) for k in keys}
+    a2 = {k: dev(inp2[k]) for k in keys}
+    sinks = dev(inp["sinks"])
+    L = m.Layer.from_spec(spec)
+    cap = S + S2
+    pcap = cap // spec.ratio if spec.ratio else 1
+
+    def run(cache, p0, pmax, t, **geo):
+        return layer_step(cache, p0, pmax, t["q"], t["kv"], t.get("ckv"), t.get("cgate"),
+                          t.get("ikv"), t.get("igate"), t.get("qi"), t.get("wi"), sinks, **geo)
+
+    pad, pk = LayerCache(L, 3, cap, pcap), LayerCache(L, 3, cap, pcap)
+    p0 = torch.zeros(3, dtype=torch.int64, device="cuda")
+    nv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cu = torch.tensor(np.r_[0, np.cumsum(lens)], dtype=torch.int32, device="cuda")
+    packed = {k: torch.cat([v[b, :n] for b, n in enumerate(lens)]).contiguous()
+              for k, v in a.items()}
+    o1, i1 = run(pad, p0, 0, a, n_valid=nv)
+    o2, i2 = run(pk, p0, 0, packed, cu_seqlens=cu, n_new=S)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        r = int(sum(lens[:b]))
+        assert torch.equal(o1[b, :n].view(torch.int16), o2[r:r + n].view(torch.int16)), b
+        if i1 is not None:
+            assert torch.equal(i1[b, :n], i2[r:r + n]), b
+    # second call: 300 more tokens each, packed as three equal runs
+    p1 = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    cu2 = torch.tensor([0, S2, 2 * S2, 3 * S2], dtype=torch.int32, device="cuda")
+    packed2 = {k: v.reshape(3 * S2, *v.shape[2:]).contiguous() for k, v in a2.items()}
+    o3, i3 = run(pad, p1, max(lens), a2)
+    o4, i4 = run(pk, p1, max(lens), packed2, cu_seqlens=cu2, n_new=S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.reshape(3 * S2, *o3.shape[2:]).view(torch.int16),
+                       o4.view(torch.int16))
+    if i3 is not None:
+        assert torch.equal(i3.reshape(3 * S2, -1), i4)
+    assert torch.equal(pad.ring, pk.ring)
+    if spec.ratio:
+        assert torch.equal(pad.pool, pk.pool) and torch.equal(pad.cstate_kv, pk.cstate_kv)
+        if spec.has_indexer:
+            assert torch.equal(pad.ipool, pk.ipool) and torch.equal(pad.istate_gate,
+                                                                     pk.istate_gate)
+
+
+def test_packed_paged_decode_skips_absent_sequences(csa):
+    """One-token calls with packed rows (sequence 1 has no token) on
+    paged pools, against the padded call on contiguous pools: outputs and ids
+    bitwise equal, the absent sequences' caches untouched (an entry closes at
+    4099)."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache, layer_step
+    m = csa
+    pos0, B, E = 4099, 4, 128
+    lens = (1, 0, 1, 1)
+    say(f"case: packed + paged decode, csa_decode B={B} pos0={pos0} lens {lens}")
+    w = synth.workload("csa_decode", pos0=pos0, batch=B)
+    spec = w.layers[0]
+    inp = synth.decode_inputs(w, 25, 0)
+    L = m.Layer.from_spec(spec)
+    pcap = (pos0 + 1) // 4
+    P = pos0 // 4
+    tab, tab_h, nb = _shuffled_table(B, (pcap + E - 1) // E, 2, seed=9)
+    pad = LayerCache(L, B, spec.window, pcap)
+    pk = LayerCache(L, B, spec.window, pcap, block_entries=E, pool_blocks=nb, block_table=tab)
+    for c in (pad, pk):
+        c.ring.copy_(dev(inp["win"]))
+        for k in ("cstate_kv", "cstate_gate", "istate_kv", "istate_gate"):
+            getattr(c, k).copy_(dev(inp[k]))
+    pad.pool[:, :P].copy_(dev(inp["pool"]))
+    pad.ipool[:, :P].copy_(dev(inp["ipool"]))
+    for b in range(B):
+        rows = torch.from_numpy(O.paged_rows(np.arange(P), tab_h[b], E)).cuda()
+        pk.pool[rows] = dev(inp["pool"][b])
+        pk.ipool[rows] = dev(inp["ipool"][b])
+    keys = ("q", "kv", "ckv", "cgate", "ikv", "igate", "qi", "wi")
+    a = {k: dev(inp[k]) for k in keys}
+    present = [b for b in range(B) if lens[b]]
+    packed = {k: v[present, 0].contiguous() for k, v in a.items()}
+    p0 = torch.full((B,), pos0, dtype=torch.int64, device="cuda")
+    nv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cu = torch.tensor(np.r_[0, np.cumsum(lens)], dtype=torch.int32, device="cuda")
+    sk = dev(inp["sinks"])
+    o1, i1 = layer_step(pad, p0, pos0, *(a[k] for k in keys), sk, n_valid=nv)
+    o2, i2 = layer_step(pk, p0, pos0, *(packed[k] for k in keys), sk, cu_seqlens=cu, n_new=1)
+    torch.cuda.synchronize()
+    for r, b in enumerate(present):
+        assert torch.equal(o1[b, 0].view(torch.int16), o2[r].view(torch.int16)), b
+        assert torch.equal(i1[b, 0], i2[r]), b
+    got = _gather_paged(pk.pool, tab_h, E, pcap)
+    assert np.array_equal(got, host(pad.pool))
+    for b in [b for b in range(B) if lens[b] == 0]:  # absent: no new entry, state as it was
+        assert not got[b, P:].any()
+        assert torch.equal(pk.cstate_kv[b], dev(inp["cstate_kv"])[b])

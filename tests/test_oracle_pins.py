@@ -515,6 +515,72 @@ def test_decode_step_equals_prefill_row(kind):
 
 
 # ----------------------------------------------------------------------------
+# paged pools
+
+def test_paged_rows_is_a_bijection_onto_the_sequences_blocks():
+    E, table = 4, np.array([5, 0, 3])
+    rows = O.paged_rows(np.arange(12), table, E)
+    assert list(rows[:4]) == [20, 21, 22, 23] and list(rows[4:8]) == [0, 1, 2, 3]
+    assert sorted(rows) == sorted(set(rows))                 # no two entries share a row
+    assert set(rows // E) == set(table)                        # exactly the table's blocks
+    assert np.array_equal(rows % E, np.arange(12) % E)         # offsets within a block kept
+    # two sequences with disjoint tables never share a row
+    other = O.paged_rows(np.arange(12), np.array([1, 2, 4]), E)
+    assert not set(rows) & set(other)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_decode_step_on_paged_pools_equals_contiguous(kind):
+    """A decode step reading its pools through a shuffled block table gives the
+    contiguous result exactly (ids, output, the entry that closes)."""
+    L = small_layer(kind, window=8)
+    S = 63 if kind == "csa" else 47          # an entry closes at t = S (csa: 64 % 4, hca: 48 % 8)
+    inp = rand_inputs(L, S + 1, seed=31, q_scale=2.0)
+    full = {"csa": O.csa_prefill, "hca": O.hca_prefill}[kind](
+        L, {k: (v[:S] if k != "sinks" else v) for k, v in inp.items()}, dtype="f64")
+    t = S
+    m, Ls = L.ratio, (1 + L.overlap) * L.ratio
+    P = t // m
+    win = np.zeros((L.window, L.head_dim))
+    for s_ in range(t - L.window, t):
+        win[s_ % L.window] = full["win"][s_]
+    cache = {"win": win}
+    for pre, kk, gk in (("c", "ckv", "cgate"), ("i", "ikv", "igate")):
+        st_kv, st_g = np.zeros((Ls, inp[kk].shape[1])), np.zeros((Ls, inp[kk].shape[1]))
+        for s_ in range(t - Ls, t):
+            st_kv[s_ % Ls], st_g[s_ % Ls] = inp[kk][s_], inp[gk][s_]
+        cache[pre + "state_kv"], cache[pre + "state_gate"] = st_kv, st_g
+    new = {k: (v[t] if k != "sinks" else v) for k, v in inp.items()}
+    E = 4
+    nblk = (P + E - 1) // E
+    rng = np.random.default_rng(5)
+    table = rng.permutation(3 * nblk)[:nblk]                  # shuffled, sparse blocks
+    cont = dict(cache, pool=full["pool"][:P])
+    paged = dict(cache, pool=O.PagedPool(O.page_pool(full["pool"][:P], table, E, 3 * nblk),
+                                         table, E, P))
+    if L.has_indexer:
+        cont["ipool"] = full["ipool"][:P]
+        paged["ipool"] = O.PagedPool(O.page_pool(full["ipool"][:P], table, E, 3 * nblk),
+                                     table, E, P)
+    a = O.decode_step(L, t, new, cont, dtype="f64")
+    b = O.decode_step(L, t, new, paged, dtype="f64")
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["new_pool"], b["new_pool"])
+    if L.has_indexer:
+        assert np.array_equal(a["idx"], b["idx"])
+    # a wrong table (the block of an attended entry pointing at an unused
+    # block) reads other rows and changes the result
+    if nblk > 0:
+        bad = table.copy()
+        j0 = int(a["idx"][0]) // E if L.has_indexer else 0
+        bad[j0] = [j for j in range(3 * nblk) if j not in set(table)][0]
+        c = dict(paged, pool=O.PagedPool(paged["pool"].rows, bad, E, P))
+        if L.has_indexer:
+            c["ipool"] = O.PagedPool(paged["ipool"].rows, bad, E, P)
+        assert not np.array_equal(O.decode_step(L, t, new, c, dtype="f64")["out"], a["out"])
+
+
+# ----------------------------------------------------------------------------
 # grouped output projection
 
 def _oproj_inputs(T, H, D, G, R, hidden, seed):
