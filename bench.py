@@ -118,26 +118,104 @@ def measured_traffic():
         return None
 
 
+def host_info():
+    """The host cores this process may use, the CPU model and numpy's BLAS."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", 1
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(d.get("num_threads", 1) for d in info)
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "host_cores": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": int(threads)}
+
+
+def _baseline(value, unit, dt, sample):
+    h = host_info()
+    return {"value": value, "unit": unit, "cores": h["blas_threads"], "kind": "oracle",
+            "sample": f"{sample}; {dt:.1f} s of oracle time", **h}
+
+
 def cpu_baseline(spec, inp, stride):
     """The oracle as it stands, on every `stride`-th query of the same layer."""
     from oracle import csa_oracle as O
     from synth import to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
     x = {k: (to_f64(v) if k == "sinks" else to_f64(v[0])) for k, v in inp.items()}
     S = x["q"].shape[0]
     qs = list(range(S - 1, -1, -stride))
     t0 = time.perf_counter()
     O.csa_prefill(spec, x, queries=qs)
     dt = time.perf_counter() - t0
-    return {"value": len(qs) / dt, "unit": "tokens/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"csa_prefill S={S}: full compressor passes + every {stride}-th query "
-                      f"({len(qs)} queries, incl. the last), {dt:.1f} s on "
-                      f"{len(os.sched_getaffinity(0))} host cores"}
+    return _baseline(len(qs) / dt, "tokens/s", dt,
+                     f"csa_prefill S={S}: full compressor passes + every {stride}-th query "
+                     f"({len(qs)} queries, incl. the last)")
+
+
+class _Rows:
+    """Float64 view of a stored tensor, decoded where indexed (bounded memory)."""
+
+    def __init__(self, arr):
+        self.arr, self.shape = arr, arr.shape
+
+    def __getitem__(self, i):
+        from synth import to_f64
+        return to_f64(self.arr[i])
+
+
+def cpu_baseline_hca(spec, inp, nq=256):
+    """The oracle on the HCA S=65536 layer: full compressor and window passes,
+    then nq queries spread over the sequence (rows decoded as gathered)."""
+    import numpy as np
+    from oracle import csa_oracle as O
+    from synth import to_f64
+    S = inp["q"].shape[1]
+    x = {"q": _Rows(inp["q"][0]), "kv": to_f64(inp["kv"][0]), "ckv": to_f64(inp["ckv"][0]),
+         "cgate": to_f64(inp["cgate"][0]), "sinks": to_f64(inp["sinks"])}
+    qs = sorted(set(np.linspace(0, S - 1, nq).astype(int).tolist()))
+    t0 = time.perf_counter()
+    O.hca_prefill(spec, x, queries=qs)
+    dt = time.perf_counter() - t0
+    return _baseline(len(qs) / dt, "tokens/s", dt,
+                     f"hca_prefill S={S}: full compressor and window passes + {len(qs)} "
+                     "queries spread over the sequence")
+
+
+def cpu_baseline_decode(name, seqs):
+    """The oracle's decode step of the first `seqs` sequences of a decode
+    workload, every layer; the cache draws are not timed."""
+    import synth
+    from oracle import csa_oracle as O
+    from synth import to_f64
+    w = synth.workload(name)
+    t, dt = w.pos0, 0.0
+    for li, spec in enumerate(w.layers):
+        new_all = synth.prefill_inputs(w, 0, li)
+        for b in range(seqs):
+            names = list(synth.cache_shapes(w, li))
+            c = synth.decode_cache_seq(w, 0, li, b, names=[n for n in names if n != "pool"])
+            cache = {k: to_f64(v) for k, v in c.items()}
+            if spec.ratio:
+                cache["pool"] = _Rows(synth.decode_cache_seq(w, 0, li, b, names=["pool"])["pool"])
+            new = {k: (to_f64(v) if k == "sinks" else to_f64(v[b, 0]))
+                   for k, v in new_all.items()}
+            t0 = time.perf_counter()
+            O.decode_step(spec, t, new, cache)
+            dt += time.perf_counter() - t0
+            del c, cache
+    return _baseline(seqs / dt, "tokens/s", dt,
+                     f"{name}: {seqs} of {w.batch} sequences at t={t}, every layer")
 
 
 def _dev(torch, a):
@@ -428,11 +506,18 @@ def calib_copy(torch, mib):
     del src, dst
 
 
+BASELINE_SEQS = {"csa_decode": 16, "mixed_decode": 2}   # sequences the oracle decodes
+_HCA_INPUTS = []
+
+
 def run_leg(torch, m, name, args):
     if name in ("csa_prefill", "hca_prefill"):
         steps = args.steps if name == "csa_prefill" else max(2, args.steps // 4)
-        _, _, r = prefill_leg(torch, m, name, steps, min(args.warmup, 1 if
-                              name == "hca_prefill" else args.warmup), attn_events=True)
+        spec, inp, r = prefill_leg(torch, m, name, steps, min(args.warmup, 1 if
+                                   name == "hca_prefill" else args.warmup), attn_events=True)
+        if name == "hca_prefill" and not args.no_cpu_baseline:
+            _HCA_INPUTS.append((spec, inp))
+        del inp
         r["roofline"] = {"bound": "mfma", "kernel": "attend_mfma",
                          "achieved": r["attend_flop"] / (r["attend_ms"] * 1e-3) / 1e12,
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
@@ -498,6 +583,10 @@ def main():
     for name in [x for x in args.legs.split(",") if x]:
         legs[name] = run_leg(torch, m, name, args)
         torch.cuda.empty_cache()
+        if not args.no_cpu_baseline and name in BASELINE_SEQS:
+            legs[name]["cpu_baseline"] = cpu_baseline_decode(name, BASELINE_SEQS[name])
+        if not args.no_cpu_baseline and name == "hca_prefill":
+            legs[name]["cpu_baseline"] = cpu_baseline_hca(*_HCA_INPUTS.pop())
 
     S = 8192
     achieved = head["attend_flop"] / (head["attend_ms"] * 1e-3) / 1e12
@@ -516,7 +605,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "csa_prefill", "batch": 1, "seq_len": S, "heads": 64,
                    "head_dim": 512, "rope_dim": 64, "window": 128, "compress_ratio": 4,
-                   "index_heads": 64, "index_dim": 128, "index_topk": 512},
+                   "index_heads": 64, "index_dim": 128, "index_topk": 512,
+                   "rope_theta": spec.rope_theta, "rope_factor": spec.rope_factor,
+                   "rope_original_context": spec.rope_original_context},
         "roofline": {"bound": "mfma", "kernel": "attend_mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),

@@ -560,7 +560,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 // (token, head): lane s first reads split s's (m, l), then every lane merges
 // 8 channels over all splits.
 constexpr int kMergeHeads = 4;  // heads (waves) per merge block
-constexpr int kMaxSplits = 256;
 
 __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
     const float* __restrict__ part, const float* __restrict__ sinks, bf16_t* __restrict__ out,
@@ -756,50 +755,6 @@ size_t attend_generic_shm(const Layer& L) {
 }
 
 // ---------------------------------------------------------------------------
-
-bool attend_fast_shape(const Layer& L) {
-  return L.dtype == 1 && L.H == kAH && L.D == kAD && L.W >= 1 &&
-         (L.R == 16 || L.R == 32 || L.R == 64 || L.R == 128);
-}
-
-static int64_t attend_rows(const Layer& L, int64_t pool_cap, bool csa) {
-  int64_t npool = 0;
-  if (L.m > 0) npool = csa ? (pool_cap < L.k ? pool_cap : (int64_t)L.k) : pool_cap;
-  return (int64_t)L.W + npool;
-}
-
-// Calls of fewer than 256 tokens run attend_decode (rows and head groups
-// spread over the chip), except a few tokens with long row lists: there
-// attend_mfma's 64-head blocks, each splitting a list over many blocks, keep
-// more rows in flight per block.
-static bool attend_dec(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
-  const int64_t tokens = (int64_t)B * n;
-  return tokens < 256 && (tokens >= 16 || attend_rows(L, pool_cap, csa) <= 256);
-}
-
-int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
-  if (!attend_fast_shape(L)) return 1;
-  if (attend_dec(L, B, n, pool_cap, csa)) return attend_decode_splits(L, B, n, pool_cap, csa);
-  const int64_t nch = (attend_rows(L, pool_cap, csa) + kCH - 1) / kCH;
-  const int64_t tokens = (int64_t)B * n;
-  // no block above kMaxRows rows; calls of fewer than 256 tokens also split
-  // while the grid is short of ~2 blocks per CU and every split keeps >= 4
-  // chunks (128 rows: its float32 partial, 64 x 516 words, costs about as
-  // much traffic as the rows)
-  const int64_t need = (nch * kCH + kMaxRows - 1) / kMaxRows;
-  int64_t s = tokens >= 256 ? 1 : (512 + tokens - 1) / tokens;
-  const int64_t cap = nch / (128 / kCH) > 1 ? nch / (128 / kCH) : 1;
-  if (s > cap) s = cap;
-  if (s < need) s = need;
-  if (s < 1) s = 1;
-  return s > kMaxSplits ? -1 : (int)s;  // -1: too many rows
-}
-
-size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
-  const int s = attend_splits(L, B, n, pool_cap, csa);
-  if (s <= 1) return 0;
-  return (size_t)B * n * s * kAH * kPart * sizeof(float);
-}
 
 hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const void* win,
                          int64_t win_cap, const void* pool, int64_t pool_cap, const int32_t* idx,

@@ -16,10 +16,7 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-constexpr int kAH = 64, kAD = 512, kCH = 32;
-constexpr int kMaxRows = 1024;   // rows handled by one block
 constexpr int kMaxRope = 128;    // rope channels supported by the fast path
-constexpr int kPart = kAD + 4;   // split partial row: O[512], m, l, 2 pad (16-byte rows)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max is raised
 // Tuning (compile time): the blocks per CU the register budget targets.

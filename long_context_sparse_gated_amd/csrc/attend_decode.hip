@@ -32,8 +32,6 @@
 
 namespace csa {
 
-constexpr int kDCh = 64;              // rows per chunk
-constexpr int kDMaxRows = 2048;       // rows of one block (ids kept in LDS)
 constexpr int kDPRow = 2 * 32 + 8;    // LDS row of P^T per head: 2 x 32 row slots + pad
 
 template <int R>
@@ -325,22 +323,6 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
       prow[kAD + 1] = lb;
     }
   }
-}
-
-// Row slices per token: about 256 blocks over the call, whole chunks each,
-// at most kDMaxRows rows per block; -1 if more slices than the merge takes.
-int attend_decode_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa) {
-  int64_t npool = 0;
-  if (L.m > 0) npool = csa ? (pool_cap < L.k ? pool_cap : (int64_t)L.k) : pool_cap;
-  const int64_t rows = (int64_t)L.W + npool;
-  const int64_t nch = (rows + kDCh - 1) / kDCh;
-  const int64_t tokens = (int64_t)B * n;
-  int64_t s = 64 / tokens;
-  if (s > nch) s = nch;
-  const int64_t need = (nch * kDCh + kDMaxRows - 1) / kDMaxRows;
-  if (s < need) s = need;
-  if (s < 1) s = 1;
-  return s > 256 ? -1 : (int)s;
 }
 
 hipError_t launch_attend_decode(const Layer& L, const Batch& bt, const void* q, const void* win,

@@ -11,6 +11,20 @@ typedef uint16_t bf16_t;  // bfloat16 carried as its raw bits
 
 constexpr int kMaxTopK = 4096;  // largest index_topk the library accepts
 
+// Tile sizes shared by the kernels and the host planning (plan.hip).
+constexpr int kAH = 64, kAD = 512;  // heads and head_dim of the attention fast path
+constexpr int kCH = 32;             // rows per chunk of attend_mfma
+constexpr int kMaxRows = 1024;      // rows of one attend_mfma block
+constexpr int kPart = kAD + 4;      // split partial row: O[512], m, l, 2 pad (16-byte rows)
+constexpr int kMaxSplits = 256;     // row splits the merge takes
+constexpr int kDCh = 64;            // rows per chunk of attend_decode
+constexpr int kDMaxRows = 2048;     // rows of one attend_decode block (ids kept in LDS)
+constexpr int kIdxQPB = 8;          // queries per block of index_prefill_mfma; fewer new
+                                    // tokens per sequence take the decode indexer
+constexpr int kHBits = 12, kHBins = 1 << kHBits;  // decode score histogram
+constexpr int kSlice = 1024;        // keys per topk_collect wave
+constexpr int kMaxSlices = 2048;    // topk_final keeps slice offsets in LDS
+
 // Rope frequencies of a layer: pair j of R rope channels turns at
 // base^(-2j/R) per position, remapped by YaRN when factor > 1 (rope_freq in
 // csa_device.h).
@@ -119,17 +133,21 @@ hipError_t launch_rope(const Layer& L, const Batch& b, void* x, int rows, int wi
 hipError_t launch_compress(const Layer& L, const Batch& b, int width, int rope_dim, const void* kv,
                            const void* gate, const float* norm_w, float eps, void* st_kv,
                            void* st_gate, void* pool, int64_t pool_cap, hipStream_t s);
-// index.hip
+// plan.hip
+size_t align256(size_t x);
+bool index_fast_shape(const Layer& L);
+bool index_decode_path(const Layer& L, int n, int64_t pool_cap);
 size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap);
+bool attend_dec(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
+// index.hip
 hipError_t launch_index_topk(const Layer& L, const Batch& b, const void* q, const void* w,
                              const void* keys, int64_t pool_cap, int32_t* idx, float* scores_out,
                              void* ws, hipStream_t s);
-// attend.hip
 bool attend_fast_shape(const Layer& L);
 int attend_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
 size_t attend_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
-// attend_decode.hip
 int attend_decode_splits(const Layer& L, int B, int n, int64_t pool_cap, bool csa);
+// attend_decode.hip
 hipError_t launch_attend_decode(const Layer& L, const Batch& b, const void* q, const void* win,
                                 int64_t win_cap, const void* pool, int64_t pool_cap,
                                 const int32_t* idx, const float* sinks, void* out, void* ws,

@@ -112,7 +112,6 @@ __device__ __forceinline__ uint4 rope4_fast(uint4 v, const float2 (&c)[4], int d
 // ---------------------------------------------------------------------------
 // prefill: 8 queries per block, keys through LDS
 
-constexpr int kIdxQPB = 8;    // queries per block
 constexpr int kIdxKT = 64;    // keys per LDS tile
 constexpr int kIdxRow = 136;  // LDS row stride in bf16 (128 + 8 pad)
 
@@ -463,9 +462,7 @@ __global__ void __launch_bounds__(256, 2) index_prefill_x32(
 // those inside it; topk_final settles the bin by radix select over the few
 // keys in it and merges both id lists in ascending order.
 
-constexpr int kHBits = 12, kHBins = 1 << kHBits, kHShift = 32 - kHBits;
-constexpr int kSlice = 1024;         // keys per collect wave
-constexpr int kMaxSlices = 2048;     // topk_final keeps slice offsets in LDS
+constexpr int kHShift = 32 - kHBits;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -1426,33 +1423,6 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
 }
 
 // ---------------------------------------------------------------------------
-
-static bool index_fast_shape(const Layer& L) {
-  return L.dtype == 1 && L.Hi == 64 && L.Di == 128 && L.Ri <= 128;
-}
-
-// Few new tokens per sequence over a pool the selection buffers can index.
-static bool index_decode_path(const Layer& L, int n, int64_t pool_cap) {
-  return index_fast_shape(L) && n < kIdxQPB &&
-         (pool_cap + kSlice - 1) / kSlice <= kMaxSlices;
-}
-
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t index_workspace_bytes(const Layer& L, int B, int n, int64_t pool_cap) {
-  const size_t bn = (size_t)B * n;
-  size_t s = align256(bn * pool_cap * sizeof(float));
-  if (index_decode_path(L, n, pool_cap)) {
-    const size_t nslice = (size_t)((pool_cap + kSlice - 1) / kSlice);
-    s += align256(bn * L.Hi * L.Di * 2);              // rotated queries
-    s += align256(bn * kHBins * sizeof(uint32_t));    // score histograms
-    s += 2 * align256(bn * pool_cap * sizeof(int32_t));  // candidate ids
-    s += align256(bn * nslice * 2 * sizeof(uint32_t) + 64);  // per-slice counts, discard
-  } else if (index_fast_shape(L)) {
-    s += 256;  // discard slots of index_prefill_x32
-  }
-  return s;
-}
 
 hipError_t launch_index_topk(const Layer& L, const Batch& bt, const void* q, const void* w,
                              const void* keys, int64_t pool_cap, int32_t* idx, float* scores_out,
