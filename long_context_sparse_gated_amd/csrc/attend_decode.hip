@@ -5,34 +5,89 @@
 // (eq. 26)].
 //
 // With few tokens the whole chip has to work on few row lists, and the cost
-// is memory traffic and latency, not MFMA time.  attend_decode divides the
-// work by (token, group of 16 heads, slice of rows):
-//  * a block holds only its 16 heads' rotated queries (16 KB, not the
-//    token's 64 KB), and its float32 partial (with several row slices) is a
-//    quarter of a 64-head one, so split partials stay small;
+// is moving rows, not MFMA time.  attend_decode divides the work by (token,
+// group of 16 heads, slice of rows):
+//  * a block holds only its 16 heads' rotated queries, and its float32
+//    partial (with several row slices) is a quarter of a 64-head one;
 //  * the four head groups of a token gather the same rows; their blocks get
 //    ids of equal residue mod 8, which the dispatcher places on one XCD
 //    (workgroups go to the XCDs round-robin), so the second to fourth
 //    gathers of a row hit that XCD's L2;
-//  * rows come in chunks of 64 through LDS (LDS-DMA, double buffered); wave
-//    w scores rows 16w .. 16w+15 of a chunk for the 16 heads (S^T = K Q^T,
-//    queries as the B operand), the chunk maximum per head is shared through
-//    LDS, and P^T (64 rows x 16 heads, bf16) goes to LDS; wave w then
-//    accumulates O^T for channels 128w .. 128w+127 of the 16 heads over all
-//    64 rows (V^T through the LDS transpose read);
-//  * the running maximum is raised lazily (by more than 2^8 only); every
-//    wave takes the same decision from the same shared maxima, so no rescale
-//    factors are exchanged;
-//  * a single row slice ends like attend_mfma (sink folded once, rotation at
-//    -t, bf16 rows staged through LDS); several slices write float32
-//    partials (O, m, l) in the layout attend_merge reads.
+//  * inside a block each wave owns whole 16-row groups of the row list
+//    (groups w, w + 4, w + 8, ...): it gathers them into its own two LDS
+//    buffers by LDS-DMA (one group in flight while the other is scored),
+//    scores them (S^T = K Q^T, 16 x 16 x 32 MFMA, queries as the B operand),
+//    keeps its own running maximum and sum per head, and accumulates
+//    O^T += V^T P^T over all 512 channels (16 x 16 x 16 MFMA: the P^T
+//    operand is exactly the lanes' own softmax values, V^T comes from the
+//    same LDS rows through the transpose read).  No wave waits for another
+//    inside the loop: the rate of a CU's row gathers (not the MFMA work)
+//    bounds the kernel, and a gather issue that stalls holds up only the
+//    wave issuing it.
+//  * the four waves' (m, l, O) are merged once at the end through LDS; one
+//    row slice ends with the sink folded once, rotation at -t and bf16 rows;
+//    several slices write float32 partials (O, m, l) in attend_merge's
+//    layout.
+//  * the running maximum is raised lazily (by more than 2^8 only).
 #include "csa_device.h"
 #include "csa_internal.h"
 #include "attend_common.h"
 
 namespace csa {
 
-constexpr int kDPRow = 2 * 32 + 8;    // LDS row of P^T per head: 2 x 32 row slots + pad
+constexpr int kGR = 16;  // rows per wave group
+
+// LDS reads of the DMA-filled group buffers, out of the compiler's sight: a
+// compiler-visible LDS load there would first wait for every LDS-DMA in
+// flight (the compiler cannot tell the buffer read from the one being
+// filled).  Each block waits for its own data before returning.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// four 16-byte reads at a[j] + OFF
+template <int OFF>
+__device__ __forceinline__ void lds_rd4x128(const uint32_t (&a)[4], uint4 (&o)[4]) {
+  u32x4 x0, x1, x2, x3;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(OFF)
+      : "memory");
+  o[0] = __builtin_bit_cast(uint4, x0);
+  o[1] = __builtin_bit_cast(uint4, x1);
+  o[2] = __builtin_bit_cast(uint4, x2);
+  o[3] = __builtin_bit_cast(uint4, x3);
+}
+// eight transposed 8-byte reads (ds_read_b64_tr_b16) at a[j] + OFF
+template <int OFF>
+__device__ __forceinline__ void lds_rdtr8(const uint32_t (&a)[8], uint2 (&o)[8]) {
+  u32x2 x[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "n"(OFF)
+      : "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = make_uint2(x[j][0], x[j][1]);
+}
+
+typedef short bf16x4_s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16k16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_s, a),
+                                                  __builtin_bit_cast(bf16x4_s, b), c, 0, 0, 0);
+}
 
 template <int R>
 __global__ void __launch_bounds__(256, 1) attend_decode(
@@ -41,14 +96,13 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     const float* __restrict__ sinks, bf16_t* __restrict__ out, float* __restrict__ part,
     Seqs sq, int tokens, int W, int m, Rope base, float scale, int nsplit, int csa) {
   static_assert(R % 16 == 0 && R <= kMaxRope, "rope channels: multiple of 16, <= 128");
-  __shared__ __attribute__((aligned(1024))) bf16_t kb0[kDCh * kAD];
-  __shared__ __attribute__((aligned(1024))) bf16_t kb1[kDCh * kAD];
+  // per wave two 16-row group buffers (8 named arrays so the compiler can
+  // tell the DMA target from the buffer being read); after the loop the
+  // same 128 KB hold the waves' O for the merge
+  __shared__ __attribute__((aligned(1024))) bf16_t gb[8][kGR * kAD];
   __shared__ __attribute__((aligned(16))) int32_t rid[kDMaxRows];
-  __shared__ uint32_t vmask[kDMaxRows / 32 + 2];
   __shared__ double2 cs[kMaxRope / 2];
-  __shared__ __attribute__((aligned(16))) bf16_t ps[16 * kDPRow];
-  __shared__ float cmx[4][16];   // each wave's chunk maximum per head
-  __shared__ float lsum[4][16];  // each wave's running sum per head
+  __shared__ float wm[4][16], wl[4][16];  // each wave's running maximum and sum per head
 
   // block -> (token, head group, row slice); a token's blocks share id mod 8
   const int G = 4 * nsplit;
@@ -58,7 +112,8 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   const int jg = (id >> 3) % G;
   const int hg = jg & 3, sp = jg >> 2;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = tq / sq.n, i = tq % sq.n;
   if (i >= sq.len(b)) return;  // padding slot (block-uniform, before any barrier)
   const int64_t t = sq.pos0[b] + i;
@@ -74,253 +129,255 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   const int cps = (nch + nsplit - 1) / nsplit;
   const int c0 = min(nch, sp * cps), c1 = min(nch, c0 + cps);
   const int r0 = c0 * kDCh, r1 = min(nrows, c1 * kDCh);
+  const int nr = r1 - r0;                   // rows of this block
+  const int ngr = (nr + kGR - 1) / kGR;     // 16-row groups (whole kDCh chunks: <= kDMaxRows)
   const int32_t* idx_row = csa ? idx + tok * k : nullptr;
   const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
-  for (int j = tid; j < r1 - r0; j += 256)
-    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq);
+  for (int j = tid; j < ngr * kGR; j += 256)
+    rid[j] = j < nr ? row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq) : -1;
   for (int j = tid; j < R / 2; j += 256) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
   __syncthreads();
-  // bits of vmask[2 (c - c0)], [2 (c - c0) + 1]: rows of chunk c that take part
-  for (int j0 = 64 * wv; j0 < r1 - r0; j0 += 256) {
-    const bool ok = j0 + lane < r1 - r0 && rid[j0 + lane] != -1;
-    const unsigned long long bal = __ballot(ok);
-    if (lane == 0) {
-      vmask[j0 >> 5] = (uint32_t)bal;
-      vmask[(j0 >> 5) + 1] = (uint32_t)(bal >> 32);
-    }
-  }
-  __syncthreads();
 
-  // gather of chunk c into dst: this wave moves rows 16 wv .. 16 wv + 15 (one
-  // 1 KB row per DMA instruction).  The row ids are read in one go; the lane
-  // id is copied opaquely and the wave index made scalar so that nothing
-  // here is spilled (a scratch reload would wait on every DMA in flight).
-  struct Gather {
-    int ids[16];
-    int ln, wvs, c;
-    bf16_t* dst;
-  };
-  auto gather_prep = [&](Gather& Gt, int c, bf16_t* dst) {
-    asm volatile("v_mov_b32 %0, %1" : "=v"(Gt.ln) : "v"(lane));
-    Gt.wvs = __builtin_amdgcn_readfirstlane(wv);
-    Gt.c = c;
-    Gt.dst = dst;
-    const int base_r = (c - c0) * kDCh + 16 * Gt.wvs;
+  // DMA of group gi into buffer dst: 16 rows of 1 KB, one per instruction;
+  // 16-byte chunk c of row e lands at slot c ^ swz(e).  Masked rows load the
+  // token's own window row (finite; its weight is zero).  The lane id is
+  // copied opaquely so that the per-lane offset is not hoisted and spilled
+  // (a scratch reload would wait on every DMA in flight).
+  auto issue = [&](int gi, bf16_t* dst) {
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int4* rp = (const int4*)&rid[gi * kGR];
+    int ids[kGR];
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const int4 v = *(const int4*)&rid[base_r + e];
-      Gt.ids[e] = v.x;
-      Gt.ids[e + 1] = v.y;
-      Gt.ids[e + 2] = v.z;
-      Gt.ids[e + 3] = v.w;
+    for (int e = 0; e < kGR; e += 4) {
+      const int4 v = rp[e >> 2];
+      ids[e] = v.x;
+      ids[e + 1] = v.y;
+      ids[e + 2] = v.z;
+      ids[e + 3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < kGR; ++e) {
+      const int rw = ids[e] == -1 ? self_id : ids[e];
+      const bf16_t* src = rw >= 0 ? win + (int64_t)rw * kAD : pool + (int64_t)(-2 - rw) * kAD;
+      __builtin_amdgcn_global_load_lds((const void*)(src + 8 * (ln ^ swz(e))),
+                                       (lds_void*)(dst + e * kAD), 16, 0, 0);
     }
   };
-  auto gather_row = [&](const Gather& Gt, int e) {
-    const int rr = 16 * Gt.wvs + e;
-    const int jr = Gt.c * kDCh + rr;
-    int rw = jr < r1 ? Gt.ids[e] : -1;
-    if (rw == -1) rw = self_id;  // masked in the softmax; any finite row will do
-    const bf16_t* src = rw >= 0 ? win + (int64_t)rw * kAD : pool + (int64_t)(-2 - rw) * kAD;
-    src += 8 * (Gt.ln ^ swz(rr));
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(Gt.dst + rr * kAD), 16, 0, 0);
-  };
-  if (c0 < c1) {
-    Gather Gt;
-    gather_prep(Gt, c0, kb0);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) gather_row(Gt, e);
-  }
 
   // the 16 heads' rotated queries: head 16 hg + r16, channels 32 kk + 8 g ..
   uint4 Qf[16];
   load_qfrag<R>(q + (tok * kAH + 16 * hg + r16) * kAD, cs, g, Qf);
 
-  // O^T of the wave's channel slice: channel 128 wv + 16 dt + 4 g + e, head r16
-  f32x4 O[8];
+  // O^T of all 512 channels for the wave's rows: channel 16 d + 4 g + e, head r16
+  f32x4 O[32];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;  // head r16: shared maximum, this wave's rows' sum
+  for (int d = 0; d < 32; ++d) O[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // head r16 (l: this lane's rows)
   const float sl2 = scale * kLog2e;
 
-  // per-lane LDS byte offsets (see attend_mfma): K fragment of row
-  // 16 wv + r16, chunk 4 kk + g at kb_v[kk & 3] + (kk >> 2) 256 + 16 wv KB;
-  // transpose read for channel tile dt of the wave's slice and row step ks at
-  // tr_v[dt] + 32 ks KB (+16 KB for the upper 16 rows of the step)
-  int kb_v[4], tr_v[8];
+  // per-lane LDS byte offsets inside a group buffer.  K fragment kk (row
+  // r16, chunk 4 kk + g) sits at kofs[kk & 3] + 256 (kk >> 2).  The V^T
+  // fragment of channel tile d (rows 4 g + r16 / 4, channels 16 d + 4 (r16 & 3)
+  // .. + 3, 8 bytes) sits at tofs[d & 7] + 256 (d >> 3): chunk 2 d + (r16 & 3) / 2
+  // at slot chunk ^ swz(row), and the swizzle only moves the low four bits.
+  uint32_t kofs[4], tofs[8];
+  const int trow = 4 * g + (r16 >> 2), tsel = (r16 & 3) >> 1;
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    kb_v[v] = 16 * wv * 1024 + r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
-  {
-    const int trA = 4 * g + (r16 >> 2);
-    const int trc = (r16 & 3) >> 1, trh = (r16 & 1) * 8;
+  for (int v = 0; v < 4; ++v) kofs[v] = r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
-      tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh + 256 * wv;
-  }
+  for (int d = 0; d < 8; ++d)
+    tofs[d] = trow * 1024 + (((2 * d + tsel) ^ swz(trow)) << 4) + (r16 & 1) * 8;
 
-  auto chunk = [&](int c, const bf16_t* cur, int cn, bf16_t* nxt) {
-    const char* kbp = (const char*)cur;
-    Gather Gt;
-    const bool gat = cn < c1;
-    if (gat) gather_prep(Gt, cn, nxt);
-    // ---- S^T = K Q^T: the wave's 16 rows x 16 heads
-    f32x4 S = (f32x4){0.f, 0.f, 0.f, 0.f};
-    auto kfrag = [&](int kk) {
-      return *(const uint4*)(kbp + kb_v[kk & 3] + (kk >> 2) * 256);
-    };
-    uint4 kf[2];
-    kf[0] = kfrag(0);
-    kf[1] = kfrag(1);
-    __builtin_amdgcn_sched_barrier(0);
+  auto group = [&](int gi, const bf16_t* buf) {
+    const uint32_t kb = lds_addr(buf);
+    uint32_t ka[4], ta[8];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      S = mfma16(kf[kk & 1], Qf[kk], S);
-      if (kk + 2 < 16) kf[kk & 1] = kfrag(kk + 2);
-      if (gat) gather_row(Gt, kk);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // ---- softmax (log2 domain); lane (g, r16): rows 16 wv + 4 g + ii, head r16
-    const int cl = c - c0;
-    const uint32_t vm = vmask[2 * cl + (wv >> 1)] >> (16 * (wv & 1) + 4 * g);
+    for (int v = 0; v < 4; ++v) ka[v] = kb + kofs[v];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ta[d] = kb + tofs[d];
+    // ---- S^T = K Q^T: the group's 16 rows x 16 heads, two accumulation chains
+    f32x4 Sa = (f32x4){0.f, 0.f, 0.f, 0.f}, Sb = Sa;
+    uint4 kf[4];
+    lds_rd4x128<0>(ka, kf);
+    Sa = mfma16(kf[0], Qf[0], Sa);
+    Sb = mfma16(kf[1], Qf[1], Sb);
+    Sa = mfma16(kf[2], Qf[2], Sa);
+    Sb = mfma16(kf[3], Qf[3], Sb);
+    lds_rd4x128<256>(ka, kf);
+    Sa = mfma16(kf[0], Qf[4], Sa);
+    Sb = mfma16(kf[1], Qf[5], Sb);
+    Sa = mfma16(kf[2], Qf[6], Sa);
+    Sb = mfma16(kf[3], Qf[7], Sb);
+    lds_rd4x128<512>(ka, kf);
+    Sa = mfma16(kf[0], Qf[8], Sa);
+    Sb = mfma16(kf[1], Qf[9], Sb);
+    Sa = mfma16(kf[2], Qf[10], Sa);
+    Sb = mfma16(kf[3], Qf[11], Sb);
+    lds_rd4x128<768>(ka, kf);
+    Sa = mfma16(kf[0], Qf[12], Sa);
+    Sb = mfma16(kf[1], Qf[13], Sb);
+    Sa = mfma16(kf[2], Qf[14], Sa);
+    Sb = mfma16(kf[3], Qf[15], Sb);
+    // ---- softmax (log2 domain): lane (g, r16) holds rows 4 g .. 4 g + 3, head r16
+    const int4 vr = *(const int4*)&rid[gi * kGR + 4 * g];
+    const int vids[4] = {vr.x, vr.y, vr.z, vr.w};
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      sv[ii] = (vm >> ii) & 1u ? S[ii] * sl2 : -INFINITY;
-      mx = fmaxf(mx, sv[ii]);
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = vids[e] != -1 ? (Sa[e] + Sb[e]) * sl2 : -INFINITY;
+      mx = fmaxf(mx, sv[e]);
     }
-    mx = xmax32(xmax16(mx));
-    if (g == 0) cmx[wv][r16] = mx;
-    __syncthreads();
-    const float cmax = fmaxf(fmaxf(cmx[0][r16], cmx[1][r16]), fmaxf(cmx[2][r16], cmx[3][r16]));
-    if (__any(cmax > m_run + kLazy)) {  // the same decision in every wave
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    mx = xmax32(xmax16(mx));  // over the group's 16 rows
+    if (mx > m_run + kLazy) {  // per head (lane-wise): rescale this lane's O
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-      m_run = m_new;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+      for (int d = 0; d < 32; ++d) O[d] *= alpha;
+      m_run = m_new;
     }
     float p[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      // exp2(-inf) = 0 for masked rows; m_run is finite once a row was seen
-      p[ii] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[ii] - m_run);
-      l_run += p[ii];
+    for (int e = 0; e < 4; ++e) {
+      p[e] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_run);
+      l_run += p[e];
     }
-    // P^T slots of row step ks = wv / 2: lane group g' holds rows 4 g' ..
-    // 4 g' + 3 of wave 2 ks (slots 8 g' .. +3) and of wave 2 ks + 1 (+4 ..)
-    *(uint2*)&ps[r16 * kDPRow + (wv >> 1) * 32 + 8 * g + 4 * (wv & 1)] =
-        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    __syncthreads();
-    // ---- O^T += V^T P^T over the wave's channel slice, all 64 rows
-    uint4 Pf[2];
+    // P^T operand of the 16 x 16 x 16 MFMA: rows 4 g .. 4 g + 3 of head r16
+    const uint2 pf = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    // ---- O^T += V^T P^T over the 32 channel tiles (8 transposed reads at a time)
+    uint2 vf[8];
+    lds_rdtr8<0>(ta, vf);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Pf[ks] = *(const uint4*)&ps[r16 * kDPRow + ks * 32 + 8 * g];
-    auto vfrag = [&](int dt, int ks) {
-      const char* pa = kbp + tr_v[dt] + ks * 32768;
-      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)pa);
-      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 16384));
-      return make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
-                        (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
-                        (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
-                        (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
-    };
-    uint4 vf[2];
-    vf[0] = vfrag(0, 0);
-    vf[1] = vfrag(0, 1);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int d = 0; d < 8; ++d) O[d] = mfma16k16(vf[d], pf, O[d]);
+    lds_rdtr8<256>(ta, vf);
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {  // step st: channel tile st / 2, row step st % 2
-      const uint4 a = vf[st & 1];
-      if (st + 2 < 16) vf[st & 1] = vfrag((st + 2) >> 1, st & 1);
-      O[st >> 1] = mfma16(a, Pf[st & 1], O[st >> 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int d = 0; d < 8; ++d) O[8 + d] = mfma16k16(vf[d], pf, O[8 + d]);
+    lds_rdtr8<512>(ta, vf);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) O[16 + d] = mfma16k16(vf[d], pf, O[16 + d]);
+    lds_rdtr8<768>(ta, vf);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) O[24 + d] = mfma16k16(vf[d], pf, O[24 + d]);
   };
-  for (int c = c0; c < c1; c += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    chunk(c, kb0, c + 1, kb1);
-    if (c + 1 < c1) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      chunk(c + 1, kb1, c + 2, kb0);
+
+  // groups wv, wv + 4, ...; buffer gb[2 wv + (j & 1)] for the wave's j-th
+  // group.  Before scoring group j the wave's DMA of it has landed (at most
+  // the 16 instructions of group j + 1 still in flight); after scoring, the
+  // buffer is refilled with group j + 2.
+  const int nmine = ngr > wv ? (ngr - wv + 3) / 4 : 0;  // wave-uniform
+  bf16_t* B0 = gb[2 * wv];
+  bf16_t* B1 = gb[2 * wv + 1];
+  if (nmine > 0) issue(wv, B0);
+  if (nmine > 1) issue(wv + 4, B1);
+  for (int j = 0; j < nmine; j += 2) {
+    if (j + 1 < nmine) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    group(wv + 4 * j, B0);
+    if (j + 2 < nmine) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this buffer's reads are done
+      issue(wv + 4 * (j + 2), B0);
+    }
+    if (j + 1 < nmine) {
+      if (j + 2 < nmine) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      group(wv + 4 * (j + 1), B1);
+      if (j + 3 < nmine) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(wv + 4 * (j + 3), B1);
+      }
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA outlives the loop
 
-  l_run = xsum32(xsum16(l_run));
-  if (g == 0) lsum[wv][r16] = l_run;
-  __syncthreads();  // every wave is done with the chunk buffers; sums published
-  const float lb = (lsum[0][r16] + lsum[1][r16]) + (lsum[2][r16] + lsum[3][r16]);
-  const int head = 16 * hg + r16;
+  // ---- merge of the four waves: M = max_w m_w, L = sum_w l_w 2^(m_w - M),
+  // O = sum_w O_w 2^(m_w - M), through LDS (the group buffers, 128 KB:
+  // wave w's O at [w][head][512] floats, 16-byte chunk c of head row h at
+  // slot c ^ h)
+  l_run = xsum32(xsum16(l_run));  // over the lanes holding head r16's rows
+  if (g == 0) {
+    wm[wv][r16] = m_run;
+    wl[wv][r16] = l_run;
+  }
+  __syncthreads();  // every wave is done with the group buffers; maxima published
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][r16]);
+  const float fw = M == -INFINITY || m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  float* ob = (float*)&gb[0][0];
+  {
+    float* mine = ob + wv * (16 * kAD) + r16 * kAD;
+#pragma unroll
+    for (int d = 0; d < 32; ++d)
+      *(f32x4*)(mine + (((4 * d + g) ^ r16) << 2)) = O[d] * fw;
+  }
+  __syncthreads();
+  // wave wv writes channels 128 wv .. 128 wv + 127 of the 16 heads: lane l
+  // takes head h = l / 4 and channels 128 wv + 32 (l & 3) .. + 31
+  const int h = lane >> 2;
+  float Mh = -INFINITY, Lh = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, wm[w][h]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (wm[w][h] != -INFINITY) Lh += wl[w][h] * __builtin_amdgcn_exp2f(wm[w][h] - Mh);
+  const int ch0 = 128 * wv + 32 * (lane & 3);
+  float o[32];
+#pragma unroll
+  for (int c = 0; c < 32; c += 4) {
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += *(const f32x4*)(ob + w * (16 * kAD) + h * kAD + ((((ch0 + c) >> 2) ^ h) << 2));
+    o[c] = acc[0];
+    o[c + 1] = acc[1];
+    o[c + 2] = acc[2];
+    o[c + 3] = acc[3];
+  }
+  const int head = 16 * hg + h;
   constexpr int first = kAD - R;
   if (nsplit == 1) {
-    // 16 bf16 rows staged in kb0, 16-byte chunk c of head row h at slot c ^ h
     const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
-    const float M = fmaxf(m_run, sink);
-    const float f = __builtin_amdgcn_exp2f(m_run - M);
-    const float lt = lb * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
+    const float Mt = fmaxf(Mh, sink);
+    const float f = Mh == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mh - Mt);
+    const float lt = Lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - Mt) : 0.f);
     const float inv = f / lt;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 128 * wv + 16 * dt + 4 * g;
-      float o0 = O[dt][0] * inv, o1 = O[dt][1] * inv, o2 = O[dt][2] * inv, o3 = O[dt][3] * inv;
-      if (d >= first) {  // pair (d, d+1) rotated at -t
-        const double2 ca = cs[(d - first) >> 1];
-        const float cf = (float)ca.x, sf = (float)ca.y;
-        const float a0 = o0 * cf + o1 * sf, a1 = o1 * cf - o0 * sf;
-        o0 = a0;
-        o1 = a1;
-      }
-      if (d + 2 >= first) {  // pair (d+2, d+3)
-        const double2 cb = cs[(d + 2 - first) >> 1];
-        const float cf = (float)cb.x, sf = (float)cb.y;
-        const float b0 = o2 * cf + o3 * sf, b1 = o3 * cf - o2 * sf;
-        o2 = b0;
-        o3 = b1;
-      }
-      char* rowb = (char*)kb0 + r16 * 1024;
-      *(uint2*)(rowb + (((d >> 3) ^ r16) << 4) + ((d & 7) << 1)) =
-          make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-    }
-    __syncthreads();
-    bf16_t* orow = out + (tok * kAH + 16 * hg) * kAD;
+    for (int c = 0; c < 32; ++c) o[c] *= inv;
+    if (ch0 + 32 > first) {
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const int h = 4 * wv + hh;
-      const uint4 v = *(const uint4*)((const char*)kb0 + h * 1024 + ((lane ^ h) << 4));
-      *(uint4*)(orow + h * kAD + 8 * lane) = v;
+      for (int c = 0; c < 32; c += 2) {
+        const int d = ch0 + c;
+        if (d >= first) {  // pair (d, d+1) rotated at -t
+          const double2 ca = cs[(d - first) >> 1];
+          const float cf = (float)ca.x, sf = (float)ca.y;
+          const float a0 = o[c] * cf + o[c + 1] * sf, a1 = o[c + 1] * cf - o[c] * sf;
+          o[c] = a0;
+          o[c + 1] = a1;
+        }
+      }
     }
+    bf16_t* orow = out + (tok * kAH + head) * kAD + ch0;
+#pragma unroll
+    for (int c = 0; c < 32; c += 8)
+      *(uint4*)(orow + c) = make_uint4(pack_bf16x2(o[c], o[c + 1]), pack_bf16x2(o[c + 2], o[c + 3]),
+                                       pack_bf16x2(o[c + 4], o[c + 5]),
+                                       pack_bf16x2(o[c + 6], o[c + 7]));
   } else {
-    // float32 partial rows staged in kb0 (2 KB per head, 16-byte chunk c of
-    // head row h at slot c ^ h), then written whole
-    float* pbase = part + ((slot * nsplit + sp) * kAH + 16 * hg) * kPart;
+    // float32 partial row of head `head`: O (relative to M), then m = M, l = L
+    float* prow = part + ((slot * nsplit + sp) * kAH + head) * kPart;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int ch = 32 * wv + 4 * dt + g;  // 16-byte chunk of the 512-float row
-      *(f32x4*)((char*)kb0 + r16 * 2048 + ((ch ^ r16) << 4)) = O[dt];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const int h = 4 * wv + hh;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int ch = lane + 64 * it;
-        *(f32x4*)(pbase + h * kPart + 4 * ch) =
-            *(const f32x4*)((const char*)kb0 + h * 2048 + ((ch ^ h) << 4));
-      }
-    }
-    if (wv == 0 && g == 0) {
-      float* prow = pbase + r16 * kPart;
-      prow[kAD] = m_run;
-      prow[kAD + 1] = lb;
+    for (int c = 0; c < 32; c += 4)
+      *(f32x4*)(prow + ch0 + c) = (f32x4){o[c], o[c + 1], o[c + 2], o[c + 3]};
+    if (wv == 0 && (lane & 3) == 0) {
+      prow[kAD] = Mh;
+      prow[kAD + 1] = Lh;
     }
   }
 }
