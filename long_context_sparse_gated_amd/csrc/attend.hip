@@ -128,8 +128,45 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   const int32_t* idx_row = csa ? idx + tok * k : nullptr;
   const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
-  for (int j = tid; j < r1 - r0; j += NTH)
-    rid[j] = row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq);
+  // the wave's query fragments (head 16*wv + r16, channels 32*kk + 8*g +
+  // 0..7) start loading now; they are rotated once the rope table is in LDS
+  constexpr int first = kAD - R;
+  uint4 Qf[16];
+  {
+    const bf16_t* qrow = q + (tok * kAH + 16 * wv + r16) * kAD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) Qf[kk] = *(const uint4*)(qrow + 32 * kk);
+  }
+  // row ids: every selected index of the thread's rows is loaded first (one
+  // memory latency, not one per row); window row j is ring slot
+  // (lo + j) mod cap, and j < nwin <= cap (the ring holds the window or the
+  // whole sequence) leaves one wrap at most
+  {
+    constexpr int U = kMaxRows / NTH;
+    int32_t sel[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = r0 + tid + NTH * u - nwin;
+      sel[u] = (csa && tid + NTH * u < r1 - r0 && e >= 0) ? idx_row[e] : 0;
+    }
+    const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = tid + NTH * u;
+      if (j < r1 - r0) {
+        const int jr = r0 + j;
+        int id;
+        if (jr < nwin) {
+          const int v = lo_mod + jr;
+          id = wb + (v >= cap ? v - cap : v);
+        } else {
+          const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
+          id = (w < 0 || w >= nvis) ? -1 : (int)(-2 - sq.prow(b, w, pool_cap));
+        }
+        rid[j] = id;
+      }
+    }
+  }
   for (int j = tid; j < R / 2; j += NTH) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
@@ -191,11 +228,27 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   };
   if (c0 < c1) issue(c0, kbuf0);
 
-  // rotated query fragments of the wave's head group: head 16*wv + r16,
-  // channels 32*kk + 8*g + 0..7
-  constexpr int first = kAD - R;
-  uint4 Qf[16];
-  load_qfrag<R>(q + (tok * kAH + 16 * wv + r16) * kAD, cs, g, Qf);
+  // the rope channels of the query fragments rotated at t in float64 and
+  // rounded to bf16 once
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int d0 = 32 * kk + 8 * g;
+    if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
+      uint32_t w4[4] = {Qf[kk].x, Qf[kk].y, Qf[kk].z, Qf[kk].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int d = d0 + 2 * p;
+        if (d >= first) {
+          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
+          double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+          const double2 c = cs[(d - first) >> 1];
+          rot64(a, bb, c.x, c.y);
+          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+        }
+      }
+      Qf[kk] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
 
 #if CSA_ATTN_PV32
   // O^T tiles of the wave's channel slice (channel tile ct, head tile hh):

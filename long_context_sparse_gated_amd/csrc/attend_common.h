@@ -1,6 +1,6 @@
 // Shared pieces of the attention kernels (H = 64, D = 512, bf16 fast paths):
-// MFMA and lane-swap wrappers, the row-id encoding of the row list, the LDS
-// chunk swizzle and the rotated query fragments.
+// MFMA and lane-swap wrappers, the row-id encoding of the row list and the LDS
+// chunk swizzle.
 #pragma once
 
 #include "csa_device.h"
@@ -161,37 +161,6 @@ __device__ __forceinline__ void lds_ld_8x128_2x32(const void* a, const void* b, 
   for (int j = 0; j < 4; ++j) {
     o[0][j] = __builtin_bit_cast(uint4, x[j]);
     o[1][j] = __builtin_bit_cast(uint4, x[4 + j]);
-  }
-}
-
-// Query fragments of head row `qrow` (512 channels) for a 16 x 16 x 32 MFMA B
-// operand: fragment kk holds channels 32 kk + 8 g .. +7; the last R channels
-// are rotated at the query's position (cs[j] = (cos, sin) of pair j) in
-// float64 and rounded to bf16 once.
-template <int R>
-__device__ __forceinline__ void load_qfrag(const bf16_t* __restrict__ qrow, const double2* cs,
-                                           int g, uint4 (&Qf)[16]) {
-  constexpr int first = kAD - R;
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk) {
-    const int d0 = 32 * kk + 8 * g;
-    uint4 v = *(const uint4*)(qrow + d0);
-    if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
-      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int d = d0 + 2 * p;
-        if (d >= first) {
-          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
-          double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
-          const double2 c = cs[(d - first) >> 1];
-          rot64(a, bb, c.x, c.y);
-          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
-        }
-      }
-      v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-    Qf[kk] = v;
   }
 }
 

@@ -134,8 +134,46 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   const int32_t* idx_row = csa ? idx + tok * k : nullptr;
   const int self_id = (int)((int64_t)b * win_cap + t % win_cap);  // always a valid row
 
-  for (int j = tid; j < ngr * kGR; j += 256)
-    rid[j] = j < nr ? row_id(r0 + j, nwin, lo, win_cap, b, pool_cap, idx_row, csa, nvis, sq) : -1;
+  // the 16 heads' query fragments (head 16 hg + r16, channels 32 kk + 8 g ..)
+  // start loading now; they are rotated once the rope table is in LDS
+  constexpr int first = kAD - R;
+  uint4 Qf[16];
+  {
+    const bf16_t* qrow = q + (tok * kAH + 16 * hg + r16) * kAD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) Qf[kk] = *(const uint4*)(qrow + 32 * kk);
+  }
+  // row ids: every selected index of the thread's rows is loaded first (one
+  // memory latency, not one per row); window row j is ring slot
+  // (lo + j) mod cap, and j < nwin <= cap (the ring holds the window or the
+  // whole sequence) leaves one wrap at most
+  {
+    constexpr int U = kDMaxRows / 256;
+    int32_t sel[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = r0 + tid + 256 * u - nwin;
+      sel[u] = (csa && tid + 256 * u < nr && e >= 0) ? idx_row[e] : 0;
+    }
+    const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = tid + 256 * u;
+      if (j < ngr * kGR) {
+        const int jr = r0 + j;
+        int id = -1;
+        if (j >= nr) {
+        } else if (jr < nwin) {
+          const int v = lo_mod + jr;
+          id = wb + (v >= cap ? v - cap : v);
+        } else {
+          const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
+          if (w >= 0 && w < nvis) id = (int)(-2 - sq.prow(b, w, pool_cap));
+        }
+        rid[j] = id;
+      }
+    }
+  }
   for (int j = tid; j < R / 2; j += 256) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
@@ -170,9 +208,27 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     }
   };
 
-  // the 16 heads' rotated queries: head 16 hg + r16, channels 32 kk + 8 g ..
-  uint4 Qf[16];
-  load_qfrag<R>(q + (tok * kAH + 16 * hg + r16) * kAD, cs, g, Qf);
+  // the rope channels of the query fragments rotated at t in float64 and
+  // rounded to bf16 once
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int d0 = 32 * kk + 8 * g;
+    if (32 * kk + 32 > first && d0 + 8 > first) {  // first test is compile time
+      uint32_t w4[4] = {Qf[kk].x, Qf[kk].y, Qf[kk].z, Qf[kk].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int d = d0 + 2 * p;
+        if (d >= first) {
+          double a = bf16_to_f32((bf16_t)(w4[p] & 0xffffu));
+          double bb = bf16_to_f32((bf16_t)(w4[p] >> 16));
+          const double2 c = cs[(d - first) >> 1];
+          rot64(a, bb, c.x, c.y);
+          w4[p] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(bb) << 16);
+        }
+      }
+      Qf[kk] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
 
   // O^T of all 512 channels for the wave's rows: channel 16 d + 4 g + e, head r16
   f32x4 O[32];
@@ -341,7 +397,6 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     o[c + 3] = acc[3];
   }
   const int head = 16 * hg + h;
-  constexpr int first = kAD - R;
   if (nsplit == 1) {
     const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
     const float Mt = fmaxf(Mh, sink);
