@@ -206,6 +206,29 @@ csa_status csa_compress(const csa_layer* layer, const csa_batch* batch,
                         float norm_eps, void* state_kv, void* state_gate,
                         void* pool, int64_t pool_cap, hipStream_t stream);
 
+/* All of a layer call's cache updates in one call: csa_window_append of kv
+ * into ring, then (compress_ratio > 0) csa_compress of the main stream
+ * (width head_dim, rope_dim qk_rope_head_dim, ckv / cgate / norm_weight,
+ * state_kv / state_gate / pool) and (index_topk > 0) of the indexer's key
+ * stream (width index_head_dim, rope_dim index_rope_dim, ikv / igate /
+ * inorm_weight, istate_kv / istate_gate / ipool); both pools share pool_cap
+ * and the batch's block table.  Arguments, layouts and results are those of
+ * the separate calls, bit for bit; pointers of a stream the layer does not
+ * have are ignored (may be NULL).  With n_new == 1 (a decode step) the three
+ * updates run as one launch, one block per (sequence, stream): a decode
+ * step is a chain of small launches, each costing a few microseconds of
+ * launch latency.  With n_new > 1 the separate kernels run in order.
+ * Source: model page, "Cache layers" (the window, the compressor buffer /
+ * pool / counter / overlap state, the indexer's own buffer and pool, one
+ * cache update per call) and sec. 2.3. */
+csa_status csa_cache_update(const csa_layer* layer, const csa_batch* batch,
+                            const void* kv, void* ring, int64_t win_cap,
+                            const void* ckv, const void* cgate, const float* norm_weight,
+                            void* state_kv, void* state_gate, void* pool,
+                            const void* ikv, const void* igate, const float* inorm_weight,
+                            void* istate_kv, void* istate_gate, void* ipool,
+                            int64_t pool_cap, float norm_eps, hipStream_t stream);
+
 /* Lightning Indexer and per-query top-k (CSA layers).
  *  q_idx    [B, n_new, H_I, D_I] dtype: indexer queries, un-rotated (rotated
  *           here at t on their last R_I channels, stored at dtype).

@@ -23,7 +23,7 @@ __all__ = [
     "csa_index_topk", "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
     "CSA_OP_INDEX_TOPK", "CSA_OP_ATTEND", "CSA_OP_HCA_ATTEND", "EXPORTED_SYMBOLS",
     "csa_output_projection", "csa_project", "csa_index_topk_noalloc",
-    "CSA_NOALLOC_SCRATCH_BYTES", "Paged",
+    "CSA_NOALLOC_SCRATCH_BYTES", "Paged", "csa_cache_update",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,8 @@ CSA_NOALLOC_SCRATCH_BYTES = 32 << 20    # CSA_NOALLOC_SCRATCH_BYTES of csa.h
 EXPORTED_SYMBOLS = ("csa_window_append", "csa_rope", "csa_compress", "csa_index_topk",
                     "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_status_str",
                     "csa_version", "csa_output_projection", "csa_output_projection_workspace_bytes",
-                    "csa_project", "csa_project_workspace_bytes", "csa_index_topk_noalloc")
+                    "csa_project", "csa_project_workspace_bytes", "csa_index_topk_noalloc",
+                    "csa_cache_update")
 
 
 class _CLayer(ctypes.Structure):
@@ -141,6 +142,8 @@ def load_library():
         "csa_window_append": [LP, BP, P, P, I64, P],
         "csa_rope": [LP, BP, P, I32, I32, I32, I32, P],
         "csa_compress": [LP, BP, I32, I32, P, P, P, ctypes.c_float, P, P, P, I64, P],
+        "csa_cache_update": [LP, BP, P, P, I64, P, P, P, P, P, P, P, P, P, P, P, P, I64,
+                             ctypes.c_float, P],
         "csa_index_topk": [LP, BP, P, P, P, I64, P, P, P, SZ, P],
         "csa_index_topk_noalloc": [LP, BP, P, P, P, I64, P, P, P],
         "csa_attend": [LP, BP, P, P, I64, P, I64, P, P, P, P, SZ, P],
@@ -318,6 +321,32 @@ def csa_compress(layer: Layer, pos0, pos0_max: int, kv, gate, state_kv, state_ga
         _ptr(gate, "gate", dt), _ptr(norm_weight, "norm_weight", torch.float32), norm_eps,
         _ptr(state_kv, "state_kv", dt), _ptr(state_gate, "state_gate", dt),
         _ptr(pool, "pool", dt), _pool_cap(pool, paged), _stream()), "csa_compress")
+
+
+def csa_cache_update(layer: Layer, pos0, pos0_max: int, kv, ring, ckv=None, cgate=None,
+                     state_kv=None, state_gate=None, pool=None, ikv=None, igate=None,
+                     istate_kv=None, istate_gate=None, ipool=None, norm_weight=None,
+                     inorm_weight=None, norm_eps: float = 1e-6, n_valid=None, cu_seqlens=None,
+                     n_new=None, paged: Optional[Paged] = None):
+    """The window append and the compressor(s) of one layer call in one call (one
+    launch for a decode step): as csa_window_append(kv, ring), then csa_compress of
+    (ckv, cgate) into (state_kv, state_gate, pool) and of (ikv, igate) into the
+    indexer's state and ipool, for the streams the layer has."""
+    torch = _torch()
+    dt = _store_dtype(layer)
+    B, n = _lead(kv, 1, cu_seqlens, n_new, pos0)
+    bt = _batch(pos0, pos0_max, B, n, n_valid, cu_seqlens, paged, pool)
+    lay = layer._c()
+    f32 = torch.float32
+    _check(load_library().csa_cache_update(
+        ctypes.byref(lay), ctypes.byref(bt), _ptr(kv, "kv", dt), _ptr(ring, "ring", dt),
+        ring.shape[1], _ptr(ckv, "ckv", dt), _ptr(cgate, "cgate", dt),
+        _ptr(norm_weight, "norm_weight", f32), _ptr(state_kv, "state_kv", dt),
+        _ptr(state_gate, "state_gate", dt), _ptr(pool, "pool", dt), _ptr(ikv, "ikv", dt),
+        _ptr(igate, "igate", dt), _ptr(inorm_weight, "inorm_weight", f32),
+        _ptr(istate_kv, "istate_kv", dt), _ptr(istate_gate, "istate_gate", dt),
+        _ptr(ipool, "ipool", dt), _pool_cap(pool, paged) if pool is not None else 0, norm_eps,
+        _stream()), "csa_cache_update")
 
 
 def csa_index_topk(layer: Layer, pos0, pos0_max: int, q_idx, weights, k_pool, topk_idx,

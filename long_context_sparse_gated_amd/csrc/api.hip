@@ -263,6 +263,46 @@ csa_status csa_compress(const csa_layer* layer, const csa_batch* batch, int32_t 
                                          state_kv, state_gate, pool, pool_cap, stream));
 }
 
+csa_status csa_cache_update(const csa_layer* layer, const csa_batch* batch, const void* kv,
+                            void* ring, int64_t win_cap, const void* ckv, const void* cgate,
+                            const float* norm_weight, void* state_kv, void* state_gate,
+                            void* pool, const void* ikv, const void* igate,
+                            const float* inorm_weight, void* istate_kv, void* istate_gate,
+                            void* ipool, int64_t pool_cap, float norm_eps, hipStream_t stream) {
+  Layer L;
+  Batch b;
+  int64_t prow = 0;
+  csa_status st = to_layer(layer, &L);
+  if (st != CSA_OK) return st;
+  if ((st = to_batch(batch, &b, &prow)) != CSA_OK) return st;
+  if (!kv || !ring) return CSA_ERR_NULL;
+  if ((st = window_ok(L, b, win_cap)) != CSA_OK) return st;
+  const bool main = L.m > 0, index = main && L.k > 0;
+  if (main) {
+    if (!ckv || !cgate || !state_kv || !state_gate || !pool) return CSA_ERR_NULL;
+    if (index && (!ikv || !igate || !istate_kv || !istate_gate || !ipool)) return CSA_ERR_NULL;
+    if (L.D > kMaxWidth || !(norm_eps >= 0.f)) return CSA_ERR_SHAPE;
+    if (index && (L.Di < 2 || (L.Di & 1) || L.Di > kMaxWidth || L.Ri < 0 || (L.Ri & 1) ||
+                  L.Ri > L.Di))
+      return CSA_ERR_SHAPE;
+    if (pool_cap < entries_needed(L, b)) return CSA_ERR_SHAPE;
+    if ((st = pool_ok(b, pool_cap, prow)) != CSA_OK) return st;
+  }
+  if (b.n == 1)
+    return hip_status(csa::launch_cache_update_one(
+        L, b, kv, ring, win_cap, ckv, cgate, norm_weight, state_kv, state_gate, pool, ikv, igate,
+        inorm_weight, istate_kv, istate_gate, ipool, pool_cap, norm_eps,
+        index ? 3 : (main ? 2 : 1), stream));
+  hipError_t e = csa::launch_window_append(L, b, kv, ring, win_cap, stream);
+  if (e == hipSuccess && main)
+    e = csa::launch_compress(L, b, L.D, L.R, ckv, cgate, norm_weight, norm_eps, state_kv,
+                             state_gate, pool, pool_cap, stream);
+  if (e == hipSuccess && index)
+    e = csa::launch_compress(L, b, L.Di, L.Ri, ikv, igate, inorm_weight, norm_eps, istate_kv,
+                             istate_gate, ipool, pool_cap, stream);
+  return hip_status(e);
+}
+
 csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch, const void* q_idx,
                           const void* weights, const void* k_pool, int64_t pool_cap,
                           int32_t* topk_idx, float* scores_out, void* workspace,

@@ -45,19 +45,8 @@
 namespace csa {
 
 constexpr int kPRow = kCH + 8;  // LDS row of P^T per head: 32 row slots + pad (bf16)
-// Software-pipeline depths of the LDS fragment reads (steps ahead).
-#ifndef CSA_ATTN_QD
-#define CSA_ATTN_QD 2
-#endif
-#ifndef CSA_ATTN_PD
-#define CSA_ATTN_PD 2
-#endif
-constexpr int kQD = CSA_ATTN_QD, kPD = CSA_ATTN_PD;
-// O^T += V^T P^T on 32 x 32 x 16 tiles (about twice the 16 x 16 x 32 rate
-// on gfx950) instead of 16 x 16 x 32 ones.
-#ifndef CSA_ATTN_PV32
-#define CSA_ATTN_PV32 1
-#endif
+// Software-pipeline depth of the K fragment reads (steps ahead).
+constexpr int kQD = 2;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma32x(uint4 a, uint4 b, f32x16 c) {
@@ -105,6 +94,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   __shared__ __attribute__((aligned(16))) bf16_t ps[kAH * kPRow];  // P^T, row slots per head
   __shared__ float alph[kAH];   // this chunk's rescale of O per head
   __shared__ float mlf[2][kAH];  // final running max and sum per head
+  __shared__ float sinkl[kAH];   // sink logits (log2 units), -inf without sinks
 
   constexpr int NTH = 256;
   constexpr int RPW = kCH / 4;  // rows each wave gathers per chunk
@@ -137,6 +127,8 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) Qf[kk] = *(const uint4*)(qrow + 32 * kk);
   }
+  // the sink logits (log2 units), used at the end, go to LDS now
+  if (tid < kAH) sinkl[tid] = sinks ? sinks[tid] * kLog2e : -INFINITY;
   // row ids: every selected index of the thread's rows is loaded first (one
   // memory latency, not one per row); window row j is ring slot
   // (lo + j) mod cap, and j < nwin <= cap (the ring holds the window or the
@@ -250,7 +242,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     }
   }
 
-#if CSA_ATTN_PV32
   // O^T tiles of the wave's channel slice (channel tile ct, head tile hh):
   // lane (l32, h32) holds channels 128*wv + 32*ct + 8*(v/4) + 4*h32 + v%4 of
   // head 32*hh + l32
@@ -262,15 +253,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int v = 0; v < 16; ++v) O[ct][hh][v] = 0.f;
-#else
-  // O^T accumulators of the wave's channel slice: channel 128*wv + 16*dt +
-  // 4*g + e, head 16*ht + r16
-  f32x4 O[8][4];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) O[dt][ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#endif
   float m_run = -INFINITY, l_run = 0.f;  // head 16*wv + r16
   const float sl2 = scale * kLog2e;
 
@@ -287,7 +269,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   int kb_v[4], tr_v[8];
 #pragma unroll
   for (int v = 0; v < 4; ++v) kb_v[v] = r16 * 1024 + (((4 * v + g) ^ swz(r16)) << 4);
-#if CSA_ATTN_PV32
   // 32 x 32 x 16 V^T fragment of channel tile ct, row step ks, half h2: the
   // address lane a = 4 j + q of 16-lane group (sub, h32) names row
   // 16 ks + 8 h32 + 4 h2 + j and channels 32 ct + 16 sub + 4 q .. +3 of the
@@ -304,15 +285,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
             r * 1024 + (((4 * ct + 2 * sub + (q4 >> 1)) ^ swz(r)) << 4) + (q4 & 1) * 8 + 256 * wv;
       }
   }
-#else
-  {
-    const int trA = 4 * g + (r16 >> 2);
-    const int trc = (r16 & 3) >> 1, trh = (r16 & 1) * 8;
-#pragma unroll
-    for (int v = 0; v < 8; ++v)
-      tr_v[v] = trA * 1024 + (((2 * v + trc) ^ swz(trA)) << 4) + trh + 256 * wv;
-  }
-#endif
 
   auto chunk = [&](int c, const bf16_t* cur, int cn, bf16_t* nxt) {
     const char* kb = (const char*)cur;
@@ -382,18 +354,13 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     // P^T slots of lane group g hold rows 4g..4g+3 and 16+4g..16+4g+3; the
     // next chunk's gather is in flight, so these LDS accesses and the
     // barrier go through lds_* (they must not wait for it)
-#if CSA_ATTN_PV32
     // rows in natural order: slots 4g..4g+3 and 16+4g..16+4g+3
     lds_st64(&ps[(16 * wv + r16) * kPRow + 4 * g], pk[0], pk[1]);
     lds_st64(&ps[(16 * wv + r16) * kPRow + 16 + 4 * g], pk[2], pk[3]);
-#else
-    lds_st128(&ps[(16 * wv + r16) * kPRow + 8 * g], make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#endif
     if (g == 0) lds_st32(&alph[16 * wv + r16], __float_as_uint(alpha));
     lds_barrier();
 
     // ---- O^T += V^T P^T over the wave's channel slice, all 64 heads
-#if CSA_ATTN_PV32
     // P^T fragment (head tile hh, row step ks): rows 16 ks + 8 h32 .. +7 of
     // head 32 hh + l32
     uint4 Pf[2][2];
@@ -434,46 +401,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-#else
-    uint4 Pf[4];
-    uint32_t a4u[4];
-    lds_ld_4x128_4x32<16 * kPRow * 2, 16 * 4>(&ps[r16 * kPRow + 8 * g], &alph[r16], Pf, a4u);
-    {
-      float a4[4];
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) a4[ht] = __uint_as_float(a4u[ht]);
-      // a head whose maximum was not raised has alpha exactly 1
-      if (__any(a4[0] != 1.f || a4[1] != 1.f || a4[2] != 1.f || a4[3] != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int ht = 0; ht < 4; ++ht) O[dt][ht] *= a4[ht];
-      }
-    }
-    // V^T fragments (two transpose reads each) kPD channel tiles ahead
-    auto vfrag = [&](int dt) {
-      const char* pa = kb + tr_v[dt];
-      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)pa);
-      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 16384));
-      return make_uint4((uint32_t)(uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
-                        (uint32_t)(uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
-                        (uint32_t)(uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
-                        (uint32_t)(uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16));
-    };
-    uint4 vf[kPD];
-#pragma unroll
-    for (int j = 0; j < kPD; ++j) vf[j] = vfrag(j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4 a = vf[dt % kPD];
-      if (dt + kPD < 8) vf[dt % kPD] = vfrag(dt + kPD);
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) O[dt][ht] = mfma16(a, Pf[ht], O[dt][ht]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-#endif
   for (int c = c0; c < c1; c += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this chunk's rows are in LDS
     lds_barrier();
@@ -495,25 +422,11 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   if (nsplit == 1) {
     // the whole [64 heads][512] bf16 output, chunks swizzled by head: heads
     // 0..31 in kbuf0, 32..63 in kbuf1
-#if !CSA_ATTN_PV32
-    float inv[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const int head = 16 * ht + r16;
-      const float mh = mlf[0][head], lh = mlf[1][head];
-      const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
-      const float M = fmaxf(mh, sink);
-      const float f = __builtin_amdgcn_exp2f(mh - M);
-      const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
-      inv[ht] = f / lt;
-    }
-#endif
-#if CSA_ATTN_PV32
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int head = 32 * hh + l32;
       const float mh = mlf[0][head], lh = mlf[1][head];
-      const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
+      const float sink = sinkl[head];
       const float M = fmaxf(mh, sink);
       const float f = __builtin_amdgcn_exp2f(mh - M);
       const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
@@ -541,37 +454,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
               make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
     }
-#else
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 128 * wv + 16 * dt + 4 * g;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const int head = 16 * ht + r16;
-        float o0 = O[dt][ht][0] * inv[ht], o1 = O[dt][ht][1] * inv[ht];
-        float o2 = O[dt][ht][2] * inv[ht], o3 = O[dt][ht][3] * inv[ht];
-        if (d >= first) {  // pair (d, d+1) rotated at -t
-          const double2 ca = cs[(d - first) >> 1];
-          const float cf = (float)ca.x, sf = (float)ca.y;
-          const float a0 = o0 * cf + o1 * sf, a1 = o1 * cf - o0 * sf;
-          o0 = a0;
-          o1 = a1;
-        }
-        if (d + 2 >= first) {  // pair (d+2, d+3)
-          const double2 cb = cs[(d + 2 - first) >> 1];
-          const float cf = (float)cb.x, sf = (float)cb.y;
-          const float b0 = o2 * cf + o3 * sf, b1 = o3 * cf - o2 * sf;
-          o2 = b0;
-          o3 = b1;
-        }
-        uint2 st;
-        st.x = pack_bf16x2(o0, o1);
-        st.y = pack_bf16x2(o2, o3);
-        char* ob = (head < 32 ? (char*)kbuf0 : (char*)kbuf1) + (head & 31) * 1024;
-        *(uint2*)(ob + ((((d >> 3) ^ (head & 15))) << 4) + ((d & 7) << 1)) = st;
-      }
-    }
-#endif
     __syncthreads();
     bf16_t* orow = out + tok * kAH * kAD;
 #pragma unroll 4
@@ -583,7 +465,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     }
   } else {
     float* pbase = part + (slot * nsplit + split) * kAH * kPart;
-#if CSA_ATTN_PV32
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -593,13 +474,6 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
           *(f32x4*)(pbase + (32 * hh + l32) * kPart + 128 * wv + 32 * ct + 8 * a + 4 * h32) =
               f32x4{O[ct][hh][4 * a], O[ct][hh][4 * a + 1], O[ct][hh][4 * a + 2],
                     O[ct][hh][4 * a + 3]};
-#else
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-        *(f32x4*)(pbase + (16 * ht + r16) * kPart + 128 * wv + 16 * dt + 4 * g) = O[dt][ht];
-#endif
     if (g == 0) {
       float* prow = pbase + (16 * wv + r16) * kPart;
       prow[kAD] = m_run;

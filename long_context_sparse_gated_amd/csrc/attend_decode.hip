@@ -103,6 +103,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   __shared__ __attribute__((aligned(16))) int32_t rid[kDMaxRows];
   __shared__ double2 cs[kMaxRope / 2];
   __shared__ float wm[4][16], wl[4][16];  // each wave's running maximum and sum per head
+  __shared__ float sinkl[16];             // the group's sink logits (log2 units)
 
   // block -> (token, head group, row slice); a token's blocks share id mod 8
   const int G = 4 * nsplit;
@@ -179,6 +180,8 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
+  // the sink logits, used at the end, go to LDS now
+  if (tid < 16) sinkl[tid] = sinks ? sinks[16 * hg + tid] * kLog2e : -INFINITY;
   __syncthreads();
 
   // DMA of group gi into buffer dst: 16 rows of 1 KB, one per instruction;
@@ -398,7 +401,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   }
   const int head = 16 * hg + h;
   if (nsplit == 1) {
-    const float sink = sinks ? sinks[head] * kLog2e : -INFINITY;
+    const float sink = sinkl[h];
     const float Mt = fmaxf(Mh, sink);
     const float f = Mh == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mh - Mt);
     const float lt = Lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - Mt) : 0.f);

@@ -230,14 +230,11 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
 // earlier tokens sit in the other Ls - 1 slots, so the slot written here
 // (p0 mod Ls, holding position p0 - Ls) is never one the entry reads.
 template <typename T>
-__global__ void __launch_bounds__(256) compress_one_kernel(
+__device__ __forceinline__ void compress_one_seq(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
-    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool, Seqs sq,
-    int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
-  __shared__ double pooled[kMaxWidth];
-  __shared__ double red[256 / 64];
-  const int b = blockIdx.x;
-  if (sq.len(b) == 0) return;  // a padding token: nothing to record
+    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
+    const Seqs& sq, int b, int width, int R, const Rope& base, int m, int overlap,
+    int64_t pool_cap, double* pooled, double* red) {
   const int64_t p0 = sq.pos0[b];
   const int Ls = (1 + overlap) * m;
   const int64_t w = p0 / m;
@@ -253,6 +250,68 @@ __global__ void __launch_bounds__(256) compress_one_kernel(
     dk[c] = src_kv[c];
     dg[c] = src_g[c];
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) compress_one_kernel(
+    const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
+    float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool, Seqs sq,
+    int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double red[256 / 64];
+  const int b = blockIdx.x;
+  if (sq.len(b) == 0) return;  // a padding token: nothing to record
+  compress_one_seq<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, sq, b, width, R, base, m,
+                      overlap, pool_cap, pooled, red);
+}
+
+// The token's K=V row appended to sequence b's window ring (slot = position
+// mod cap): channels before the rope slice copied, the slice rotated at the
+// token's position in float64 and rounded once (as window_append_kernel).
+template <typename T>
+__device__ __forceinline__ void window_one_seq(const T* __restrict__ kv, T* __restrict__ ring,
+                                               const Seqs& sq, int b, int D, int R,
+                                               const Rope& base, int64_t cap, double* freq) {
+  const int64_t t = sq.pos0[b];
+  const T* src = kv + sq.row(b, 0) * D;
+  T* dst = ring + ((int64_t)b * cap + t % cap) * D;
+  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) freq[j] = rope_freq(base, j, R);
+  for (int c = threadIdx.x; c < D - R; c += blockDim.x) dst[c] = src[c];
+  __syncthreads();
+  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) {
+    const int c = D - R + 2 * j;
+    double sn, cs;
+    sincos((double)t * freq[j], &sn, &cs);
+    double a = store_t<T>::ld(src + c), bb = store_t<T>::ld(src + c + 1);
+    rot64(a, bb, cs, sn);
+    store_t<T>::st64(dst + c, a);
+    store_t<T>::st64(dst + c + 1, bb);
+  }
+}
+
+// A decode step's cache updates in one launch: block (b, role) takes
+// sequence b's new token into the window ring (role 0), the main
+// compressor (role 1) or the indexer's compressor (role 2).
+template <typename T>
+__global__ void __launch_bounds__(256) cache_update_one_kernel(
+    const T* __restrict__ kv, T* __restrict__ ring, int64_t cap, const T* __restrict__ ckv,
+    const T* __restrict__ cgate, const float* __restrict__ norm_w, T* __restrict__ st_kv,
+    T* __restrict__ st_gate, T* __restrict__ pool, const T* __restrict__ ikv,
+    const T* __restrict__ igate, const float* __restrict__ inorm_w, T* __restrict__ ist_kv,
+    T* __restrict__ ist_gate, T* __restrict__ ipool, float eps, Seqs sq, int D, int R, int Di,
+    int Ri, Rope base, int m, int overlap, int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double red[256 / 64];
+  const int b = blockIdx.x;
+  if (sq.len(b) == 0) return;  // a padding token: nothing to record
+  if (blockIdx.y == 0)
+    window_one_seq<T>(kv, ring, sq, b, D, R, base, cap, pooled);
+  else if (blockIdx.y == 1)
+    compress_one_seq<T>(ckv, cgate, norm_w, eps, st_kv, st_gate, pool, sq, b, D, R, base, m,
+                        overlap, pool_cap, pooled, red);
+  else
+    compress_one_seq<T>(ikv, igate, inorm_w, eps, ist_kv, ist_gate, ipool, sq, b, Di, Ri, base,
+                        m, overlap, pool_cap, pooled, red);
 }
 
 // Keep the raw rows of the last (1 + overlap) m positions for later calls.
@@ -313,6 +372,27 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
     state_update_kernel<float><<<g2, 256, 0, s>>>((const float*)kv, (const float*)gate,
                                                   (float*)st_kv, (float*)st_gate, sq, width, Ls);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_update_one(const Layer& L, const Batch& bt, const void* kv, void* ring,
+                                   int64_t cap, const void* ckv, const void* cgate,
+                                   const float* norm_w, void* st_kv, void* st_gate, void* pool,
+                                   const void* ikv, const void* igate, const float* inorm_w,
+                                   void* ist_kv, void* ist_gate, void* ipool, int64_t pool_cap,
+                                   float eps, int roles, hipStream_t s) {
+  const dim3 grid(bt.B, roles);
+  const Seqs sq = seqs_of(bt);
+#define CSA_CU_LAUNCH(T)                                                                       \
+  cache_update_one_kernel<T><<<grid, 256, 0, s>>>(                                            \
+      (const T*)kv, (T*)ring, cap, (const T*)ckv, (const T*)cgate, norm_w, (T*)st_kv,          \
+      (T*)st_gate, (T*)pool, (const T*)ikv, (const T*)igate, inorm_w, (T*)ist_kv, (T*)ist_gate, \
+      (T*)ipool, eps, sq, L.D, L.R, L.Di, L.Ri, L.base, L.m, L.overlap, pool_cap)
+  if (L.dtype == 1)
+    CSA_CU_LAUNCH(bf16_t);
+  else
+    CSA_CU_LAUNCH(float);
+#undef CSA_CU_LAUNCH
   return hipGetLastError();
 }
 

@@ -133,6 +133,14 @@ hipError_t launch_rope(const Layer& L, const Batch& b, void* x, int rows, int wi
 hipError_t launch_compress(const Layer& L, const Batch& b, int width, int rope_dim, const void* kv,
                            const void* gate, const float* norm_w, float eps, void* st_kv,
                            void* st_gate, void* pool, int64_t pool_cap, hipStream_t s);
+// One launch for a decode step's cache updates: roles 1 (window), 2 (+ main
+// compressor) or 3 (+ indexer compressor) per sequence.
+hipError_t launch_cache_update_one(const Layer& L, const Batch& b, const void* kv, void* ring,
+                                   int64_t cap, const void* ckv, const void* cgate,
+                                   const float* norm_w, void* st_kv, void* st_gate, void* pool,
+                                   const void* ikv, const void* igate, const float* inorm_w,
+                                   void* ist_kv, void* ist_gate, void* ipool, int64_t pool_cap,
+                                   float eps, int roles, hipStream_t s);
 // plan.hip
 size_t align256(size_t x);
 bool index_fast_shape(const Layer& L);

@@ -9,7 +9,8 @@ width]`` tensors addressed through a per-sequence block table of the layer
 (each layer has its own table and block count, since the layers' pools
 differ in ratio and size).  ``layer_step`` runs one call of the layer: window
 append, compressor(s), indexer + top-k (CSA), attention.  It only orders
-calls; all arithmetic is in libcsa.
+calls; all arithmetic is in libcsa.  The window append and the compressors
+go through csa_cache_update (one launch for a decode step).
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ import dataclasses
 from typing import Optional
 
 from . import (CSA_OP_ATTEND, CSA_OP_HCA_ATTEND, CSA_OP_INDEX_TOPK, Layer, Paged, csa_attend,
-               csa_compress, csa_index_topk, csa_window_append, csa_workspace_bytes, hca_attend)
+               csa_cache_update, csa_index_topk, csa_workspace_bytes, hca_attend)
 
 __all__ = ["LayerCache", "layer_step"]
 
@@ -95,20 +96,25 @@ def layer_step(cache: LayerCache, pos0, pos0_max: int, q, kv, ckv=None, cgate=No
     geo = dict(n_valid=n_valid, cu_seqlens=cu_seqlens, n_new=n_new)
     if out is None:
         out = torch.empty_like(q)
-    csa_window_append(L, pos0, pos0_max, kv, cache.ring, **geo)
+    # the window append and the compressor(s): one launch for a decode step
+    pg = dict(geo, paged=cache.paged)
     if L.compress_ratio == 0:
+        csa_cache_update(L, pos0, pos0_max, kv, cache.ring, **geo)
         hca_attend(L, pos0, pos0_max, q, cache.ring, None, sinks, out,
                    cache.workspace(n, CSA_OP_HCA_ATTEND), **geo)
         return out, None
-    pg = dict(geo, paged=cache.paged)
-    csa_compress(L, pos0, pos0_max, ckv, cgate, cache.cstate_kv, cache.cstate_gate, cache.pool,
-                 L.qk_rope_head_dim, norm_weight, norm_eps, **pg)
+    idx_streams = {}
+    if L.index_topk > 0:
+        idx_streams = dict(ikv=ikv, igate=igate, istate_kv=cache.istate_kv,
+                           istate_gate=cache.istate_gate, ipool=cache.ipool,
+                           inorm_weight=inorm_weight)
+    csa_cache_update(L, pos0, pos0_max, kv, cache.ring, ckv, cgate, cache.cstate_kv,
+                     cache.cstate_gate, cache.pool, norm_weight=norm_weight, norm_eps=norm_eps,
+                     **idx_streams, **pg)
     if L.index_topk == 0:
         hca_attend(L, pos0, pos0_max, q, cache.ring, cache.pool, sinks, out,
                    cache.workspace(n, CSA_OP_HCA_ATTEND), **pg)
         return out, None
-    csa_compress(L, pos0, pos0_max, ikv, igate, cache.istate_kv, cache.istate_gate, cache.ipool,
-                 L.index_rope_dim, inorm_weight, norm_eps, **pg)
     if topk_idx is None:
         topk_idx = torch.empty(*lead, L.index_topk, dtype=torch.int32, device=q.device)
     csa_index_topk(L, pos0, pos0_max, qi, wi, cache.ipool, topk_idx,

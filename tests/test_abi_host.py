@@ -145,6 +145,28 @@ def test_rejections_return_before_launch(lib):
     assert lib.csa_compress(ctypes.byref(L), ctypes.byref(
         batch(block_table=FAKE.value, block_entries=128, block_table_stride=15, pool_blocks=16)),
         512, 64, FAKE, FAKE, None, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 2048, None) == SHAPE
+    # the fused cache update: the window's and each compressor's checks
+    def cache_update(layer=L, b=B, kv=FAKE, ring=FAKE, win_cap=8192, ckv=FAKE, ikv=FAKE,
+                     ipool=FAKE, pool_cap=2048, eps=1e-6):
+        return lib.csa_cache_update(ctypes.byref(layer), ctypes.byref(b), kv, ring, win_cap, ckv,
+                                    FAKE, None, FAKE, FAKE, FAKE, ikv, FAKE, None, FAKE, FAKE,
+                                    ipool, pool_cap, ctypes.c_float(eps), None)
+    assert cache_update(kv=None) == NULL
+    assert cache_update(win_cap=100) == SHAPE
+    assert cache_update(ckv=None) == NULL
+    assert cache_update(ikv=None) == NULL
+    assert cache_update(ipool=None) == NULL
+    assert cache_update(pool_cap=2047) == SHAPE
+    assert cache_update(eps=-1.0) == SHAPE
+    assert cache_update(layer=csa_layer(index_rope_dim=200)) == SHAPE
+    assert cache_update(b=batch(block_table=FAKE.value, block_entries=128, block_table_stride=15,
+                                pool_blocks=16)) == SHAPE
+    # an HCA layer needs no indexer pointers (the call fails on the pool capacity, after the
+    # pointers were accepted); a sliding-only layer none of the compressors' (window capacity)
+    assert cache_update(layer=csa_layer(compress_ratio=0, overlap=0, index_topk=0), ckv=None,
+                        ikv=None, ipool=None, win_cap=100) == SHAPE
+    assert cache_update(layer=csa_layer(compress_ratio=128, overlap=0, index_topk=0), ikv=None,
+                        ipool=None, pool_cap=63) == SHAPE
     # rope / window
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 64, 2, None) == SHAPE
     assert lib.csa_rope(ctypes.byref(L), ctypes.byref(B), FAKE, 1, 512, 65, 1, None) == SHAPE

@@ -1105,3 +1105,79 @@ def test_packed_paged_decode_skips_absent_sequences(csa):
     for b in [b for b in range(B) if lens[b] == 0]:  # absent: no new entry, state as it was
         assert not got[b, P:].any()
         assert torch.equal(pk.cstate_kv[b], dev(inp["cstate_kv"])[b])
+
+
+@pytest.mark.parametrize("kind,n,pos,paged", [
+    ("csa", 1, 131071, False),   # a decode step that closes an entry ((p + 1) % 4 == 0)
+    ("csa", 1, 131072, False),   # one that does not
+    ("csa", 1, 5003, True),      # paged pools (shuffled block table)
+    ("hca", 1, 8191, False),
+    ("sliding", 1, 777, False),
+    ("csa", 37, 3001, False),    # a prefill chunk: the separate kernels behind the same call
+])
+def test_cache_update_matches_separate_calls(csa, kind, n, pos, paged):
+    """csa_cache_update (one launch for a decode step) writes the window ring, the
+    compressor states and the pools bit for bit as csa_window_append and csa_compress
+    called one after the other."""
+    import torch
+    from long_context_sparse_gated_amd.layer import LayerCache
+    say(f"case: cache update {kind} n={n} pos={pos} paged={paged}")
+    m = csa
+    spec = {"csa": synth.workload("csa_decode").layers[0],
+            "hca": synth.workload("mixed_decode").layers[1],
+            "sliding": synth.workload("mixed_decode").layers[2]}[kind]
+    L = m.Layer.from_spec(spec)
+    B, W = 3, spec.window
+    ratio = spec.ratio
+    pool_cap = (pos + n) // ratio + 1 if ratio else 0
+    g = torch.Generator(device="cuda").manual_seed(11)
+    bf = torch.bfloat16
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda").to(bf)
+
+    kw = {}
+    if paged and ratio:
+        E = 256
+        per = (pool_cap + E - 1) // E
+        perm = torch.randperm(B * per, generator=torch.Generator().manual_seed(3))
+        kw = dict(block_entries=E, pool_blocks=B * per,
+                  block_table=perm.view(B, per).to(torch.int32).cuda())
+    caches = [LayerCache(L, B, W + n, max(pool_cap, 1), **kw) for _ in range(2)]
+    # the same random cache contents in both
+    for name in ("ring", "pool", "ipool", "cstate_kv", "cstate_gate", "istate_kv", "istate_gate"):
+        a = getattr(caches[0], name, None)
+        if a is not None:
+            a.copy_(torch.randn(a.shape, generator=g, device="cuda").to(a.dtype))
+            getattr(caches[1], name).copy_(a)
+    D, Di = spec.head_dim, spec.index_dim
+    kv, ckv, cgate = rnd(B, n, D), rnd(B, n, D), rnd(B, n, D)
+    ikv, igate = rnd(B, n, Di), rnd(B, n, Di)
+    nw = torch.rand(D, generator=g, device="cuda") + 0.5
+    inw = torch.rand(Di, generator=g, device="cuda") + 0.5
+    p0 = torch.tensor([pos, pos + 1, pos + 2], dtype=torch.int64, device="cuda")
+    pm = pos + 2
+    c0, c1 = caches
+    # separate calls
+    m.csa_window_append(L, p0, pm, kv, c0.ring)
+    if ratio:
+        m.csa_compress(L, p0, pm, ckv, cgate, c0.cstate_kv, c0.cstate_gate, c0.pool,
+                       spec.rope_dim, nw, 1e-6, paged=c0.paged)
+        if spec.has_indexer:
+            m.csa_compress(L, p0, pm, ikv, igate, c0.istate_kv, c0.istate_gate, c0.ipool,
+                           spec.index_rope_dim, inw, 1e-6, paged=c0.paged)
+    # one call
+    if not ratio:
+        m.csa_cache_update(L, p0, pm, kv, c1.ring)
+    elif not spec.has_indexer:
+        m.csa_cache_update(L, p0, pm, kv, c1.ring, ckv, cgate, c1.cstate_kv, c1.cstate_gate,
+                           c1.pool, norm_weight=nw, paged=c1.paged)
+    else:
+        m.csa_cache_update(L, p0, pm, kv, c1.ring, ckv, cgate, c1.cstate_kv, c1.cstate_gate,
+                           c1.pool, ikv, igate, c1.istate_kv, c1.istate_gate, c1.ipool,
+                           norm_weight=nw, inorm_weight=inw, paged=c1.paged)
+    torch.cuda.synchronize()
+    for name in ("ring", "pool", "ipool", "cstate_kv", "cstate_gate", "istate_kv", "istate_gate"):
+        a = getattr(c0, name, None)
+        if a is not None:
+            assert torch.equal(a.view(torch.int16), getattr(c1, name).view(torch.int16)), name
