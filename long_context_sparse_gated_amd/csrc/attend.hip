@@ -91,10 +91,11 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   __shared__ __attribute__((aligned(16))) int32_t rid[kMaxRows];
   __shared__ uint32_t vmask[kMaxRows / 32 + 1];
   __shared__ double2 cs[kMaxRope / 2];
+  __shared__ __attribute__((aligned(16))) float2 csf[kMaxRope / 2];  // cs rounded to float
   __shared__ __attribute__((aligned(16))) bf16_t ps[kAH * kPRow];  // P^T, row slots per head
   __shared__ float alph[kAH];   // this chunk's rescale of O per head
   __shared__ float mlf[2][kAH];  // final running max and sum per head
-  __shared__ float sinkl[kAH];   // sink logits (log2 units), -inf without sinks
+  __shared__ float sinkl[kAH];   // sink logits (natural units)
 
   constexpr int NTH = 256;
   constexpr int RPW = kCH / 4;  // rows each wave gathers per chunk
@@ -127,27 +128,30 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) Qf[kk] = *(const uint4*)(qrow + 32 * kk);
   }
-  // the sink logits (log2 units), used at the end, go to LDS now
-  if (tid < kAH) sinkl[tid] = sinks ? sinks[tid] * kLog2e : -INFINITY;
-  // row ids: every selected index of the thread's rows is loaded first (one
-  // memory latency, not one per row); window row j is ring slot
-  // (lo + j) mod cap, and j < nwin <= cap (the ring holds the window or the
-  // whole sequence) leaves one wrap at most
-  {
-    constexpr int U = kMaxRows / NTH;
-    int32_t sel[U];
+  // the sink logit and every selected index of the thread's rows are loaded
+  // next, so that all the prologue's loads share one memory latency (every
+  // lane loads a sink, so that no branch holds a wait for it)
+  const float sink_raw = sinks ? sinks[tid & (kAH - 1)] : 0.f;
+  constexpr int U = kMaxRows / NTH;
+  int32_t sel[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = r0 + tid + NTH * u - nwin;
-      sel[u] = (csa && tid + NTH * u < r1 - r0 && e >= 0) ? idx_row[e] : 0;
-    }
+  for (int u = 0; u < U; ++u) {
+    const int e = r0 + tid + NTH * u - nwin;
+    sel[u] = (csa && tid + NTH * u < r1 - r0 && e >= 0) ? idx_row[e] : 0;
+  }
+  // row ids: window row j is ring slot (lo + j) mod cap, and j < nwin <= cap
+  // (the ring holds the window or the whole sequence) leaves one wrap at
+  // most.  Bit r of vmask[c - c0]: row r of chunk c takes part in the
+  // softmax; wave wv holds rows 256 u + 64 wv + lane, so one ballot per u
+  // gives two whole words.
+  {
     const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = tid + NTH * u;
+      int id = -1;
       if (j < r1 - r0) {
         const int jr = r0 + j;
-        int id;
         if (jr < nwin) {
           const int v = lo_mod + jr;
           id = wb + (v >= cap ? v - cap : v);
@@ -157,23 +161,15 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
         }
         rid[j] = id;
       }
+      const unsigned long long bal = __ballot(id != -1);
+      if (lane == 0) {
+        const int j0 = NTH * u + 64 * wv;
+        vmask[j0 >> 5] = (uint32_t)bal;
+        vmask[(j0 >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
     }
   }
-  for (int j = tid; j < R / 2; j += NTH) {
-    double sn, c;
-    sincos((double)t * rope_freq(base, j, R), &sn, &c);
-    cs[j] = make_double2(c, sn);
-  }
-  __syncthreads();
-  // bit r of vmask[c - c0]: row r of chunk c takes part in the softmax
-  for (int j0 = 64 * wv; j0 < r1 - r0; j0 += 256) {
-    const bool ok = j0 + lane < r1 - r0 && rid[j0 + lane] != -1;
-    const unsigned long long bal = __ballot(ok);
-    if (lane == 0) {
-      vmask[j0 >> 5] = (uint32_t)bal;
-      vmask[(j0 >> 5) + 1] = (uint32_t)(bal >> 32);
-    }
-  }
+  if (tid < kAH) sinkl[tid] = sink_raw;  // scaled to log2 units at the end
   __syncthreads();
 
   // gather of chunk c into dst: this wave moves rows RPW*wv .. +RPW-1.
@@ -219,6 +215,16 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
     for (int e = 0; e < RPW; ++e) gather_row(G, e);
   };
   if (c0 < c1) issue(c0, kbuf0);
+
+  // the rope table (float64 for the query, float32 for the output), computed
+  // while the first chunk is in flight
+  for (int j = tid; j < R / 2; j += NTH) {
+    double sn, c;
+    sincos((double)t * rope_freq(base, j, R), &sn, &c);
+    cs[j] = make_double2(c, sn);
+    csf[j] = make_float2((float)c, (float)sn);
+  }
+  __syncthreads();
 
   // the rope channels of the query fragments rotated at t in float64 and
   // rounded to bf16 once
@@ -422,38 +428,55 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   if (nsplit == 1) {
     // the whole [64 heads][512] bf16 output, chunks swizzled by head: heads
     // 0..31 in kbuf0, 32..63 in kbuf1
+    float iv[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int head = 32 * hh + l32;
       const float mh = mlf[0][head], lh = mlf[1][head];
-      const float sink = sinkl[head];
+      const float sink = sinks ? sinkl[head] * kLog2e : -INFINITY;
       const float M = fmaxf(mh, sink);
       const float f = __builtin_amdgcn_exp2f(mh - M);
       const float lt = lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - M) : 0.f);
-      const float iv = f / lt;
-      char* ob = (hh == 0 ? (char*)kbuf0 : (char*)kbuf1) + (head & 31) * 1024;
+      iv[hh] = f / lt;
+    }
+    // the lane's channels d .. d + 3, d = 128 wv + 32 ct + 8 a + 4 h32.  The
+    // rope slice (at most 128 channels, starting at a multiple of 16) lies in
+    // wave 3's channels, and the 16 channels from 384 + 32 ct + 16 (a / 2)
+    // on are all rope channels or none: for each (ct, a) the test is known
+    // at compile time up to the wave index, which is uniform.  Every wave
+    // reads the table entries wave 3 would use (unconditional reads issue
+    // together instead of each waiting in a branch).
+    static_assert(kAD - kMaxRope >= 384, "rope channels within wave 3's slice");
+    const int wvs = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int d = 128 * wv + 32 * ct + 8 * a + 4 * h32;
+      for (int a = 0; a < 4; ++a) {
+        const int d = 128 * wvs + 32 * ct + 8 * a + 4 * h32;
+        const bool rope_w3 = 384 + 32 * ct + 16 * (a >> 1) >= first;
+        const bool rope = rope_w3 && wvs == 3;
+        float4 cz = make_float4(1.f, 0.f, 1.f, 0.f);
+        if (rope_w3)  // pairs (d, d+1), (d+2, d+3) of wave 3
+          cz = *(const float4*)&csf[(384 + 32 * ct + 8 * a + 4 * h32 - first) >> 1];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int head = 32 * hh + l32;
           float o[4];
 #pragma unroll
-          for (int bq = 0; bq < 4; ++bq) o[bq] = O[ct][hh][4 * a + bq] * iv;
-#pragma unroll
-          for (int bq = 0; bq < 4; bq += 2) {
-            if (d + bq >= first) {  // pair (d + bq, d + bq + 1) rotated at -t
-              const double2 cz = cs[(d + bq - first) >> 1];
-              const float cf = (float)cz.x, sf = (float)cz.y;
-              const float x0 = o[bq] * cf + o[bq + 1] * sf, x1 = o[bq + 1] * cf - o[bq] * sf;
-              o[bq] = x0;
-              o[bq + 1] = x1;
-            }
+          for (int bq = 0; bq < 4; ++bq) o[bq] = O[ct][hh][4 * a + bq] * iv[hh];
+          if (rope) {  // pairs rotated at -t
+            const float x0 = o[0] * cz.x + o[1] * cz.y, x1 = o[1] * cz.x - o[0] * cz.y;
+            const float x2 = o[2] * cz.z + o[3] * cz.w, x3 = o[3] * cz.z - o[2] * cz.w;
+            o[0] = x0;
+            o[1] = x1;
+            o[2] = x2;
+            o[3] = x3;
           }
+          char* ob = (hh == 0 ? (char*)kbuf0 : (char*)kbuf1) + (head & 31) * 1024;
           *(uint2*)(ob + (((d >> 3) ^ (head & 15)) << 4) + ((d & 7) << 1)) =
               make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
-    }
+      }
     __syncthreads();
     bf16_t* orow = out + tok * kAH * kAD;
 #pragma unroll 4

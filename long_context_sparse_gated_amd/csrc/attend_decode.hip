@@ -102,8 +102,9 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   __shared__ __attribute__((aligned(1024))) bf16_t gb[8][kGR * kAD];
   __shared__ __attribute__((aligned(16))) int32_t rid[kDMaxRows];
   __shared__ double2 cs[kMaxRope / 2];
+  __shared__ __attribute__((aligned(16))) float2 csf[kMaxRope / 2];  // cs rounded to float
   __shared__ float wm[4][16], wl[4][16];  // each wave's running maximum and sum per head
-  __shared__ float sinkl[16];             // the group's sink logits (log2 units)
+  __shared__ float sinkl[16];             // the group's sink logits (natural units)
 
   // block -> (token, head group, row slice); a token's blocks share id mod 8
   const int G = 4 * nsplit;
@@ -144,6 +145,8 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) Qf[kk] = *(const uint4*)(qrow + 32 * kk);
   }
+  // the sink logit is loaded by every lane (no branch holds a wait for it)
+  const float sink_raw = sinks ? sinks[16 * hg + (tid & 15)] : 0.f;
   // row ids: every selected index of the thread's rows is loaded first (one
   // memory latency, not one per row); window row j is ring slot
   // (lo + j) mod cap, and j < nwin <= cap (the ring holds the window or the
@@ -179,9 +182,9 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
+    csf[j] = make_float2((float)c, (float)sn);
   }
-  // the sink logits, used at the end, go to LDS now
-  if (tid < 16) sinkl[tid] = sinks ? sinks[16 * hg + tid] * kLog2e : -INFINITY;
+  if (tid < 16) sinkl[tid] = sink_raw;  // scaled to log2 units at the end
   __syncthreads();
 
   // DMA of group gi into buffer dst: 16 rows of 1 KB, one per instruction;
@@ -401,7 +404,7 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
   }
   const int head = 16 * hg + h;
   if (nsplit == 1) {
-    const float sink = sinkl[h];
+    const float sink = sinks ? sinkl[h] * kLog2e : -INFINITY;
     const float Mt = fmaxf(Mh, sink);
     const float f = Mh == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mh - Mt);
     const float lt = Lh * f + (sinks ? __builtin_amdgcn_exp2f(sink - Mt) : 0.f);
@@ -409,13 +412,14 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] *= inv;
     if (ch0 + 32 > first) {
+      // pairs (d, d+1) at and above `first` rotated at -t; the table reads
+      // are unconditional (clamped index) so that they issue together
 #pragma unroll
       for (int c = 0; c < 32; c += 2) {
         const int d = ch0 + c;
-        if (d >= first) {  // pair (d, d+1) rotated at -t
-          const double2 ca = cs[(d - first) >> 1];
-          const float cf = (float)ca.x, sf = (float)ca.y;
-          const float a0 = o[c] * cf + o[c + 1] * sf, a1 = o[c + 1] * cf - o[c] * sf;
+        const float2 cz = csf[d >= first ? (d - first) >> 1 : 0];
+        const float a0 = o[c] * cz.x + o[c + 1] * cz.y, a1 = o[c + 1] * cz.x - o[c] * cz.y;
+        if (d >= first) {
           o[c] = a0;
           o[c + 1] = a1;
         }
