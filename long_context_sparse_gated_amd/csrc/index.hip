@@ -470,6 +470,23 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One count into bins[bin] for every active lane with `add`.  When all the
+// adding lanes of the wave name the same bin (ties: every key equal, as with
+// all-zero scores) a single atomic adds their number; otherwise each lane
+// adds its own.  One LDS address hit by a whole row of equal keys otherwise
+// serialises tens of thousands of atomics.
+__device__ __forceinline__ void bin_add(uint32_t* bins, bool add, uint32_t bin) {
+  const unsigned long long am = __ballot(add);
+  if (am == 0ull) return;
+  const int first = __ffsll((long long)am) - 1;
+  const uint32_t fb = (uint32_t)__shfl((int)bin, first, 64);
+  if (__ballot(add && bin == fb) == am) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&bins[fb], (uint32_t)__popcll(am));
+  } else if (add) {
+    atomicAdd(&bins[bin], 1u);
+  }
+}
+
 __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __restrict__ q,
                                                            bf16_t* __restrict__ qr,
                                                            uint32_t* __restrict__ hist, Seqs sq,
@@ -876,7 +893,7 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
     for (uint32_t e = tid; e < C; e += 256) {
       int32_t id;
       const uint32_t key = tie_at(e, id);
-      if ((key & mask) == prefix) atomicAdd(&bins[(key >> shift) & (nb - 1u)], 1u);
+      bin_add(bins, (key & mask) == prefix, (key >> shift) & (nb - 1u));
     }
     __syncthreads();
     if (tid < 64) {
@@ -1113,8 +1130,8 @@ __global__ void __launch_bounds__(kBlkTopKT) topk_block(const float* __restrict_
     __syncthreads();
     for (uint32_t e = tid; e < N; e += kBlkTopKT) {
       const uint32_t key = key_of(e);
-      if ((key >> kHShift) == T && ((key & kLow) & mask) == prefix)
-        atomicAdd(&bins[((key & kLow) >> shift) & (nb - 1u)], 1u);
+      bin_add(bins, (key >> kHShift) == T && ((key & kLow) & mask) == prefix,
+              ((key & kLow) >> shift) & (nb - 1u));
     }
     __syncthreads();
     if (tid < 64) {
@@ -1265,7 +1282,7 @@ __global__ void __launch_bounds__(BS) topk_radix(const float* __restrict__ score
     __syncthreads();
     for (int j = threadIdx.x; j < n; j += BS) {
       const uint32_t key = order_key(sc[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      bin_add(hist, (key & mask) == prefix, (key >> shift) & 255u);
     }
     __syncthreads();
     if (threadIdx.x < 64) {

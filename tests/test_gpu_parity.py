@@ -456,7 +456,10 @@ def test_decode_graph_replay_matches_eager(csa):
     (1, 30000, 7, 119999), (3, 2048, 3, 8191), (7, 12000, 0, 47990), (5, 600, 0, 2048),
     (2, 3001, 0, 11990), (1, 32768, 2, 131071),
     # the mixed long-context decode row length (262144 keys), plain and tie-heavy
-    (1, 262144, 0, 1048575), (2, 262144, 3, 1048574)])
+    (1, 262144, 0, 1048575), (2, 262144, 3, 1048574),
+    # every key equal, so every score ties and the lowest ids win: prefill
+    # (one-wave and block selection) and decode (one block, and slices)
+    (37, 700, 1, 2700), (8, 12000, 1, 47990), (1, 32768, 1, 131071), (1, 262144, 1, 1048575)])
 def test_topk_bit_exact_on_grid_inputs(csa, n_q, pool, distinct, pos0):
     """Exact-arithmetic scores: both sides must select identical ids (ties: lowest id)."""
     _grid_topk_case(csa, n_q, pool, distinct, pos0)
