@@ -103,6 +103,27 @@ __device__ __forceinline__ void ld2<float>(const float* p, double& a, double& b)
   b = f.y;
 }
 
+// A channel pair as stored: two bf16 in one word, or two floats.
+template <typename T> struct pair_t;
+template <> struct pair_t<bf16_t> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw ld(const bf16_t* p) { return *(const uint32_t*)p; }
+  static __device__ __forceinline__ void cvt(raw u, double& a, double& b) {
+    a = bf16_to_f32((bf16_t)(u & 0xffffu));
+    b = bf16_to_f32((bf16_t)(u >> 16));
+  }
+};
+template <> struct pair_t<float> {
+  typedef float2 raw;
+  static __device__ __forceinline__ raw ld(const float* p) { return *(const float2*)p; }
+  static __device__ __forceinline__ void cvt(raw u, double& a, double& b) {
+    a = u.x;
+    b = u.y;
+  }
+};
+// Tokens a thread of the register path holds (window of at most G * kTokReg).
+constexpr int kTokReg = 8;
+
 template <typename T>
 __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
@@ -111,6 +132,8 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
   __shared__ double pooled[kMaxWidth];
   __shared__ double pa[kCmpT][2], pb[kCmpT][2];
   __shared__ double red[kCmpT / 64];
+  constexpr int kTab = 128;              // rope pairs kept in the table
+  __shared__ double2 csr[kTab];          // (cos, sin) of the rope pairs at w m
   const int b = blockIdx.y;
   const int64_t p0 = sq.pos0[b];
   const int64_t w = p0 / m + blockIdx.x;
@@ -127,7 +150,82 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     return s >= p0 ? cur + (s - p0) * width : st + (int64_t)(s % Ls) * width;
   };
   const int P = width / 2;
-  if (P < kCmpT) {
+  // the rope table of the entry, while the loads below are in flight
+  auto rope_table = [&]() __attribute__((always_inline)) {
+    for (int j = tid; j < R / 2 && j < kTab; j += kCmpT) {
+      double sn, cs;
+      sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
+      csr[j] = make_double2(cs, sn);
+    }
+  };
+  if (P < kCmpT && hi - lo <= (int64_t)(kCmpT / P) * kTokReg) {
+    // register path (windows of at most G * kTokReg tokens, e.g. the CSA
+    // window of 8): every thread loads its tokens' gate and kv pairs once,
+    // then the maximum and the sums come from registers
+    typedef typename pair_t<T>::raw raw;
+    const int G = kCmpT / P, p = tid % P, g = tid / P;
+    const bool act = g < G;
+    raw gq[kTokReg], vq[kTokReg];
+#pragma unroll
+    for (int u = 0; u < kTokReg; ++u) {
+      const int64_t s = lo + g + (int64_t)u * G;
+      if (act && s < hi) {
+        gq[u] = pair_t<T>::ld(row(g_b, sg_b, s) + 2 * p);
+        vq[u] = pair_t<T>::ld(row(kv_b, skv_b, s) + 2 * p);
+      }
+    }
+    rope_table();
+    double mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kTokReg; ++u) {
+      if (act && lo + g + (int64_t)u * G < hi) {
+        double a, c;
+        pair_t<T>::cvt(gq[u], a, c);
+        mx0 = fmax(mx0, a);
+        mx1 = fmax(mx1, c);
+      }
+    }
+    pa[tid][0] = mx0;
+    pa[tid][1] = mx1;
+    __syncthreads();
+    double M0 = -INFINITY, M1 = -INFINITY;
+    for (int k = 0; k < G; ++k) {
+      M0 = fmax(M0, pa[p + k * P][0]);
+      M1 = fmax(M1, pa[p + k * P][1]);
+    }
+    double l0 = 0.0, l1 = 0.0, n0 = 0.0, n1 = 0.0;
+#pragma unroll
+    for (int u = 0; u < kTokReg; ++u) {
+      if (act && lo + g + (int64_t)u * G < hi) {
+        double ga, gc, va, vc;
+        pair_t<T>::cvt(gq[u], ga, gc);
+        pair_t<T>::cvt(vq[u], va, vc);
+        const double e0 = exp(ga - M0), e1 = exp(gc - M1);
+        l0 += e0;
+        l1 += e1;
+        n0 += e0 * va;
+        n1 += e1 * vc;
+      }
+    }
+    __syncthreads();  // the maxima are read
+    pa[tid][0] = l0;
+    pa[tid][1] = l1;
+    pb[tid][0] = n0;
+    pb[tid][1] = n1;
+    __syncthreads();
+    if (tid < P) {
+      double L0 = 0.0, L1 = 0.0, N0 = 0.0, N1 = 0.0;
+      for (int k = 0; k < G; ++k) {
+        L0 += pa[p + k * P][0];
+        L1 += pa[p + k * P][1];
+        N0 += pb[p + k * P][0];
+        N1 += pb[p + k * P][1];
+      }
+      pooled[2 * p] = N0 / L0;
+      pooled[2 * p + 1] = N1 / L1;
+    }
+  } else if (P < kCmpT) {
+    rope_table();
     const int G = kCmpT / P, p = tid % P, g = tid / P;
     const bool act = g < G;
     double mx0 = -INFINITY, mx1 = -INFINITY;
@@ -176,6 +274,7 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
       pooled[2 * p + 1] = N1 / L1;
     }
   } else {
+    rope_table();
     for (int p = tid; p < P; p += kCmpT) {
       double mx0 = -INFINITY, mx1 = -INFINITY;
       for (int64_t s = lo; s < hi; ++s) {
@@ -216,8 +315,14 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
   for (int c = tid; c < width - R; c += kCmpT) store_t<T>::st64(dst + c, pooled[c]);
   for (int j = tid; j < R / 2; j += kCmpT) {
     const int c = width - R + 2 * j;
-    double sn, cs;
-    sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
+    double cs, sn;
+    if (j < kTab) {
+      const double2 cz = csr[j];
+      cs = cz.x;
+      sn = cz.y;
+    } else {
+      sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
+    }
     double a = pooled[c], bb = pooled[c + 1];
     rot64(a, bb, cs, sn);
     store_t<T>::st64(dst + c, a);
