@@ -732,12 +732,15 @@ __global__ void __launch_bounds__(256) topk_collect(const float* __restrict__ sc
   int32_t* ti = cand_tie + (int64_t)tok * pool_cap + c0;
   const unsigned long long lt = (1ull << lane) - 1ull;
   constexpr int U = kSlice / 64;
+  // all loads first, unconditional (ids past the slice re-read its last
+  // score and are never counted): one latency per slice.  Guarded loads were
+  // each waited for inside their own branch.
+  float v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = sc[min(c0 + 64 * u + lane, c1 - 1)];
   uint32_t bin[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {  // all loads first: one latency per slice
-    const int64_t j = c0 + 64 * u + lane;
-    bin[u] = j < c1 ? (order_key(sc[j]) >> kHShift) : 0u;
-  }
+  for (int u = 0; u < U; ++u) bin[u] = order_key(v[u]) >> kHShift;
   uint32_t nh = 0, nt = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -835,40 +838,53 @@ __global__ void __launch_bounds__(256) topk_final(const float* __restrict__ scor
   const uint32_t C = carry_t < (uint32_t)nv ? carry_t : (uint32_t)nv;
   const uint32_t need = (uint32_t)k - A < C ? (uint32_t)k - A : C;
   const bool in_lds = C <= (uint32_t)kTieCap;
-  // id of list entry e of a slice list (offsets `off`), clamped into the token's rows
-  auto list_id = [&](const int32_t* base, const uint32_t* off, uint32_t e) -> int32_t {
+  // position of list entry e of a slice list (offsets `off`) in its buffer,
+  // and the id stored there, clamped into the token's rows
+  auto list_pos = [&](const uint32_t* off, uint32_t e) -> int64_t {
     const int s = slice_of(off, ns, e);
     uint32_t d = e - off[s];
     if (d > (uint32_t)kSlice - 1u) d = (uint32_t)kSlice - 1u;
     int64_t p = (int64_t)s * kSlice + d;
-    if (p > pool_cap - 1) p = pool_cap - 1;
-    int32_t id = base[p];
+    return p > pool_cap - 1 ? pool_cap - 1 : p;
+  };
+  auto clamp_id = [&](int32_t id) -> int32_t {
     return id < 0 ? 0 : (id >= nv ? (int32_t)(nv - 1) : id);
+  };
+  auto list_id = [&](const int32_t* base, const uint32_t* off, uint32_t e) -> int32_t {
+    return clamp_id(base[list_pos(off, e)]);
   };
   const float* sc = scores + (int64_t)tok * pool_cap;
   const int32_t* hb = cand_hi + (int64_t)tok * pool_cap;
   const int32_t* tb = cand_tie + (int64_t)tok * pool_cap;
   // the cut bin's keys share their top kHBits bits: keep the low ones
   constexpr uint32_t kLow = (1u << kHShift) - 1u;
-  // gather both id lists (4 items per thread in flight)
+  // gather both id lists, 4 items per thread in flight: the positions first
+  // (LDS searches), then every id load, then every score load, all
+  // unconditional (positions and ids clamped into the buffers; items past a
+  // list are not kept), so that each group shares one latency (loads guarded
+  // by their own branches were each waited for inside it)
   for (uint32_t e0 = 0; e0 < (A > C ? A : C); e0 += 1024) {
-    int32_t ida[4], idt[4];
+    int64_t pa[4], pt[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t e = e0 + 256 * u + tid;
-      ida[u] = -1;
-      idt[u] = -1;
-      if (e < A) ida[u] = list_id(hb, off_hi, e);
-      if (in_lds && e < C) idt[u] = list_id(tb, off_tie, e);
+      pa[u] = list_pos(off_hi, e);
+      pt[u] = list_pos(off_tie, e);
+    }
+    int32_t ida[4], idt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ida[u] = clamp_id(hb[pa[u]]);
+      idt[u] = clamp_id(tb[pt[u]]);
     }
     float v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = idt[u] >= 0 ? sc[idt[u]] : 0.f;
+    for (int u = 0; u < 4; ++u) v[u] = sc[idt[u]];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t e = e0 + 256 * u + tid;
       if (e < A) sel_hi[e] = ida[u];
-      if (idt[u] >= 0) {
+      if (in_lds && e < C) {
         tie_id[e] = idt[u];
         tie_key[e] = order_key(v[u]) & kLow;
       }
@@ -1378,12 +1394,16 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     for (int j = lane; j < k; j += 64) o[j] = j < n ? j : -1;
     return;
   }
+  // every load is unconditional (ids past the row re-read its last score,
+  // never counted) so that all 32 are in flight at once; a load guarded by
+  // its own branch was waited for inside that branch, one latency each
+  float v[kTkPer];
+#pragma unroll
+  for (int u = 0; u < kTkPer; ++u) v[u] = sc[min(64 * u + lane, n - 1)];
   uint32_t key[kTkPer];
 #pragma unroll
-  for (int u = 0; u < kTkPer; ++u) {
-    const int j = 64 * u + lane;
-    key[u] = j < n ? order_key(sc[j]) : 0u;
-  }
+  for (int u = 0; u < kTkPer; ++u)  // masked, not branched: keeps the loads together
+    key[u] = order_key(v[u]) & (0u - (uint32_t)(64 * u + lane < n));
   uint32_t* myh = hist[lane & 3];
   uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
 #pragma unroll 1
