@@ -21,14 +21,48 @@ namespace csa {
 
 constexpr int kMaxWidth = 2048;
 
-// Entry w of sequence b, one block serially over the window (the one-token
-// decode call; pooled and red in LDS).
+// Eight consecutive channels (16 bytes of bf16, 32 of float32) as floats.
+template <typename T> struct row8;
+template <> struct row8<bf16_t> {
+  typedef uint4 raw;
+  static __device__ __forceinline__ raw ld(const bf16_t* p) { return *(const uint4*)p; }
+  static __device__ __forceinline__ float get(const raw& r, int e) {
+    const uint32_t u = e < 2 ? r.x : (e < 4 ? r.y : (e < 6 ? r.z : r.w));
+    return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+  }
+};
+template <> struct row8<float> {
+  struct raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ raw ld(const float* p) {
+    return raw{*(const float4*)p, *(const float4*)(p + 4)};
+  }
+  static __device__ __forceinline__ float get(const raw& r, int e) {
+    const float4 v = e < 4 ? r.a : r.b;
+    const int k = e & 3;
+    return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));
+  }
+};
+
+// LDS of the one-token pooling's token-group partials: per (group, channel)
+// the group's maximum (float) and its two sums (double); groups x width is
+// at most 2048.
+constexpr int kPoolWideBytes = kMaxWidth * (4 + 8 + 8);
+
+// Entry w of sequence b by one block of 256 threads (the one-token decode
+// call; pooled and red in LDS).  Widths of 8 c channels with c dividing 256
+// go "wide": thread t takes the 8 channels of chunk t mod c and every
+// (256/c)-th token of the window from token t / c on, with 16-byte loads,
+// eight tokens in flight; the groups' maxima and sums meet in LDS (`wide`),
+// summed in group order.  Other widths take one channel per thread over the
+// whole window, eight tokens at a time.
 template <typename T>
 __device__ __forceinline__ void pool_entry(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
     int b, int64_t p0, int64_t w, int64_t row0, int64_t dst_row, int width, int R, Rope base,
-    int m, int overlap, double* pooled, double* red) {
+    int m, int overlap, double* pooled, double* red, void* wide) {
   const int Ls = (1 + overlap) * m;
   const int64_t lo = max((w - overlap) * (int64_t)m, (int64_t)0), hi = (w + 1) * (int64_t)m;
   const T* kv_b = kv + row0 * width;  // the call's token rows of sequence b
@@ -36,19 +70,116 @@ __device__ __forceinline__ void pool_entry(
   const T* skv_b = st_kv + (int64_t)b * Ls * width;
   const T* sg_b = st_gate + (int64_t)b * Ls * width;
   double ss = 0.0;
+  // the window's tokens go eight at a time: their loads are unconditional
+  // (tokens past the window re-read its last one and are masked out) so that
+  // the eight share one latency; a load per loop step was waited for at
+  // once, one latency per token (128 for an HCA entry)
+  constexpr int TB = 8;
+  auto grow = [&](int64_t s) {
+    return s >= p0 ? g_b + (s - p0) * width : sg_b + (int64_t)(s % Ls) * width;
+  };
+  auto vrow = [&](int64_t s) {
+    return s >= p0 ? kv_b + (s - p0) * width : skv_b + (int64_t)(s % Ls) * width;
+  };
+  const int NC = width >> 3;
+  const bool wide_ok = (width & 7) == 0 && NC >= 1 && NC <= 256 && (256 % NC) == 0 &&
+                       blockDim.x == 256;
+  if (wide_ok) {
+    typedef typename row8<T>::raw raw;
+    float* mx = (float*)wide;
+    double* dn = (double*)(mx + kMaxWidth);
+    double* nm = dn + kMaxWidth;
+    const int t = threadIdx.x, QG = 256 / NC, c8 = 8 * (t % NC), q = t / NC;
+    const int64_t span = hi - lo - q;
+    const int64_t nt = span > 0 ? (span + QG - 1) / QG : 0;  // this thread's tokens
+    auto tok = [&](int64_t u) { return lo + q + (int64_t)QG * (u < nt ? u : nt - 1); };
+    float gm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gm[e] = -INFINITY;
+    for (int64_t u0 = 0; u0 < nt; u0 += TB) {
+      raw gr[TB];
+#pragma unroll
+      for (int k = 0; k < TB; ++k) gr[k] = row8<T>::ld(grow(tok(u0 + k)) + c8);
+#pragma unroll
+      for (int k = 0; k < TB; ++k)
+        if (u0 + k < nt)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gm[e] = fmaxf(gm[e], row8<T>::get(gr[k], e));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx[q * width + c8 + e] = gm[e];
+    __syncthreads();
+    double M[8], L[8], N[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = -INFINITY;
+      for (int k = 0; k < QG; ++k) v = fmaxf(v, mx[k * width + c8 + e]);
+      M[e] = v;
+      L[e] = 0.0;
+      N[e] = 0.0;
+    }
+    for (int64_t u0 = 0; u0 < nt; u0 += TB) {
+      raw gr[TB], vr[TB];
+#pragma unroll
+      for (int k = 0; k < TB; ++k) {
+        const int64_t sk = tok(u0 + k);
+        gr[k] = row8<T>::ld(grow(sk) + c8);
+        vr[k] = row8<T>::ld(vrow(sk) + c8);
+      }
+#pragma unroll
+      for (int k = 0; k < TB; ++k)
+        if (u0 + k < nt)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double ex = exp((double)row8<T>::get(gr[k], e) - M[e]);
+            L[e] += ex;
+            N[e] += ex * (double)row8<T>::get(vr[k], e);
+          }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dn[q * width + c8 + e] = L[e];
+      nm[q * width + c8 + e] = N[e];
+    }
+    __syncthreads();
+    for (int c = t; c < width; c += 256) {
+      double Lt = 0.0, Nt = 0.0;
+      for (int k = 0; k < QG; ++k) {
+        Lt += dn[k * width + c];
+        Nt += nm[k * width + c];
+      }
+      const double x = Nt / Lt;
+      pooled[c] = x;
+      ss += x * x;
+    }
+  } else
   for (int c = threadIdx.x; c < width; c += blockDim.x) {
     double gmax = -INFINITY;
-    for (int64_t s = lo; s < hi; ++s) {
-      const T* g = s >= p0 ? g_b + (s - p0) * width : sg_b + (int64_t)(s % Ls) * width;
-      gmax = fmax(gmax, (double)store_t<T>::ld(g + c));
+    for (int64_t s0 = lo; s0 < hi; s0 += TB) {
+      float gv[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) gv[u] = store_t<T>::ld(grow(min(s0 + u, hi - 1)) + c);
+#pragma unroll
+      for (int u = 0; u < TB; ++u)
+        if (s0 + u < hi) gmax = fmax(gmax, (double)gv[u]);
     }
     double num = 0.0, den = 0.0;
-    for (int64_t s = lo; s < hi; ++s) {
-      const T* g = s >= p0 ? g_b + (s - p0) * width : sg_b + (int64_t)(s % Ls) * width;
-      const T* v = s >= p0 ? kv_b + (s - p0) * width : skv_b + (int64_t)(s % Ls) * width;
-      const double e = exp((double)store_t<T>::ld(g + c) - gmax);
-      den += e;
-      num += e * (double)store_t<T>::ld(v + c);
+    for (int64_t s0 = lo; s0 < hi; s0 += TB) {
+      float gv[TB], vv[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int64_t sc = min(s0 + u, hi - 1);
+        gv[u] = store_t<T>::ld(grow(sc) + c);
+        vv[u] = store_t<T>::ld(vrow(sc) + c);
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        if (s0 + u < hi) {
+          const double e = exp((double)gv[u] - gmax);
+          den += e;
+          num += e * (double)vv[u];
+        }
+      }
     }
     const double x = num / den;
     pooled[c] = x;
@@ -339,14 +470,14 @@ __device__ __forceinline__ void compress_one_seq(
     const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
     float eps, T* __restrict__ st_kv, T* __restrict__ st_gate, T* __restrict__ pool,
     const Seqs& sq, int b, int width, int R, const Rope& base, int m, int overlap,
-    int64_t pool_cap, double* pooled, double* red) {
+    int64_t pool_cap, double* pooled, double* red, void* wide) {
   const int64_t p0 = sq.pos0[b];
   const int Ls = (1 + overlap) * m;
   const int64_t w = p0 / m;
   const int64_t r = sq.row(b, 0);
   if ((p0 + 1) % m == 0 && w < pool_cap)  // uniform per block
     pool_entry<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, b, p0, w, r,
-                  sq.prow(b, w, pool_cap), width, R, base, m, overlap, pooled, red);
+                  sq.prow(b, w, pool_cap), width, R, base, m, overlap, pooled, red, wide);
   const T* src_kv = kv + r * width;
   const T* src_g = gate + r * width;
   T* dk = st_kv + ((int64_t)b * Ls + p0 % Ls) * width;
@@ -364,10 +495,11 @@ __global__ void __launch_bounds__(256) compress_one_kernel(
     int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];
+  __shared__ __attribute__((aligned(16))) unsigned char wide[kPoolWideBytes];
   const int b = blockIdx.x;
   if (sq.len(b) == 0) return;  // a padding token: nothing to record
   compress_one_seq<T>(kv, gate, norm_w, eps, st_kv, st_gate, pool, sq, b, width, R, base, m,
-                      overlap, pool_cap, pooled, red);
+                      overlap, pool_cap, pooled, red, wide);
 }
 
 // The token's K=V row appended to sequence b's window ring (slot = position
@@ -407,16 +539,17 @@ __global__ void __launch_bounds__(256) cache_update_one_kernel(
     int Ri, Rope base, int m, int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
   __shared__ double red[256 / 64];
+  __shared__ __attribute__((aligned(16))) unsigned char wide[kPoolWideBytes];
   const int b = blockIdx.x;
   if (sq.len(b) == 0) return;  // a padding token: nothing to record
   if (blockIdx.y == 0)
     window_one_seq<T>(kv, ring, sq, b, D, R, base, cap, pooled);
   else if (blockIdx.y == 1)
     compress_one_seq<T>(ckv, cgate, norm_w, eps, st_kv, st_gate, pool, sq, b, D, R, base, m,
-                        overlap, pool_cap, pooled, red);
+                        overlap, pool_cap, pooled, red, wide);
   else
     compress_one_seq<T>(ikv, igate, inorm_w, eps, ist_kv, ist_gate, ipool, sq, b, Di, Ri, base,
-                        m, overlap, pool_cap, pooled, red);
+                        m, overlap, pool_cap, pooled, red, wide);
 }
 
 // Keep the raw rows of the last (1 + overlap) m positions for later calls.
