@@ -83,9 +83,15 @@ struct Seqs {
   __device__ __forceinline__ int64_t row(int b, int i) const {
     return cu ? (int64_t)cu[b] + i : (int64_t)b * n + i;
   }
+  // The block table is read through the constant address space: a lookup
+  // whose index is the same for the whole wave (a tile's first entry) then
+  // becomes a scalar load, waited for on the scalar counter instead of
+  // draining the LDS-DMA in flight (per-lane lookups stay vector loads).
+  // The table is not written while a kernel runs.
   __device__ __forceinline__ int64_t prow(int b, int64_t w, int64_t cap) const {
     if (!table) return (int64_t)b * cap + w;
-    const int64_t blk = table[(int64_t)b * tstride + (w >> bshift)];
+    typedef const __attribute__((address_space(4))) int32_t ctab;
+    const int64_t blk = ((ctab*)table)[(int64_t)b * tstride + (w >> bshift)];
     return (blk << bshift) + (w & (((int64_t)1 << bshift) - 1));
   }
 };
