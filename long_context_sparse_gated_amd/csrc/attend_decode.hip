@@ -159,6 +159,13 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
       const int e = r0 + tid + 256 * u - nwin;
       sel[u] = (csa && tid + 256 * u < nr && e >= 0) ? idx_row[e] : 0;
     }
+    // the rope table while the loads are in flight
+    for (int j = tid; j < R / 2; j += 256) {
+      double sn, c;
+      sincos((double)t * rope_freq(base, j, R), &sn, &c);
+      cs[j] = make_double2(c, sn);
+      csf[j] = make_float2((float)c, (float)sn);
+    }
     const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -177,12 +184,6 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
         rid[j] = id;
       }
     }
-  }
-  for (int j = tid; j < R / 2; j += 256) {
-    double sn, c;
-    sincos((double)t * rope_freq(base, j, R), &sn, &c);
-    cs[j] = make_double2(c, sn);
-    csf[j] = make_float2((float)c, (float)sn);
   }
   if (tid < 16) sinkl[tid] = sink_raw;  // scaled to log2 units at the end
   __syncthreads();

@@ -496,6 +496,14 @@ __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __rest
   if (i >= sq.len(b)) return;  // padding slot: no query
   const int64_t t = sq.pos0[b] + i;
   const int64_t tok = (int64_t)b * sq.n + i;  // the query's slot in the workspace
+  const int64_t off = tok * Hi * Di, qoff = sq.row(b, i) * Hi * Di;
+  const int chunks = Hi * Di / 8;
+  // the thread's first chunk is loaded before the rope table is computed, so
+  // that the two overlap (with 1024 threads and 64 x 128 channels, the only
+  // chunk)
+  const int e0 = threadIdx.x;
+  uint4 v0 = make_uint4(0, 0, 0, 0);
+  if (e0 < chunks) v0 = *(const uint4*)(q + qoff + (int64_t)e0 * 8);
   for (int j = threadIdx.x; j < kHBins; j += blockDim.x) hist[tok * kHBins + j] = 0u;
   for (int j = threadIdx.x; j < Ri / 2; j += blockDim.x) {
     double sn, c;
@@ -503,11 +511,9 @@ __global__ void __launch_bounds__(1024) rotate_queries_bf16(const bf16_t* __rest
     cs[j] = make_double2(c, sn);
   }
   __syncthreads();
-  const int64_t off = tok * Hi * Di, qoff = sq.row(b, i) * Hi * Di;
-  const int chunks = Hi * Di / 8;
-  for (int e = threadIdx.x; e < chunks; e += blockDim.x) {
+  for (int e = e0; e < chunks; e += blockDim.x) {
     const int d0 = (e * 8) % Di;
-    uint4 v = *(const uint4*)(q + qoff + (int64_t)e * 8);
+    const uint4 v = e == e0 ? v0 : *(const uint4*)(q + qoff + (int64_t)e * 8);
     *(uint4*)(qr + off + (int64_t)e * 8) = rope8_bf16(v, d0, Di, Ri, cs);
   }
 }
