@@ -522,39 +522,65 @@ __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
   const int b = (int)(tok / sq.n), i = (int)(tok % sq.n);
   if (i >= sq.len(b)) return;  // padding slot (block-uniform)
   const int64_t t = sq.pos0[b] + i;
+  const float* ph = part + (tok * nsplit * kAH + h) * kPart;  // split s at + s * kAH * kPart
+  // every lane's (m, l) of its splits and the sink are loaded first (one
+  // latency), the rope table is computed meanwhile
+  constexpr int KS = kMaxSplits / 64;  // splits per lane at most
+  float msv[KS], lsv[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int s = min(lane + 64 * k, nsplit - 1);  // clamped: masked below
+    msv[k] = ph[(int64_t)s * kAH * kPart + kAD];
+    lsv[k] = ph[(int64_t)s * kAH * kPart + kAD + 1];
+  }
+  const float sink_raw = sinks ? sinks[h] : 0.f;
   for (int j = threadIdx.x; j < R / 2; j += 64 * kMergeHeads) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
   }
-  const float sink = sinks ? sinks[h] * kLog2e : -INFINITY;
-  const float* ph = part + (tok * nsplit * kAH + h) * kPart;  // split s at + s * kAH * kPart
+  const float sink = sinks ? sink_raw * kLog2e : -INFINITY;
   float M = sink;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ph[(int64_t)s * kAH * kPart + kAD]);
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+    if (lane + 64 * k < nsplit) M = fmaxf(M, msv[k]);
   M = wave_max(M);
   float lt = 0.f;
-  for (int s = lane; s < nsplit; s += 64) {
-    const float* pr = ph + (int64_t)s * kAH * kPart;
-    const float ms = pr[kAD];
-    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    fs[hh][s] = f;
-    lt += f * pr[kAD + 1];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const int s = lane + 64 * k;
+    if (s < nsplit) {
+      const float f = msv[k] == -INFINITY ? 0.f : exp2f(msv[k] - M);
+      fs[hh][s] = f;
+      lt += f * lsv[k];
+    }
   }
   lt = wave_sum(lt);
   if (sinks) lt += exp2f(sink - M);
   __syncthreads();
   const int d0 = 8 * lane;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // a split without rows holds O = 0 and f = 0, so every split is summed
-#pragma unroll 4
-  for (int s = 0; s < nsplit; ++s) {
-    const float f = fs[hh][s];
-    const float* pr = ph + (int64_t)s * kAH * kPart + d0;
-    const f32x4 v0 = *(const f32x4*)pr, v1 = *(const f32x4*)(pr + 4);
+  // a split without rows holds O = 0 and f = 0, so every split is summed;
+  // eight splits' loads at a time are in flight (splits past the last
+  // re-read it with weight 0, which adds exact zeros)
+  constexpr int SB = 8;
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    f32x4 va[SB], vb[SB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] += f * v0[e];
-      o[4 + e] += f * v1[e];
+    for (int k = 0; k < SB; ++k) {
+      const float* pr = ph + (int64_t)min(s0 + k, nsplit - 1) * kAH * kPart + d0;
+      va[k] = *(const f32x4*)pr;
+      vb[k] = *(const f32x4*)(pr + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      const float f = s0 + k < nsplit ? fs[hh][s0 + k] : 0.f;
+      const f32x4 v0 = va[k], v1 = vb[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] += f * v0[e];
+        o[4 + e] += f * v1[e];
+      }
     }
   }
   const float inv = 1.f / lt;
