@@ -146,6 +146,18 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
   // gives two whole words.
   {
     const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
+    // pool rows of all the thread's entries first (with a block table these
+    // are loads: all in flight at once; entries that are not visible pool
+    // rows look up entry 0 and are not used)
+    int64_t prw[U];
+    bool vis[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jr = r0 + tid + NTH * u;
+      const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
+      vis[u] = w >= 0 && w < nvis;
+      prw[u] = sq.prow(b, vis[u] ? w : 0, pool_cap);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = tid + NTH * u;
@@ -156,8 +168,7 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
           const int v = lo_mod + jr;
           id = wb + (v >= cap ? v - cap : v);
         } else {
-          const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
-          id = (w < 0 || w >= nvis) ? -1 : (int)(-2 - sq.prow(b, w, pool_cap));
+          id = vis[u] ? (int)(-2 - prw[u]) : -1;
         }
         rid[j] = id;
       }

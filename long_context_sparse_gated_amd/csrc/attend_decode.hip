@@ -167,6 +167,18 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
       csf[j] = make_float2((float)c, (float)sn);
     }
     const int lo_mod = (int)(lo % win_cap), cap = (int)win_cap, wb = (int)((int64_t)b * win_cap);
+    // pool rows of all the thread's entries first (with a block table these
+    // are loads: all in flight at once; entries that are not visible pool
+    // rows look up entry 0 and are not used)
+    int64_t prw[U];
+    bool vis[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jr = r0 + tid + 256 * u;
+      const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
+      vis[u] = w >= 0 && w < nvis;
+      prw[u] = sq.prow(b, vis[u] ? w : 0, pool_cap);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = tid + 256 * u;
@@ -177,9 +189,8 @@ __global__ void __launch_bounds__(256, 1) attend_decode(
         } else if (jr < nwin) {
           const int v = lo_mod + jr;
           id = wb + (v >= cap ? v - cap : v);
-        } else {
-          const int64_t w = csa ? (int64_t)sel[u] : (int64_t)(jr - nwin);
-          if (w >= 0 && w < nvis) id = (int)(-2 - sq.prow(b, w, pool_cap));
+        } else if (vis[u]) {
+          id = (int)(-2 - prw[u]);
         }
         rid[j] = id;
       }
