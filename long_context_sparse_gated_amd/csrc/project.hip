@@ -38,11 +38,19 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_bf16(bf16_t* __restrict__ x,
   bf16_t* p = x + row * ld;
   double ss = 0.0;
   if constexpr (C > 0) {
+    // the row's chunks and their weights are all loaded before any is used
+    // (a weight load inside the scaling loop was waited for at each use)
     uint4 v[C];
+    float4 wa[C], wb[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int i = 8 * (lane + 64 * c);
       v[c] = i < n ? *(const uint4*)(p + i) : make_uint4(0, 0, 0, 0);
+      if (w) {
+        const int iw = i < n ? i : 0;
+        wa[c] = *(const float4*)(w + iw);
+        wb[c] = *(const float4*)(w + iw + 4);
+      }
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -68,8 +76,9 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_bf16(bf16_t* __restrict__ x,
         double a = (double)__uint_as_float(u[e] << 16) * r;
         double b = (double)__uint_as_float(u[e] & 0xffff0000u) * r;
         if (w) {
-          a *= (double)w[i + 2 * e];
-          b *= (double)w[i + 2 * e + 1];
+          const float4 wq = e < 2 ? wa[c] : wb[c];
+          a *= (double)((e & 1) ? wq.z : wq.x);
+          b *= (double)((e & 1) ? wq.w : wq.y);
         }
         o[e] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(b) << 16);
       }
@@ -95,7 +104,8 @@ static hipError_t launch_rmsnorm(bf16_t* x, int64_t nrows, int n, int64_t ld, co
   if (nrows <= 0 || n <= 0) return hipSuccess;
   const unsigned g = (unsigned)((nrows + 3) / 4);
   // the register path needs whole 16-byte chunks on 16-byte aligned rows
-  const bool vec = n % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x & 15u) == 0;
+  const bool vec = n % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x & 15u) == 0 &&
+                   ((uintptr_t)w & 15u) == 0;  // (null passes)
   const int c = vec ? (n + 511) / 512 : 0;
   if (c == 1)
     rmsnorm_rows_bf16<1><<<g, 256, 0, s>>>(x, nrows, n, ld, w, eps);
