@@ -359,14 +359,28 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
     rope_table();
     const int G = kCmpT / P, p = tid % P, g = tid / P;
     const bool act = g < G;
+    // the thread's tokens lo + g, lo + g + G, ... go eight at a time with
+    // unconditional loads (past the window: its last token again, masked
+    // out), so that eight share one latency instead of one each
+    typedef typename pair_t<T>::raw raw;
+    const int64_t span = hi - lo - g;
+    const int64_t nt = act && span > 0 ? (span + G - 1) / G : 0;
+    auto tk = [&](int64_t u) { return lo + g + (int64_t)G * (u < nt ? u : nt - 1); };
     double mx0 = -INFINITY, mx1 = -INFINITY;
-    if (act)
-      for (int64_t s = lo + g; s < hi; s += G) {
-        double a, c;
-        ld2<T>(row(g_b, sg_b, s) + 2 * p, a, c);
-        mx0 = fmax(mx0, a);
-        mx1 = fmax(mx1, c);
+    for (int64_t u0 = 0; u0 < nt; u0 += kTokReg) {
+      raw gq[kTokReg];
+#pragma unroll
+      for (int u = 0; u < kTokReg; ++u) gq[u] = pair_t<T>::ld(row(g_b, sg_b, tk(u0 + u)) + 2 * p);
+#pragma unroll
+      for (int u = 0; u < kTokReg; ++u) {
+        if (u0 + u < nt) {
+          double a, c;
+          pair_t<T>::cvt(gq[u], a, c);
+          mx0 = fmax(mx0, a);
+          mx1 = fmax(mx1, c);
+        }
       }
+    }
     pa[tid][0] = mx0;
     pa[tid][1] = mx1;
     __syncthreads();
@@ -376,17 +390,28 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
       M1 = fmax(M1, pa[p + k * P][1]);
     }
     double l0 = 0.0, l1 = 0.0, n0 = 0.0, n1 = 0.0;
-    if (act)
-      for (int64_t s = lo + g; s < hi; s += G) {
-        double ga, gc, va, vc;
-        ld2<T>(row(g_b, sg_b, s) + 2 * p, ga, gc);
-        ld2<T>(row(kv_b, skv_b, s) + 2 * p, va, vc);
-        const double e0 = exp(ga - M0), e1 = exp(gc - M1);
-        l0 += e0;
-        l1 += e1;
-        n0 += e0 * va;
-        n1 += e1 * vc;
+    for (int64_t u0 = 0; u0 < nt; u0 += kTokReg) {
+      raw gq[kTokReg], vq[kTokReg];
+#pragma unroll
+      for (int u = 0; u < kTokReg; ++u) {
+        const int64_t sk = tk(u0 + u);
+        gq[u] = pair_t<T>::ld(row(g_b, sg_b, sk) + 2 * p);
+        vq[u] = pair_t<T>::ld(row(kv_b, skv_b, sk) + 2 * p);
       }
+#pragma unroll
+      for (int u = 0; u < kTokReg; ++u) {
+        if (u0 + u < nt) {
+          double ga, gc, va, vc;
+          pair_t<T>::cvt(gq[u], ga, gc);
+          pair_t<T>::cvt(vq[u], va, vc);
+          const double e0 = exp(ga - M0), e1 = exp(gc - M1);
+          l0 += e0;
+          l1 += e1;
+          n0 += e0 * va;
+          n1 += e1 * vc;
+        }
+      }
+    }
     __syncthreads();  // the maxima are read
     pa[tid][0] = l0;
     pa[tid][1] = l1;
