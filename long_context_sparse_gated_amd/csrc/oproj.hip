@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32g(fa[s][mt], fb[s][nt], acc[mt][nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32g(fb[s][nt], fa[s][mt], acc[mt][nt]);
   };
   auto stage = [&](int kt, frags_t& fa, frags_t& fb, frags_t& na, frags_t& nb) {
     mfma_step(fa, fb, 0);
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
     const uint4* lb = lds[(kt + 1) & 3][1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc[i >> 2][i & 3] = mfma32g(fa[1][i >> 2], fb[1][i & 3], acc[i >> 2][i & 3]);
+      acc[i >> 2][i & 3] = mfma32g(fb[1][i & 3], fa[1][i >> 2], acc[i >> 2][i & 3]);
       const int st = i >> 3, t = (i >> 1) & 3;
       const int sl = (2 * st + h32) ^ fsw;
       if (i & 1)
@@ -192,61 +192,92 @@ __global__ void __launch_bounds__(256, 1) gemm_nt_bf16(
   }
   if (kt < nk) stage(kt, fa0, fb0, fa1, fb1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // Epilogue through LDS (free once every wave is past its last reads): each
-  // wave writes its 128 x 128 part as bf16 rows of 256 bytes into its own
-  // 32 KB, then reads 16-byte pieces back, 16 lanes per row, and stores them
-  // (four 256-byte row pieces per instruction instead of two 64-byte ones
-  // per 2-byte store).  Register v of tile (mt, nt) is row
-  // 8 (v / 4) + 4 h32 + v % 4, column l32.
+  // Epilogue through LDS, free once every wave is past its last reads.  The
+  // MFMAs take the B fragment as their first operand, so tile (mt, nt) holds
+  // C^T: register v of lane (l32, h32) is row 32 mt + l32 and column
+  // 32 nt + 8 (v / 4) + 4 h32 + v % 4 of the wave's part, four adjacent
+  // columns per group of four registers.  Each wave writes its 128 x 128
+  // part as bf16 rows of 256 bytes into its own 32 KB, 8 bytes per write,
+  // 16-byte chunk k of row r at slot k ^ (r & 15) (the 32 rows of one write
+  // spread over the banks); lane l then reads back columns 8 (l mod 16) ..
+  // +7 of rows l / 16 + 4 j and stores them, 256 contiguous bytes per 16
+  // lanes.  (Stores of the groups of four straight from the registers, 32
+  // rows of 16 bytes per instruction, made twice the memory requests and
+  // took the latent product of the producer projections from 0.83 to
+  // 1.54 ms, its rows being 64 KB apart.)
   __syncthreads();
-  bf16_t* st = (bf16_t*)&lds[0][0][0] + (size_t)wv * 128 * 128;
+  char* st = (char*)&lds[0][0][0] + (size_t)wv * 128 * 256;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt) {
+    char* sr = st + (32 * mt + l32) * 256 + 8 * h32;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * mt + 8 * (v / 4) + 4 * h32 + v % 4;
-        st[r * 128 + 32 * nt + l32] = f32_to_bf16(acc[mt][nt][v]);
-      }
-  const int rbase = m0 + 128 * wm, cbase = n0 + 128 * wn;
-#pragma unroll 4
-  for (int j = 0; j < 32; ++j) {
-    const int qd = lane + 64 * j, r = qd >> 4, c8 = (qd & 15) * 8;
-    const uint4 v = *(const uint4*)(st + r * 128 + c8);
-    const int row = rbase + r, col = cbase + c8;
-    if (row >= M || col >= N) continue;
-    bf16_t* cp = C + col;
-    int64_t cld = ldc;
-    int cend = N;  // first column past this output
-    if (kRouted) {
-      int sg = 0;
+      for (int i = 0; i < 4; ++i)
+        *(uint2*)(sr + (((4 * nt + i) ^ (l32 & 15)) << 4)) =
+            make_uint2(pack_bf16x2(acc[mt][nt][4 * i], acc[mt][nt][4 * i + 1]),
+                       pack_bf16x2(acc[mt][nt][4 * i + 2], acc[mt][nt][4 * i + 3]));
+  }
+  // The lane's columns are the same in every row it stores, so their output
+  // is found once, by selects over the map's (uniform) entries: indexing the
+  // map by a lane's segment number made the compiler load the entry from
+  // memory and wait for it before each store.
+  const int rbase = m0 + 128 * wm, c8 = (lane & 15) * 8, col = n0 + 128 * wn + c8;
+  bf16_t* cp;
+  int64_t cld = ldc;
+  int cend = N;  // first column past this output
+  if (!kRouted) {
+    cp = C + col;
+  } else {
+    bf16_t* sp = map.ptr[0];
+    int64_t sld = map.ld[0];
+    int sc0 = map.col0[0];
 #pragma unroll
-      for (int q = 1; q < kGemmOutMax; ++q)
-        if (q < map.nseg && map.col0[q] <= col) sg = q;
-      cp = map.ptr[sg] + (col - map.col0[sg]);
-      cld = map.ld[sg];
-      if (sg + 1 < map.nseg) cend = min(cend, map.col0[sg + 1]);
+    for (int q = 1; q < kGemmOutMax; ++q) {
+      const bool live = q < map.nseg;
+      const bool in = live && map.col0[q] <= col;
+      sp = in ? map.ptr[q] : sp;
+      sld = in ? map.ld[q] : sld;
+      sc0 = in ? map.col0[q] : sc0;
+      if (live && map.col0[q] > col) cend = min(cend, map.col0[q]);
     }
-    bf16_t* dst = cp + (int64_t)row * cld;
-    if (col + 7 < cend && ((uintptr_t)dst & 15u) == 0) {
-      *(uint4*)dst = v;
-    } else {
-      // edge of the matrix, of an output, or an unaligned row: one value at
-      // a time, each routed on its own
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    cp = sp + (col - sc0);
+    cld = sld;
+  }
+  // eight pieces are read from LDS before any is stored, so that the reads
+  // share one latency
+#pragma unroll 1
+  for (int j0 = 0; j0 < 32; j0 += 8) {
+    uint4 vv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ce = col + e;
-        if (ce >= N) break;
-        bf16_t* de = C + (int64_t)row * ldc + ce;
-        if (kRouted) {
-          int sg = 0;
-          for (int q = 1; q < map.nseg; ++q)
-            if (map.col0[q] <= ce) sg = q;
-          de = map.ptr[sg] + (int64_t)row * map.ld[sg] + (ce - map.col0[sg]);
+    for (int u = 0; u < 8; ++u) {
+      const int r = (lane >> 4) + 4 * (j0 + u);
+      vv[u] = *(const uint4*)(st + r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = rbase + (lane >> 4) + 4 * (j0 + u);
+      if (row >= M || col >= N) continue;
+      bf16_t* dst = cp + (int64_t)row * cld;
+      if (col + 7 < cend && ((uintptr_t)dst & 15u) == 0) {
+        *(uint4*)dst = vv[u];
+      } else {
+        // edge of the matrix, of an output, or an unaligned row: one value
+        // at a time, each routed on its own
+        const uint32_t w4[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ce = col + e;
+          if (ce >= N) break;
+          bf16_t* de = C + (int64_t)row * ldc + ce;
+          if (kRouted) {
+            int sg = 0;
+            for (int q = 1; q < map.nseg; ++q)
+              if (map.col0[q] <= ce) sg = q;
+            de = map.ptr[sg] + (int64_t)row * map.ld[sg] + (ce - map.col0[sg]);
+          }
+          *de = (bf16_t)(w4[e >> 1] >> (16 * (e & 1)));
         }
-        *de = (bf16_t)(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
   }
