@@ -116,6 +116,10 @@ struct GemmOut {
   int64_t ld[kGemmOutMax];
   int col0[kGemmOutMax];
   int nseg;
+  // 1 + the output whose rows are RMS-normalised per 512 columns (no
+  // weight) in the GEMM's epilogue, 0 for none; its eps
+  int norm_seg1;
+  double norm_eps;
 };
 
 hipError_t launch_gemm_nt_routed(const bf16_t* A, const bf16_t* B, int M, int N, int K,

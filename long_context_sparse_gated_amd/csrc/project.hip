@@ -148,9 +148,17 @@ hipError_t launch_project(int T, int hidden, int q_lora, int H, int D, int comp,
   col = 0;
   add(m2, col, q, H * D);
   add(m2, col, qi, Hi * Di);
+  // heads of 512 channels: q_b_norm in the product's epilogue (128 x 512
+  // tiles, one head per tile column, stored 16 bytes at a time), otherwise a
+  // pass of its own
+  const bool fused = q_head_norm && D == 512 && ((uintptr_t)q & 15u) == 0;
+  if (fused) {
+    m2.norm_seg1 = 1;
+    m2.norm_eps = (double)eps;
+  }
   e = launch_gemm_nt_routed(latent, w_q, T, col, q_lora, q_lora, q_lora, m2, s);
   if (e != hipSuccess) return e;
-  if (q_head_norm) e = launch_rmsnorm(q, (int64_t)T * H, D, D, nullptr, (double)eps, s);
+  if (q_head_norm && !fused) e = launch_rmsnorm(q, (int64_t)T * H, D, D, nullptr, (double)eps, s);
   return e;
 }
 

@@ -667,6 +667,10 @@ def _proj_check(got, ref, rows=None):
     (129, 128, 64, 2, 128, 0, 0, 0, False),      # sliding-only layer, no q_b_norm
     (1, 64, 32, 3, 32, 32, 0, 0, True),          # one token, compressor without indexer
     (77, 96, 32, 2, 36, 20, 12, 4, True),        # stream widths off 8-column pieces
+    (300, 128, 96, 3, 512, 32, 40, 3, True),     # heads of 512: q_b_norm in the product's
+                                                 # epilogue; ragged rows, q_I's 120 columns
+                                                 # a partial last tile
+    (65, 64, 32, 2, 512, 0, 0, 0, False),        # heads of 512 without q_b_norm
 ])
 def test_project_small(csa, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
     say(f"projections T={T} hidden={hidden} q_lora={q_lora} H={H} D={D} comp={comp} "
