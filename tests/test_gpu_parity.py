@@ -633,7 +633,7 @@ def test_output_projection_full_size_sampled(csa):
 # ----------------------------------------------------------------------------
 # producer projections
 
-def _proj_gpu(m, inp, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
+def _proj_gpu(m, inp, T, hidden, q_lora, H, D, comp, Di, Hi, qn, q_offset=0):
     import torch
     bf = torch.bfloat16
     shapes = {"q": (T, H, D), "kv": (T, D), "ckv": (T, comp), "cgate": (T, comp),
@@ -641,6 +641,9 @@ def _proj_gpu(m, inp, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
     outs = {k: torch.full(v, float("nan"), dtype=bf, device="cuda") for k, v in shapes.items()
             if (k in ("q", "kv")) or (k in ("ckv", "cgate") and comp) or
             (k in ("ikv", "igate", "qi", "wi") and Di)}
+    if q_offset:  # q as a contiguous view q_offset elements into its buffer
+        buf = torch.full((T * H * D + q_offset,), float("nan"), dtype=bf, device="cuda")
+        outs["q"] = buf[q_offset:].view(T, H, D)
     need = m.load_library().csa_project_workspace_bytes(
         m._CProj(T, hidden, q_lora, H, D, comp, Di, Hi, 1e-6, 1 if qn else 0))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
@@ -680,6 +683,19 @@ def test_project_small(csa, T, hidden, q_lora, H, D, comp, Di, Hi, qn):
     ref = O.project_inputs(to_f64(inp["x"]), to_f64(inp["w_x"]), inp["g_qa"], inp["g_kv"],
                            to_f64(inp["w_q"]), O.ProjSizes(q_lora, H, D, comp, Di, Hi), 1e-6,
                            qn, "bf16")
+    _proj_check(got, ref)
+
+
+def test_project_unaligned_q_heads_of_512(csa):
+    # q two bytes off a 16-byte boundary: the per-head norm cannot be fused
+    # into the product's 16-byte stores and runs as a pass of its own
+    T, hidden, q_lora, H, D, comp, Di, Hi = 130, 64, 32, 2, 512, 16, 24, 2
+    say(f"projections, q at a 2-byte offset, T={T} H={H} D={D}")
+    inp = synth.proj_inputs(T, hidden, q_lora, H, D, comp, Di, Hi, seed=11)
+    got = _proj_gpu(csa, inp, T, hidden, q_lora, H, D, comp, Di, Hi, True, q_offset=1)
+    ref = O.project_inputs(to_f64(inp["x"]), to_f64(inp["w_x"]), inp["g_qa"], inp["g_kv"],
+                           to_f64(inp["w_q"]), O.ProjSizes(q_lora, H, D, comp, Di, Hi), 1e-6,
+                           True, "bf16")
     _proj_check(got, ref)
 
 
