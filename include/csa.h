@@ -383,8 +383,10 @@ size_t csa_output_projection_workspace_bytes(const csa_oproj* p);
  *  latent = q_a_norm(x w_qa^T), kv = kv_norm(x w_kv^T), q = latent w_qb^T
  *  (then, with q_head_norm, each head divided by its RMS over D), the other
  *  streams plain products; every product and norm output is stored at bf16
- *  (float32 accumulation; the norms in float64 over the stored values,
- *  RMSNorm(y) = y / sqrt(mean(y^2) + eps) * g).
+ *  (float32 accumulation; the norms over the stored values, RMSNorm(y) =
+ *  y / sqrt(mean(y^2) + eps) * g, in float64, except q_head_norm on heads
+ *  of D = 512 with q 16-byte aligned: float32, inside the product's
+ *  epilogue, one bf16 unit at most from the float64 result).
  *  workspace >= csa_project_workspace_bytes(p) bytes (holds the latent).
  * Requires hidden and q_lora to be multiples of 32, every width to be >= 0
  * (q_lora, H, D >= 1), comp, D_I and H_I either all set or zero as the layer
