@@ -265,13 +265,17 @@ def prefill_leg(torch, m, name, steps, warmup, attn_events=False):
 
     # every step prefills the same sequence from position 0 (a prefill from 0
     # never reads the compressor state, so steps are identical)
+    # the caches' update (window append, the compressor of each stream) is
+    # one call, as in the layer step
+    istreams = {}
+    if spec.has_indexer:
+        istreams = dict(ikv=a["ikv"], igate=a["igate"], istate_kv=cache.istate_kv,
+                        istate_gate=cache.istate_gate, ipool=cache.ipool)
+
     def step(ev):
-        m.csa_window_append(L, pos0, 0, a["kv"], cache.ring)
-        m.csa_compress(L, pos0, 0, a["ckv"], a["cgate"], cache.cstate_kv, cache.cstate_gate,
-                       cache.pool, spec.rope_dim)
+        m.csa_cache_update(L, pos0, 0, a["kv"], cache.ring, a["ckv"], a["cgate"], cache.cstate_kv,
+                           cache.cstate_gate, cache.pool, **istreams)
         if spec.has_indexer:
-            m.csa_compress(L, pos0, 0, a["ikv"], a["igate"], cache.istate_kv,
-                           cache.istate_gate, cache.ipool, spec.index_rope_dim)
             m.csa_index_topk(L, pos0, 0, a["qi"], a["wi"], cache.ipool, idx, workspace=ws_i)
         if ev is not None:
             ev[0].record(stream)

@@ -14,6 +14,8 @@
 // float64 (exp, sums, norm, rotation) and each pooled value is rounded once
 // to the storage dtype.  The work is a few hundred bytes per entry channel
 // and is bound by reading kv and gate once from HBM.
+#include <type_traits>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -255,11 +257,33 @@ template <> struct pair_t<float> {
 // Tokens a thread of the register path holds (window of at most G * kTokReg).
 constexpr int kTokReg = 8;
 
+// One stream of a prefill compressor launch: its token rows, state slots,
+// pool, width and rope channels.  A launch takes up to two streams (main and
+// indexer, blockIdx.z), so the indexer's entries fill the chip beside the
+// main ones instead of waiting for a launch of their own.
+template <typename T> struct CmpStream {
+  const T* kv;
+  const T* gate;
+  const float* norm_w;
+  T* st_kv;
+  T* st_gate;
+  T* pool;
+  int width, R;
+};
+
 template <typename T>
-__global__ void __launch_bounds__(kCmpT) compress_entry_kernel(
-    const T* __restrict__ kv, const T* __restrict__ gate, const float* __restrict__ norm_w,
-    float eps, const T* __restrict__ st_kv, const T* __restrict__ st_gate, T* __restrict__ pool,
-    Seqs sq, int width, int R, Rope base, int m, int overlap, int64_t pool_cap) {
+__global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, CmpStream<T> s1,
+                                                                float eps, Seqs sq, Rope base,
+                                                                int m, int overlap,
+                                                                int64_t pool_cap) {
+  const CmpStream<T> cs = blockIdx.z ? s1 : s0;  // uniform
+  const T* __restrict__ kv = cs.kv;
+  const T* __restrict__ gate = cs.gate;
+  const float* __restrict__ norm_w = cs.norm_w;
+  const T* __restrict__ st_kv = cs.st_kv;
+  const T* __restrict__ st_gate = cs.st_gate;
+  T* __restrict__ pool = cs.pool;
+  const int width = cs.width, R = cs.R;
   __shared__ double pooled[kMaxWidth];
   __shared__ double pa[kCmpT][2], pb[kCmpT][2];
   __shared__ double red[kCmpT / 64];
@@ -581,11 +605,14 @@ __global__ void __launch_bounds__(256) cache_update_one_kernel(
 // Runs after compress_entry_kernel on the same stream (it overwrites slots that
 // kernel reads).
 template <typename T>
-__global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__ kv,
-                                                           const T* __restrict__ gate,
-                                                           T* __restrict__ st_kv,
-                                                           T* __restrict__ st_gate, Seqs sq,
-                                                           int width, int Ls) {
+__global__ void __launch_bounds__(256) state_update_kernel(CmpStream<T> s0, CmpStream<T> s1,
+                                                           Seqs sq, int Ls) {
+  const CmpStream<T> cs = blockIdx.z ? s1 : s0;  // uniform
+  const T* __restrict__ kv = cs.kv;
+  const T* __restrict__ gate = cs.gate;
+  T* __restrict__ st_kv = cs.st_kv;
+  T* __restrict__ st_gate = cs.st_gate;
+  const int width = cs.width;
   const int b = blockIdx.y;
   const int64_t p0 = sq.pos0[b];
   // the last Ls valid positions (padding rows are never kept)
@@ -604,11 +631,12 @@ __global__ void __launch_bounds__(256) state_update_kernel(const T* __restrict__
 hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_dim,
                            const void* kv, const void* gate, const float* norm_w, float eps,
                            void* st_kv, void* st_gate, void* pool, int64_t pool_cap,
-                           hipStream_t s) {
+                           hipStream_t s, const CmpArgs* second) {
   const int m = L.m, Ls = (1 + L.overlap) * m;
   const int max_entries = bt.n / m + 1;
   const Seqs sq = seqs_of(bt);
-  dim3 g1(max_entries, bt.B), g2(Ls, bt.B);
+  const unsigned ns = second ? 2 : 1;
+  dim3 g1(max_entries, bt.B, ns), g2(Ls, bt.B, ns);
   if (bt.n == 1) {
     if (L.dtype == 1)
       compress_one_kernel<bf16_t><<<bt.B, 256, 0, s>>>(
@@ -618,23 +646,32 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
       compress_one_kernel<float><<<bt.B, 256, 0, s>>>(
           (const float*)kv, (const float*)gate, norm_w, eps, (float*)st_kv, (float*)st_gate,
           (float*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !second) return e;
+    return launch_compress(L, bt, second->width, second->rope_dim, second->kv, second->gate,
+                           second->norm_w, eps, second->st_kv, second->st_gate, second->pool,
+                           pool_cap, s, nullptr);
   }
-  if (L.dtype == 1) {
-    compress_entry_kernel<bf16_t><<<g1, kCmpT, 0, s>>>(
-        (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (const bf16_t*)st_kv,
-        (const bf16_t*)st_gate, (bf16_t*)pool, sq, width, rope_dim, L.base, m, L.overlap,
-        pool_cap);
-    state_update_kernel<bf16_t><<<g2, 256, 0, s>>>((const bf16_t*)kv, (const bf16_t*)gate,
-                                                   (bf16_t*)st_kv, (bf16_t*)st_gate, sq, width,
-                                                   Ls);
-  } else {
-    compress_entry_kernel<float><<<g1, kCmpT, 0, s>>>(
-        (const float*)kv, (const float*)gate, norm_w, eps, (const float*)st_kv,
-        (const float*)st_gate, (float*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
-    state_update_kernel<float><<<g2, 256, 0, s>>>((const float*)kv, (const float*)gate,
-                                                  (float*)st_kv, (float*)st_gate, sq, width, Ls);
-  }
+  auto stream_of = [&](auto* tag, int w, int r, const void* k, const void* g, const float* nw,
+                       void* sk, void* sg, void* pl) {
+    typedef std::remove_pointer_t<decltype(tag)> T;
+    return CmpStream<T>{(const T*)k, (const T*)g, nw, (T*)sk, (T*)sg, (T*)pl, w, r};
+  };
+  auto launch = [&](auto* tag) {
+    typedef std::remove_pointer_t<decltype(tag)> T;
+    const CmpStream<T> a0 = stream_of(tag, width, rope_dim, kv, gate, norm_w, st_kv, st_gate, pool);
+    const CmpStream<T> a1 =
+        second ? stream_of(tag, second->width, second->rope_dim, second->kv, second->gate,
+                           second->norm_w, second->st_kv, second->st_gate, second->pool)
+               : a0;
+    compress_entry_kernel<T><<<g1, kCmpT, 0, s>>>(a0, a1, eps, sq, L.base, m, L.overlap,
+                                                  pool_cap);
+    state_update_kernel<T><<<g2, 256, 0, s>>>(a0, a1, sq, Ls);
+  };
+  if (L.dtype == 1)
+    launch((bf16_t*)nullptr);
+  else
+    launch((float*)nullptr);
   return hipGetLastError();
 }
 

@@ -140,9 +140,21 @@ hipError_t launch_window_append(const Layer& L, const Batch& b, const void* kv, 
 hipError_t launch_rope(const Layer& L, const Batch& b, void* x, int rows, int width, int rope_dim,
                        int sign, hipStream_t s);
 // compress.hip
+// A second stream of the same layer (the indexer's), pooled in the same
+// launches as the first.
+struct CmpArgs {
+  int width, rope_dim;
+  const void* kv;
+  const void* gate;
+  const float* norm_w;
+  void* st_kv;
+  void* st_gate;
+  void* pool;
+};
 hipError_t launch_compress(const Layer& L, const Batch& b, int width, int rope_dim, const void* kv,
                            const void* gate, const float* norm_w, float eps, void* st_kv,
-                           void* st_gate, void* pool, int64_t pool_cap, hipStream_t s);
+                           void* st_gate, void* pool, int64_t pool_cap, hipStream_t s,
+                           const CmpArgs* second = nullptr);
 // One launch for a decode step's cache updates: roles 1 (window), 2 (+ main
 // compressor) or 3 (+ indexer compressor) per sequence.
 hipError_t launch_cache_update_one(const Layer& L, const Batch& b, const void* kv, void* ring,
