@@ -211,13 +211,14 @@ __device__ __forceinline__ void pool_entry(
   }
 }
 
-// Prefill pooling, one 512-thread block per entry.  With P = width / 2
-// channel pairs below 512, thread (g, p) takes the pair (2p, 2p + 1) and the
-// window's tokens lo + g, lo + g + G, ... (G = 512 / P token groups): first
+// Prefill pooling, one block of NT threads per entry (NT = 256 for windows of
+// at most kTokReg tokens, else 512).  With P = width / 2 channel pairs, at
+// most NT, thread (g, p) takes the pair (2p, 2p + 1) and the window's tokens
+// lo + g, lo + g + G, ... (G = NT / P token groups): first
 // the per-channel window maximum (the groups' maxima merged through LDS), then
 // exp(gate - max) and the weighted sums over the same tokens (merged through
 // LDS).  These are the float64 terms of a serial pass, summed in another
-// order.  Wider rows take G = 1 and several pairs per thread.  Then the
+// order.  Wider rows take several pairs per thread.  Then the
 // optional RMSNorm over the entry and the rotation at position w m.
 constexpr int kCmpT = 512;
 
@@ -271,8 +272,8 @@ template <typename T> struct CmpStream {
   int width, R;
 };
 
-template <typename T>
-__global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, CmpStream<T> s1,
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) compress_entry_kernel(CmpStream<T> s0, CmpStream<T> s1,
                                                                 float eps, Seqs sq, Rope base,
                                                                 int m, int overlap,
                                                                 int64_t pool_cap) {
@@ -285,8 +286,8 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, 
   T* __restrict__ pool = cs.pool;
   const int width = cs.width, R = cs.R;
   __shared__ double pooled[kMaxWidth];
-  __shared__ double pa[kCmpT][2], pb[kCmpT][2];
-  __shared__ double red[kCmpT / 64];
+  __shared__ double pa[NT][2], pb[NT][2];
+  __shared__ double red[NT / 64];
   constexpr int kTab = 128;              // rope pairs kept in the table
   __shared__ double2 csr[kTab];          // (cos, sin) of the rope pairs at w m
   const int b = blockIdx.y;
@@ -307,18 +308,18 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, 
   const int P = width / 2;
   // the rope table of the entry, while the loads below are in flight
   auto rope_table = [&]() __attribute__((always_inline)) {
-    for (int j = tid; j < R / 2 && j < kTab; j += kCmpT) {
+    for (int j = tid; j < R / 2 && j < kTab; j += NT) {
       double sn, cs;
       sincos((double)(w * m) * rope_freq(base, j, R), &sn, &cs);
       csr[j] = make_double2(cs, sn);
     }
   };
-  if (P < kCmpT && hi - lo <= (int64_t)(kCmpT / P) * kTokReg) {
+  if (P <= NT && hi - lo <= (int64_t)(NT / P) * kTokReg) {
     // register path (windows of at most G * kTokReg tokens, e.g. the CSA
     // window of 8): every thread loads its tokens' gate and kv pairs once,
     // then the maximum and the sums come from registers
     typedef typename pair_t<T>::raw raw;
-    const int G = kCmpT / P, p = tid % P, g = tid / P;
+    const int G = NT / P, p = tid % P, g = tid / P;
     const bool act = g < G;
     raw gq[kTokReg], vq[kTokReg];
 #pragma unroll
@@ -379,9 +380,9 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, 
       pooled[2 * p] = N0 / L0;
       pooled[2 * p + 1] = N1 / L1;
     }
-  } else if (P < kCmpT) {
+  } else if (P <= NT) {
     rope_table();
-    const int G = kCmpT / P, p = tid % P, g = tid / P;
+    const int G = NT / P, p = tid % P, g = tid / P;
     const bool act = g < G;
     // the thread's tokens lo + g, lo + g + G, ... go eight at a time with
     // unconditional loads (past the window: its last token again, masked
@@ -455,7 +456,7 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, 
     }
   } else {
     rope_table();
-    for (int p = tid; p < P; p += kCmpT) {
+    for (int p = tid; p < P; p += NT) {
       double mx0 = -INFINITY, mx1 = -INFINITY;
       for (int64_t s = lo; s < hi; ++s) {
         double a, c;
@@ -481,19 +482,19 @@ __global__ void __launch_bounds__(kCmpT) compress_entry_kernel(CmpStream<T> s0, 
   __syncthreads();
   if (norm_w != nullptr) {
     double ss = 0.0;
-    for (int c = tid; c < width; c += kCmpT) ss += pooled[c] * pooled[c];
+    for (int c = tid; c < width; c += NT) ss += pooled[c] * pooled[c];
     ss = wave_sum64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     double tot = 0.0;
-    for (int k = 0; k < kCmpT / 64; ++k) tot += red[k];
+    for (int k = 0; k < NT / 64; ++k) tot += red[k];
     const double inv = 1.0 / sqrt(tot / (double)width + (double)eps);
-    for (int c = tid; c < width; c += kCmpT) pooled[c] = pooled[c] * inv * (double)norm_w[c];
+    for (int c = tid; c < width; c += NT) pooled[c] = pooled[c] * inv * (double)norm_w[c];
     __syncthreads();
   }
   T* dst = pool + sq.prow(b, w, pool_cap) * width;
-  for (int c = tid; c < width - R; c += kCmpT) store_t<T>::st64(dst + c, pooled[c]);
-  for (int j = tid; j < R / 2; j += kCmpT) {
+  for (int c = tid; c < width - R; c += NT) store_t<T>::st64(dst + c, pooled[c]);
+  for (int j = tid; j < R / 2; j += NT) {
     const int c = width - R + 2 * j;
     double cs, sn;
     if (j < kTab) {
@@ -664,8 +665,16 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
         second ? stream_of(tag, second->width, second->rope_dim, second->kv, second->gate,
                            second->norm_w, second->st_kv, second->st_gate, second->pool)
                : a0;
-    compress_entry_kernel<T><<<g1, kCmpT, 0, s>>>(a0, a1, eps, sq, L.base, m, L.overlap,
-                                                  pool_cap);
+    // windows that fit one thread's registers (the CSA window of 8) take
+    // 256-thread blocks, one channel pair per thread: twice the blocks
+    // resident per CU as with 512 threads, and no merge of token groups
+    if ((1 + L.overlap) * m <= kTokReg && width <= 512 &&
+        (!second || second->width <= 512))
+      compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, eps, sq, L.base, m, L.overlap,
+                                                       pool_cap);
+    else
+      compress_entry_kernel<T, kCmpT><<<g1, kCmpT, 0, s>>>(a0, a1, eps, sq, L.base, m,
+                                                           L.overlap, pool_cap);
     state_update_kernel<T><<<g2, 256, 0, s>>>(a0, a1, sq, Ls);
   };
   if (L.dtype == 1)
