@@ -293,15 +293,14 @@ csa_status csa_cache_update(const csa_layer* layer, const csa_batch* batch, cons
         L, b, kv, ring, win_cap, ckv, cgate, norm_weight, state_kv, state_gate, pool, ikv, igate,
         inorm_weight, istate_kv, istate_gate, ipool, pool_cap, norm_eps,
         index ? 3 : (main ? 2 : 1), stream));
-  hipError_t e = csa::launch_window_append(L, b, kv, ring, win_cap, stream);
-  if (e == hipSuccess && main) {
-    // both compressors' entries in one launch (and their state updates in
-    // another)
-    const csa::CmpArgs ix{L.Di, L.Ri, ikv, igate, inorm_weight, istate_kv, istate_gate, ipool};
-    e = csa::launch_compress(L, b, L.D, L.R, ckv, cgate, norm_weight, norm_eps, state_kv,
-                             state_gate, pool, pool_cap, stream, index ? &ix : nullptr);
-  }
-  return hip_status(e);
+  if (!main) return hip_status(csa::launch_window_append(L, b, kv, ring, win_cap, stream));
+  // the window append and both compressors' entries in one launch (and the
+  // compressors' state updates in another)
+  const csa::CmpArgs ix{L.Di, L.Ri, ikv, igate, inorm_weight, istate_kv, istate_gate, ipool};
+  const csa::WinArgs wa{kv, ring, win_cap};
+  return hip_status(csa::launch_compress(L, b, L.D, L.R, ckv, cgate, norm_weight, norm_eps,
+                                         state_kv, state_gate, pool, pool_cap, stream,
+                                         index ? &ix : nullptr, &wa));
 }
 
 csa_status csa_index_topk(const csa_layer* layer, const csa_batch* batch, const void* q_idx,

@@ -211,6 +211,76 @@ __device__ __forceinline__ void pool_entry(
   }
 }
 
+// Window ring append of a prefill call: a block takes kWaTok consecutive
+// tokens of one sequence; the channels before the rope slice are copied with
+// 16-byte moves where rows allow it, then each (token, pair) of the slice is
+// rotated by one thread at the token's position (pair j = (c, c+1),
+// c = D - R + 2j, times exp(i t base^(-2j/R)) [transformers PR 45616, RoPE
+// apply notes; DeepSeek-V4 model page, sec. 2.3]), in float64 and rounded
+// once, with the pair frequencies computed once per block (freq: R / 2
+// doubles of LDS).  Any block size; block-uniform control flow.
+constexpr int kWaTok = 8;
+
+template <typename T>
+__device__ __forceinline__ void window_block(const T* __restrict__ kv, T* __restrict__ ring,
+                                             const Seqs& sq, int D, int R, const Rope& base,
+                                             int64_t cap, double* freq, int i0, int b) {
+  // padding tokens of a variable-length call are not appended
+  const int nt = min(kWaTok, sq.len(b) - i0);
+  if (nt <= 0) return;  // block-uniform
+  const int64_t p0 = sq.pos0[b];
+  const int64_t r0 = sq.row(b, i0);  // the block's tokens sit in rows r0 .. r0 + nt - 1
+  for (int j = threadIdx.x; j < R / 2; j += blockDim.x) freq[j] = rope_freq(base, j, R);
+  const int plain = D - R;  // channels copied unchanged
+  constexpr int V = 16 / (int)sizeof(T);
+  if ((D % V) == 0 && (plain % V) == 0) {
+    const int per = plain / V;
+    for (int e = threadIdx.x; e < nt * per; e += blockDim.x) {
+      const int k = e / per, c = (e % per) * V;
+      const int64_t t = p0 + i0 + k;
+      *(uint4*)(ring + ((int64_t)b * cap + t % cap) * D + c) =
+          *(const uint4*)(kv + (r0 + k) * D + c);
+    }
+  } else {
+    for (int e = threadIdx.x; e < nt * plain; e += blockDim.x) {
+      const int k = e / plain, c = e % plain;
+      const int64_t t = p0 + i0 + k;
+      ring[((int64_t)b * cap + t % cap) * D + c] = kv[(r0 + k) * D + c];
+    }
+  }
+  __syncthreads();
+  const int np = R / 2;
+  for (int e = threadIdx.x; e < nt * np; e += blockDim.x) {
+    const int k = e / np, j = e % np, c = D - R + 2 * j;
+    const int64_t t = p0 + i0 + k;
+    const T* src = kv + (r0 + k) * D;
+    T* dst = ring + ((int64_t)b * cap + t % cap) * D;
+    double sn, cs;
+    sincos((double)t * freq[j], &sn, &cs);
+    double a = store_t<T>::ld(src + c), bb = store_t<T>::ld(src + c + 1);
+    rot64(a, bb, cs, sn);
+    store_t<T>::st64(dst + c, a);
+    store_t<T>::st64(dst + c + 1, bb);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) window_append_kernel(const T* __restrict__ kv,
+                                                            T* __restrict__ ring,
+                                                            Seqs sq, int D, int R, Rope base,
+                                                            int64_t cap) {
+  extern __shared__ double freq[];  // R / 2 pair frequencies
+  window_block<T>(kv, ring, sq, D, R, base, cap, freq, blockIdx.x * kWaTok, blockIdx.y);
+}
+
+// The window append beside a prefill compressor launch: its rows and ring.
+template <typename T> struct WinArgsT {
+  const T* kv;
+  T* ring;
+  int64_t cap;
+  int D, R;
+};
+
 // Prefill pooling, one block of NT threads per entry (NT = 256 for windows of
 // at most kTokReg tokens, else 512).  With P = width / 2 channel pairs, at
 // most NT, thread (g, p) takes the pair (2p, 2p + 1) and the window's tokens
@@ -274,9 +344,19 @@ template <typename T> struct CmpStream {
 
 template <typename T, int NT>
 __global__ void __launch_bounds__(NT) compress_entry_kernel(CmpStream<T> s0, CmpStream<T> s1,
-                                                                float eps, Seqs sq, Rope base,
-                                                                int m, int overlap,
-                                                                int64_t pool_cap) {
+                                                            WinArgsT<T> wa, int wz, float eps,
+                                                            Seqs sq, Rope base, int m,
+                                                            int overlap, int64_t pool_cap) {
+  __shared__ double pooled[kMaxWidth];
+  __shared__ double pa[NT][2], pb[NT][2];
+  __shared__ double red[NT / 64];
+  constexpr int kTab = 128;              // rope pairs kept in the table
+  __shared__ double2 csr[kTab];          // (cos, sin) of the rope pairs at w m
+  if ((int)blockIdx.z == wz) {  // the window append's blocks (block-uniform)
+    window_block<T>(wa.kv, wa.ring, sq, wa.D, wa.R, base, wa.cap, pooled, blockIdx.x * kWaTok,
+                    blockIdx.y);
+    return;
+  }
   const CmpStream<T> cs = blockIdx.z ? s1 : s0;  // uniform
   const T* __restrict__ kv = cs.kv;
   const T* __restrict__ gate = cs.gate;
@@ -285,11 +365,6 @@ __global__ void __launch_bounds__(NT) compress_entry_kernel(CmpStream<T> s0, Cmp
   const T* __restrict__ st_gate = cs.st_gate;
   T* __restrict__ pool = cs.pool;
   const int width = cs.width, R = cs.R;
-  __shared__ double pooled[kMaxWidth];
-  __shared__ double pa[NT][2], pb[NT][2];
-  __shared__ double red[NT / 64];
-  constexpr int kTab = 128;              // rope pairs kept in the table
-  __shared__ double2 csr[kTab];          // (cos, sin) of the rope pairs at w m
   const int b = blockIdx.y;
   const int64_t p0 = sq.pos0[b];
   const int64_t w = p0 / m + blockIdx.x;
@@ -629,16 +704,29 @@ __global__ void __launch_bounds__(256) state_update_kernel(CmpStream<T> s0, CmpS
   }
 }
 
+hipError_t launch_window_append(const Layer& L, const Batch& bt, const void* kv, void* ring,
+                                int64_t cap, hipStream_t s) {
+  dim3 grid((bt.n + kWaTok - 1) / kWaTok, bt.B);
+  const size_t shm = (size_t)(L.R / 2) * sizeof(double);
+  if (L.dtype == 1)
+    window_append_kernel<bf16_t><<<grid, 256, shm, s>>>((const bf16_t*)kv, (bf16_t*)ring,
+                                                        seqs_of(bt), L.D, L.R, L.base, cap);
+  else
+    window_append_kernel<float><<<grid, 256, shm, s>>>((const float*)kv, (float*)ring,
+                                                       seqs_of(bt), L.D, L.R, L.base, cap);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_dim,
                            const void* kv, const void* gate, const float* norm_w, float eps,
                            void* st_kv, void* st_gate, void* pool, int64_t pool_cap,
-                           hipStream_t s, const CmpArgs* second) {
+                           hipStream_t s, const CmpArgs* second, const WinArgs* win) {
   const int m = L.m, Ls = (1 + L.overlap) * m;
-  const int max_entries = bt.n / m + 1;
   const Seqs sq = seqs_of(bt);
-  const unsigned ns = second ? 2 : 1;
-  dim3 g1(max_entries, bt.B, ns), g2(Ls, bt.B, ns);
   if (bt.n == 1) {
+    hipError_t e = hipSuccess;
+    if (win) e = launch_window_append(L, bt, win->kv, win->ring, win->cap, s);
+    if (e != hipSuccess) return e;
     if (L.dtype == 1)
       compress_one_kernel<bf16_t><<<bt.B, 256, 0, s>>>(
           (const bf16_t*)kv, (const bf16_t*)gate, norm_w, eps, (bf16_t*)st_kv, (bf16_t*)st_gate,
@@ -647,12 +735,18 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
       compress_one_kernel<float><<<bt.B, 256, 0, s>>>(
           (const float*)kv, (const float*)gate, norm_w, eps, (float*)st_kv, (float*)st_gate,
           (float*)pool, sq, width, rope_dim, L.base, m, L.overlap, pool_cap);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || !second) return e;
     return launch_compress(L, bt, second->width, second->rope_dim, second->kv, second->gate,
                            second->norm_w, eps, second->st_kv, second->st_gate, second->pool,
-                           pool_cap, s, nullptr);
+                           pool_cap, s, nullptr, nullptr);
   }
+  // grid.z: the streams' entries (z = 0, 1), then the window append's
+  // blocks of kWaTok tokens (z = ns) if it comes along
+  const int ns = second ? 2 : 1;
+  const int max_entries = bt.n / m + 1;
+  const int wblocks = win ? (bt.n + kWaTok - 1) / kWaTok : 0;
+  dim3 g1(max(max_entries, wblocks), bt.B, ns + (win ? 1 : 0)), g2(Ls, bt.B, ns);
   auto stream_of = [&](auto* tag, int w, int r, const void* k, const void* g, const float* nw,
                        void* sk, void* sg, void* pl) {
     typedef std::remove_pointer_t<decltype(tag)> T;
@@ -665,15 +759,19 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
         second ? stream_of(tag, second->width, second->rope_dim, second->kv, second->gate,
                            second->norm_w, second->st_kv, second->st_gate, second->pool)
                : a0;
+    const WinArgsT<T> wa =
+        win ? WinArgsT<T>{(const T*)win->kv, (T*)win->ring, win->cap, L.D, L.R}
+            : WinArgsT<T>{nullptr, nullptr, 1, L.D, L.R};
+    const int wz = win ? ns : -1;
     // windows that fit one thread's registers (the CSA window of 8) take
     // 256-thread blocks, one channel pair per thread: twice the blocks
     // resident per CU as with 512 threads, and no merge of token groups
     if ((1 + L.overlap) * m <= kTokReg && width <= 512 &&
         (!second || second->width <= 512))
-      compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, eps, sq, L.base, m, L.overlap,
-                                                       pool_cap);
+      compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, wa, wz, eps, sq, L.base, m,
+                                                       L.overlap, pool_cap);
     else
-      compress_entry_kernel<T, kCmpT><<<g1, kCmpT, 0, s>>>(a0, a1, eps, sq, L.base, m,
+      compress_entry_kernel<T, kCmpT><<<g1, kCmpT, 0, s>>>(a0, a1, wa, wz, eps, sq, L.base, m,
                                                            L.overlap, pool_cap);
     state_update_kernel<T><<<g2, 256, 0, s>>>(a0, a1, sq, Ls);
   };

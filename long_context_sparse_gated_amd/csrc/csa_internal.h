@@ -151,10 +151,17 @@ struct CmpArgs {
   void* st_gate;
   void* pool;
 };
+// The window append of the same call (kv rows into the ring), in the same
+// launch as the compressors' entries.
+struct WinArgs {
+  const void* kv;
+  void* ring;
+  int64_t cap;
+};
 hipError_t launch_compress(const Layer& L, const Batch& b, int width, int rope_dim, const void* kv,
                            const void* gate, const float* norm_w, float eps, void* st_kv,
                            void* st_gate, void* pool, int64_t pool_cap, hipStream_t s,
-                           const CmpArgs* second = nullptr);
+                           const CmpArgs* second = nullptr, const WinArgs* win = nullptr);
 // One launch for a decode step's cache updates: roles 1 (window), 2 (+ main
 // compressor) or 3 (+ indexer compressor) per sequence.
 hipError_t launch_cache_update_one(const Layer& L, const Batch& b, const void* kv, void* ring,

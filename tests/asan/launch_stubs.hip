@@ -24,7 +24,7 @@ CSA_STUB(launch_window_append(const Layer&, const Batch&, const void*, void*, in
 CSA_STUB(launch_rope(const Layer&, const Batch&, void*, int, int, int, int, hipStream_t))
 CSA_STUB(launch_compress(const Layer&, const Batch&, int, int, const void*, const void*,
                          const float*, float, void*, void*, void*, int64_t, hipStream_t,
-                         const CmpArgs*))
+                         const CmpArgs*, const WinArgs*))
 CSA_STUB(launch_cache_update_one(const Layer&, const Batch&, const void*, void*, int64_t,
                                  const void*, const void*, const float*, void*, void*, void*,
                                  const void*, const void*, const float*, void*, void*, void*,
