@@ -741,6 +741,19 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
                            second->norm_w, eps, second->st_kv, second->st_gate, second->pool,
                            pool_cap, s, nullptr, nullptr);
   }
+  // windows that fit one thread's registers (the CSA window of 8) take
+  // 256-thread blocks, one channel pair per thread: twice the blocks
+  // resident per CU as with 512 threads, and no merge of token groups
+  const bool narrow = (1 + L.overlap) * m <= kTokReg && width <= 512 &&
+                      (!second || second->width <= 512);
+  // the window append joins the launch there; with HCA's few long entries
+  // its 8-token blocks would outnumber them 16 to 1 (one launch: 135-162
+  // us, two: 113-157), so it keeps its own launch
+  if (win && !narrow) {
+    const hipError_t e = launch_window_append(L, bt, win->kv, win->ring, win->cap, s);
+    if (e != hipSuccess) return e;
+    win = nullptr;
+  }
   // grid.z: the streams' entries (z = 0, 1), then the window append's
   // blocks of kWaTok tokens (z = ns) if it comes along
   const int ns = second ? 2 : 1;
@@ -763,11 +776,7 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
         win ? WinArgsT<T>{(const T*)win->kv, (T*)win->ring, win->cap, L.D, L.R}
             : WinArgsT<T>{nullptr, nullptr, 1, L.D, L.R};
     const int wz = win ? ns : -1;
-    // windows that fit one thread's registers (the CSA window of 8) take
-    // 256-thread blocks, one channel pair per thread: twice the blocks
-    // resident per CU as with 512 threads, and no merge of token groups
-    if ((1 + L.overlap) * m <= kTokReg && width <= 512 &&
-        (!second || second->width <= 512))
+    if (narrow)
       compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, wa, wz, eps, sq, L.base, m,
                                                        L.overlap, pool_cap);
     else
