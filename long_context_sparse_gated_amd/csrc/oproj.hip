@@ -15,11 +15,13 @@
 // gemm_nt_bf16: C[b][m, n] = sum_k A[b][m, k] B[b][n, k], all row-major
 // with k contiguous in A and B (a weight in (out, in) layout is B as it is),
 // bf16 inputs, float32 accumulation, bf16 output rounded to nearest even.
-// A block of four waves computes a 256 x 256 tile, each wave a 128 x 128
-// part as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs,
-// one wave per SIMD): per 16-deep step 16 MFMAs from eight 16-byte fragment
-// reads.  K advances 32 per stage; stages reach LDS by LDS-DMA into four
-// buffers.  One barrier per stage, between its two steps: after it the next
+// A block of four waves computes a 256 x 256 tile (or 128 x 512, the waves
+// side by side, where a row of 512 columns must stay in one block), each
+// wave a 128 x 128 part as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16
+// (accumulators in AGPRs, one wave per SIMD): per 16-deep step 16 MFMAs from
+// eight 16-byte fragment reads.  K advances 32 per stage; stages reach LDS
+// by LDS-DMA into four buffers.  One barrier per stage, between its two
+// steps: after it the next
 // stage is complete in LDS and the buffer just read is free, so the wave
 // issues the DMA four stages ahead into it and reads the next stage's
 // fragments while the second step's MFMAs run.
