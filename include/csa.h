@@ -107,7 +107,9 @@ typedef struct {
   int32_t n_new;            /* tokens per sequence in this call, >= 1          */
   const int64_t* pos0;      /* device [B]: position of each first new token    */
   int64_t pos0_max;         /* host: an upper bound of every pos0[b] (>= 0),
-                               used to validate capacities                     */
+                               used to validate capacities; 0 also lets a
+                               prefill's compressor state update run in the
+                               entries' launch (no entry reads the state)      */
   const int32_t* n_valid;   /* device [B] or NULL: variable-length calls.
                                Sequence b has n_valid[b] valid tokens (clamped
                                to 0 .. n_new), the first ones of its n_new

@@ -342,9 +342,34 @@ template <typename T> struct CmpStream {
   int width, R;
 };
 
+// Keep the raw rows of the last (1 + overlap) m = Ls positions of sequence b
+// for later calls: slot j of the block (j < Ls) copies one row of kv and
+// gate into the stream's state ring.  It overwrites slots the entries of the
+// same call read when the call starts past position 0, so it then runs after
+// them (its own launch); a call that starts at 0 reads no state and runs it
+// in the entries' launch.
+template <typename T>
+__device__ __forceinline__ void state_rows(const CmpStream<T>& cs, const Seqs& sq, int Ls, int j,
+                                           int b) {
+  const int width = cs.width;
+  const int64_t p0 = sq.pos0[b];
+  // the last Ls valid positions (padding rows are never kept)
+  const int64_t s = p0 + sq.len(b) - Ls + j;
+  if (j >= Ls || s < p0) return;
+  const T* src_kv = cs.kv + (sq.row(b, 0) + (s - p0)) * width;
+  const T* src_g = cs.gate + (sq.row(b, 0) + (s - p0)) * width;
+  T* dk = cs.st_kv + ((int64_t)b * Ls + (s % Ls)) * width;
+  T* dg = cs.st_gate + ((int64_t)b * Ls + (s % Ls)) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) {
+    dk[c] = src_kv[c];
+    dg[c] = src_g[c];
+  }
+}
+
 template <typename T, int NT>
 __global__ void __launch_bounds__(NT) compress_entry_kernel(CmpStream<T> s0, CmpStream<T> s1,
-                                                            WinArgsT<T> wa, int wz, float eps,
+                                                            WinArgsT<T> wa, int wz, int sz0,
+                                                            float eps,
                                                             Seqs sq, Rope base, int m,
                                                             int overlap, int64_t pool_cap) {
   __shared__ double pooled[kMaxWidth];
@@ -352,6 +377,10 @@ __global__ void __launch_bounds__(NT) compress_entry_kernel(CmpStream<T> s0, Cmp
   __shared__ double red[NT / 64];
   constexpr int kTab = 128;              // rope pairs kept in the table
   __shared__ double2 csr[kTab];          // (cos, sin) of the rope pairs at w m
+  if (sz0 >= 0 && (int)blockIdx.z >= sz0) {  // the state updates' blocks (block-uniform)
+    state_rows<T>((int)blockIdx.z == sz0 ? s0 : s1, sq, (1 + overlap) * m, blockIdx.x, blockIdx.y);
+    return;
+  }
   if ((int)blockIdx.z == wz) {  // the window append's blocks (block-uniform)
     window_block<T>(wa.kv, wa.ring, sq, wa.D, wa.R, base, wa.cap, pooled, blockIdx.x * kWaTok,
                     blockIdx.y);
@@ -677,31 +706,11 @@ __global__ void __launch_bounds__(256) cache_update_one_kernel(
                         m, overlap, pool_cap, pooled, red, wide);
 }
 
-// Keep the raw rows of the last (1 + overlap) m positions for later calls.
-// Runs after compress_entry_kernel on the same stream (it overwrites slots that
-// kernel reads).
+// The state update as a launch of its own, after the entries' launch.
 template <typename T>
 __global__ void __launch_bounds__(256) state_update_kernel(CmpStream<T> s0, CmpStream<T> s1,
                                                            Seqs sq, int Ls) {
-  const CmpStream<T> cs = blockIdx.z ? s1 : s0;  // uniform
-  const T* __restrict__ kv = cs.kv;
-  const T* __restrict__ gate = cs.gate;
-  T* __restrict__ st_kv = cs.st_kv;
-  T* __restrict__ st_gate = cs.st_gate;
-  const int width = cs.width;
-  const int b = blockIdx.y;
-  const int64_t p0 = sq.pos0[b];
-  // the last Ls valid positions (padding rows are never kept)
-  const int64_t s = p0 + sq.len(b) - Ls + blockIdx.x;
-  if (s < p0) return;
-  const T* src_kv = kv + (sq.row(b, 0) + (s - p0)) * width;
-  const T* src_g = gate + (sq.row(b, 0) + (s - p0)) * width;
-  T* dk = st_kv + ((int64_t)b * Ls + (s % Ls)) * width;
-  T* dg = st_gate + ((int64_t)b * Ls + (s % Ls)) * width;
-  for (int c = threadIdx.x; c < width; c += blockDim.x) {
-    dk[c] = src_kv[c];
-    dg[c] = src_g[c];
-  }
+  state_rows<T>(blockIdx.z ? s1 : s0, sq, Ls, blockIdx.x, blockIdx.y);
 }
 
 hipError_t launch_window_append(const Layer& L, const Batch& bt, const void* kv, void* ring,
@@ -759,7 +768,12 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
   const int ns = second ? 2 : 1;
   const int max_entries = bt.n / m + 1;
   const int wblocks = win ? (bt.n + kWaTok - 1) / kWaTok : 0;
-  dim3 g1(max(max_entries, wblocks), bt.B, ns + (win ? 1 : 0)), g2(Ls, bt.B, ns);
+  // a call from position 0 reads no state: the state updates join the
+  // launch (grid.z after the entries and the window append)
+  const bool fold_state = bt.pos0_max == 0;
+  const int nz = ns + (win ? 1 : 0);
+  dim3 g1(max(max(max_entries, wblocks), fold_state ? Ls : 0), bt.B, nz + (fold_state ? ns : 0));
+  dim3 g2(Ls, bt.B, ns);
   auto stream_of = [&](auto* tag, int w, int r, const void* k, const void* g, const float* nw,
                        void* sk, void* sg, void* pl) {
     typedef std::remove_pointer_t<decltype(tag)> T;
@@ -775,14 +789,14 @@ hipError_t launch_compress(const Layer& L, const Batch& bt, int width, int rope_
     const WinArgsT<T> wa =
         win ? WinArgsT<T>{(const T*)win->kv, (T*)win->ring, win->cap, L.D, L.R}
             : WinArgsT<T>{nullptr, nullptr, 1, L.D, L.R};
-    const int wz = win ? ns : -1;
+    const int wz = win ? ns : -1, sz0 = fold_state ? nz : -1;
     if (narrow)
-      compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, wa, wz, eps, sq, L.base, m,
+      compress_entry_kernel<T, 256><<<g1, 256, 0, s>>>(a0, a1, wa, wz, sz0, eps, sq, L.base, m,
                                                        L.overlap, pool_cap);
     else
-      compress_entry_kernel<T, kCmpT><<<g1, kCmpT, 0, s>>>(a0, a1, wa, wz, eps, sq, L.base, m,
-                                                           L.overlap, pool_cap);
-    state_update_kernel<T><<<g2, 256, 0, s>>>(a0, a1, sq, Ls);
+      compress_entry_kernel<T, kCmpT><<<g1, kCmpT, 0, s>>>(a0, a1, wa, wz, sz0, eps, sq, L.base,
+                                                           m, L.overlap, pool_cap);
+    if (!fold_state) state_update_kernel<T><<<g2, 256, 0, s>>>(a0, a1, sq, Ls);
   };
   if (L.dtype == 1)
     launch((bf16_t*)nullptr);
