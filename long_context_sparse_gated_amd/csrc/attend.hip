@@ -517,19 +517,23 @@ __global__ void __launch_bounds__(256, CSA_ATTN_MIN_BLOCKS) attend_mfma(
 }
 
 // Merge of split partials (m in log2 units, l, unnormalised O) with the sink,
-// then the -t rotation of the rope slice and the store.  One wave per
-// (token, head): lane s first reads split s's (m, l), then every lane merges
-// 8 channels over all splits.
-constexpr int kMergeHeads = 4;  // heads (waves) per merge block
+// then the -t rotation of the rope slice and the store.  One block of four
+// waves per (token, head), wave q merging channels 128 q .. 128 q + 127
+// (two per lane): lane s first reads split s's (m, l), then every lane sums
+// its two channels over all splits, sixteen splits' loads in flight at a
+// time.  (One wave per (token, head) over all 512 channels kept a quarter
+// of the CUs busy for the four tokens of a long-context decode step, with
+// 16 KB in flight per wave.)
+constexpr int kMergeQ = 4;  // waves (channel quarters) per merge block
 
-__global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
+__global__ void __launch_bounds__(64 * kMergeQ) attend_merge(
     const float* __restrict__ part, const float* __restrict__ sinks, bf16_t* __restrict__ out,
     Seqs sq, int R, Rope base, int nsplit) {
   __shared__ double2 cs[kAD / 2];
-  __shared__ float fs[kMergeHeads][kMaxSplits];
+  __shared__ float fs[kMergeQ][kMaxSplits];
   const int64_t tok = blockIdx.x;  // the token's slot b n + i (partials)
-  const int lane = threadIdx.x & 63, hh = threadIdx.x >> 6;
-  const int h = blockIdx.y * kMergeHeads + hh;
+  const int lane = threadIdx.x & 63, qd = threadIdx.x >> 6;
+  const int h = blockIdx.y;
   const int b = (int)(tok / sq.n), i = (int)(tok % sq.n);
   if (i >= sq.len(b)) return;  // padding slot (block-uniform)
   const int64_t t = sq.pos0[b] + i;
@@ -545,7 +549,7 @@ __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
     lsv[k] = ph[(int64_t)s * kAH * kPart + kAD + 1];
   }
   const float sink_raw = sinks ? sinks[h] : 0.f;
-  for (int j = threadIdx.x; j < R / 2; j += 64 * kMergeHeads) {
+  for (int j = threadIdx.x; j < R / 2; j += 64 * kMergeQ) {
     double sn, c;
     sincos((double)t * rope_freq(base, j, R), &sn, &c);
     cs[j] = make_double2(c, sn);
@@ -562,58 +566,42 @@ __global__ void __launch_bounds__(64 * kMergeHeads) attend_merge(
     const int s = lane + 64 * k;
     if (s < nsplit) {
       const float f = msv[k] == -INFINITY ? 0.f : exp2f(msv[k] - M);
-      fs[hh][s] = f;
+      fs[qd][s] = f;
       lt += f * lsv[k];
     }
   }
   lt = wave_sum(lt);
   if (sinks) lt += exp2f(sink - M);
   __syncthreads();
-  const int d0 = 8 * lane;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int d0 = 128 * qd + 2 * lane;
+  float o0 = 0.f, o1 = 0.f;
   // a split without rows holds O = 0 and f = 0, so every split is summed;
-  // eight splits' loads at a time are in flight (splits past the last
-  // re-read it with weight 0, which adds exact zeros)
-  constexpr int SB = 8;
+  // splits past the last re-read it with weight 0, which adds exact zeros
+  constexpr int SB = 16;
   for (int s0 = 0; s0 < nsplit; s0 += SB) {
-    f32x4 va[SB], vb[SB];
+    float2 v[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      v[k] = *(const float2*)(ph + (int64_t)min(s0 + k, nsplit - 1) * kAH * kPart + d0);
 #pragma unroll
     for (int k = 0; k < SB; ++k) {
-      const float* pr = ph + (int64_t)min(s0 + k, nsplit - 1) * kAH * kPart + d0;
-      va[k] = *(const f32x4*)pr;
-      vb[k] = *(const f32x4*)(pr + 4);
-    }
-#pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      const float f = s0 + k < nsplit ? fs[hh][s0 + k] : 0.f;
-      const f32x4 v0 = va[k], v1 = vb[k];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] += f * v0[e];
-        o[4 + e] += f * v1[e];
-      }
+      const float f = s0 + k < nsplit ? fs[qd][s0 + k] : 0.f;
+      o0 += f * v[k].x;
+      o1 += f * v[k].y;
     }
   }
   const float inv = 1.f / lt;
+  o0 *= inv;
+  o1 *= inv;
   const int first = kAD - R;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] *= inv;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    if (d0 + e >= first) {
-      const double2 c = cs[(d0 + e - first) >> 1];
-      const float cf = (float)c.x, sf = (float)c.y;
-      const float a = o[e] * cf + o[e + 1] * sf, bb = o[e + 1] * cf - o[e] * sf;
-      o[e] = a;
-      o[e + 1] = bb;
-    }
+  if (d0 >= first) {
+    const double2 c = cs[(d0 - first) >> 1];
+    const float cf = (float)c.x, sf = (float)c.y;
+    const float a = o0 * cf + o1 * sf, bb = o1 * cf - o0 * sf;
+    o0 = a;
+    o1 = bb;
   }
-  uint4 st;
-  st.x = pack_bf16x2(o[0], o[1]);
-  st.y = pack_bf16x2(o[2], o[3]);
-  st.z = pack_bf16x2(o[4], o[5]);
-  st.w = pack_bf16x2(o[6], o[7]);
-  *(uint4*)(out + (sq.row(b, i) * kAH + h) * kAD + d0) = st;
+  *(uint32_t*)(out + (sq.row(b, i) * kAH + h) * kAD + d0) = pack_bf16x2(o0, o1);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,7 +742,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
       hipError_t e = launch_attend_decode(L, bt, q, win, win_cap, pool, pool_cap, idx, sinks, out,
                                           ws, csa, ns, s);
       if (e != hipSuccess || ns == 1) return e;
-      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
+      attend_merge<<<dim3(bt.B * bt.n, kAH), 64 * kMergeQ, 0, s>>>(
           (const float*)ws, sinks, (bf16_t*)out, sq, L.R, L.base, ns);
       return hipGetLastError();
     }
@@ -774,7 +762,7 @@ hipError_t launch_attend(const Layer& L, const Batch& bt, const void* q, const v
     if (ns > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      attend_merge<<<dim3(bt.B * bt.n, kAH / kMergeHeads), 64 * kMergeHeads, 0, s>>>(
+      attend_merge<<<dim3(bt.B * bt.n, kAH), 64 * kMergeQ, 0, s>>>(
           (const float*)ws, sinks, (bf16_t*)out, sq, L.R, L.base, ns);
     }
     return hipGetLastError();
