@@ -86,6 +86,19 @@ def test_tiny_csa_layer_f32(csa):
         _check_csa_prefill(csa, w.layers[0], w, seed)
 
 
+def test_csa_layer_f32_medium(csa):
+    # float32 through the generic kernels beyond the tiny shape: 16 heads x 128
+    # (rope 32), window 64, indexer 8 x 64 (rope 32), top-32, S = 400 (no tile
+    # divides it), a sample of queries
+    import dataclasses
+    say("case: csa f32 H=16 D=128 W=64 S=400 (generic kernels)")
+    w = synth.workload("tiny_csa", S=400)
+    spec = dataclasses.replace(w.layers[0], num_heads=16, head_dim=128, rope_dim=32, window=64,
+                               index_heads=8, index_dim=64, index_rope_dim=32, topk=32)
+    w = dataclasses.replace(w, layers=[spec])
+    _check_csa_prefill(csa, spec, w, 4, queries_per_seq=[0, 3, 63, 64, 200, 255, 256, 399])
+
+
 def test_tiny_csa_layer_f32_peaked(csa):
     say("case: tiny_csa f32 peaked")
     w = synth.workload("tiny_csa", variant="peaked")
